@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                    [--only decode|prefill|q4|sweep]
+
+A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one batch of seeded
+synthetic input, with packed weights, activations and output already resident in HBM.  The
+headline workload is the decode GEMV on the Llama-3-8B up-projection shape (M=1, K=4096,
+N=14336, group-128 asymmetric format); its value is effective weight bytes (codes + scales +
+mins) per second.  To keep the 256 MB Infinity Cache from serving the weights, the steps rotate
+over enough packed copies to exceed 512 MB.  The K timed steps are captured once into a HIP
+graph (so host launch cost does not pace the GPU) and replayed; HIP events on the launch stream
+bracket the replay and give the average duration per launch used for the roofline.
+
+Prints ONE JSON line.  Secondary figures (prefill TFLOPS at M=1024 with a hipBLASLt bf16-weight
+GEMM beside it, the Q4 block-32 GEMV, the batch sweep) go under "extra".
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+CACHE_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache (MALL)
+METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1700)
+    ap.add_argument("--warmup", type=int, default=170)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep"], default=None,
+                    help="time one workload only (for profiler runs); prints its JSON line")
+    return ap.parse_args()
+
+
+class Setup:
+    """Packed weight copies, activations and output for one workload, resident on the GPU."""
+
+    def __init__(self, fmt, M, N, K, x_bits, W, copies):
+        import torch
+        import gemm_w4a16_amd as w
+        self.w, self.fmt, self.M, self.N, self.K = w, fmt, M, N, K
+        self.act = w.W4A16_BF16 if fmt == w.W4A16_FMT_G128_ASYM_BF16 else w.W4A16_FP16
+        Wd = torch.from_numpy(W).cuda()
+        base = w.alloc_packed(fmt, N, K)
+        w.w4a16_quantize_pack(fmt, Wd, N, K, *base)
+        del Wd
+        self.copies = [base] + [tuple(None if t is None else t.clone() for t in base) for _ in range(copies - 1)]
+        self.x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+        self.y = torch.empty((M, N), dtype=torch.int16, device="cuda")
+        self.ws, self.ws_bytes = w.alloc_workspace(fmt, M, N, K)
+        c, s, m = w.w4a16_packed_sizes(fmt, N, K)
+        self.weight_bytes = c + s + m
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        c, s, m = self.copies[i % len(self.copies)]
+        self.w.w4a16_matmul(self.fmt, self.act, self.x, self.M, c, s, m, self.N, self.K, self.y,
+                            self.ws, self.ws_bytes)
+
+
+def time_steps(setup: Setup, steps: int, warmup: int):
+    """W eager warmup steps, then EXACTLY `steps` steps captured in one HIP graph and replayed
+    once, bracketed by synchronize.  Returns (wall seconds, event seconds)."""
+    import torch
+    for i in range(warmup):
+        setup.step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            setup.step(i)
+    g.replay()  # untimed: first replay uploads the graph
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    g.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, start.elapsed_time(end) / 1e3
+
+
+def copies_for(weight_bytes: int) -> int:
+    return max(1, math.ceil(2 * CACHE_BYTES / weight_bytes))
+
+
+def bench_decode(steps, warmup):
+    import gemm_w4a16_amd as w
+    import workloads
+    wl = workloads.DECODE
+    W, x = workloads.inputs(wl)
+    c, s, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl.N, wl.K)
+    R = copies_for(c + s + m)
+    st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, R)
+    wall, ev = time_steps(st, steps, warmup)
+    algo_bytes = st.weight_bytes + wl.M * wl.K * 2 + wl.M * wl.N * 2
+    return wl, st, R, wall, ev, algo_bytes, W, x
+
+
+def bench_prefill(steps, warmup):
+    import torch
+    import gemm_w4a16_amd as w
+    import workloads
+    wl = workloads.PREFILL
+    W, x = workloads.inputs(wl)
+    st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, 1)
+    wall, ev = time_steps(st, steps, warmup)
+    flops = 2.0 * wl.M * wl.N * wl.K
+    # comparator: the same product with bf16 weights (the GPU's own dequantized weights) through
+    # torch.matmul (hipBLASLt)
+    Wb = torch.empty((wl.N, wl.K), dtype=torch.int16, device="cuda")
+    w.w4a16_dequant(w.W4A16_FMT_G128_ASYM_BF16, *st.copies[0], wl.N, wl.K, w.W4A16_BF16, Wb)
+    Wt = Wb.view(torch.bfloat16).t().contiguous()   # [K][N]
+    xb = st.x.view(torch.bfloat16)
+    for _ in range(5):
+        yb = torch.matmul(xb, Wt)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        yb = torch.matmul(xb, Wt)
+    e1.record()
+    torch.cuda.synchronize()
+    t_bf16 = e0.elapsed_time(e1) / 1e3 / steps
+    del Wb, Wt, yb
+    return {
+        "workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "steps": steps,
+        "us_per_step_wall": wall / steps * 1e6, "us_per_launch_events": ev / steps * 1e6,
+        "tflops": flops / (ev / steps) / 1e12,
+        "frac_mfma_bf16_peak": flops / (ev / steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "bf16_weight_gemm_hipblaslt_tflops": flops / t_bf16 / 1e12,
+        "bf16_weight_gemm_us": t_bf16 * 1e6,
+    }
+
+
+def bench_q4(steps, warmup):
+    import gemm_w4a16_amd as w
+    import workloads
+    wl = workloads.Q4
+    W, x = workloads.inputs(wl)
+    c, s, m = w.w4a16_packed_sizes(w.W4A16_FMT_Q4_B32_SYM_FP16, wl.N, wl.K)
+    R = copies_for(c + s + m)
+    st = Setup(w.W4A16_FMT_Q4_B32_SYM_FP16, wl.M, wl.N, wl.K, x, W, R)
+    del W
+    wall, ev = time_steps(st, steps, warmup)
+    return {
+        "workload": wl.name, "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R, "steps": steps,
+        "weight_bytes": st.weight_bytes, "us_per_launch_events": ev / steps * 1e6,
+        "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
+        "frac_hbm_peak": st.weight_bytes * steps / ev / 1e9 / HBM_PEAK_GBS,
+    }
+
+
+def bench_sweep(steps, warmup, W=None):
+    import gemm_w4a16_amd as w
+    import workloads
+    wl1 = workloads.DECODE
+    if W is None:
+        W = workloads.weights(wl1.N, wl1.K, wl1.outliers, wl1.seed_w)
+    c, s, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl1.N, wl1.K)
+    R = copies_for(c + s + m)
+    out = []
+    base = None
+    for M in workloads.SWEEP_MS:
+        wl = workloads.sweep(M)
+        x = workloads.activations(M, wl.K, "bf16", wl.seed_x, rows_drawn=max(workloads.SWEEP_MS))
+        st = Setup(w.W4A16_FMT_G128_ASYM_BF16, M, wl.N, wl.K, x, W, R if base is None else 1)
+        if base is None:
+            base = st.copies
+        else:
+            st.copies = base  # reuse the rotated weight copies
+        wall, ev = time_steps(st, steps, warmup)
+        t = ev / steps
+        out.append({"M": M, "path": "gemv" if M <= w.w4a16_matmul_gemv_cutoff() else "gemm",
+                    "us": t * 1e6, "effective_weight_gbs": st.weight_bytes / t / 1e9,
+                    "tflops": 2.0 * M * wl.N * wl.K / t / 1e12})
+    return out
+
+
+def cpu_baseline(W, x):
+    """The oracle as it stands (single-threaded C, fp64) on the full decode GEMV."""
+    import oracle
+    codes, scales, mins = oracle.quantize_g128(W)
+    weight_bytes = codes.nbytes + scales.nbytes + mins.nbytes
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or (time.perf_counter() - t_start < 10.0 and len(times) < 20):
+        t0 = time.perf_counter()
+        oracle.matmul_g128(x, codes, scales, mins)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": weight_bytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full decode GEMV (M=1, K=4096, N=14336) in fp64, {len(times)} runs, median "
+                      f"{t:.3f} s, on {platform.processor() or platform.machine()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        msg = (f"bench.py runs on one GPU only: --gpus {args.gpus} was asked for, but this build has no "
+               "multi-GPU path (the N-split and K-split shardings are described in DESIGN.md, not built).")
+        print(msg, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    import gemm_w4a16_amd as w  # fails loudly if libw4a16.so is missing
+    props = torch.cuda.get_device_properties(0)
+
+    if args.only and args.only != "decode":
+        fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep}[args.only]
+        print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
+        return
+
+    log(f"decode: {args.warmup} warmup + {args.steps} timed steps")
+    wl, st, R, wall, ev, algo_bytes, W, x = bench_decode(args.steps, args.warmup)
+    per_launch = ev / args.steps
+    value = st.weight_bytes * args.steps / wall / 1e9
+    achieved = algo_bytes / per_launch / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
+                   "format": "int4 codes, group 128 along K, bf16 scale + bf16 min",
+                   "weights": "N(0,0.02) fp32 with 0.1% x20 outliers, seed 0", "activations": "bf16 N(0,1)",
+                   "weight_copies_rotated": R, "weight_bytes": st.weight_bytes,
+                   "timing": "K steps in one HIP graph replay", "device": props.name,
+                   "compute_units": props.multi_processor_count,
+                   "frac_hbm_peak_effective_weight": value / HBM_PEAK_GBS},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_g128_kernel<1>", "us_per_launch": per_launch * 1e6,
+                     "algorithmic_bytes_per_launch": algo_bytes},
+    }
+    del st
+    torch.cuda.empty_cache()
+    if not args.no_extra and args.only is None:
+        extra = {}
+        log("prefill M=1024")
+        extra["prefill_m1024"] = bench_prefill(20, 3)
+        torch.cuda.empty_cache()
+        log("q4 block-32 GEMV")
+        extra["q4b32_m1"] = bench_q4(40, 4)
+        torch.cuda.empty_cache()
+        log("batch sweep")
+        extra["sweep"] = bench_sweep(34, 3, W)
+        torch.cuda.empty_cache()
+        line["extra"] = extra
+    if not args.no_cpu_baseline and args.only is None:
+        log("cpu baseline (oracle)")
+        line["cpu_baseline"] = cpu_baseline(W, x)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

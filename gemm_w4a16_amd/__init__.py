@@ -1,0 +1,160 @@
+"""Python binding of libw4a16 (MI355X / gfx950 W4A16 matmul).
+
+Argument marshalling only: every function below forwards to the C entry point of the same
+name in ``libw4a16.so`` (declared in ``include/w4a16.h``) and does no arithmetic of its own.
+PyTorch supplies device memory and the current HIP stream; nothing here falls back to torch or
+to the CPU.  If the library has not been built, importing this package fails with an error
+that says how to build it.
+
+Array arguments may be torch tensors (their ``data_ptr()`` is passed), plain integers (raw
+device pointers) or ``None`` (a NULL pointer).
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+_LIB_PATH = Path(__file__).resolve().parent / "libw4a16.so"
+
+W4A16_OK, W4A16_ERR_INVALID, W4A16_ERR_UNSUPPORTED, W4A16_ERR_DEVICE = 0, 1, 2, 3
+W4A16_FMT_G128_ASYM_BF16, W4A16_FMT_Q4_B32_SYM_FP16 = 0, 1
+W4A16_BF16, W4A16_FP16, W4A16_FP32 = 0, 1, 2
+
+# Every symbol include/w4a16.h declares.
+EXPORTED = (
+    "w4a16_status_string", "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant",
+    "w4a16_gemv", "w4a16_gemv_max_rows", "w4a16_gemm_workspace_bytes", "w4a16_gemm",
+    "w4a16_matmul", "w4a16_matmul_gemv_cutoff",
+)
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not _LIB_PATH.exists():
+        raise ImportError(f"{_LIB_PATH} is not built; run `python -m gemm_w4a16_amd.build` "
+                          "(hipcc for gfx950). There is no fallback path.")
+    L = ctypes.CDLL(str(_LIB_PATH))
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    L.w4a16_status_string.argtypes, L.w4a16_status_string.restype = [I], ctypes.c_char_p
+    L.w4a16_packed_sizes.argtypes = [I, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
+    L.w4a16_quantize_pack.argtypes = [I, P, I64, I64, P, P, P, P]
+    L.w4a16_dequant.argtypes = [I, P, P, P, I64, I64, I, P, P]
+    L.w4a16_gemv.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P]
+    L.w4a16_gemv_max_rows.argtypes, L.w4a16_gemv_max_rows.restype = [], I64
+    L.w4a16_gemm_workspace_bytes.argtypes, L.w4a16_gemm_workspace_bytes.restype = [I, I64, I64, I64], SZ
+    L.w4a16_gemm.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P, SZ, P]
+    L.w4a16_matmul.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P, SZ, P]
+    L.w4a16_matmul_gemv_cutoff.argtypes, L.w4a16_matmul_gemv_cutoff.restype = [], I64
+    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant", "w4a16_gemv",
+                 "w4a16_gemm", "w4a16_matmul"):
+        getattr(L, name).restype = I
+    return L
+
+
+lib = _load()
+library_path = str(_LIB_PATH)
+
+
+def _p(a):
+    """Device pointer of a torch tensor / raw int / None."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    return a.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ok(status: int, call: str) -> None:
+    if status != W4A16_OK:
+        raise W4A16Error(status, call)
+
+
+def status_string(status: int) -> str:
+    return lib.w4a16_status_string(int(status)).decode()
+
+
+w4a16_status_string = status_string
+
+
+def w4a16_packed_sizes(fmt: int, N: int, K: int):
+    c, s, m = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    _ok(lib.w4a16_packed_sizes(fmt, N, K, ctypes.byref(c), ctypes.byref(s), ctypes.byref(m)),
+        "w4a16_packed_sizes")
+    return c.value, s.value, m.value
+
+
+def w4a16_quantize_pack(fmt: int, W, N: int, K: int, codes, scales, mins, stream=None) -> None:
+    _ok(lib.w4a16_quantize_pack(fmt, _p(W), N, K, _p(codes), _p(scales), _p(mins), _stream(stream)),
+        "w4a16_quantize_pack")
+
+
+def w4a16_dequant(fmt: int, codes, scales, mins, N: int, K: int, out_dtype: int, W_hat, stream=None) -> None:
+    _ok(lib.w4a16_dequant(fmt, _p(codes), _p(scales), _p(mins), N, K, out_dtype, _p(W_hat), _stream(stream)),
+        "w4a16_dequant")
+
+
+def w4a16_gemv(fmt: int, act: int, x, M: int, codes, scales, mins, N: int, K: int, y, stream=None) -> None:
+    _ok(lib.w4a16_gemv(fmt, act, _p(x), M, _p(codes), _p(scales), _p(mins), N, K, _p(y), _stream(stream)),
+        "w4a16_gemv")
+
+
+def w4a16_gemv_max_rows() -> int:
+    return int(lib.w4a16_gemv_max_rows())
+
+
+def w4a16_gemm_workspace_bytes(fmt: int, M: int, N: int, K: int) -> int:
+    return int(lib.w4a16_gemm_workspace_bytes(fmt, M, N, K))
+
+
+def w4a16_gemm(fmt: int, act: int, x, M: int, codes, scales, mins, N: int, K: int, y, workspace=None,
+               workspace_bytes: int = 0, stream=None) -> None:
+    _ok(lib.w4a16_gemm(fmt, act, _p(x), M, _p(codes), _p(scales), _p(mins), N, K, _p(y), _p(workspace),
+                       workspace_bytes, _stream(stream)), "w4a16_gemm")
+
+
+def w4a16_matmul(fmt: int, act: int, x, M: int, codes, scales, mins, N: int, K: int, y, workspace=None,
+                 workspace_bytes: int = 0, stream=None) -> None:
+    _ok(lib.w4a16_matmul(fmt, act, _p(x), M, _p(codes), _p(scales), _p(mins), N, K, _p(y), _p(workspace),
+                         workspace_bytes, _stream(stream)), "w4a16_matmul")
+
+
+def w4a16_matmul_gemv_cutoff() -> int:
+    return int(lib.w4a16_matmul_gemv_cutoff())
+
+
+# ---- memory plumbing (torch allocations with the ABI's shapes and dtypes) ------------------------
+
+def alloc_packed(fmt: int, N: int, K: int, device="cuda"):
+    """Empty (codes, scales, mins) device tensors for an N x K weight (mins is None for Q4)."""
+    import torch
+    w4a16_packed_sizes(fmt, N, K)  # validates the shape
+    if fmt == W4A16_FMT_G128_ASYM_BF16:
+        return (torch.empty((K // 8, N), dtype=torch.int32, device=device),
+                torch.empty((K // 128, N), dtype=torch.int16, device=device),
+                torch.empty((K // 128, N), dtype=torch.int16, device=device))
+    return (torch.empty((N, K // 32, 16), dtype=torch.uint8, device=device),
+            torch.empty((N, K // 32), dtype=torch.int16, device=device),
+            None)
+
+
+def alloc_workspace(fmt: int, M: int, N: int, K: int, device="cuda"):
+    """(tensor or None, bytes) sized for w4a16_gemm / w4a16_matmul on this shape."""
+    import torch
+    nbytes = w4a16_gemm_workspace_bytes(fmt, M, N, K)
+    if nbytes == 0:
+        return None, 0
+    return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes

@@ -1,0 +1,72 @@
+"""Build libw4a16.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
+
+    python -m gemm_w4a16_amd.build          # or gemm_w4a16_amd.build.build()
+
+Flags that matter for the numerics:
+  -fhip-fp32-correctly-rounded-divide-sqrt  the quantizers use IEEE fp32 division
+  -fno-gpu-flush-denormals-to-zero          fp32 denormals are kept
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                                            no packed-fp32 (v_pk_*_f32) instructions are emitted
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+from pathlib import Path
+
+PKG = Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIB = PKG / "libw4a16.so"
+BUILD_DIR = PKG / "_build"
+ARCH = "gfx950"
+
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm.hip"]
+
+HIPCC_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
+    "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{ROOT / 'include'}", f"-I{CSRC}",
+]
+
+
+def hipcc() -> str:
+    path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(path):
+        raise RuntimeError("hipcc not found: the W4A16 HIP library cannot be built")
+    return path
+
+
+def _compile(src: str) -> Path:
+    obj = BUILD_DIR / (Path(src).stem + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
+    noise = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(noise))
+    if noise:
+        sys.stderr.write("\n".join(noise) + "\n")
+    return obj
+
+
+def build() -> Path:
+    """Compile every source (in parallel) and link libw4a16.so; always rebuilds."""
+    BUILD_DIR.mkdir(exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+    tmp = LIB.with_suffix(f".so.tmp{os.getpid()}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", str(tmp), *map(str, objs)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc link failed:\n" + res.stderr)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

@@ -1,0 +1,165 @@
+// api.hip -- the C ABI of libw4a16: argument validation, dispatch by M, launches.
+// Every check runs on the host before anything is enqueued; see include/w4a16.h for the
+// contract of each entry point.
+#include <algorithm>
+
+#include "../../include/w4a16.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kGroupG128 = 128;
+constexpr int64_t kBlockQ4 = 32;
+// Largest extents the kernels index with 32-bit ints (element offsets stay 64-bit).
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// M at and below which w4a16_matmul uses the GEMV path for G128 (from the batch sweep).
+constexpr int64_t kGemvCutoff = 4;
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t group_of(w4a16_format_t fmt) { return fmt == W4A16_FMT_G128_ASYM_BF16 ? kGroupG128 : kBlockQ4; }
+
+bool valid_format(w4a16_format_t fmt) {
+    return fmt == W4A16_FMT_G128_ASYM_BF16 || fmt == W4A16_FMT_Q4_B32_SYM_FP16;
+}
+
+w4a16_status_t check_shape(w4a16_format_t fmt, int64_t N, int64_t K) {
+    if (!valid_format(fmt)) return W4A16_ERR_INVALID;
+    if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return W4A16_ERR_INVALID;
+    if (K % group_of(fmt) != 0) return W4A16_ERR_INVALID;
+    return W4A16_OK;
+}
+
+// Packed weights: codes and scales always; mins for G128 only (must be NULL for Q4).
+w4a16_status_t check_packed(w4a16_format_t fmt, const void* codes, const void* scales, const void* mins) {
+    if (!aligned16(codes) || !aligned16(scales)) return W4A16_ERR_INVALID;
+    if (fmt == W4A16_FMT_G128_ASYM_BF16 && !aligned16(mins)) return W4A16_ERR_INVALID;
+    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 && mins != nullptr) return W4A16_ERR_INVALID;
+    return W4A16_OK;
+}
+
+w4a16_status_t check_act(w4a16_format_t fmt, w4a16_dtype_t act) {
+    if (act != W4A16_BF16 && act != W4A16_FP16 && act != W4A16_FP32) return W4A16_ERR_INVALID;
+    if (fmt == W4A16_FMT_G128_ASYM_BF16 && act != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
+    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 && act == W4A16_FP32) return W4A16_ERR_UNSUPPORTED;
+    return W4A16_OK;
+}
+
+w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_DEVICE; }
+
+w4a16_status_t check_matmul_common(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                                   const void* codes, const void* scales, const void* mins, int64_t N, int64_t K,
+                                   const void* y) {
+    w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    if (M <= 0 || M > kMaxDim) return W4A16_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(y)) return W4A16_ERR_INVALID;
+    st = check_packed(fmt, codes, scales, mins);
+    if (st != W4A16_OK) return st;
+    return check_act(fmt, act);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a16_status_string(w4a16_status_t status) {
+    switch (status) {
+        case W4A16_OK: return "ok";
+        case W4A16_ERR_INVALID: return "invalid argument";
+        case W4A16_ERR_UNSUPPORTED: return "unsupported combination";
+        case W4A16_ERR_DEVICE: return "HIP launch error";
+    }
+    return "unknown status";
+}
+
+w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K, size_t* codes_bytes,
+                                  size_t* scales_bytes, size_t* mins_bytes) {
+    const w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    const size_t codes = (size_t)N * (size_t)K / 2;  // 4 bits per weight in both formats
+    const size_t scales = (size_t)N * (size_t)(K / group_of(fmt)) * 2;
+    const size_t mins = fmt == W4A16_FMT_G128_ASYM_BF16 ? scales : 0;
+    if (codes_bytes) *codes_bytes = codes;
+    if (scales_bytes) *scales_bytes = scales;
+    if (mins_bytes) *mins_bytes = mins;
+    return W4A16_OK;
+}
+
+w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N, int64_t K, void* codes,
+                                   void* scales, void* mins, hipStream_t stream) {
+    w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(W)) return W4A16_ERR_INVALID;
+    st = check_packed(fmt, codes, scales, mins);
+    if (st != W4A16_OK) return st;
+    if (fmt == W4A16_FMT_G128_ASYM_BF16)
+        return from_hip(w4a16::launch_pack_g128(W, N, K, static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
+                                                static_cast<uint16_t*>(mins), stream));
+    return from_hip(w4a16::launch_pack_q4b32(W, N, K, static_cast<uint8_t*>(codes), static_cast<uint16_t*>(scales),
+                                             stream));
+}
+
+w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* scales, const void* mins, int64_t N,
+                             int64_t K, w4a16_dtype_t out_dtype, void* W_hat, hipStream_t stream) {
+    w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    st = check_packed(fmt, codes, scales, mins);
+    if (st != W4A16_OK) return st;
+    if (!aligned16(W_hat)) return W4A16_ERR_INVALID;
+    if (out_dtype != W4A16_BF16 && out_dtype != W4A16_FP16 && out_dtype != W4A16_FP32) return W4A16_ERR_INVALID;
+    const int dt = (int)out_dtype;
+    if (fmt == W4A16_FMT_G128_ASYM_BF16)
+        return from_hip(w4a16::launch_dequant_g128(static_cast<const uint32_t*>(codes),
+                                                   static_cast<const uint16_t*>(scales),
+                                                   static_cast<const uint16_t*>(mins), N, K, dt, W_hat, stream));
+    return from_hip(w4a16::launch_dequant_q4b32(static_cast<const uint8_t*>(codes),
+                                                static_cast<const uint16_t*>(scales), N, K, dt, W_hat, stream));
+}
+
+int64_t w4a16_gemv_max_rows(void) { return w4a16::kGemvMaxRows; }
+
+int64_t w4a16_matmul_gemv_cutoff(void) { return kGemvCutoff; }
+
+w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
+                          const void* scales, const void* mins, int64_t N, int64_t K, void* y, hipStream_t stream) {
+    const w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
+    if (st != W4A16_OK) return st;
+    if (M > w4a16::kGemvMaxRows) return W4A16_ERR_UNSUPPORTED;
+    if (fmt == W4A16_FMT_G128_ASYM_BF16)
+        return from_hip(w4a16::launch_gemv_g128(static_cast<const uint16_t*>(x), M, static_cast<const uint32_t*>(codes),
+                                                static_cast<const uint16_t*>(scales),
+                                                static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
+                                                stream));
+    return from_hip(w4a16::launch_gemv_q4b32(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
+                                             static_cast<const uint8_t*>(codes), static_cast<const uint16_t*>(scales),
+                                             N, K, static_cast<uint16_t*>(y), stream));
+}
+
+size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K) {
+    if (fmt != W4A16_FMT_G128_ASYM_BF16 || check_shape(fmt, N, K) != W4A16_OK || M <= 0 || M > kMaxDim) return 0;
+    return w4a16::gemm_g128_workspace_bytes(M, N, K);
+}
+
+w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
+                          const void* scales, const void* mins, int64_t N, int64_t K, void* y, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+    const w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
+    if (st != W4A16_OK) return st;
+    if (fmt != W4A16_FMT_G128_ASYM_BF16) return W4A16_ERR_UNSUPPORTED;
+    const size_t need = w4a16::gemm_g128_workspace_bytes(M, N, K);
+    if (need > 0 && (workspace_bytes < need || !aligned16(workspace))) return W4A16_ERR_INVALID;
+    return from_hip(w4a16::launch_gemm_g128(static_cast<const uint16_t*>(x), M, static_cast<const uint32_t*>(codes),
+                                            static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(mins),
+                                            N, K, static_cast<uint16_t*>(y), static_cast<float*>(workspace), stream));
+}
+
+w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
+                            const void* scales, const void* mins, int64_t N, int64_t K, void* y, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 || (M > 0 && M <= kGemvCutoff))
+        return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
+    return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"

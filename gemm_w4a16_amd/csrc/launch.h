@@ -1,0 +1,35 @@
+// launch.h -- internal host-side launchers of the libw4a16 kernels (not part of the C ABI).
+// Each returns hipSuccess or the HIP error of the launch; arguments are validated by the
+// C-ABI layer before these are called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+hipError_t launch_pack_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,
+                            uint16_t* mins, hipStream_t stream);
+hipError_t launch_pack_q4b32(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales,
+                             hipStream_t stream);
+// dtype: 0 bf16, 1 fp16, 2 fp32
+hipError_t launch_dequant_g128(const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N,
+                               int64_t K, int dtype, void* out, hipStream_t stream);
+hipError_t launch_dequant_q4b32(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, int dtype,
+                                void* out, hipStream_t stream);
+
+// Small-M G128 path, bf16 activations, M <= kGemvMaxRows.
+constexpr int kGemvMaxRows = 4;
+hipError_t launch_gemv_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+// Q4 path, one activation row per pass; act_f16: fp16 (true) or bf16 (false) activations.
+hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
+                             const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+
+// Large-M G128 path on bf16 MFMA.
+size_t gemm_g128_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace,
+                            hipStream_t stream);
+
+}  // namespace w4a16

@@ -1,0 +1,197 @@
+// pack.hip -- quantize/pack and reference dequant kernels for both weight formats.
+//
+// G128 (vidyal.ai "Low-Precision Kernels", Step 2): per (column n, group of 128 k):
+//   lo/hi = min/max (a zero taken as +0), s = (hi - lo)/15 in fp32, s_b = bf16(s) (1.0 if 0),
+//   m_b = bf16(lo), q = clamp(rint((w - m_b)/s_b), 0, 15), eight codes per word along k with
+//   k = 8r in the lowest nibble, words stored [K/8][N].
+// Q4B32 (thuongvuho.com "Why My 4-Bit CUDA Kernel Wasn't Faster", introduction and "Loading the
+//   same bytes differently"): per (row n, block of 32 k): s = max|w|/7, s_h = fp16(s) (1.0 if
+//   0), q = clamp(rint(w/s_h) + 8, 0, 15), byte j = q[2j] | q[2j+1] << 4.
+//
+// The arithmetic is IEEE fp32 with a correctly rounded divide (-fhip-fp32-correctly-rounded-
+// divide-sqrt), rint = round-half-to-even, and no expression here is eligible for FMA
+// contraction, so the codes are bit-identical to any other IEEE implementation of the rule.
+#include "device_common.h"
+#include "launch.h"
+
+namespace w4a16 {
+
+// ---- G128 quantize/pack -------------------------------------------------------------------
+// Block: 256 threads = 64 columns x 4 quarters of a 128-k group; grid (ceil(N/64), K/128).
+// Thread (c, p) reads W[n][128g + 32p .. +31] (8 x 16-byte loads), the 4 quarters of a column
+// combine their min/max with two lane swaps, then each thread writes the 4 words of its
+// quarter: packed rows 16g + 4p + i, column n.
+__global__ __launch_bounds__(256) void pack_g128_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                        uint32_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                        uint16_t* __restrict__ mins) {
+    const int c = threadIdx.x >> 2, p = threadIdx.x & 3;
+    const int64_t n = (int64_t)blockIdx.x * 64 + c;
+    const int64_t g = blockIdx.y;
+    const bool live = n < N;
+    const int64_t nr = live ? n : N - 1;  // clamped row for the loads; dead lanes store nothing
+    const float4* src = reinterpret_cast<const float4*>(W + nr * K + g * 128 + p * 32);
+    float w[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float4 v = src[i];
+        w[4 * i] = v.x;
+        w[4 * i + 1] = v.y;
+        w[4 * i + 2] = v.z;
+        w[4 * i + 3] = v.w;
+    }
+    float lo = w[0], hi = w[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+        lo = fminf(lo, w[j]);
+        hi = fmaxf(hi, w[j]);
+    }
+    lo = fminf(lo, __shfl_xor(lo, 1));
+    hi = fmaxf(hi, __shfl_xor(hi, 1));
+    lo = fminf(lo, __shfl_xor(lo, 2));
+    hi = fmaxf(hi, __shfl_xor(hi, 2));
+    if (lo == 0.0f) lo = 0.0f;  // -0 -> +0
+    if (hi == 0.0f) hi = 0.0f;
+    const float s = (hi - lo) / 15.0f;
+    uint16_t s_b = f32_to_bf16_bits(s);
+    if (bf16_bits_to_f32(s_b) == 0.0f) s_b = 0x3F80;
+    const uint16_t m_b = f32_to_bf16_bits(lo);
+    const float sf = bf16_bits_to_f32(s_b), mf = bf16_bits_to_f32(m_b);
+    if (!live) return;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float t = __builtin_rintf((w[8 * i + j] - mf) / sf);
+            const uint32_t q = t < 0.0f ? 0u : (t > 15.0f ? 15u : (uint32_t)t);
+            word |= q << (4 * j);
+        }
+        codes[(g * 16 + p * 4 + i) * N + n] = word;
+    }
+    if (p == 0) {
+        scales[g * N + n] = s_b;
+        mins[g * N + n] = m_b;
+    }
+}
+
+// ---- Q4B32 quantize/pack ------------------------------------------------------------------
+// One thread per (row, block of 32); consecutive threads take consecutive blocks of a row, so
+// the 128-byte reads and the 16-byte code stores are contiguous across the wave.
+__global__ __launch_bounds__(256) void pack_q4b32_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                         uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+    const int64_t B = K / 32;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= N * B) return;
+    const float4* src = reinterpret_cast<const float4*>(W + i * 32);  // row n, block b = i / B, i % B
+    float w[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float4 v = src[j];
+        w[4 * j] = v.x;
+        w[4 * j + 1] = v.y;
+        w[4 * j + 2] = v.z;
+        w[4 * j + 3] = v.w;
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(w[j]));
+    const float s = a / 7.0f;
+    uint16_t s_h = f32_to_f16_bits(s);
+    if (f16_bits_to_f32(s_h) == 0.0f) s_h = 0x3C00;
+    const float sf = f16_bits_to_f32(s_h);
+    uint32_t out[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float t = __builtin_rintf(w[8 * d + j] / sf) + 8.0f;
+            const uint32_t q = t < 0.0f ? 0u : (t > 15.0f ? 15u : (uint32_t)t);
+            word |= q << (4 * j);  // k = 8d + j: byte j/2, low nibble for even j
+        }
+        out[d] = word;
+    }
+    *reinterpret_cast<uint4*>(codes + i * 16) = make_uint4(out[0], out[1], out[2], out[3]);
+    scales[i] = s_h;
+}
+
+// ---- reference dequant ----------------------------------------------------------------------
+// Eight fp32 values -> out[idx .. idx+7] as bf16 (dtype 0), fp16 (1) or fp32 (2), each rounded
+// to nearest even.
+__device__ __forceinline__ void store8(void* out, int64_t idx, const float* v, int dtype) {
+    if (dtype == 2) {  // fp32
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(out) + idx);
+        o[0] = make_float4(v[0], v[1], v[2], v[3]);
+        o[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else {
+        uint32_t p[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            p[j] = dtype == 0 ? pack2_bf16(v[2 * j], v[2 * j + 1])
+                              : ((uint32_t)f32_to_f16_bits(v[2 * j]) | ((uint32_t)f32_to_f16_bits(v[2 * j + 1]) << 16));
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + idx) = make_uint4(p[0], p[1], p[2], p[3]);
+    }
+}
+
+// One thread per packed word (r, n): w_hat[n][8r .. 8r+7] = fmaf(q, s_b, m_b), then rounded.
+__global__ __launch_bounds__(256) void dequant_g128_kernel(const uint32_t* __restrict__ codes,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint16_t* __restrict__ mins, int64_t N, int64_t K,
+                                                           int dtype, void* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (K / 8) * N) return;
+    const int64_t r = i / N, n = i % N;
+    const uint32_t word = codes[i];
+    const float s = bf16_bits_to_f32(scales[(r / 16) * N + n]);
+    const float m = bf16_bits_to_f32(mins[(r / 16) * N + n]);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_fmaf((float)((word >> (4 * j)) & 0xFu), s, m);
+    store8(out, n * K + r * 8, v, dtype);
+}
+
+// One thread per 8 codes of a Q4 block: w_hat = (q - 8) * s_h, exact in fp32, then rounded.
+__global__ __launch_bounds__(256) void dequant_q4b32_kernel(const uint32_t* __restrict__ codes,
+                                                            const uint16_t* __restrict__ scales, int64_t N, int64_t K,
+                                                            int dtype, void* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // dword index = k/8 over all rows
+    if (i >= N * (K / 8)) return;
+    const uint32_t word = codes[i];
+    const float s = f16_bits_to_f32(scales[i / 4]);  // 4 dwords per 32-k block
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (float)((int)((word >> (4 * j)) & 0xFu) - 8) * s;
+    store8(out, i * 8, v, dtype);
+}
+
+hipError_t launch_pack_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,
+                            uint16_t* mins, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + 63) / 64), (unsigned)(K / 128));
+    hipLaunchKernelGGL(pack_g128_kernel, grid, dim3(256), 0, stream, W, N, K, codes, scales, mins);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_q4b32(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales,
+                             hipStream_t stream) {
+    const int64_t blocks = (N * (K / 32) + 255) / 256;
+    hipLaunchKernelGGL(pack_q4b32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, W, N, K, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_g128(const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N,
+                               int64_t K, int dtype, void* out, hipStream_t stream) {
+    const int64_t blocks = ((K / 8) * N + 255) / 256;
+    hipLaunchKernelGGL(dequant_g128_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, mins, N, K,
+                       dtype, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q4b32(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, int dtype,
+                                void* out, hipStream_t stream) {
+    const int64_t blocks = (N * (K / 8) + 255) / 256;
+    hipLaunchKernelGGL(dequant_q4b32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const uint32_t*>(codes), scales, N, K, dtype, out);
+    return hipGetLastError();
+}
+
+}  // namespace w4a16

@@ -1,0 +1,149 @@
+/*
+ * w4a16.h -- C ABI of libw4a16: 4-bit-weight, 16-bit-activation matmul y = x . W_hat^T on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation and the two weight formats follow:
+ *  - vidyal.ai, "Low-Precision Kernels: INT4, INT8 and FP8 Matmuls, Measured", section
+ *    "Step 2: a W4A16 kernel in Triton": groups of 128 consecutive weights along K with a bf16
+ *    scale (max - min)/15 and a bf16 minimum; codes round((w - min)/scale) in 0..15; eight
+ *    codes per 32-bit word along K, first k in the lowest nibble, giving a K/8 x N word matrix
+ *    and K/128 x N scales and minimums; dequantized in registers as q*scale + min; bf16
+ *    activations, fp32 accumulation, bf16 output.  (Format W4A16_FMT_G128_ASYM_BF16.)
+ *  - thuongvuho.com, "Why My 4-Bit CUDA Kernel Wasn't Faster", sections "Why fewer bytes should
+ *    have helped" and "Loading the same bytes differently": blocks of 32 weights with 16 bytes
+ *    of codes and one fp16 scale, decoded as (code - bias) * scale, code byte j holding weight
+ *    2j in its low nibble and 2j+1 in its high nibble; fp16 activations.  The bias is 8 and the
+ *    scale max|w|/7.  (Format W4A16_FMT_Q4_B32_SYM_FP16.)
+ *  - anrans.github.io, "Quantization and GEMV", sections "Writing a GEMV kernel" and
+ *    "W4A16: dequantizing in registers": the small-batch GEMV structure and the zero-range
+ *    rule (a group whose max equals its min gets scale 1).
+ *
+ * Rounding (both formats, identical in every entry point): codes use the STORED rounded scale
+ * and minimum, IEEE fp32 division and round-half-to-even, clamped to 0..15; bf16/fp16 values
+ * are rounded to nearest even; a zero min/max counts as +0.
+ *
+ * Conventions for every call:
+ *  - All array arguments are DEVICE pointers (hipMalloc'd or equivalent) owned by the caller;
+ *    the library allocates nothing, frees nothing and keeps no global mutable state.
+ *  - All calls are asynchronous on `stream` (NULL = the default stream).  A returned
+ *    W4A16_OK means the work was enqueued; device-side completion is the caller's to await.
+ *  - Arguments are validated on the host, before anything is enqueued.  A failed check
+ *    returns W4A16_ERR_INVALID (bad value, null or misaligned pointer) or
+ *    W4A16_ERR_UNSUPPORTED (a valid combination this build does not implement) and touches
+ *    no memory.  A HIP error while enqueuing returns W4A16_ERR_DEVICE.
+ *  - Every pointer must be 16-byte aligned; arrays are dense and row-major as documented.
+ *  - Sizes are int64_t; M, N, K must be positive.  N needs no particular multiple.
+ *  - Weights given to the quantizers must be finite (non-finite input is undefined).
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4A16_OK = 0,
+    W4A16_ERR_INVALID = 1,      /* a bad argument: value, null or misaligned pointer, size */
+    W4A16_ERR_UNSUPPORTED = 2,  /* a valid request outside what this build implements */
+    W4A16_ERR_DEVICE = 3        /* the HIP runtime refused a launch */
+} w4a16_status_t;
+
+typedef enum {
+    /* codes  uint32 [K/8][N]  word (r, n) = codes of k = 8r..8r+7 of column n, k = 8r in bits 0..3
+     * scales bf16   [K/128][N]
+     * mins   bf16   [K/128][N]
+     * w_hat = bf16-or-fp32 of fmaf(q, scale, min); K % 128 == 0 */
+    W4A16_FMT_G128_ASYM_BF16 = 0,
+    /* codes  uint8  [N][K/32][16]  byte j of block b = code of k = 32b+2j (low nibble) and
+     *                              k = 32b+2j+1 (high nibble)
+     * scales fp16   [N][K/32]
+     * mins   unused (pass NULL)
+     * w_hat = (q - 8) * scale (exact in fp32); K % 32 == 0 */
+    W4A16_FMT_Q4_B32_SYM_FP16 = 1
+} w4a16_format_t;
+
+typedef enum {
+    W4A16_BF16 = 0,
+    W4A16_FP16 = 1,
+    W4A16_FP32 = 2
+} w4a16_dtype_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* w4a16_status_string(w4a16_status_t status);
+
+/* Bytes of the three packed arrays of an N x K weight in `fmt` (mins is 0 for the Q4 format).
+ * Pure host arithmetic; any output pointer may be NULL.  ERR_INVALID if N, K <= 0 or K is not a
+ * multiple of the format's group (128 or 32). */
+w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K,
+                                  size_t* codes_bytes, size_t* scales_bytes, size_t* mins_bytes);
+
+/* Quantize and pack fp32 weights W [N][K] (row-major) into `fmt`.
+ * Vidyal.ai "Low-Precision Kernels", Step 2 (G128: per (n, group) min/max, scale, min, codes);
+ * thuongvuho.com "Why My 4-Bit CUDA Kernel Wasn't Faster", introduction and "Loading the same
+ * bytes differently" (Q4: per (n, block) absmax/7 fp16 scale, codes + 8).
+ * Output arrays as described by w4a16_format_t, all written in full (mins: G128 only; NULL
+ * for Q4).  The result is bit-identical to the CPU definition. */
+w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N, int64_t K,
+                                   void* codes, void* scales, void* mins, hipStream_t stream);
+
+/* Reference dequant: W_hat [N][K] (row-major) in `out_dtype` (BF16, FP16 or FP32), each value
+ * the round-to-nearest-even of the fp32 dequantized weight (fmaf(q, s, m) for G128,
+ * (q - 8) * s for Q4).  Same pages as w4a16_quantize_pack. */
+w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* scales,
+                             const void* mins, int64_t N, int64_t K, w4a16_dtype_t out_dtype,
+                             void* W_hat, hipStream_t stream);
+
+/* Small-M path: y [M][N] = x [M][K] . W_hat^T for 1 <= M <= w4a16_gemv_max_rows().
+ * Streams the packed words once with 128-bit or 32-bit coalesced loads, unpacks nibbles in
+ * registers, sums x.q per group in fp32 and applies the group scale and minimum once per group
+ * (the factored form s * sum(x*q) + min * sum(x) that vidyal.ai's M = 1 kernel uses, section
+ * "How the measurements were taken"; P3's one-row-per-warp GEMV, "Writing a GEMV kernel").
+ * act: BF16 for G128; FP16 (or BF16) for Q4.  y has the activation dtype, rounded to nearest
+ * even from fp32.  Row-major x and y; x, y 16-byte aligned. */
+w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                          const void* codes, const void* scales, const void* mins, int64_t N,
+                          int64_t K, void* y, hipStream_t stream);
+
+/* Largest M that w4a16_gemv accepts. */
+int64_t w4a16_gemv_max_rows(void);
+
+/* Bytes of device workspace w4a16_gemm needs for this shape (0 if none).  The workspace holds
+ * split-K partial sums; it is caller-owned, needs no initialisation, and must not be shared by
+ * two calls that may run at the same time. */
+size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K);
+
+/* Large-M path (G128 only): y [M][N] = x [M][K] . W_hat^T on bf16 MFMA with fp32 accumulation.
+ * Packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai Step 2 builds its
+ * B tile) into LDS and fed to v_mfma_f32_16x16x32_bf16.  When a K split is used, partial sums go
+ * to `workspace` and are added in a fixed order, so results are bitwise reproducible run to
+ * run.  workspace_bytes must be >= w4a16_gemm_workspace_bytes(...); workspace may be NULL if
+ * that is 0. */
+w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                          const void* codes, const void* scales, const void* mins, int64_t N,
+                          int64_t K, void* y, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/* Dispatch on M (vidyal.ai "How the measurements were taken": a GEMV kernel for one row, tiles
+ * chosen per M; anrans "Exercises": kernels chosen by batch size): M <= w4a16_matmul_gemv_cutoff()
+ * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4 always takes the GEMV path and then needs
+ * M <= w4a16_gemv_max_rows().  Workspace as for w4a16_gemm (w4a16_gemm_workspace_bytes of the
+ * same shape is always enough). */
+w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                            const void* codes, const void* scales, const void* mins, int64_t N,
+                            int64_t K, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* The M at and below which w4a16_matmul takes the GEMV path for the G128 format. */
+int64_t w4a16_matmul_gemv_cutoff(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -1,0 +1,110 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the header declares, and
+rejects bad arguments on the host before anything touches a device (no compute calls here)."""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+import gemm_w4a16_amd as w
+
+ROOT = Path(__file__).resolve().parent.parent
+HEADER = ROOT / "include" / "w4a16.h"
+
+G128, Q4 = w.W4A16_FMT_G128_ASYM_BF16, w.W4A16_FMT_Q4_B32_SYM_FP16
+BF16, F16, F32 = w.W4A16_BF16, w.W4A16_FP16, w.W4A16_FP32
+FAKE = 0x10000   # a 16-byte-aligned address that is never dereferenced: every call below fails validation
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const char\*|w4a16_status_t|int64_t|size_t)\s+(w4a16_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(w.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(w.library_path)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert w.status_string(0) == "ok"
+    for s in (1, 2, 3):
+        assert w.status_string(s) and w.status_string(s) != "ok"
+    assert w.status_string(99) == "unknown status"
+
+
+def test_packed_sizes_match_the_formats():
+    # G128: 4 bits per weight + bf16 scale and minimum per 128 (the decode matrix is 31,195,136 B)
+    assert w.w4a16_packed_sizes(G128, 14336, 4096) == (29_360_128, 917_504, 917_504)
+    # Q4: 16 B of codes + 2 B scale per 32 weights (16384^2: 144 MiB in all)
+    c, s, m = w.w4a16_packed_sizes(Q4, 16384, 16384)
+    assert (c, s, m) == (134_217_728, 16_777_216, 0) and c + s == 144 * 2 ** 20
+    assert w.w4a16_packed_sizes(G128, 1, 128) == (64, 2, 2)
+
+
+@pytest.mark.parametrize("fmt,N,K", [(G128, 0, 128), (G128, 5, 0), (G128, 5, 64), (G128, 5, 200), (Q4, 5, 48),
+                                     (Q4, -1, 32), (7, 5, 128), (G128, 1 << 31, 128)])
+def test_packed_sizes_rejects_bad_shapes(fmt, N, K):
+    with pytest.raises(w.W4A16Error) as e:
+        w.w4a16_packed_sizes(fmt, N, K)
+    assert e.value.status == w.W4A16_ERR_INVALID
+
+
+def _status(fn, *args):
+    try:
+        fn(*args)
+    except w.W4A16Error as e:
+        return e.status
+    return w.W4A16_OK
+
+
+def test_quantize_pack_validation():
+    q = w.w4a16_quantize_pack
+    assert _status(q, G128, FAKE, 4, 100, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID     # K % 128
+    assert _status(q, G128, FAKE + 4, 4, 128, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID  # misaligned W
+    assert _status(q, G128, None, 4, 128, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID      # null W
+    assert _status(q, G128, FAKE, 4, 128, FAKE, FAKE, None, 0) == w.W4A16_ERR_INVALID      # G128 needs mins
+    assert _status(q, Q4, FAKE, 4, 32, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID         # Q4 takes no mins
+    assert _status(q, Q4, FAKE, 0, 32, FAKE, FAKE, None, 0) == w.W4A16_ERR_INVALID
+
+
+def test_dequant_validation():
+    d = w.w4a16_dequant
+    assert _status(d, G128, FAKE, FAKE, FAKE, 4, 128, 7, FAKE, 0) == w.W4A16_ERR_INVALID   # dtype
+    assert _status(d, G128, FAKE, FAKE, FAKE, 4, 128, BF16, FAKE + 2, 0) == w.W4A16_ERR_INVALID
+    assert _status(d, Q4, FAKE, FAKE, None, 4, 40, BF16, FAKE, 0) == w.W4A16_ERR_INVALID    # K % 32
+
+
+def test_gemv_validation():
+    g = w.w4a16_gemv
+    mx = w.w4a16_gemv_max_rows()
+    assert mx >= 1
+    assert _status(g, G128, BF16, FAKE, mx + 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, G128, BF16, FAKE, 0, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, F16, FAKE, 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, Q4, F32, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, G128, BF16, FAKE + 8, 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, BF16, FAKE, 1, FAKE, FAKE, FAKE, 8, 128, None, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, 9, FAKE, 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+
+
+def test_gemm_validation_and_workspace():
+    # a shape whose tile grid is small needs a K-split workspace; too little is refused on the host
+    need = w.w4a16_gemm_workspace_bytes(G128, 64, 256, 4096)
+    assert need > 0 and need % (64 * 256 * 4) == 0
+    assert w.w4a16_gemm_workspace_bytes(Q4, 64, 256, 4096) == 0
+    assert w.w4a16_gemm_workspace_bytes(G128, 0, 256, 4096) == 0
+    g = w.w4a16_gemm
+    assert _status(g, G128, BF16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, FAKE, need - 4, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, BF16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, Q4, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_UNSUPPORTED
+    m = w.w4a16_matmul
+    assert _status(m, Q4, F16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, None, 64, 64, FAKE, None, 0, 0) \
+        == w.W4A16_ERR_UNSUPPORTED
+    assert 1 <= w.w4a16_matmul_gemv_cutoff() <= w.w4a16_gemv_max_rows()
