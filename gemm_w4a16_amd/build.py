@@ -24,7 +24,7 @@ LIB = PKG / "libw4a16.so"
 BUILD_DIR = PKG / "_build"
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "skinny.hip", "gemm.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

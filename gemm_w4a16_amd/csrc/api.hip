@@ -13,7 +13,7 @@ constexpr int64_t kBlockQ4 = 32;
 // Largest extents the kernels index with 32-bit ints (element offsets stay 64-bit).
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // M at and below which w4a16_matmul uses the GEMV path for G128 (from the batch sweep).
-constexpr int64_t kGemvCutoff = 4;
+constexpr int64_t kGemvCutoff = 16;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -126,11 +126,13 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
     const w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
     if (st != W4A16_OK) return st;
     if (M > w4a16::kGemvMaxRows) return W4A16_ERR_UNSUPPORTED;
-    if (fmt == W4A16_FMT_G128_ASYM_BF16)
-        return from_hip(w4a16::launch_gemv_g128(static_cast<const uint16_t*>(x), M, static_cast<const uint32_t*>(codes),
-                                                static_cast<const uint16_t*>(scales),
-                                                static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
-                                                stream));
+    if (fmt == W4A16_FMT_G128_ASYM_BF16) {
+        return from_hip(w4a16::launch_skinny_g128(static_cast<const uint16_t*>(x), M,
+                                                  static_cast<const uint32_t*>(codes),
+                                                  static_cast<const uint16_t*>(scales),
+                                                  static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
+                                                  stream));
+    }
     return from_hip(w4a16::launch_gemv_q4b32(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
                                              static_cast<const uint8_t*>(codes), static_cast<const uint16_t*>(scales),
                                              N, K, static_cast<uint16_t*>(y), stream));

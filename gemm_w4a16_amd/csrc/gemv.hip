@@ -1,24 +1,18 @@
-// gemv.hip -- small-M W4A16 kernels: the memory-bound path.
+// gemv.hip -- the Q4 block-32 GEMV (thuongvuho.com "Why My 4-Bit CUDA Kernel Wasn't Faster":
+// 16 code bytes + one fp16 scale per 32 weights, fp16 activations).
 //
-// Both kernels use the factored per-group form of vidyal.ai "Low-Precision Kernels" ("How the
-// measurements were taken": for one row, s * sum(x*q) + min * sum(x) per group in FP32, no
-// matrix cores) and the register dequant of anrans "Quantization and GEMV" ("W4A16:
-// dequantizing in registers"), reorganised for CDNA4:
+// It uses the per-block factored form (scale applied once per block after an unscaled dot, as
+// that page and anrans "Quantization and GEMV", exercise 1, do) and the register dequant of
+// anrans "W4A16: dequantizing in registers", reorganised for CDNA4:
 //
 //  * Nibbles become bf16/fp16 numbers with one AND-OR each pair: (w >> 4j) & 0x000F000F with
 //    exponent bits 0x4300 (bf16) or 0x6400 (fp16) OR-ed in is the pair (B + q_j, B + q_{j+4})
 //    with B = 128 or 1024 (the magic-number trick both pages describe).  v_dot2c_f32_{bf16,f16}
 //    then multiplies two weights per instruction with fp32 accumulation.  The activations are
 //    paired the same way, (x_j, x_{j+4}), so no nibble has to move.
-//  * The offset B is removed once per group: s*sum(x*(B+q)) + (min - B*s)*sum(x).
+//  * The offset B and the bias 8 are removed once per block: s * (sum(x*(B+q)) - (B+8)*sum(x)).
 //
-// G128 kernel: the packed matrix is [K/8][N] (N contiguous), so a wave reads one packed row of
-// 64 consecutive columns per load (256 B, coalesced); the eight k of that row are the same for
-// every lane, so x comes through the scalar cache into SGPRs.  A 512-thread block owns 64
-// columns; its 8 waves split K by groups and add their partial sums through LDS in a fixed
-// order.  All of a wave's loads (up to 4 groups = 64 words per lane) are issued before any math.
-//
-// Q4 kernel: codes are [N][K/32][16] bytes (a row's blocks contiguous), so 16 lanes read 512 B
+// Layout: codes are [N][K/32][16] bytes (a row's blocks contiguous), so 16 lanes read 512 B
 // of one row per pair of 16-byte loads and a wave covers 4 rows per step.  Each lane always
 // handles the same 64 k of the row, so its activations are loaded once, kept in VGPRs already
 // paired, and their per-block sums folded into a constant.  The 16 lanes of a row finish with a
@@ -39,103 +33,6 @@ constexpr uint32_t kF16OnePair = 0x3C003C00u;
 // (lo half of a, lo half of b) and (hi half of a, hi half of b) as one dword each.
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// ---------------------------------------------------------------------------------------------
-// G128: 512 threads, 64 columns per block, groups strided over the 8 waves.
-// ---------------------------------------------------------------------------------------------
-constexpr int kG128Waves = 8;
-constexpr int kG128GroupsPerPass = 4;  // per wave: 4 x 16 packed rows in flight
-
-template <int MR>
-__global__ __launch_bounds__(512) void gemv_g128_kernel(const uint16_t* __restrict__ x,
-                                                        const uint32_t* __restrict__ codes,
-                                                        const uint16_t* __restrict__ scales,
-                                                        const uint16_t* __restrict__ mins,
-                                                        uint16_t* __restrict__ y, int M, int N, int K) {
-    __shared__ float part[kG128Waves][MR][64];
-    const int lane = lane_id(), wave = wave_id();
-    const int n = blockIdx.x * 64 + lane;
-    const int nc = n < N ? n : N - 1;  // dead lanes read a valid column and never store
-    const int G = K >> 7;
-    float yacc[MR];
-#pragma unroll
-    for (int m = 0; m < MR; ++m) yacc[m] = 0.0f;
-
-    for (int g0 = wave; g0 < G; g0 += kG128Waves * kG128GroupsPerPass) {
-        // 1) per-group activation sums first: one dword of x per lane per (group, row), summed
-        //    across the wave with DPP (their loads are the oldest, so they are waited for first).
-        float sx[kG128GroupsPerPass][MR];
-        uint32_t xp[kG128GroupsPerPass][MR];
-#pragma unroll
-        for (int j = 0; j < kG128GroupsPerPass; ++j) {
-            const int g = g0 + kG128Waves * j;
-#pragma unroll
-            for (int m = 0; m < MR; ++m)
-                xp[j][m] = (g < G && m < M)
-                               ? reinterpret_cast<const uint32_t*>(x + (size_t)m * K + (size_t)g * 128)[lane]
-                               : 0u;
-        }
-        // 2) all packed words and group parameters of this pass.
-        uint32_t w[kG128GroupsPerPass][16];
-        uint32_t sb[kG128GroupsPerPass], mb[kG128GroupsPerPass];
-#pragma unroll
-        for (int j = 0; j < kG128GroupsPerPass; ++j) {
-            const int g = g0 + kG128Waves * j;
-            if (g < G) {
-                const uint32_t* col = codes + (size_t)g * 16 * N + nc;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) w[j][i] = col[(size_t)i * N];
-                sb[j] = scales[(size_t)g * N + nc];
-                mb[j] = mins[(size_t)g * N + nc];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < kG128GroupsPerPass; ++j)
-#pragma unroll
-            for (int m = 0; m < MR; ++m) sx[j][m] = wave_sum(dot2_bf16(xp[j][m], kBf16OnePair, 0.0f));
-        // 3) dot products, one group at a time as its words arrive.
-#pragma unroll
-        for (int j = 0; j < kG128GroupsPerPass; ++j) {
-            const int g = g0 + kG128Waves * j;
-            if (g >= G) break;
-            const float s = bf16_bits_to_f32(sb[j]);
-            const float c = __builtin_fmaf(-128.0f, s, bf16_bits_to_f32(mb[j]));  // min - 128 s
-#pragma unroll
-            for (int m = 0; m < MR; ++m) {
-                if (m >= M) break;
-                const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)m * K + (size_t)g * 128);
-                float acc = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const uint4 xv = xr[i];  // x[8i .. 8i+7], the same for every lane
-                    const uint32_t x04 = pack_lo(xv.x, xv.z), x15 = pack_hi(xv.x, xv.z);
-                    const uint32_t x26 = pack_lo(xv.y, xv.w), x37 = pack_hi(xv.y, xv.w);
-                    const uint32_t wd = w[j][i];
-                    acc = dot2_bf16((wd & kNibblePairMask) | kBf16Magic, x04, acc);
-                    acc = dot2_bf16(((wd >> 4) & kNibblePairMask) | kBf16Magic, x15, acc);
-                    acc = dot2_bf16(((wd >> 8) & kNibblePairMask) | kBf16Magic, x26, acc);
-                    acc = dot2_bf16(((wd >> 12) & kNibblePairMask) | kBf16Magic, x37, acc);
-                }
-                yacc[m] = __builtin_fmaf(s, acc, yacc[m]);
-                yacc[m] = __builtin_fmaf(c, sx[j][m], yacc[m]);
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 0; m < MR; ++m) part[wave][m][lane] = yacc[m];
-    __syncthreads();
-    const int t = threadIdx.x;
-    if (t < MR * 64) {
-        const int m = t >> 6, l = t & 63;
-        const int col = blockIdx.x * 64 + l;
-        if (m < M && col < N) {
-            float sum = 0.0f;
-#pragma unroll
-            for (int v = 0; v < kG128Waves; ++v) sum += part[v][m][l];
-            y[(size_t)m * N + col] = f32_to_bf16_bits(sum);
-        }
-    }
-}
 
 // ---------------------------------------------------------------------------------------------
 // Q4 block-32: 1024 threads = 16 waves = 16 K-slices of 1024 k; 64 rows per block.
@@ -235,19 +132,6 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
 }
 
 }  // namespace
-
-hipError_t launch_gemv_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
-                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-    const dim3 grid((unsigned)((N + 63) / 64)), block(512);
-    const int m = (int)M, n = (int)N, k = (int)K;
-    if (M == 1)
-        hipLaunchKernelGGL(gemv_g128_kernel<1>, grid, block, 0, stream, x, codes, scales, mins, y, m, n, k);
-    else if (M == 2)
-        hipLaunchKernelGGL(gemv_g128_kernel<2>, grid, block, 0, stream, x, codes, scales, mins, y, m, n, k);
-    else
-        hipLaunchKernelGGL(gemv_g128_kernel<4>, grid, block, 0, stream, x, codes, scales, mins, y, m, n, k);
-    return hipGetLastError();
-}
 
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {

@@ -18,10 +18,10 @@ hipError_t launch_dequant_g128(const uint32_t* codes, const uint16_t* scales, co
 hipError_t launch_dequant_q4b32(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, int dtype,
                                 void* out, hipStream_t stream);
 
-// Small-M G128 path, bf16 activations, M <= kGemvMaxRows.
-constexpr int kGemvMaxRows = 4;
-hipError_t launch_gemv_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
-                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+// Small-M G128 path (the skinny MFMA kernel), bf16 activations, M <= kGemvMaxRows.
+constexpr int kGemvMaxRows = 16;
+hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                              const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 // Q4 path, one activation row per pass; act_f16: fp16 (true) or bf16 (false) activations.
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
