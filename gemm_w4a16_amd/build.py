@@ -25,6 +25,8 @@ BUILD_DIR = PKG / "_build"
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "pack.hip", "gemv.hip", "skinny.hip", "gemm.hip"]
+# Per-file extra flags (none at present).
+FILE_FLAGS: dict = {}
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -43,7 +45,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> Path:
     obj = BUILD_DIR / (Path(src).stem + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(src, []), "-c", str(CSRC / src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
     noise = [l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip()]

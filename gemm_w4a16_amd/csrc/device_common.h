@@ -10,6 +10,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(2 * sizeof(_Float16)))) _Float16 f16x2_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
 constexpr int kWave = 64;
@@ -27,8 +28,11 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 // Two fp32 values -> one dword holding two bf16, `lo` in bits 0..15 (one v_cvt_pk_bf16_f32).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-    return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
 // fp32 dot of two bf16 pairs plus an accumulator: v_dot2c_f32_bf16.
