@@ -35,6 +35,23 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 CACHE_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache (MALL)
 METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
+DECODE_KERNEL = "skinny_g128_kernel<1, 4, 16, true>"
+PREFILL_KERNEL = "gemm_g128_kernel<256>"
+
+
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by a copy-kernel calibration) from
+    the committed counter summary profiles/traffic.json -- or None if the kernel's source has
+    changed since those counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))["kernels"][kernel]
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, KeyError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
 
 
 def log(*a):
@@ -50,7 +67,15 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every step directly instead of replaying a HIP graph (counter runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also copy a buffer of this many MiB 5 times (a known-size reference kernel "
+                         "for scaling hardware byte counters)")
     return ap.parse_args()
+
+
+EAGER = False
 
 
 class Setup:
@@ -86,6 +111,15 @@ def time_steps(setup: Setup, steps: int, warmup: int):
     for i in range(warmup):
         setup.step(i)
     torch.cuda.synchronize()
+    if EAGER:
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            setup.step(i)
+        end.record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, start.elapsed_time(end) / 1e3
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(steps):
@@ -151,6 +185,10 @@ def bench_prefill(steps, warmup):
         "us_per_step_wall": wall / steps * 1e6, "us_per_launch_events": ev / steps * 1e6,
         "tflops": flops / (ev / steps) / 1e12,
         "frac_mfma_bf16_peak": flops / (ev / steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": flops / (ev / steps) / 1e12,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": flops / (ev / steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(PREFILL_KERNEL)},
         "bf16_weight_gemm_hipblaslt_tflops": flops / t_bf16 / 1e12,
         "bf16_weight_gemm_us": t_bf16 * 1e6,
     }
@@ -217,11 +255,24 @@ def cpu_baseline(W, x):
                       f"{t:.3f} s, on {platform.processor() or platform.machine()}"}
 
 
+def copy_calibration(mib: int):
+    """Copy a buffer of known size: FETCH_SIZE / WRITE_SIZE of this kernel calibrate the counters."""
+    import torch
+    src = torch.empty(mib * 2 ** 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: 5 x {mib} MiB device-to-device")
+
+
 def main():
+    global EAGER
     args = parse()
+    EAGER = args.eager
     if args.gpus != 1:
-        msg = (f"bench.py runs on one GPU only: --gpus {args.gpus} was asked for, but this build has no "
-               "multi-GPU path (the N-split and K-split shardings are described in DESIGN.md, not built).")
+        msg = (f"bench.py runs on one GPU only: --gpus {args.gpus} was asked for, but the library has no "
+               "multi-GPU path (sharding the weight matrix by columns or by K groups is not implemented).")
         print(msg, file=sys.stderr)
         sys.exit(2)
     import torch
@@ -230,6 +281,8 @@ def main():
     import gemm_w4a16_amd as w  # fails loudly if libw4a16.so is missing
     props = torch.cuda.get_device_properties(0)
 
+    if args.copy_calibration_mib:
+        copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
         fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep}[args.only]
         print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
@@ -257,12 +310,13 @@ def main():
                    "format": "int4 codes, group 128 along K, bf16 scale + bf16 min",
                    "weights": "N(0,0.02) fp32 with 0.1% x20 outliers, seed 0", "activations": "bf16 N(0,1)",
                    "weight_copies_rotated": R, "weight_bytes": st.weight_bytes,
-                   "timing": "K steps in one HIP graph replay", "device": props.name,
+                   "timing": "K eager launches" if EAGER else "K steps in one HIP graph replay",
+                   "device": props.name,
                    "compute_units": props.multi_processor_count,
                    "frac_hbm_peak_effective_weight": value / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "gemv_g128_kernel<1>", "us_per_launch": per_launch * 1e6,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(DECODE_KERNEL),
+                     "kernel": DECODE_KERNEL, "us_per_launch": per_launch * 1e6,
                      "algorithmic_bytes_per_launch": algo_bytes},
     }
     del st
