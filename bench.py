@@ -10,8 +10,9 @@ headline workload is the decode GEMV on the Llama-3-8B up-projection shape (M=1,
 N=14336, group-128 asymmetric format); its value is effective weight bytes (codes + scales +
 mins) per second.  To keep the 256 MB Infinity Cache from serving the weights, the steps rotate
 over enough packed copies to exceed 512 MB.  The K timed steps are captured once into a HIP
-graph (so host launch cost does not pace the GPU) and replayed; HIP events on the launch stream
-bracket the replay and give the average duration per launch used for the roofline.
+graph (so host launch cost does not pace the GPU) and replayed; the graph is first replayed
+untimed for WARM_SECONDS so that the GPU's clocks have settled, then HIP events on the launch
+stream bracket one replay and give the average duration per launch used for the roofline.
 
 Prints ONE JSON line.  Secondary figures (prefill TFLOPS at M=1024 with a hipBLASLt bf16-weight
 GEMM beside it, the Q4 block-32 GEMV, the batch sweep) go under "extra".
@@ -34,9 +35,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 CACHE_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache (MALL)
+WARM_SECONDS = 0.25            # untimed run-up of each workload before its timed replay
 METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
 DECODE_KERNEL = "skinny_g128_kernel<1, 4, 16, true>"
-PREFILL_KERNEL = "gemm_g128_kernel<256>"
+PREFILL_KERNEL = "gemm_g128_kernel<256, true>"
 
 
 def recorded_traffic(kernel: str):
@@ -124,8 +126,14 @@ def time_steps(setup: Setup, steps: int, warmup: int):
     with torch.cuda.graph(g):
         for i in range(steps):
             setup.step(i)
-    g.replay()  # untimed: first replay uploads the graph
-    torch.cuda.synchronize()
+    # untimed replays (the first uploads the graph) until the GPU has run this work for
+    # WARM_SECONDS: its clocks settle over milliseconds, far longer than a short graph takes
+    t_warm = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_warm >= WARM_SECONDS:
+            break
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -169,9 +177,11 @@ def bench_prefill(steps, warmup):
     w.w4a16_dequant(w.W4A16_FMT_G128_ASYM_BF16, *st.copies[0], wl.N, wl.K, w.W4A16_BF16, Wb)
     Wt = Wb.view(torch.bfloat16).t().contiguous()   # [K][N]
     xb = st.x.view(torch.bfloat16)
-    for _ in range(5):
-        yb = torch.matmul(xb, Wt)
-    torch.cuda.synchronize()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < WARM_SECONDS:
+        for _ in range(steps):
+            yb = torch.matmul(xb, Wt)
+        torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(steps):

@@ -38,6 +38,12 @@ def _load() -> ctypes.CDLL:
     if not _LIB_PATH.exists():
         raise ImportError(f"{_LIB_PATH} is not built; run `python -m gemm_w4a16_amd.build` "
                           "(hipcc for gfx950). There is no fallback path.")
+    # PyTorch ships its own HIP runtime (libamdhip64.so.7).  It must be the one in the process
+    # before libw4a16.so is loaded, so that the library's dependency on libamdhip64.so.7 binds to
+    # it: loaded first, libw4a16.so would pull in the system runtime and torch would then load a
+    # second one, whose streams and allocations the library's runtime does not know (every
+    # launch on a torch stream would then fail).
+    import torch  # noqa: F401
     L = ctypes.CDLL(str(_LIB_PATH))
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     L.w4a16_status_string.argtypes, L.w4a16_status_string.restype = [I], ctypes.c_char_p
@@ -143,9 +149,12 @@ def alloc_packed(fmt: int, N: int, K: int, device="cuda"):
     import torch
     w4a16_packed_sizes(fmt, N, K)  # validates the shape
     if fmt == W4A16_FMT_G128_ASYM_BF16:
+        # scales/mins: [K/128][N] views of buffers padded to the size w4a16_packed_sizes asks for
+        n = K // 128 * N
+        padded = n + (n & 1)
         return (torch.empty((K // 8, N), dtype=torch.int32, device=device),
-                torch.empty((K // 128, N), dtype=torch.int16, device=device),
-                torch.empty((K // 128, N), dtype=torch.int16, device=device))
+                torch.empty(padded, dtype=torch.int16, device=device)[:n].view(K // 128, N),
+                torch.empty(padded, dtype=torch.int16, device=device)[:n].view(K // 128, N))
     return (torch.empty((N, K // 32, 16), dtype=torch.uint8, device=device),
             torch.empty((N, K // 32), dtype=torch.int16, device=device),
             None)

@@ -78,7 +78,10 @@ w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K, size
     const w4a16_status_t st = check_shape(fmt, N, K);
     if (st != W4A16_OK) return st;
     const size_t codes = (size_t)N * (size_t)K / 2;  // 4 bits per weight in both formats
-    const size_t scales = (size_t)N * (size_t)(K / group_of(fmt)) * 2;
+    size_t scales = (size_t)N * (size_t)(K / group_of(fmt)) * 2;
+    // G128: the GEMM reads scales and minimums as aligned 4-byte words, so an odd element count
+    // gets 2 bytes of padding (never written, never used)
+    if (fmt == W4A16_FMT_G128_ASYM_BF16) scales = (scales + 3) & ~(size_t)3;
     const size_t mins = fmt == W4A16_FMT_G128_ASYM_BF16 ? scales : 0;
     if (codes_bytes) *codes_bytes = codes;
     if (scales_bytes) *scales_bytes = scales;
@@ -93,6 +96,7 @@ w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N
     if (!aligned16(W)) return W4A16_ERR_INVALID;
     st = check_packed(fmt, codes, scales, mins);
     if (st != W4A16_OK) return st;
+    w4a16::clear_stale_error();
     if (fmt == W4A16_FMT_G128_ASYM_BF16)
         return from_hip(w4a16::launch_pack_g128(W, N, K, static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
                                                 static_cast<uint16_t*>(mins), stream));
@@ -109,6 +113,7 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
     if (!aligned16(W_hat)) return W4A16_ERR_INVALID;
     if (out_dtype != W4A16_BF16 && out_dtype != W4A16_FP16 && out_dtype != W4A16_FP32) return W4A16_ERR_INVALID;
     const int dt = (int)out_dtype;
+    w4a16::clear_stale_error();
     if (fmt == W4A16_FMT_G128_ASYM_BF16)
         return from_hip(w4a16::launch_dequant_g128(static_cast<const uint32_t*>(codes),
                                                    static_cast<const uint16_t*>(scales),
@@ -126,6 +131,7 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
     const w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
     if (st != W4A16_OK) return st;
     if (M > w4a16::kGemvMaxRows) return W4A16_ERR_UNSUPPORTED;
+    w4a16::clear_stale_error();
     if (fmt == W4A16_FMT_G128_ASYM_BF16) {
         return from_hip(w4a16::launch_skinny_g128(static_cast<const uint16_t*>(x), M,
                                                   static_cast<const uint32_t*>(codes),
@@ -151,6 +157,7 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
     if (fmt != W4A16_FMT_G128_ASYM_BF16) return W4A16_ERR_UNSUPPORTED;
     const size_t need = w4a16::gemm_g128_workspace_bytes(M, N, K);
     if (need > 0 && (workspace_bytes < need || !aligned16(workspace))) return W4A16_ERR_INVALID;
+    w4a16::clear_stale_error();
     return from_hip(w4a16::launch_gemm_g128(static_cast<const uint16_t*>(x), M, static_cast<const uint32_t*>(codes),
                                             static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(mins),
                                             N, K, static_cast<uint16_t*>(y), static_cast<float*>(workspace), stream));

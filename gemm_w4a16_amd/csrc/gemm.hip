@@ -9,15 +9,19 @@
 //    for the 256 CUs (a power-of-two N tile would leave 1/8 of the chip idle);
 //  * 256 threads = 4 waves stacked along M; a wave owns (BM/4) x 224 outputs as (BM/128) x 7
 //    v_mfma_f32_32x32x16_bf16 accumulators (on gfx950 this shape runs at twice the rate of
-//    16x16x32 -- measured ~2.4 vs ~1.3 PFLOP/s over the whole chip);
-//  * LDS double buffer: while the MFMAs of k-tile t run from one buffer, the load unit copies the
-//    A tile of t+1 straight into the other buffer (global_load_lds_dwordx4, XOR-swizzled rows)
-//    and the threads hold the packed B words of t+1 in registers, dequantizing them into the
-//    other buffer after their MFMAs; one barrier per k-tile;
-//  * the packed B tile (8 packed rows x 224 columns) is dequantized by threads 0..223, one column
-//    each: w_hat = bf16_rne(fmaf(q, s, min)) -- the same value as the reference dequant -- and
-//    each 32-bit word becomes one 16-byte row segment of an [n][k] LDS tile, which is exactly an
-//    MFMA B fragment; LDS rows are padded to 144 B so fragment reads are conflict-free;
+//    16x16x32);
+//  * every global read in the k-loop is a direct-to-LDS copy by the load unit (global_load_lds)
+//    issued ahead of its use: the A tile one k-tile ahead (two LDS stages, XOR-swizzled rows),
+//    the packed B words three k-tiles ahead (three stages) and each group's scales and minimums
+//    with its first k-tile.  The copies are issued in an order that lets one `s_waitcnt vmcnt(n)`
+//    before each k-tile's barrier wait only for what the next k-tile needs, so no wave waits on
+//    HBM latency inside the loop;
+//  * while the MFMAs of k-tile t read one dequantized B stage, thread c < 224 turns the 8 packed
+//    words of column c of k-tile t+1 into the other: w_hat = bf16_rne(fmaf(q, s, min)), the
+//    same value as the reference dequant, 22 VALU instructions per word, interleaved with the
+//    MFMAs (about four VALU instructions fit under one 32x32x16 MFMA).  Each word becomes one
+//    16-byte row segment of an [n][k] tile, which is exactly an MFMA B fragment; rows are padded
+//    to 144 B, so fragment reads and dequant writes are free of bank conflicts;
 //  * when the tile grid alone cannot fill the chip, K is split in whole groups; fp32 partials go
 //    to the caller's workspace and a second kernel adds them in split order, so the result does
 //    not depend on scheduling.
@@ -29,182 +33,290 @@ namespace w4a16 {
 namespace {
 
 constexpr int BN = 224, BK = 64;
-constexpr int LDT = BK + 8;  // B tile LDS row pitch in bf16 (144 B)
+constexpr int LDT = BK + 8;  // dequantized B tile row pitch in bf16 (144 B)
 constexpr int kThreads = 256;
 constexpr int kCUs = 256;
 constexpr int kNT = BN / 32;  // 32-column MFMA tiles per wave (each wave spans all 224 columns)
+constexpr int kBpStages = 3;  // packed-word stages: k-tiles t+1 (being dequantized) .. t+3 (in flight)
 
-// A tiles are copied global -> LDS by the load unit (global_load_lds_dwordx4), rows of 64 bf16
-// (128 B) unpadded; the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7), which keeps
-// the 16 rows of a fragment read on 16 distinct 4-bank groups.
+// LDS map (byte offsets).  A and the dequantized B have two stages (k-tiles t and t+1), the
+// packed words three, the scales/minimums two (one per group; a group is two k-tiles).
+template <int BM>
+struct Smem {
+    static constexpr int kA = BM * BK * 2;     // A stage: BM rows x 64 bf16
+    static constexpr int kBdq = BN * LDT * 2;  // dequantized B stage: 224 rows x 144 B
+    static constexpr int kBp = 512 * 16;       // packed stage: [8 packed rows][224 columns] u32 + pad
+    static constexpr int kSc = 512 * 4;        // 256 scale slots + 256 minimum slots, a dword each
+    static constexpr int oA = 0;
+    static constexpr int oBdq = oA + 2 * kA;
+    // written by the 32 threads past column 223: thread 224 + u stores its row segment r at
+    // 16 (u + r), so (32 + 7) x 16 B, rounded up
+    static constexpr int oSink = oBdq + 2 * kBdq;
+    static constexpr int oBp = oSink + 640;
+    static constexpr int oSc = oBp + kBpStages * kBp;
+    static constexpr int kTotal = oSc + 2 * kSc;
+};
+static_assert(Smem<256>::kTotal <= 160 * 1024, "LDS budget");
+
+// A tiles: rows of 64 bf16 (128 B), unpadded; the 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7), which keeps the 16 rows of a fragment read on 16 distinct 4-bank groups.
 __device__ __forceinline__ int a_swizzle(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-// B rows 224..255 are scratch: threads 224..255 dequantize a duplicate column into them, which
-// keeps the k-loop free of branches.
-constexpr int kBRows = kThreads;
-
-// Direct-to-LDS copies of the A tile (rows m0.., k0..k0+63) into `As`: wave w copies rows
-// [w * BM/4, (w+1) * BM/4), 8 rows (1 KB) per instruction; lane l lands on chunk l % 8 of row
-// l / 8 and so fetches the global chunk that the swizzle maps there.  Rows past M repeat row
-// M-1: they only feed output rows that are never stored.  The per-lane byte offsets from x do
-// not depend on k0 and are computed once; the k0 part is a wave-uniform base.
-template <int BM>
-struct ACopy {
-    uint32_t off[BM / 32];
-    __device__ __forceinline__ void init(int M, int K, int m0) {
-        const int lane = lane_id(), wave = wave_id();
-#pragma unroll
-        for (int i = 0; i < BM / 32; ++i) {
-            const int r = wave * (BM / 4) + 8 * i + (lane >> 3);
-            const int gm = min(m0 + r, M - 1);
-            off[i] = (uint32_t)(((size_t)gm * K + 8 * a_swizzle(r, lane & 7)) * 2);
-        }
-    }
-    __device__ __forceinline__ void issue(const uint16_t* __restrict__ x, uint16_t* As, int k0) const {
-        const int wave = wave_id();
-        const char* base = reinterpret_cast<const char*>(x + k0);
-#pragma unroll
-        for (int i = 0; i < BM / 32; ++i)
-            __builtin_amdgcn_global_load_lds(base + off[i], As + (wave * (BM / 4) + 8 * i) * BK, 16, 0, 0);
-    }
-};
-
-// B: thread t < 224 owns column n0 + t of the tile: the 8 packed words of the k-tile.  `off` is
-// the column's byte offset; each packed row start is wave-uniform.
-__device__ __forceinline__ void load_b(uint32_t (&w)[BK / 8], const uint32_t* __restrict__ codes, int N, uint32_t off,
-                                       int k0) {
-#pragma unroll
-    for (int r = 0; r < BK / 8; ++r) {
-        const char* row = reinterpret_cast<const char*>(codes + (size_t)(k0 / 8 + r) * N);
-        w[r] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(row + off));
-    }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// w_hat = bf16_rne(fmaf(q, s, min)) for 8 k of this thread's column (packed row r of the tile),
-// as one 16-byte row segment of the [n][k] tile (threads past column 223 write their duplicate
-// into the scratch rows).
-__device__ __forceinline__ void dequant_word(uint32_t w, int r, uint16_t* Bs, float s, float m) {
-    const int t = threadIdx.x;
-    {
-        const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;  // q0 q2 q4 q6 / q1 q3 q5 q7
-        const float v0 = __builtin_fmaf((float)(ev & 0xFF), s, m);
-        const float v2 = __builtin_fmaf((float)((ev >> 8) & 0xFF), s, m);
-        const float v4 = __builtin_fmaf((float)((ev >> 16) & 0xFF), s, m);
-        const float v6 = __builtin_fmaf((float)(ev >> 24), s, m);
-        const float v1 = __builtin_fmaf((float)(od & 0xFF), s, m);
-        const float v3 = __builtin_fmaf((float)((od >> 8) & 0xFF), s, m);
-        const float v5 = __builtin_fmaf((float)((od >> 16) & 0xFF), s, m);
-        const float v7 = __builtin_fmaf((float)(od >> 24), s, m);
-        *reinterpret_cast<uint4*>(Bs + t * LDT + r * 8) =
-            make_uint4(pack2_bf16(v0, v1), pack2_bf16(v2, v3), pack2_bf16(v4, v5), pack2_bf16(v6, v7));
-    }
+// Direct-to-LDS copies: lane l reads 16 (or 4) bytes at sbase + voff and the load unit writes
+// them to LDS byte m0 + 16 l (or 4 l).  They are issued from inline assembly so that the
+// compiler does not track them: the compiler cannot tell the LDS stages apart and would wait for
+// every copy in flight before any LDS access.  The only waits for them are the explicit ones
+// before the k-tile barriers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(n): at most n of this wave's copies are still in flight.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | 0x0F70 /* expcnt, lgkmcnt: no wait */);
 }
 
-__device__ __forceinline__ void dequant_b(const uint32_t (&w)[BK / 8], uint16_t* Bs, float s, float m) {
-#pragma unroll
-    for (int r = 0; r < BK / 8; ++r) dequant_word(w[r], r, Bs, s, m);
+// One dequantized word: 8 k of one column -> 16 bytes of bf16, w_hat = bf16_rne(fmaf(q, s, m)).
+// Codes 0, 2, 4, 6 come from w & 0x0F0F0F0F and codes 1, 3, 5, 7 from w & 0xF0F0F0F0 as 16 q,
+// multiplied by s/16: the product is the same exact value, so the fma rounds identically.  The
+// masks arrive as kernel arguments so that each byte converts with one v_cvt_f32_ubyteN.
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, uint32_t mlo, uint32_t mhi, float s, float s16, float m) {
+    const uint32_t ev = w & mlo, od = w & mhi;
+    const float v0 = __builtin_fmaf((float)(ev & 0xFF), s, m);
+    const float v2 = __builtin_fmaf((float)((ev >> 8) & 0xFF), s, m);
+    const float v4 = __builtin_fmaf((float)((ev >> 16) & 0xFF), s, m);
+    const float v6 = __builtin_fmaf((float)(ev >> 24), s, m);
+    const float v1 = __builtin_fmaf((float)(od & 0xFF), s16, m);
+    const float v3 = __builtin_fmaf((float)((od >> 8) & 0xFF), s16, m);
+    const float v5 = __builtin_fmaf((float)((od >> 16) & 0xFF), s16, m);
+    const float v7 = __builtin_fmaf((float)(od >> 24), s16, m);
+    return make_uint4(pack2_bf16(v0, v1), pack2_bf16(v2, v3), pack2_bf16(v4, v5), pack2_bf16(v6, v7));
 }
 
-// Instruction interleaving inside one k-step region: each MFMA is followed by one LDS read (the
-// next step's fragments) and a few VALU instructions (the dequant), so neither waits in a clump.
-#ifndef W4A16_GEMM_VALU_PER_MFMA
-#define W4A16_GEMM_VALU_PER_MFMA 3
-#endif
-template <int kMT>
-__device__ __forceinline__ void gemm_step_schedule() {
-#ifndef W4A16_GEMM_NO_SCHEDULE
+// Instruction interleaving inside one k-step region: MFMAs alternate with the LDS reads of the
+// next step's fragments and with the dequant; the first `lead` MFMAs carry no dequant (its words
+// are still on their way from LDS).
+template <int kMFMA, int kValu>
+__device__ __forceinline__ void step_schedule(int lead) {
 #pragma unroll
-    for (int i = 0; i < kMT * (BN / 32); ++i) {
+    for (int i = 0; i < kMFMA; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-        __builtin_amdgcn_sched_group_barrier(0x002, W4A16_GEMM_VALU_PER_MFMA, 0);  // VALU
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        if (i >= lead) {
+            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);      // DS write
+        }
     }
-#endif
 }
 
-__device__ __forceinline__ void wait_vm_all() {
-    // s_waitcnt vmcnt(0): the direct-to-LDS copies of this wave have landed
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-}
+template <int BM, bool kVec>
+struct Gemm {
+    static constexpr int kMT = BM / 128;        // 32-row MFMA tiles per wave (a wave owns BM/4 rows)
+    static constexpr int kAInst = BM / 32;      // A copies per wave per k-tile (1 KB each)
+    static constexpr int kBInst = kVec ? 2 : 7;  // packed-word copies per wave per k-tile
+    using S = Smem<BM>;
 
-// One k-tile: MFMAs on (As, Bs) while the next tile is prepared in (As_n, Bs_n) -- A by the
-// load unit (issued here), B by dequantizing the words `wb` fetched one iteration earlier -- and
-// the words of the tile after are requested into `wn`.  The four LDS buffers are distinct
-// objects, so the compiler can see that the direct-to-LDS copy into As_n does not touch Bs_n or
-// As and only the barrier at the end waits for it.
-template <int BM>
-struct KTile {
-    static constexpr int kMT = BM / 128;  // 32-row MFMA tiles per wave (a wave owns BM/4 rows)
-    f32x16_t acc[kMT][kNT];
-    // two sets of B words (and their raw bf16 scale / min) used alternately: one being
-    // dequantized, the other being fetched
-    uint32_t w0[BK / 8], w1[BK / 8];
-    uint32_t sb0, mb0, sb1, mb1;
-    ACopy<BM> acopy;
-    uint32_t boff;
-    int bcol;
+    const uint16_t* x;
+    const uint32_t* codes;
+    const uint16_t* scales;
+    const uint16_t* mins;
+    uint8_t* smem;
+    uint32_t sm;  // LDS address of smem
+    int M, N, K, m0, n0, kbeg, ntiles;
+    uint32_t mlo, mhi;
+    // per-lane byte offsets of the copies (constant over the k-loop)
+    uint32_t a_off[kAInst];  // from the k-tile's A base
+    uint32_t b_off[kBInst];  // from the k-tile's first packed row
+    uint32_t sc_off[2];      // scale/min dword for even / odd g*N
+    // this thread's LDS byte offsets (from smem, without the stage)
+    uint32_t a_rd[kMT][BK / 16];  // A fragment (i, k-step)
+    uint32_t b_rd;                // B fragment of j = 0, k-step 0
+    uint32_t bq_wr[2];            // dequantized row segment, per destination stage
+    uint32_t bp_rd;               // packed word of row 0 of this thread's column
+    uint32_t sc_rd[2];            // scale of this thread's column, for even / odd g*N
 
-    __device__ __forceinline__ void run(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
-                                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
-                                        int N, int kn, int kn2, const uint16_t* As, const uint16_t* Bs, uint16_t* As_n,
-                                        uint16_t* Bs_n, const uint32_t (&wb)[BK / 8], uint32_t sb, uint32_t mb,
-                                        uint32_t (&wn)[BK / 8], uint32_t& sbn, uint32_t& mbn) {
-        const int lane = lane_id(), wave = wave_id();
+    __device__ __forceinline__ void init() {
+        const int lane = lane_id(), wave = wave_id(), tid = threadIdx.x;
         const int l32 = lane & 31, lh = lane >> 5;
-        load_b(wn, codes, N, boff, kn2);
-        sbn = scales[(size_t)(kn2 / 128) * N + bcol];
-        mbn = mins[(size_t)(kn2 / 128) * N + bcol];
-        acopy.issue(x, As_n, kn);
-        const float s = bf16_bits_to_f32(sb), m = bf16_bits_to_f32(mb);
-        // v_mfma_f32_32x32x16_bf16: lane holds A[row l%32][k 8*(l/32)..+7] and B[k same][col l%32].
-        // Fragments are double-buffered in registers: the reads for k-step ks+1 are issued in the
-        // scheduling region of k-step ks, so no MFMA waits on an LDS read.
+        sm = lds_addr(smem);
+        // A copies: instruction i of wave w fills rows w*BM/4 + 8i .. +7; lane l lands on chunk
+        // l % 8 of row l / 8 and so reads the global chunk that the swizzle maps there.  Rows past
+        // M repeat row M-1; they only feed outputs that are never stored.
+#pragma unroll
+        for (int i = 0; i < kAInst; ++i) {
+            const int r = wave * (BM / 4) + 8 * i + (lane >> 3);
+            const int gr = min(m0 + r, M - 1) - m0;
+            a_off[i] = (uint32_t)(((size_t)gr * K + 8 * a_swizzle(r, lane & 7)) * 2);
+        }
+        // Packed words, LDS layout [8 packed rows][224 columns] u32.  Vector copies (N % 4 == 0):
+        // 16-byte chunk c = row * 56 + column / 4; lanes past chunk 447 land in the stage's pad.
+        // Dword copies: dword d = row * 224 + column.  Columns past N repeat a valid column.
+#pragma unroll
+        for (int i = 0; i < kBInst; ++i) {
+            const int d = (i * 4 + wave) * kWave + lane;
+            int row, col;
+            if (kVec) {
+                const int c = min(d, 447);
+                row = c / 56;
+                col = min(n0 + 4 * (c % 56), N - 4);
+            } else {
+                row = d / BN;
+                col = min(n0 + d % BN, N - 1);
+            }
+            b_off[i] = (uint32_t)(((size_t)row * N + col) * 4);
+        }
+        // Scales (one copy) and minimums (another): slot w*64 + l receives the aligned dword that
+        // holds the bf16 of column min(n0 + min(w*64 + l, 223), N-1) in the group's row; where the
+        // dword starts depends on the parity of g*N, so both offsets are kept.
+        {
+            const int c = min(n0 + min(wave * kWave + lane, BN - 1), N - 1);
+            sc_off[0] = (uint32_t)((2 * c) & ~3);
+            sc_off[1] = (uint32_t)((2 + 2 * c) & ~3);
+        }
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                const int r = wave * (BM / 4) + i * 32 + l32;
+                a_rd[i][ks] = S::oA + (uint32_t)(r * BK + 8 * a_swizzle(r, 2 * ks + lh)) * 2;
+            }
+        b_rd = S::oBdq + (uint32_t)(l32 * LDT + 8 * lh) * 2;
+        // dequant: thread tid owns column min(tid, 223); threads past 223 write to the sink
+        const int col = min(tid, BN - 1);
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+            bq_wr[st] = tid < BN ? S::oBdq + st * S::kBdq + tid * LDT * 2 : S::oSink + (tid - BN) * 16;
+        bp_rd = S::oBp + col * 4;
+        // the bf16 of column c in group g is the (g*N + c) & 1 half of its slot
+        const int c = min(n0 + col, N - 1);
+        sc_rd[0] = S::oSc + col * 4 + 2 * (c & 1);
+        sc_rd[1] = S::oSc + col * 4 + 2 * ((c + 1) & 1);
+    }
+
+    __device__ __forceinline__ int64_t group_n(int t) const {
+        return (int64_t)((kbeg + min(t, ntiles - 1) * BK) / 128) * N;
+    }
+
+    // Copies i0 .. i1-1 of this wave's share of A of k-tile ta, into stage ta & 1.  Indices past
+    // the end fetch the last k-tile again (the data is never used; the stage is the one the index
+    // names, which no MFMA is reading).
+    __device__ __forceinline__ void issue_a(int ta, int i0 = 0, int i1 = kAInst) const {
+        const int wave = wave_id();
+        const char* base =
+            reinterpret_cast<const char*>(x) + ((size_t)m0 * K + kbeg + (size_t)min(ta, ntiles - 1) * BK) * 2;
+        const uint32_t dst = sm + S::oA + (ta & 1) * S::kA + wave * (BM / 4) * BK * 2;
+#pragma unroll
+        for (int i = i0; i < i1; ++i) dma16(a_off[i], base, dst + i * 8 * BK * 2);
+    }
+
+    // The packed words of k-tile tb into stage tb % 3 and, if kSc, its group's scales and
+    // minimums into stage (tb / 2) & 1 (tb is then the group's first k-tile).
+    template <bool kSc>
+    __device__ __forceinline__ void issue_b(int tb) const {
+        const int wave = wave_id();
+        const char* base =
+            reinterpret_cast<const char*>(codes) + (size_t)((kbeg + min(tb, ntiles - 1) * BK) / 8) * N * 4;
+        const uint32_t dst = sm + S::oBp + (tb % kBpStages) * S::kBp;
+#pragma unroll
+        for (int i = 0; i < kBInst; ++i) {
+            if (kVec)
+                dma16(b_off[i], base, dst + (i * 4 + wave) * 1024);
+            else
+                dma4(b_off[i], base, dst + (i * 4 + wave) * 256);
+        }
+        if (kSc) {
+            const int64_t gN = group_n(tb);
+            const uint32_t off = (gN & 1) ? sc_off[1] : sc_off[0];  // (no dynamic index: keeps it in a register)
+            const uint32_t sdst = sm + S::oSc + ((tb / 2) & 1) * S::kSc + wave * 256;
+            const int64_t row = (2 * gN) & ~(int64_t)3;
+            dma4(off, reinterpret_cast<const char*>(scales) + row, sdst);
+            dma4(off, reinterpret_cast<const char*>(mins) + row, sdst + 1024);
+        }
+    }
+
+    // This thread's 8 packed words of k-tile tn and its group's scale and minimum.
+    __device__ __forceinline__ void read_words(int tn, uint32_t (&w)[8], float& s, float& s16, float& m) const {
+        const uint8_t* bp = smem + bp_rd + (tn % kBpStages) * S::kBp;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) w[r] = *reinterpret_cast<const uint32_t*>(bp + r * BN * 4);
+        const uint8_t* sc = smem + ((group_n(tn) & 1) ? sc_rd[1] : sc_rd[0]) + ((tn / 2) & 1) * S::kSc;
+        s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc));
+        m = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc + 1024));
+        s16 = s * 0.0625f;
+    }
+
+    __device__ __forceinline__ void dequant_all(int st, const uint32_t (&w)[8], float s, float s16, float m) const {
+        uint8_t* dst = smem + bq_wr[st];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
+    }
+
+    // One k-tile: MFMAs on A stage `st` and dequantized B stage `st` while the words `w` (the next
+    // k-tile) are dequantized into the other B stage, two words per k-step.  issue(ks) runs at the
+    // top of each k-step: the copies for later k-tiles are spread over the tile rather than issued
+    // in one burst, which would hold up the wave's first MFMAs behind the load unit.
+    template <int st, typename Issue>
+    __device__ __forceinline__ void mma_tile(f32x16_t (&acc)[kMT][kNT], const uint32_t (&w)[8], float s, float s16,
+                                             float m, Issue&& issue) const {
+        const uint8_t* abase = smem + S::kA * st;
+        const uint8_t* bbase = smem + b_rd + S::kBdq * st;
+        uint8_t* dst = smem + bq_wr[st ^ 1];
         bf16x8_t af[2][kMT], bfr[2][kNT];
         auto read_frags = [&](int ks, int slot) {
 #pragma unroll
-            for (int i = 0; i < kMT; ++i) {
-                const int r = wave * (BM / 4) + i * 32 + l32;
-                af[slot][i] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const uint4*>(As + r * BK + 8 * a_swizzle(r, 2 * ks + lh)));
-            }
+            for (int i = 0; i < kMT; ++i)
+                af[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(abase + a_rd[i][ks]));
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
-                bfr[slot][j] = __builtin_bit_cast(
-                    bf16x8_t, *reinterpret_cast<const uint4*>(Bs + (j * 32 + l32) * LDT + 16 * ks + 8 * lh));
+                bfr[slot][j] =
+                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bbase + j * 32 * LDT * 2 + ks * 32));
         };
-        // One scheduling region per k-step (sched_barrier): the fragment reads of step ks+1, a
-        // quarter of the next B tile's dequant and the 7 * kMT independent MFMAs of step ks.
         read_frags(0, 0);
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
             __builtin_amdgcn_sched_barrier(0);
+            issue(ks);
             if (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
-            for (int r = 2 * ks; r < 2 * ks + 2; ++r) dequant_word(wb[r], r, Bs_n, s, m);
+            for (int r = 2 * ks; r < 2 * ks + 2; ++r)
+                *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
 #pragma unroll
                 for (int i = 0; i < kMT; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0,
                                                                         0, 0);
-            gemm_step_schedule<kMT>();
+            if (kMT == 2)
+                step_schedule<14, 4>(ks == 0 ? 2 : 0);
+            else
+                step_schedule<7, 7>(ks == 0 ? 1 : 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm_all();
-        __syncthreads();
     }
 };
 
-template <int BM>
+template <int BM, bool kVec>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                       const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
                       uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K, int k_per_split,
-                      int splits) {
-    constexpr int kMT = KTile<BM>::kMT;
-    __shared__ __attribute__((aligned(16))) uint16_t sa0[BM * BK], sa1[BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t sb0[kBRows * LDT], sb1[kBRows * LDT];
+                      int splits, uint32_t mask_lo, uint32_t mask_hi) {
+    using G = Gemm<BM, kVec>;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<BM>::kTotal];
     // XCD-aware tile order: block b runs on XCD b % 8, so XCD x takes the x-th contiguous eighth
     // of the (split, m, n) tile sequence, n fastest -- its blocks share A rows in its own L2.
     const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
@@ -213,59 +325,99 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
     const int t = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
     if (t >= total) return;
     const int split_id = t / (tiles_n * tiles_m);
-    const int m0 = (t / tiles_n % tiles_m) * BM, n0 = (t % tiles_n) * BN;
-    const int kbeg = split_id * k_per_split;
-    const int kend = min(K, kbeg + k_per_split);  // kend - kbeg: a multiple of 128 = 2 k-tiles
-    const int lane = lane_id(), wave = wave_id();
-    const int l32 = lane & 31, lh = lane >> 5;
 
-    KTile<BM> kt;
+    G g;
+    g.x = x;
+    g.codes = codes;
+    g.scales = scales;
+    g.mins = mins;
+    g.smem = smem;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.m0 = (t / tiles_n % tiles_m) * BM;
+    g.n0 = (t % tiles_n) * BN;
+    g.kbeg = split_id * k_per_split;
+    g.ntiles = (min(K, g.kbeg + k_per_split) - g.kbeg) / BK;  // even: splits are whole groups
+    g.mlo = mask_lo;
+    g.mhi = mask_hi;
+    g.init();
+    // the accumulators stay outside `g`: a local array is kept in registers across the copies'
+    // inline assembly, whose memory clobber would otherwise force them out to scratch
+    f32x16_t acc[G::kMT][kNT];
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < G::kMT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) kt.acc[i][j][e] = 0.0f;
-    // B column of this thread; threads >= 224 and columns past N repeat a valid column, never store
-    kt.bcol = min(n0 + min((int)threadIdx.x, BN - 1), N - 1);
-    kt.boff = (uint32_t)kt.bcol * 4u;
-    kt.acopy.init(M, K, m0);
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // prologue: tile kbeg into (sa0, sb0); the words of kbeg+64 into w0
-    kt.acopy.issue(x, sa0, kbeg);
-    load_b(kt.w0, codes, N, kt.boff, kbeg);
-    dequant_b(kt.w0, sb0, bf16_bits_to_f32(scales[(size_t)(kbeg / 128) * N + kt.bcol]),
-              bf16_bits_to_f32(mins[(size_t)(kbeg / 128) * N + kt.bcol]));
-    load_b(kt.w0, codes, N, kt.boff, kbeg + BK);
-    kt.sb0 = scales[(size_t)(kbeg / 128) * N + kt.bcol];  // kbeg + 64 is in the same group
-    kt.mb0 = mins[(size_t)(kbeg / 128) * N + kt.bcol];
-    wait_vm_all();
+    // Prologue: A(0), the words of k-tiles 0..2 and the scales of groups 0 and 1; k-tile 0 is
+    // then dequantized into B stage 0.
+    g.issue_a(0);
+    g.template issue_b<true>(0);
+    g.template issue_b<false>(1);
+    g.template issue_b<true>(2);
+    wait_vm<0>();
+    __syncthreads();
+    {
+        uint32_t w[8];
+        float s, s16, m;
+        g.read_words(0, w, s, s16, m);
+        g.dequant_all(0, w, s, s16, m);
+    }
     __syncthreads();
 
-    // two k-tiles per trip so every buffer and register set is fixed; the last trip's look-ahead
-    // loads are clamped to the last tile and their results unused
-    for (int k0 = kbeg; k0 < kend; k0 += 2 * BK) {
-        kt.run(x, codes, scales, mins, N, min(k0 + BK, kend - BK), min(k0 + 2 * BK, kend - BK), sa0, sb0, sa1, sb1,
-               kt.w0, kt.sb0, kt.mb0, kt.w1, kt.sb1, kt.mb1);
-        kt.run(x, codes, scales, mins, N, min(k0 + 2 * BK, kend - BK), min(k0 + 3 * BK, kend - BK), sa1, sb1, sa0,
-               sb0, kt.w1, kt.sb1, kt.mb1, kt.w0, kt.sb0, kt.mb0);
+    // k-tile t: read the words of t+1; run the MFMAs of t while dequantizing t+1 and copying
+    // A(t+1) (a quarter per k-step) and then the words of t+3 (with their group's scales when
+    // t+3 starts a group, i.e. t is odd); then wait until A(t+1) and everything issued before it
+    // has landed (the words of t+2 and their scales were issued during t-1) and meet at the
+    // barrier.
+    constexpr int kAPerStep = G::kAInst / (BK / 16);
+    constexpr int kAfterA = G::kBInst;  // copies issued after A in an even k-tile (+2 in an odd one)
+    for (int tt = 0; tt < g.ntiles; tt += 2) {
+        {
+            uint32_t w[8];
+            float s, s16, m;
+            g.read_words(tt + 1, w, s, s16, m);
+            g.template mma_tile<0>(acc, w, s, s16, m, [&](int ks) {
+                g.issue_a(tt + 1, ks * kAPerStep, (ks + 1) * kAPerStep);
+                if (ks == BK / 16 - 1) g.template issue_b<false>(tt + 3);
+            });
+            wait_vm<kAfterA>();
+            __syncthreads();
+        }
+        {
+            uint32_t w[8];
+            float s, s16, m;
+            g.read_words(tt + 2, w, s, s16, m);
+            g.template mma_tile<1>(acc, w, s, s16, m, [&](int ks) {
+                g.issue_a(tt + 2, ks * kAPerStep, (ks + 1) * kAPerStep);
+                if (ks == BK / 16 - 1) g.template issue_b<true>(tt + 4);
+            });
+            wait_vm<kAfterA + 2>();
+            __syncthreads();
+        }
     }
+    wait_vm<0>();  // no copy may still be writing this block's LDS when it exits
 
     // D fragment of a 32 x 32 tile: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+    const int lane = lane_id(), wave = wave_id();
+    const int l32 = lane & 31, lh = lane >> 5;
     const bool split = splits > 1;
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < G::kMT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
-            const int col = n0 + j * 32 + l32;
+            const int col = g.n0 + j * 32 + l32;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = m0 + wave * (BM / 4) + i * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
+                const int row = g.m0 + wave * (BM / 4) + i * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
                 if (row < M && col < N) {
                     if (split)
-                        ws[((size_t)split_id * M + row) * N + col] = kt.acc[i][j][e];
+                        ws[((size_t)split_id * M + row) * N + col] = acc[i][j][e];
                     else
-                        y[(size_t)row * N + col] = f32_to_bf16_bits(kt.acc[i][j][e]);
+                        y[(size_t)row * N + col] = f32_to_bf16_bits(acc[i][j][e]);
                 }
             }
         }
@@ -281,12 +433,12 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     y[i] = f32_to_bf16_bits(s);
 }
 
-struct Plan {
+struct GemmPlan {
     int bm, tiles_m, tiles_n, splits, k_per_split;
 };
 
-Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
-    Plan p;
+GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
+    GemmPlan p;
     p.bm = M > 128 ? 256 : 128;  // 128: a wave owns one 32-row tile
     p.tiles_m = (int)((M + p.bm - 1) / p.bm);
     p.tiles_n = (int)((N + BN - 1) / BN);
@@ -301,31 +453,39 @@ Plan plan_gemm(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
-template <int BM>
-void launch_bm(const Plan& p, const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+template <int BM, bool kVec>
+void launch_bm(const GemmPlan& p, const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace, hipStream_t stream) {
     // a 1-D grid of 8 x ceil(tiles / 8) blocks over (split, m, n); the surplus exit at once
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m * p.splits;
     const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
-    hipLaunchKernelGGL((gemm_g128_kernel<BM>), grid, dim3(kThreads), 0, stream, x, codes, scales, mins, y, workspace,
-                       (int)M, (int)N, (int)K, p.k_per_split, p.splits);
+    hipLaunchKernelGGL((gemm_g128_kernel<BM, kVec>), grid, dim3(kThreads), 0, stream, x, codes, scales, mins, y,
+                       workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu, 0xF0F0F0F0u);
 }
 
 }  // namespace
 
 size_t gemm_g128_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-    const Plan p = plan_gemm(M, N, K);
+    const GemmPlan p = plan_gemm(M, N, K);
     return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                             const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace,
                             hipStream_t stream) {
-    const Plan p = plan_gemm(M, N, K);
-    if (p.bm == 256)
-        launch_bm<256>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
-    else
-        launch_bm<128>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
+    const GemmPlan p = plan_gemm(M, N, K);
+    const bool vec = N % 4 == 0;
+    if (p.bm == 256) {
+        if (vec)
+            launch_bm<256, true>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
+        else
+            launch_bm<256, false>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
+    } else {
+        if (vec)
+            launch_bm<128, true>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
+        else
+            launch_bm<128, false>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
     const int64_t MN = M * N;

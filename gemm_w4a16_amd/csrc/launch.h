@@ -8,6 +8,12 @@
 
 namespace w4a16 {
 
+// hipGetLastError returns the last error of any runtime call made on this thread -- also of
+// calls the caller made before calling into this library and did not check (a "not ready" from
+// a query, say).  Each entry point clears it before it launches, so that the hipGetLastError
+// after a launch reports that launch alone.
+inline void clear_stale_error() { (void)hipGetLastError(); }
+
 hipError_t launch_pack_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,
                             uint16_t* mins, hipStream_t stream);
 hipError_t launch_pack_q4b32(const float* W, int64_t N, int64_t K, uint8_t* codes, uint16_t* scales,

@@ -30,7 +30,9 @@
  *  - Arguments are validated on the host, before anything is enqueued.  A failed check
  *    returns W4A16_ERR_INVALID (bad value, null or misaligned pointer) or
  *    W4A16_ERR_UNSUPPORTED (a valid combination this build does not implement) and touches
- *    no memory.  A HIP error while enqueuing returns W4A16_ERR_DEVICE.
+ *    no memory.  A HIP error while enqueuing returns W4A16_ERR_DEVICE.  Before it enqueues,
+ *    a call clears the calling thread's pending HIP error (hipGetLastError), which may have
+ *    been left by an earlier, unrelated runtime call, so that only its own launches are judged.
  *  - Every pointer must be 16-byte aligned; arrays are dense and row-major as documented.
  *  - Sizes are int64_t; M, N, K must be positive.  N needs no particular multiple.
  *  - Weights given to the quantizers must be finite (non-finite input is undefined).
@@ -77,7 +79,11 @@ typedef enum {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* w4a16_status_string(w4a16_status_t status);
 
-/* Bytes of the three packed arrays of an N x K weight in `fmt` (mins is 0 for the Q4 format).
+/* Bytes to allocate for the three packed arrays of an N x K weight in `fmt` (mins is 0 for the
+ * Q4 format).  For G128 the scale and minimum sizes are the arrays' sizes rounded up to a
+ * multiple of 4 bytes: the GEMM reads them as aligned 4-byte words, so when (K/128)*N is odd
+ * the last word covers 2 bytes past the last element (read, never written, value unused).
+ * Buffers passed to the matmul entry points must have at least these sizes.
  * Pure host arithmetic; any output pointer may be NULL.  ERR_INVALID if N, K <= 0 or K is not a
  * multiple of the format's group (128 or 32). */
 w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K,

@@ -45,7 +45,11 @@ def test_packed_sizes_match_the_formats():
     # Q4: 16 B of codes + 2 B scale per 32 weights (16384^2: 144 MiB in all)
     c, s, m = w.w4a16_packed_sizes(Q4, 16384, 16384)
     assert (c, s, m) == (134_217_728, 16_777_216, 0) and c + s == 144 * 2 ** 20
-    assert w.w4a16_packed_sizes(G128, 1, 128) == (64, 2, 2)
+    # an odd scale count is padded to whole 4-byte words (the GEMM reads scales as aligned words)
+    assert w.w4a16_packed_sizes(G128, 1, 128) == (64, 4, 4)
+    assert w.w4a16_packed_sizes(G128, 3, 384) == (576, 20, 20)
+    assert w.w4a16_packed_sizes(G128, 2, 128) == (128, 4, 4)
+    assert w.w4a16_packed_sizes(Q4, 1, 32) == (16, 2, 0)
 
 
 @pytest.mark.parametrize("fmt,N,K", [(G128, 0, 128), (G128, 5, 0), (G128, 5, 64), (G128, 5, 200), (Q4, 5, 48),
