@@ -466,6 +466,7 @@ void launch_bm(const GemmPlan& p, const uint16_t* x, int64_t M, const uint32_t* 
 }  // namespace
 
 size_t gemm_g128_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    if (M <= kMidMaxRows) return 0;
     const GemmPlan p = plan_gemm(M, N, K);
     return p.splits > 1 ? (size_t)p.splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
@@ -473,6 +474,7 @@ size_t gemm_g128_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                             const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace,
                             hipStream_t stream) {
+    if (M <= kMidMaxRows) return launch_mid_g128(x, M, codes, scales, mins, N, K, y, stream);
     const GemmPlan p = plan_gemm(M, N, K);
     const bool vec = N % 4 == 0;
     if (p.bm == 256) {

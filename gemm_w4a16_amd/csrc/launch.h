@@ -32,7 +32,13 @@ hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* code
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
-// Large-M G128 path on bf16 MFMA.
+// Mid-M G128 path (kGemvMaxRows < M <= kMidMaxRows): weights streamed once per 64-row slice,
+// dequantized straight into MFMA fragments; no workspace.
+constexpr int kMidMaxRows = 64;  // measured: beyond 64 rows the large-M kernel is faster
+hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                           const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+
+// Large-M G128 path on bf16 MFMA (the mid path below kMidMaxRows rows).
 size_t gemm_g128_workspace_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                             const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace,

@@ -99,14 +99,16 @@ def test_gemv_validation():
 
 
 def test_gemm_validation_and_workspace():
-    # a shape whose tile grid is small needs a K-split workspace; too little is refused on the host
-    need = w.w4a16_gemm_workspace_bytes(G128, 64, 256, 4096)
-    assert need > 0 and need % (64 * 256 * 4) == 0
-    assert w.w4a16_gemm_workspace_bytes(Q4, 64, 256, 4096) == 0
+    # a large-M shape whose tile grid is small needs a K-split workspace; too little is refused
+    # on the host.  Up to 64 rows the GEMM streams the weights per row slice and needs none.
+    need = w.w4a16_gemm_workspace_bytes(G128, 300, 256, 4096)
+    assert need > 0 and need % (300 * 256 * 4) == 0
+    assert w.w4a16_gemm_workspace_bytes(G128, 64, 256, 4096) == 0
+    assert w.w4a16_gemm_workspace_bytes(Q4, 300, 256, 4096) == 0
     assert w.w4a16_gemm_workspace_bytes(G128, 0, 256, 4096) == 0
     g = w.w4a16_gemm
-    assert _status(g, G128, BF16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, FAKE, need - 4, 0) == w.W4A16_ERR_INVALID
-    assert _status(g, G128, BF16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, FAKE, need - 4, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_INVALID
     assert _status(g, Q4, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_UNSUPPORTED
     m = w.w4a16_matmul
     assert _status(m, Q4, F16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, None, 64, 64, FAKE, None, 0, 0) \

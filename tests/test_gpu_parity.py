@@ -155,7 +155,7 @@ def test_gemv_g128_parity(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(5, 200, 256), (64, 256, 4096), (130, 260, 384), (257, 131, 1024),
                                    (128, 128, 128), (300, 520, 640), (17, 65, 384), (33, 131, 384),
-                                   (513, 230, 1152)])
+                                   (513, 230, 1152), (50, 97, 1152), (64, 1000, 640)])
 def test_gemm_g128_parity(M, N, K):
     say(f"gemm_g128 M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=13)
