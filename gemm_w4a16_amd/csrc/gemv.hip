@@ -13,8 +13,9 @@
 //  * The offset B and the bias 8 are removed once per block: s * (sum(x*(B+q)) - (B+8)*sum(x)).
 //
 // Layout: codes are [N][K/32][16] bytes (a row's blocks contiguous), so 16 lanes read 512 B
-// of one row per pair of 16-byte loads and a wave covers 4 rows per step.  Each lane always
-// handles the same 64 k of the row, so its activations are loaded once, kept in VGPRs already
+// of one row per pair of 16-byte loads (256 contiguous bytes each) and a wave covers 4 rows per
+// step.  Each lane always handles the same two blocks (64 k) of the row, so its activations
+// are loaded once, kept in VGPRs already
 // paired, and their per-block sums folded into a constant.  The 16 lanes of a row finish with a
 // DPP row reduction; the 16 waves of a 1024-thread block own 16 K-slices and add in LDS.
 #include "device_common.h"
@@ -38,8 +39,9 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a 
 // Q4 block-32: 1024 threads = 16 waves = 16 K-slices of 1024 k; 64 rows per block.
 // ---------------------------------------------------------------------------------------------
 constexpr int kQ4Waves = 16;
-constexpr int kQ4Rows = 64;   // rows per block = 16 steps x 4 rows
-constexpr int kQ4Unroll = 4;  // row steps whose loads are in flight together
+constexpr int kQ4Rows = 64;               // rows per block
+constexpr int kQ4Steps = kQ4Rows / 4;      // a wave step covers 4 rows
+constexpr int kQ4Pair = 4;                 // row steps whose loads are in flight together
 
 template <bool kF16>
 __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __restrict__ x,
@@ -59,19 +61,26 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
     for (int t = threadIdx.x & 63; t < kQ4Rows; t += 64) part[wave][t] = 0.0f;
 
     for (int slice = wave; slice * 32 < B; slice += kQ4Waves) {
-        const int b0 = slice * 32 + sub * 2;  // this lane's two blocks
-        const bool has0 = b0 < B, has1 = b0 + 1 < B;
+        // this lane's two blocks, 16 apart: each load instruction of a row's 16 lanes then reads
+        // 256 contiguous bytes (whole cache lines) rather than every other 16 bytes of 512
+        const int b0 = slice * 32 + sub, b1 = b0 + 16;
+        const bool has0 = b0 < B, has1 = b1 < B;
+        // A block past the row's end is read at a clamped index and its contribution dropped by a
+        // select after the load: no load sits under a branch (a branch would make every load
+        // wait for all earlier ones).
+        const int bb0 = min(b0, B - 1), bb1 = min(b1, B - 1);
         // activations of the two blocks, paired (x_j, x_{j+4}) per 8 k, and their sums
         uint32_t xq[2][16];
         float cst[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool has = h ? has1 : has0;
-            const uint4* xr = reinterpret_cast<const uint4*>(x + (size_t)(b0 + h) * 32);
+            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * 32);
             float sum = 0.0f;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const uint4 xv = has ? xr[d] : make_uint4(0, 0, 0, 0);
+                const u32x4_t xl = xr[d];
+                const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
                 xq[h][4 * d + 0] = pack_lo(xv.x, xv.z);
                 xq[h][4 * d + 1] = pack_hi(xv.x, xv.z);
                 xq[h][4 * d + 2] = pack_lo(xv.y, xv.w);
@@ -83,41 +92,52 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
             }
             cst[h] = -offset * sum;
         }
-#pragma unroll 1
-        for (int t0 = 0; t0 < kQ4Rows / 4; t0 += kQ4Unroll) {
-            uint4 cw[kQ4Unroll][2];
-            uint32_t sc[kQ4Unroll][2];
+        // Row steps of 4 rows, kQ4Pair at a time: all their loads are issued, then the rows are
+        // computed in order as their data arrives.
+        struct Rows {
+            u32x4_t c[kQ4Pair][2];
+            uint32_t s[kQ4Pair][2];
+        };
+        auto load = [&](int t0, Rows& R) {
 #pragma unroll
-            for (int u = 0; u < kQ4Unroll; ++u) {
+            for (int u = 0; u < kQ4Pair; ++u) {
                 int n = n0 + 4 * (t0 + u) + rsub;
                 n = n < N ? n : N - 1;
-                const uint4* cr = reinterpret_cast<const uint4*>(codes) + (size_t)n * B;  // 16 B per block
-                cw[u][0] = has0 ? cr[b0] : make_uint4(0, 0, 0, 0);
-                cw[u][1] = has1 ? cr[b0 + 1] : make_uint4(0, 0, 0, 0);
-                sc[u][0] = has0 ? scales[(size_t)n * B + b0] : 0u;
-                sc[u][1] = has1 ? scales[(size_t)n * B + b0 + 1] : 0u;
+                const u32x4_t* cr = reinterpret_cast<const u32x4_t*>(codes) + (size_t)n * B;  // 16 B per block
+                R.c[u][0] = cr[bb0];
+                R.c[u][1] = cr[bb1];
+                const uint32_t s0 = scales[(size_t)n * B + bb0], s1 = scales[(size_t)n * B + bb1];
+                R.s[u][0] = has0 ? s0 : 0u;  // fp16 +0: the block contributes nothing
+                R.s[u][1] = has1 ? s1 : 0u;
             }
+        };
+        auto compute = [&](int t0, const Rows& R) {
 #pragma unroll
-            for (int u = 0; u < kQ4Unroll; ++u) {
+            for (int u = 0; u < kQ4Pair; ++u) {
                 float part_row = 0.0f;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    const uint32_t wd[4] = {cw[u][h].x, cw[u][h].y, cw[u][h].z, cw[u][h].w};
                     float acc = cst[h];
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
-                            const uint32_t p = ((wd[d] >> (4 * e)) & kNibblePairMask) | magic;
+                            const uint32_t p = ((R.c[u][h][d] >> (4 * e)) & kNibblePairMask) | magic;
                             acc = kF16 ? dot2_f16(p, xq[h][4 * d + e], acc) : dot2_bf16(p, xq[h][4 * d + e], acc);
                         }
                     }
-                    part_row = __builtin_fmaf(f16_bits_to_f32(sc[u][h]), acc, part_row);
+                    part_row = __builtin_fmaf(f16_bits_to_f32(R.s[u][h]), acc, part_row);
                 }
                 // the 16 lanes of a row -> one value, added to this wave's slot for the row
                 const float v = row16_sum(part_row);
                 if (sub == 15) part[wave][4 * (t0 + u) + rsub] += v;
             }
+        };
+#pragma unroll 1
+        for (int t0 = 0; t0 < kQ4Steps; t0 += kQ4Pair) {
+            Rows r;
+            load(t0, r);
+            compute(t0, r);
         }
     }
     // the 16 K-slices of each row, added through LDS in a fixed order
