@@ -53,6 +53,8 @@ def recorded_traffic(kernel: str):
         return None
     if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
         return None
+    if rec.get("fetch_bytes") is None or rec.get("write_bytes") is None:
+        return None
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
