@@ -4,20 +4,22 @@
 // integers (shift/mask, then q * scale + min in fp32 rounded to bf16) and feeds it to the
 // tensor-core dot with fp32 accumulation; BF16 weights never reach memory.  Here that becomes:
 //
-//  * block tile BM x 224 (N) x 64 (K).  N = 224 = 7 x 32 so that the Llama up-projection width
-//    14336 = 64 x 224 splits into exactly 64 column tiles and M = 1024 into 4 x 256: 256 blocks
-//    for the 256 CUs (a power-of-two N tile would leave 1/8 of the chip idle);
-//  * 256 threads = 4 waves stacked along M; a wave owns (BM/4) x 224 outputs as (BM/128) x 7
-//    v_mfma_f32_32x32x16_bf16 accumulators (on gfx950 this shape runs at twice the rate of
-//    16x16x32);
+//  * block tile BM x BN x 64 (K), 256 threads = 4 waves in a WM x (4/WM) grid; a wave owns
+//    (BM/WM) x (BN/(4/WM)) outputs as 32x32 v_mfma_f32_32x32x16_bf16 accumulators (on gfx950
+//    this shape runs at twice the rate of 16x16x32).  The tile is chosen so that the grid fills
+//    the 256 CUs without splitting K where it can: 256 x 224 (waves stacked along M) at
+//    M = 1024, since 14336 = 64 x 224 and 1024 = 4 x 256 give exactly 256 tiles -- a
+//    power-of-two N tile would leave 1/8 of the chip idle; 128 x 256, 128 x 128 and 64 x 128
+//    (2 x 2 waves) for 512, 256 and 128 rows (224 tiles);
 //  * every global read in the k-loop is a direct-to-LDS copy by the load unit (global_load_lds)
 //    issued ahead of its use: the A tile one k-tile ahead (two LDS stages, XOR-swizzled rows),
 //    the packed B words three k-tiles ahead (three stages) and each group's scales and minimums
 //    with its first k-tile.  The copies are issued in an order that lets one `s_waitcnt vmcnt(n)`
 //    before each k-tile's barrier wait only for what the next k-tile needs, so no wave waits on
 //    HBM latency inside the loop;
-//  * while the MFMAs of k-tile t read one dequantized B stage, thread c < 224 turns the 8 packed
-//    words of column c of k-tile t+1 into the other: w_hat = bf16_rne(fmaf(q, s, min)), the
+//  * while the MFMAs of k-tile t read one dequantized B stage, the threads turn the 8 packed words
+//    of each column of k-tile t+1 into the other (one column per thread, or two or four threads
+//    per column when BN < 256): w_hat = bf16_rne(fmaf(q, s, min)), the
 //    same value as the reference dequant, 22 VALU instructions per word, interleaved with the
 //    MFMAs (about four VALU instructions fit under one 32x32x16 MFMA).  Each word becomes one
 //    16-byte row segment of an [n][k] tile, which is exactly an MFMA B fragment; rows are padded
@@ -32,31 +34,35 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int BN = 224, BK = 64;
+constexpr int BK = 64;
 constexpr int LDT = BK + 8;  // dequantized B tile row pitch in bf16 (144 B)
 constexpr int kThreads = 256;
 constexpr int kCUs = 256;
-constexpr int kNT = BN / 32;  // 32-column MFMA tiles per wave (each wave spans all 224 columns)
-constexpr int kBpStages = 3;  // packed-word stages: k-tiles t+1 (being dequantized) .. t+3 (in flight)
 
-// LDS map (byte offsets).  A and the dequantized B have two stages (k-tiles t and t+1), the
-// packed words three, the scales/minimums two (one per group; a group is two k-tiles).
-template <int BM>
+// Copy distances: at k-tile t the A tile of t+DA and the packed words of t+DB are requested.
+// A then needs DA+1 LDS stages, the packed words DB, the scales/minimums (one stage per group of
+// two k-tiles) DB/2 + 1; the dequantized B has two (k-tiles t and t+1).  Short k-tiles (small
+// tiles) need longer distances to cover the latency.
+template <int BM, int BN, int DA, int DB>
 struct Smem {
+    static_assert(DA >= 1 && DB >= DA + 2, "the words of t+2 must be requested before A(t+1)");
+    static constexpr int kAS = DA + 1, kBS = DB, kSS = DB / 2 + 1;
+    static constexpr int kBpChunks = (2 * BN + 255) / 256 * 256;  // 16-byte chunks of a packed stage
     static constexpr int kA = BM * BK * 2;     // A stage: BM rows x 64 bf16
-    static constexpr int kBdq = BN * LDT * 2;  // dequantized B stage: 224 rows x 144 B
-    static constexpr int kBp = 512 * 16;       // packed stage: [8 packed rows][224 columns] u32 + pad
+    static constexpr int kBdq = BN * LDT * 2;  // dequantized B stage: BN rows x 144 B
+    static constexpr int kBp = kBpChunks * 16;  // packed stage: [8 packed rows][BN columns] u32 + pad
     static constexpr int kSc = 512 * 4;        // 256 scale slots + 256 minimum slots, a dword each
     static constexpr int oA = 0;
-    static constexpr int oBdq = oA + 2 * kA;
-    // written by the 32 threads past column 223: thread 224 + u stores its row segment r at
-    // 16 (u + r), so (32 + 7) x 16 B, rounded up
+    static constexpr int oBdq = oA + kAS * kA;
+    // written by the threads past column BN-1 when a column has one thread: thread BN + u
+    // stores its row segment r at 16 (u + r), so (256 - BN + 7) x 16 B, rounded up
+    static constexpr int kSink = BN < 256 && BN > 128 ? ((256 - BN + 7) * 16 + 127) / 128 * 128 : 0;
     static constexpr int oSink = oBdq + 2 * kBdq;
-    static constexpr int oBp = oSink + 640;
-    static constexpr int oSc = oBp + kBpStages * kBp;
-    static constexpr int kTotal = oSc + 2 * kSc;
+    static constexpr int oBp = oSink + kSink;
+    static constexpr int oSc = oBp + kBS * kBp;
+    static constexpr int kTotal = oSc + kSS * kSc;
 };
-static_assert(Smem<256>::kTotal <= 160 * 1024, "LDS budget");
+
 
 // A tiles: rows of 64 bf16 (128 B), unpadded; the 16-byte chunk c of row r sits at chunk
 // c ^ ((r >> 1) & 7), which keeps the 16 rows of a fragment read on 16 distinct 4-bank groups.
@@ -123,12 +129,35 @@ __device__ __forceinline__ void step_schedule(int lead) {
     }
 }
 
-template <int BM, bool kVec>
+template <int BM, int BN, int WM, int DA, int DB, bool kVec>
 struct Gemm {
-    static constexpr int kMT = BM / 128;        // 32-row MFMA tiles per wave (a wave owns BM/4 rows)
-    static constexpr int kAInst = BM / 32;      // A copies per wave per k-tile (1 KB each)
-    static constexpr int kBInst = kVec ? 2 : 7;  // packed-word copies per wave per k-tile
-    using S = Smem<BM>;
+    static constexpr int WN = 4 / WM;
+    static constexpr int kWRows = BM / WM, kWCols = BN / WN;  // a wave's output tile
+    static constexpr int kMT = kWRows / 32, kNT = kWCols / 32;  // its 32 x 32 MFMA tiles
+    static_assert(kMT >= 1 && kNT >= 1 && kWRows % 32 == 0 && kWCols % 32 == 0, "wave tile");
+    static constexpr int kAInst = BM / 32;  // A copies per wave per k-tile (1 KB each)
+    static constexpr int kBInst = kVec ? Smem<BM, BN, DA, DB>::kBpChunks / 256 : 8 * BN / 256;  // packed-word copies
+    // dequant: kTPC threads per column, each converting kWPT of its 8 packed words per k-tile
+    static constexpr int kTPC = BN <= 128 ? 256 / BN : 1;
+    static constexpr int kWPT = 8 / kTPC;
+    static_assert(BN <= 256 && (BN > 128 || 256 % BN == 0), "dequant split");
+    using S = Smem<BM, BN, DA, DB>;
+    static_assert(S::kTotal <= 160 * 1024, "LDS budget");
+    // schedule: kMFMA MFMAs per k-step; the first kLead of k-step 0 carry no dequant (its words
+    // are still coming from LDS); kVPM VALU slots after each of the others
+    static constexpr int kMFMA = kMT * kNT;
+    static constexpr int kLead = kMFMA >= 8 ? 2 : 0;
+    static constexpr int kValuPerStep = 22 * kWPT / (BK / 16) + 2;
+    static constexpr int kVPM = (kValuPerStep + kMFMA - kLead - 1) / (kMFMA - kLead);
+
+    // Copies a wave may still have in flight at the end of k-tile t (parity p) once A(t+1) has
+    // landed: the rest of k-tile t+1-DA (its words and scales) and all of k-tiles t+2-DA .. t.
+    static constexpr int sc_copies(int u) { return ((u + DB) & 1) == 0 ? 2 : 0; }  // scales at k-tile u
+    static constexpr int after_a(int p) {
+        int n = kBInst + sc_copies(p + 1 - DA);
+        for (int u = p + 2 - DA; u <= p; ++u) n += kAInst + kBInst + sc_copies(u);
+        return n;
+    }
 
     const uint16_t* x;
     const uint32_t* codes;
@@ -140,18 +169,19 @@ struct Gemm {
     uint32_t mlo, mhi;
     // per-lane byte offsets of the copies (constant over the k-loop)
     uint32_t a_off[kAInst];  // from the k-tile's A base
-    uint32_t b_off[kBInst];  // from the k-tile's first packed row
+    uint32_t b_off[kBInst > 0 ? kBInst : 1];  // from the k-tile's first packed row
     uint32_t sc_off[2];      // scale/min dword for even / odd g*N
     // this thread's LDS byte offsets (from smem, without the stage)
     uint32_t a_rd[kMT][BK / 16];  // A fragment (i, k-step)
     uint32_t b_rd;                // B fragment of j = 0, k-step 0
     uint32_t bq_wr[2];            // dequantized row segment, per destination stage
-    uint32_t bp_rd;               // packed word of row 0 of this thread's column
+    uint32_t bp_rd;               // packed word of this thread's first row, this thread's column
     uint32_t sc_rd[2];            // scale of this thread's column, for even / odd g*N
 
     __device__ __forceinline__ void init() {
         const int lane = lane_id(), wave = wave_id(), tid = threadIdx.x;
         const int l32 = lane & 31, lh = lane >> 5;
+        const int wm = wave % WM, wn = wave / WM;
         sm = lds_addr(smem);
         // A copies: instruction i of wave w fills rows w*BM/4 + 8i .. +7; lane l lands on chunk
         // l % 8 of row l / 8 and so reads the global chunk that the swizzle maps there.  Rows past
@@ -162,17 +192,17 @@ struct Gemm {
             const int gr = min(m0 + r, M - 1) - m0;
             a_off[i] = (uint32_t)(((size_t)gr * K + 8 * a_swizzle(r, lane & 7)) * 2);
         }
-        // Packed words, LDS layout [8 packed rows][224 columns] u32.  Vector copies (N % 4 == 0):
-        // 16-byte chunk c = row * 56 + column / 4; lanes past chunk 447 land in the stage's pad.
-        // Dword copies: dword d = row * 224 + column.  Columns past N repeat a valid column.
+        // Packed words, LDS layout [8 packed rows][BN columns] u32.  Vector copies (N % 4 == 0):
+        // 16-byte chunk c = row * BN/4 + column / 4; lanes past the last chunk land in the stage's
+        // pad.  Dword copies: dword d = row * BN + column.  Columns past N repeat a valid column.
 #pragma unroll
         for (int i = 0; i < kBInst; ++i) {
             const int d = (i * 4 + wave) * kWave + lane;
             int row, col;
             if (kVec) {
-                const int c = min(d, 447);
-                row = c / 56;
-                col = min(n0 + 4 * (c % 56), N - 4);
+                const int c = min(d, 2 * BN - 1);
+                row = c / (BN / 4);
+                col = min(n0 + 4 * (c % (BN / 4)), N - 4);
             } else {
                 row = d / BN;
                 col = min(n0 + d % BN, N - 1);
@@ -180,8 +210,8 @@ struct Gemm {
             b_off[i] = (uint32_t)(((size_t)row * N + col) * 4);
         }
         // Scales (one copy) and minimums (another): slot w*64 + l receives the aligned dword that
-        // holds the bf16 of column min(n0 + min(w*64 + l, 223), N-1) in the group's row; where the
-        // dword starts depends on the parity of g*N, so both offsets are kept.
+        // holds the bf16 of column min(n0 + min(w*64 + l, BN-1), N-1) in the group's row; where
+        // the dword starts depends on the parity of g*N, so both offsets are kept.
         {
             const int c = min(n0 + min(wave * kWave + lane, BN - 1), N - 1);
             sc_off[0] = (uint32_t)((2 * c) & ~3);
@@ -191,16 +221,19 @@ struct Gemm {
         for (int i = 0; i < kMT; ++i)
 #pragma unroll
             for (int ks = 0; ks < BK / 16; ++ks) {
-                const int r = wave * (BM / 4) + i * 32 + l32;
+                const int r = wm * kWRows + i * 32 + l32;
                 a_rd[i][ks] = S::oA + (uint32_t)(r * BK + 8 * a_swizzle(r, 2 * ks + lh)) * 2;
             }
-        b_rd = S::oBdq + (uint32_t)(l32 * LDT + 8 * lh) * 2;
-        // dequant: thread tid owns column min(tid, 223); threads past 223 write to the sink
-        const int col = min(tid, BN - 1);
+        b_rd = S::oBdq + (uint32_t)((wn * kWCols + l32) * LDT + 8 * lh) * 2;
+        // dequant: thread tid converts words h*kWPT .. of column col (one column per thread when
+        // BN > 128, the threads past column BN-1 writing to the sink; else kTPC per column)
+        const int col = kTPC > 1 ? tid % BN : min(tid, BN - 1);
+        const int h = kTPC > 1 ? tid / BN : 0;
 #pragma unroll
         for (int st = 0; st < 2; ++st)
-            bq_wr[st] = tid < BN ? S::oBdq + st * S::kBdq + tid * LDT * 2 : S::oSink + (tid - BN) * 16;
-        bp_rd = S::oBp + col * 4;
+            bq_wr[st] = (kTPC > 1 || tid < BN) ? S::oBdq + st * S::kBdq + col * LDT * 2 + h * kWPT * 16
+                                               : S::oSink + (tid - BN) * 16;
+        bp_rd = S::oBp + col * 4 + h * kWPT * BN * 4;
         // the bf16 of column c in group g is the (g*N + c) & 1 half of its slot
         const int c = min(n0 + col, N - 1);
         sc_rd[0] = S::oSc + col * 4 + 2 * (c & 1);
@@ -211,26 +244,26 @@ struct Gemm {
         return (int64_t)((kbeg + min(t, ntiles - 1) * BK) / 128) * N;
     }
 
-    // Copies i0 .. i1-1 of this wave's share of A of k-tile ta, into stage ta & 1.  Indices past
+    // Copies i0 .. i1-1 of this wave's share of A of k-tile ta, into stage ta % kAS.  Indices past
     // the end fetch the last k-tile again (the data is never used; the stage is the one the index
     // names, which no MFMA is reading).
     __device__ __forceinline__ void issue_a(int ta, int i0 = 0, int i1 = kAInst) const {
         const int wave = wave_id();
         const char* base =
             reinterpret_cast<const char*>(x) + ((size_t)m0 * K + kbeg + (size_t)min(ta, ntiles - 1) * BK) * 2;
-        const uint32_t dst = sm + S::oA + (ta & 1) * S::kA + wave * (BM / 4) * BK * 2;
+        const uint32_t dst = sm + S::oA + (ta % S::kAS) * S::kA + wave * (BM / 4) * BK * 2;
 #pragma unroll
         for (int i = i0; i < i1; ++i) dma16(a_off[i], base, dst + i * 8 * BK * 2);
     }
 
-    // The packed words of k-tile tb into stage tb % 3 and, if kSc, its group's scales and
-    // minimums into stage (tb / 2) & 1 (tb is then the group's first k-tile).
+    // The packed words of k-tile tb into stage tb % kBS and, if kSc, its group's scales and
+    // minimums into stage (tb / 2) % kSS (tb is then the group's first k-tile).
     template <bool kSc>
     __device__ __forceinline__ void issue_b(int tb) const {
         const int wave = wave_id();
         const char* base =
             reinterpret_cast<const char*>(codes) + (size_t)((kbeg + min(tb, ntiles - 1) * BK) / 8) * N * 4;
-        const uint32_t dst = sm + S::oBp + (tb % kBpStages) * S::kBp;
+        const uint32_t dst = sm + S::oBp + (tb % S::kBS) * S::kBp;
 #pragma unroll
         for (int i = 0; i < kBInst; ++i) {
             if (kVec)
@@ -241,38 +274,39 @@ struct Gemm {
         if (kSc) {
             const int64_t gN = group_n(tb);
             const uint32_t off = (gN & 1) ? sc_off[1] : sc_off[0];  // (no dynamic index: keeps it in a register)
-            const uint32_t sdst = sm + S::oSc + ((tb / 2) & 1) * S::kSc + wave * 256;
+            const uint32_t sdst = sm + S::oSc + ((tb / 2) % S::kSS) * S::kSc + wave * 256;
             const int64_t row = (2 * gN) & ~(int64_t)3;
             dma4(off, reinterpret_cast<const char*>(scales) + row, sdst);
             dma4(off, reinterpret_cast<const char*>(mins) + row, sdst + 1024);
         }
     }
 
-    // This thread's 8 packed words of k-tile tn and its group's scale and minimum.
-    __device__ __forceinline__ void read_words(int tn, uint32_t (&w)[8], float& s, float& s16, float& m) const {
-        const uint8_t* bp = smem + bp_rd + (tn % kBpStages) * S::kBp;
+    // This thread's kWPT packed words of k-tile tn and its group's scale and minimum.
+    __device__ __forceinline__ void read_words(int tn, uint32_t (&w)[kWPT], float& s, float& s16, float& m) const {
+        const uint8_t* bp = smem + bp_rd + (tn % S::kBS) * S::kBp;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) w[r] = *reinterpret_cast<const uint32_t*>(bp + r * BN * 4);
-        const uint8_t* sc = smem + ((group_n(tn) & 1) ? sc_rd[1] : sc_rd[0]) + ((tn / 2) & 1) * S::kSc;
+        for (int r = 0; r < kWPT; ++r) w[r] = *reinterpret_cast<const uint32_t*>(bp + r * BN * 4);
+        const uint8_t* sc = smem + ((group_n(tn) & 1) ? sc_rd[1] : sc_rd[0]) + ((tn / 2) % S::kSS) * S::kSc;
         s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc));
         m = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc + 1024));
         s16 = s * 0.0625f;
     }
 
-    __device__ __forceinline__ void dequant_all(int st, const uint32_t (&w)[8], float s, float s16, float m) const {
+    __device__ __forceinline__ void dequant_all(int st, const uint32_t (&w)[kWPT], float s, float s16, float m) const {
         uint8_t* dst = smem + bq_wr[st];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
+        for (int r = 0; r < kWPT; ++r)
+            *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
     }
 
-    // One k-tile: MFMAs on A stage `st` and dequantized B stage `st` while the words `w` (the next
-    // k-tile) are dequantized into the other B stage, two words per k-step.  issue(ks) runs at the
+    // One k-tile t: MFMAs on A stage t % kAS and dequantized B stage `st` = t & 1 while the words `w` (the next
+    // k-tile) are dequantized into the other B stage, spread evenly over the k-steps.  issue(ks) runs at the
     // top of each k-step: the copies for later k-tiles are spread over the tile rather than issued
     // in one burst, which would hold up the wave's first MFMAs behind the load unit.
     template <int st, typename Issue>
-    __device__ __forceinline__ void mma_tile(f32x16_t (&acc)[kMT][kNT], const uint32_t (&w)[8], float s, float s16,
-                                             float m, Issue&& issue) const {
-        const uint8_t* abase = smem + S::kA * st;
+    __device__ __forceinline__ void mma_tile(int t, f32x16_t (&acc)[kMT][kNT], const uint32_t (&w)[kWPT], float s,
+                                             float s16, float m, Issue&& issue) const {
+        const uint8_t* abase = smem + S::kA * (S::kAS == 2 ? st : t % S::kAS);
         const uint8_t* bbase = smem + b_rd + S::kBdq * st;
         uint8_t* dst = smem + bq_wr[st ^ 1];
         bf16x8_t af[2][kMT], bfr[2][kNT];
@@ -292,31 +326,30 @@ struct Gemm {
             issue(ks);
             if (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
 #pragma unroll
-            for (int r = 2 * ks; r < 2 * ks + 2; ++r)
-                *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
+            for (int r = 0; r < kWPT; ++r)
+                if (r * (BK / 16) / kWPT == ks)
+                    *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
 #pragma unroll
             for (int j = 0; j < kNT; ++j)
 #pragma unroll
                 for (int i = 0; i < kMT; ++i)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0,
                                                                         0, 0);
-            if (kMT == 2)
-                step_schedule<14, 4>(ks == 0 ? 2 : 0);
-            else
-                step_schedule<7, 7>(ks == 0 ? 1 : 0);
+            step_schedule<kMFMA, kVPM>(ks == 0 ? kLead : 0);
         }
         __builtin_amdgcn_sched_barrier(0);
     }
 };
 
-template <int BM, bool kVec>
+template <int BM, int BN, int WM, int DA, int DB, bool kVec>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                       const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
                       uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K, int k_per_split,
                       int splits, uint32_t mask_lo, uint32_t mask_hi) {
-    using G = Gemm<BM, kVec>;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<BM>::kTotal];
+    using G = Gemm<BM, BN, WM, DA, DB, kVec>;
+    constexpr int kMT = G::kMT, kNT = G::kNT, kWPT = G::kWPT;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<BM, BN, DA, DB>::kTotal];
     // XCD-aware tile order: block b runs on XCD b % 8, so XCD x takes the x-th contiguous eighth
     // of the (split, m, n) tile sequence, n fastest -- its blocks share A rows in its own L2.
     const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
@@ -344,24 +377,29 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
     g.init();
     // the accumulators stay outside `g`: a local array is kept in registers across the copies'
     // inline assembly, whose memory clobber would otherwise force them out to scratch
-    f32x16_t acc[G::kMT][kNT];
+    f32x16_t acc[kMT][kNT];
 #pragma unroll
-    for (int i = 0; i < G::kMT; ++i)
+    for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // Prologue: A(0), the words of k-tiles 0..2 and the scales of groups 0 and 1; k-tile 0 is
-    // then dequantized into B stage 0.
-    g.issue_a(0);
-    g.template issue_b<true>(0);
-    g.template issue_b<false>(1);
-    g.template issue_b<true>(2);
+    // Prologue: A of k-tiles 0 .. DA-1, the words of 0 .. DB-1 and the scales of their groups;
+    // k-tile 0 is then dequantized into B stage 0.
+#pragma unroll
+    for (int t0 = 0; t0 < DA; ++t0) g.issue_a(t0);
+#pragma unroll
+    for (int t0 = 0; t0 < DB; ++t0) {
+        if (t0 % 2 == 0)
+            g.template issue_b<true>(t0);
+        else
+            g.template issue_b<false>(t0);
+    }
     wait_vm<0>();
     __syncthreads();
     {
-        uint32_t w[8];
+        uint32_t w[kWPT];
         float s, s16, m;
         g.read_words(0, w, s, s16, m);
         g.dequant_all(0, w, s, s16, m);
@@ -369,33 +407,38 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
     __syncthreads();
 
     // k-tile t: read the words of t+1; run the MFMAs of t while dequantizing t+1 and copying
-    // A(t+1) (a quarter per k-step) and then the words of t+3 (with their group's scales when
-    // t+3 starts a group, i.e. t is odd); then wait until A(t+1) and everything issued before it
-    // has landed (the words of t+2 and their scales were issued during t-1) and meet at the
-    // barrier.
-    constexpr int kAPerStep = G::kAInst / (BK / 16);
-    constexpr int kAfterA = G::kBInst;  // copies issued after A in an even k-tile (+2 in an odd one)
+    // A(t+DA) (spread over the k-steps) and then the words of t+DB (with their group's scales
+    // when t+DB starts a group); then wait until A(t+1) and everything issued before it has
+    // landed -- the words of t+2 and their scales were requested no later than A(t+1), since
+    // DB >= DA + 2 -- and meet at the barrier.
+    constexpr int kSteps = BK / 16;
+    constexpr int kWaitEven = G::after_a(0), kWaitOdd = G::after_a(1);
+    auto issue_a_step = [&](int ta, int ks) {  // the A copies whose turn is k-step ks
+#pragma unroll
+        for (int i = 0; i < G::kAInst; ++i)
+            if (i * kSteps / G::kAInst == ks) g.issue_a(ta, i, i + 1);
+    };
     for (int tt = 0; tt < g.ntiles; tt += 2) {
         {
-            uint32_t w[8];
+            uint32_t w[kWPT];
             float s, s16, m;
             g.read_words(tt + 1, w, s, s16, m);
-            g.template mma_tile<0>(acc, w, s, s16, m, [&](int ks) {
-                g.issue_a(tt + 1, ks * kAPerStep, (ks + 1) * kAPerStep);
-                if (ks == BK / 16 - 1) g.template issue_b<false>(tt + 3);
+            g.template mma_tile<0>(tt, acc, w, s, s16, m, [&](int ks) {
+                issue_a_step(tt + DA, ks);
+                if (ks == kSteps - 1) g.template issue_b<DB % 2 == 0>(tt + DB);
             });
-            wait_vm<kAfterA>();
+            wait_vm<kWaitEven>();
             __syncthreads();
         }
         {
-            uint32_t w[8];
+            uint32_t w[kWPT];
             float s, s16, m;
             g.read_words(tt + 2, w, s, s16, m);
-            g.template mma_tile<1>(acc, w, s, s16, m, [&](int ks) {
-                g.issue_a(tt + 2, ks * kAPerStep, (ks + 1) * kAPerStep);
-                if (ks == BK / 16 - 1) g.template issue_b<true>(tt + 4);
+            g.template mma_tile<1>(tt + 1, acc, w, s, s16, m, [&](int ks) {
+                issue_a_step(tt + 1 + DA, ks);
+                if (ks == kSteps - 1) g.template issue_b<DB % 2 == 1>(tt + 1 + DB);
             });
-            wait_vm<kAfterA + 2>();
+            wait_vm<kWaitOdd>();
             __syncthreads();
         }
     }
@@ -404,15 +447,16 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
     // D fragment of a 32 x 32 tile: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
     const int lane = lane_id(), wave = wave_id();
     const int l32 = lane & 31, lh = lane >> 5;
+    const int wm = wave % WM, wn = wave / WM;
     const bool split = splits > 1;
 #pragma unroll
-    for (int i = 0; i < G::kMT; ++i)
+    for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < kNT; ++j) {
-            const int col = g.n0 + j * 32 + l32;
+            const int col = g.n0 + wn * G::kWCols + j * 32 + l32;
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int row = g.m0 + wave * (BM / 4) + i * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
+                const int row = g.m0 + wm * G::kWRows + i * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
                 if (row < M && col < N) {
                     if (split)
                         ws[((size_t)split_id * M + row) * N + col] = acc[i][j][e];
@@ -433,19 +477,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     y[i] = f32_to_bf16_bits(s);
 }
 
+// Tile shapes by M (see the header comment): each fills the 256 CUs at N = 14336 without a K
+// split, from 128 rows (64 x 128 tiles, 2 x 2 waves) to 1024 rows (256 x 224, waves along M).
+enum TileCfg { kT64x128, kT128x128, kT128x256, kT256x224 };
+
 struct GemmPlan {
-    int bm, tiles_m, tiles_n, splits, k_per_split;
+    TileCfg cfg;
+    int bm, bn, tiles_m, tiles_n, splits, k_per_split;
 };
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p;
-    p.bm = M > 128 ? 256 : 128;  // 128: a wave owns one 32-row tile
+    if (M <= 128) p.cfg = kT64x128, p.bm = 64, p.bn = 128;
+    else if (M <= 256) p.cfg = kT128x128, p.bm = 128, p.bn = 128;
+    else if (M <= 512) p.cfg = kT128x256, p.bm = 128, p.bn = 256;
+    else p.cfg = kT256x224, p.bm = 256, p.bn = 224;
     p.tiles_m = (int)((M + p.bm - 1) / p.bm);
-    p.tiles_n = (int)((N + BN - 1) / BN);
+    p.tiles_n = (int)((N + p.bn - 1) / p.bn);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     const int groups = (int)(K / 128);
-    int splits = 1;
-    if (tiles < kCUs) splits = (int)std::min<int64_t>(groups, (kCUs + tiles - 1) / tiles);
+    int splits = 1;  // split K only when the tiles would leave more than half the CUs idle
+    if (2 * tiles <= kCUs) splits = (int)std::min<int64_t>(groups, (kCUs + tiles - 1) / tiles);
     // k per split in whole groups; recompute the split count so no split is empty
     const int groups_per_split = (groups + splits - 1) / splits;
     p.k_per_split = groups_per_split * 128;
@@ -453,14 +505,20 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
-template <int BM, bool kVec>
-void launch_bm(const GemmPlan& p, const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
-               const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace, hipStream_t stream) {
+template <int BM, int BN, int WM, int DA, int DB>
+void launch_cfg(const GemmPlan& p, const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace, hipStream_t stream) {
     // a 1-D grid of 8 x ceil(tiles / 8) blocks over (split, m, n); the surplus exit at once
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m * p.splits;
     const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
-    hipLaunchKernelGGL((gemm_g128_kernel<BM, kVec>), grid, dim3(kThreads), 0, stream, x, codes, scales, mins, y,
-                       workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu, 0xF0F0F0F0u);
+    if (N % 4 == 0)
+        hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, true>), grid, dim3(kThreads), 0, stream, x, codes, scales,
+                           mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu,
+                           0xF0F0F0F0u);
+    else
+        hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, false>), grid, dim3(kThreads), 0, stream, x, codes, scales,
+                           mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu,
+                           0xF0F0F0F0u);
 }
 
 }  // namespace
@@ -476,17 +534,11 @@ hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes,
                             hipStream_t stream) {
     if (M <= kMidMaxRows) return launch_mid_g128(x, M, codes, scales, mins, N, K, y, stream);
     const GemmPlan p = plan_gemm(M, N, K);
-    const bool vec = N % 4 == 0;
-    if (p.bm == 256) {
-        if (vec)
-            launch_bm<256, true>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
-        else
-            launch_bm<256, false>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
-    } else {
-        if (vec)
-            launch_bm<128, true>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
-        else
-            launch_bm<128, false>(p, x, M, codes, scales, mins, N, K, y, workspace, stream);
+    switch (p.cfg) {
+        case kT64x128: launch_cfg<64, 128, 2, 3, 6>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT128x128: launch_cfg<128, 128, 2, 2, 5>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT128x256: launch_cfg<128, 256, 2, 1, 4>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT256x224: launch_cfg<256, 224, 4, 1, 3>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
