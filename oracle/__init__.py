@@ -41,9 +41,7 @@ def build(force: bool = True) -> Path:
     """Compile the oracle with gcc: IEEE arithmetic, no fast-math, no FMA contraction."""
     if force or not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
         tmp = _LIB_PATH.with_suffix(f".so.tmp{os.getpid()}")
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
-               "-fno-fast-math", "-frounding-math", "-o", str(tmp), str(_SRC), "-lm"]
-        subprocess.run(cmd, check=True)
+        compile_to(_SRC, tmp)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
 
@@ -51,33 +49,47 @@ def build(force: bool = True) -> Path:
 _lib = None
 
 
+def compile_to(src: Path, out: Path) -> Path:
+    """Compile an oracle C source to a shared library with the oracle's flags (the tests use
+    this to build deliberately broken copies and check that the pins catch them)."""
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+           "-fno-fast-math", "-frounding-math", "-o", str(out), str(src), "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
         build(force=False)
-        L = ctypes.CDLL(str(_LIB_PATH))
-        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-        L.oracle_f32_to_bf16.argtypes, L.oracle_f32_to_bf16.restype = [ctypes.c_float], ctypes.c_uint16
-        L.oracle_bf16_to_f32.argtypes, L.oracle_bf16_to_f32.restype = [ctypes.c_uint16], ctypes.c_float
-        L.oracle_f32_to_f16.argtypes, L.oracle_f32_to_f16.restype = [ctypes.c_float], ctypes.c_uint16
-        L.oracle_f16_to_f64.argtypes, L.oracle_f16_to_f64.restype = [ctypes.c_uint16], ctypes.c_double
-        L.oracle_pack_word.argtypes, L.oracle_pack_word.restype = [P], ctypes.c_uint32
-        L.oracle_unpack_word.argtypes, L.oracle_unpack_word.restype = [ctypes.c_uint32, P], None
-        L.oracle_quantize_g128.argtypes = [P, I64, I64, P, P, P]
-        L.oracle_dequant_g128.argtypes = [P, P, P, I64, I64, I, P]
-        L.oracle_quantize_q4b32.argtypes = [P, I64, I64, P, P]
-        L.oracle_dequant_q4b32.argtypes = [P, P, I64, I64, I, P]
-        L.oracle_matmul_g128_f64.argtypes = [P, I, I64, P, P, P, I64, I64, P]
-        L.oracle_matmul_g128_f64_at.argtypes = [P, I, I64, P, P, P, I64, I64, P, P, I64, P]
-        L.oracle_matmul_q4b32_f64.argtypes = [P, I, I64, P, P, I64, I64, P]
-        L.oracle_matmul_q4b32_f64_at.argtypes = [P, I, I64, P, P, I64, I64, P, P, I64, P]
-        L.oracle_matmul_f32w_f64.argtypes = [P, I, I64, P, I64, I64, P]
-        for name in ("oracle_quantize_g128", "oracle_dequant_g128", "oracle_quantize_q4b32",
-                     "oracle_dequant_q4b32", "oracle_matmul_g128_f64", "oracle_matmul_g128_f64_at",
-                     "oracle_matmul_q4b32_f64", "oracle_matmul_q4b32_f64_at", "oracle_matmul_f32w_f64"):
-            getattr(L, name).restype = I
-        _lib = L
+        _lib = bind(_LIB_PATH)
     return _lib
+
+
+def bind(path) -> ctypes.CDLL:
+    """Load an oracle library and declare its signatures."""
+    L = ctypes.CDLL(str(path))
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.oracle_f32_to_bf16.argtypes, L.oracle_f32_to_bf16.restype = [ctypes.c_float], ctypes.c_uint16
+    L.oracle_bf16_to_f32.argtypes, L.oracle_bf16_to_f32.restype = [ctypes.c_uint16], ctypes.c_float
+    L.oracle_f32_to_f16.argtypes, L.oracle_f32_to_f16.restype = [ctypes.c_float], ctypes.c_uint16
+    L.oracle_f16_to_f64.argtypes, L.oracle_f16_to_f64.restype = [ctypes.c_uint16], ctypes.c_double
+    L.oracle_pack_word.argtypes, L.oracle_pack_word.restype = [P], ctypes.c_uint32
+    L.oracle_unpack_word.argtypes, L.oracle_unpack_word.restype = [ctypes.c_uint32, P], None
+    L.oracle_quantize_g128.argtypes = [P, I64, I64, P, P, P]
+    L.oracle_dequant_g128.argtypes = [P, P, P, I64, I64, I, P]
+    L.oracle_quantize_q4b32.argtypes = [P, I64, I64, P, P]
+    L.oracle_dequant_q4b32.argtypes = [P, P, I64, I64, I, P]
+    L.oracle_matmul_g128_f64.argtypes = [P, I, I64, P, P, P, I64, I64, P]
+    L.oracle_matmul_g128_f64_at.argtypes = [P, I, I64, P, P, P, I64, I64, P, P, I64, P]
+    L.oracle_matmul_q4b32_f64.argtypes = [P, I, I64, P, P, I64, I64, P]
+    L.oracle_matmul_q4b32_f64_at.argtypes = [P, I, I64, P, P, I64, I64, P, P, I64, P]
+    L.oracle_matmul_f32w_f64.argtypes = [P, I, I64, P, I64, I64, P]
+    for name in ("oracle_quantize_g128", "oracle_dequant_g128", "oracle_quantize_q4b32",
+                 "oracle_dequant_q4b32", "oracle_matmul_g128_f64", "oracle_matmul_g128_f64_at",
+                 "oracle_matmul_q4b32_f64", "oracle_matmul_q4b32_f64_at", "oracle_matmul_f32w_f64"):
+        getattr(L, name).restype = I
+    return L
 
 
 def _ptr(a: np.ndarray) -> int:

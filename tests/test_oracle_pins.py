@@ -81,7 +81,8 @@ def test_f16_rounding_matches_numpy():
     nxt = (np.arange(0x0400, 0x7BFF, 7, dtype=np.uint16) + 1).view(np.float16).astype(np.float64)
     vals = np.concatenate([vals, ((h + nxt) / 2).astype(np.float32), np.float32(2.0**-24) * np.arange(0.5, 1100, 1, dtype=np.float32)])
     ours = np.array([oracle.f32_to_f16(v) for v in vals], dtype=np.uint16)
-    ref = vals.astype(np.float16).view(np.uint16)
+    with np.errstate(over="ignore"):  # values past the fp16 range round to infinity, on purpose
+        ref = vals.astype(np.float16).view(np.uint16)
     np.testing.assert_array_equal(ours, ref)
 
 
@@ -218,6 +219,25 @@ def test_g128_codes_are_nearest_levels_bruteforce():
     W, _ = workloads.inputs(workloads.TINY)
     codes, scales, mins = oracle.quantize_g128(W)
     _g128_check_nearest(W, codes, scales, mins)
+
+
+def test_g128_codes_clamped_where_bf16_parameters_overshoot():
+    """Groups in a narrow band far from zero: bf16(min) can lie more than half a step from the
+    true minimum (and bf16(s) slightly off), so (w - m_b)/s_b leaves [0, 15] at the ends.  The
+    clamp of the codes (survey reading o1) must then give the nearest representable level,
+    checked by brute force -- an unclamped or wrapped code would be far from every level."""
+    rng = np.random.default_rng(5)
+    rows = []
+    for base in (1.0, -1.0, 3.0, 0.75):
+        for width in (0.002, 0.01, 0.05):
+            rows.append(np.float32(base) + np.float32(width) * rng.random(1024, dtype=np.float32))
+    W = np.stack(rows).astype(np.float32)
+    codes, scales, mins = oracle.quantize_g128(W)
+    lo = W.reshape(W.shape[0], -1, 128).min(axis=2)
+    s = (W.reshape(W.shape[0], -1, 128).max(axis=2) - lo) / 15
+    assert np.any(np.abs(bf16_value(mins).T - lo) > 0.5 * s), "no group exercises the clamp"
+    q, _, _ = _g128_check_nearest(W, codes, scales, mins)
+    assert q.min() == 0 and q.max() <= 15
 
 
 def test_g128_scale_and_min_definition():
