@@ -166,6 +166,56 @@ def test_gemm_g128_parity(M, N, K):
     assert rel_err(bf16_f32(y), ref) <= TOL
 
 
+@pytest.mark.parametrize("M", [100, 200, 400, 600])
+@pytest.mark.parametrize("N", [500, 499])
+def test_gemm_every_tile_shape(M, N):
+    """One M in each tile-shape range of the large-M kernel (64x128, 128x128, 128x256, 256x224),
+    with a ragged N that is (500) and is not (499) a multiple of 4 -- the vector and the dword
+    copy paths -- and K = 640 (five groups: an odd group count, so some splits are uneven)."""
+    K = 640
+    say(f"gemm tile shapes M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=17)
+    x = workloads.activations(M, K, "bf16", seed=18)
+    packed = gpu_pack(G128, W)
+    y = run_matmul(w.w4a16_gemm, G128, x, packed, N, K, BF16)
+    ref = oracle.matmul_g128(x, *oracle.quantize_g128(W))
+    assert rel_err(bf16_f32(y), ref) <= TOL
+
+
+def test_gemv_long_k_ragged_n():
+    """K = 16384 (the skinny kernel makes four passes over K) with N = 999 (not a multiple of 4:
+    the scalar column loads) at M = 5."""
+    M, N, K = 5, 999, 16384
+    say(f"gemv long K M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=19)
+    x = workloads.activations(M, K, "bf16", seed=20)
+    packed = gpu_pack(G128, W)
+    y = run_matmul(w.w4a16_gemv, G128, x, packed, N, K, BF16)
+    ref = oracle.matmul_g128(x, *oracle.quantize_g128(W))
+    assert rel_err(bf16_f32(y), ref) <= TOL
+
+
+def test_gemm_many_rows_sampled():
+    """M = 2048 over few column tiles (K split over whole groups, partials in the workspace):
+    sampled outputs against the oracle, all outputs against an fp32 product of the GPU's own
+    dequantized weights."""
+    M, N, K = 2048, 520, 1024
+    say(f"gemm many rows M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=21)
+    x = workloads.activations(M, K, "bf16", seed=22)
+    packed = gpu_pack(G128, W)
+    y = bf16_f32(run_matmul(w.w4a16_gemm, G128, x, packed, N, K, BF16))
+    rc, rs, rm = oracle.quantize_g128(W)
+    rng = np.random.default_rng(23)
+    rows = np.concatenate([rng.integers(0, M, size=2000), [0, M - 1]])
+    cols = np.concatenate([rng.integers(0, N, size=2000), [N - 1, 0]])
+    assert rel_err(y[rows, cols], oracle.matmul_g128_at(x, rc, rs, rm, rows, cols)) <= TOL
+    What = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    w.w4a16_dequant(G128, *packed, N, K, F32, What)
+    ref_all = (torch.from_numpy(workloads.bits_to_f32(x, "bf16")).cuda() @ What.T).double().cpu().numpy()
+    assert rel_err(y, ref_all) <= TOL
+
+
 @pytest.mark.parametrize("act", [F16, BF16])
 @pytest.mark.parametrize("M,N,K", [(1, 64, 1024), (1, 65, 96), (2, 130, 4096), (1, 257, 2080), (3, 31, 17408)])
 def test_gemv_q4_parity(act, M, N, K):
