@@ -38,7 +38,7 @@ CACHE_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache (MALL)
 WARM_SECONDS = 0.25            # untimed run-up of each workload before its timed replay
 METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
 DECODE_KERNEL = "skinny_g128_kernel<1, 4, 16, true>"
-PREFILL_KERNEL = "gemm_g128_kernel<256, 224, 4, 1, 3, true>"
+PREFILL_KERNEL = "gemm_g128_kernel<256, 224, 4, 1, 3, true, 1>"
 
 
 def recorded_traffic(kernel: str):

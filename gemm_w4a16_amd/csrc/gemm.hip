@@ -24,9 +24,18 @@
 //    MFMAs (about four VALU instructions fit under one 32x32x16 MFMA).  Each word becomes one
 //    16-byte row segment of an [n][k] tile, which is exactly an MFMA B fragment; rows are padded
 //    to 144 B, so fragment reads and dequant writes are free of bank conflicts;
+//  * the MFMA steps run one step behind the fragment reads and across the k-tile boundary: the
+//    first MFMAs after each barrier use fragments read before it, so no k-tile starts with a
+//    wait for LDS.  The copies' sources and LDS stages are kept in scalar cursors advanced
+//    once per k-tile (a handful of scalar instructions instead of per-tile address arithmetic,
+//    since the scalar unit is shared by the CU's waves);
+//  * the MFMA takes the B fragment first, so each lane's accumulators hold runs of four adjacent
+//    output columns, stored as one 8-byte bf16 (or 16-byte fp32) write each;
 //  * when the tile grid alone cannot fill the chip, K is split in whole groups; fp32 partials go
 //    to the caller's workspace and a second kernel adds them in split order, so the result does
 //    not depend on scheduling.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -36,27 +45,30 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int LDT = BK + 8;  // dequantized B tile row pitch in bf16 (144 B)
-constexpr int kThreads = 256;
 constexpr int kCUs = 256;
 
 // Copy distances: at k-tile t the A tile of t+DA and the packed words of t+DB are requested.
 // A then needs DA+1 LDS stages, the packed words DB, the scales/minimums (one stage per group of
 // two k-tiles) DB/2 + 1; the dequantized B has two (k-tiles t and t+1).  Short k-tiles (small
 // tiles) need longer distances to cover the latency.
-template <int BM, int BN, int DA, int DB>
+template <int BM, int BN, int DA, int DB, int KS>
 struct Smem {
     static_assert(DA >= 1 && DB >= DA + 2, "the words of t+2 must be requested before A(t+1)");
     static constexpr int kAS = DA + 1, kBS = DB, kSS = DB / 2 + 1;
-    static constexpr int kBpChunks = (2 * BN + 255) / 256 * 256;  // 16-byte chunks of a packed stage
+    static constexpr int kThr = 256 * KS;
+    // 16-byte chunks (vector copies) or dwords (dword copies) of a packed stage, padded to whole
+    // rounds of the block's lanes
+    static constexpr int kBpChunks = (2 * BN + kThr - 1) / kThr * kThr;
+    static constexpr int kBpDwords = (8 * BN + kThr - 1) / kThr * kThr;
     static constexpr int kA = BM * BK * 2;     // A stage: BM rows x 64 bf16
     static constexpr int kBdq = BN * LDT * 2;  // dequantized B stage: BN rows x 144 B
-    static constexpr int kBp = kBpChunks * 16;  // packed stage: [8 packed rows][BN columns] u32 + pad
+    static constexpr int kBp = (kBpChunks * 16 > kBpDwords * 4 ? kBpChunks * 16 : kBpDwords * 4);  // [8][BN] u32 + pad
     static constexpr int kSc = 512 * 4;        // 256 scale slots + 256 minimum slots, a dword each
     static constexpr int oA = 0;
     static constexpr int oBdq = oA + kAS * kA;
     // written by the threads past column BN-1 when a column has one thread: thread BN + u
-    // stores its row segment r at 16 (u + r), so (256 - BN + 7) x 16 B, rounded up
-    static constexpr int kSink = BN < 256 && BN > 128 ? ((256 - BN + 7) * 16 + 127) / 128 * 128 : 0;
+    // stores its row segment r at 16 (u + r), so (threads - BN + 7) x 16 B, rounded up
+    static constexpr int kSink = BN < kThr && 2 * BN > kThr ? ((kThr - BN + 7) * 16 + 127) / 128 * 128 : 0;
     static constexpr int oSink = oBdq + 2 * kBdq;
     static constexpr int oBp = oSink + kSink;
     static constexpr int oSc = oBp + kBS * kBp;
@@ -73,21 +85,53 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Direct-to-LDS copies: lane l reads 16 (or 4) bytes at sbase + voff and the load unit writes
-// them to LDS byte m0 + 16 l (or 4 l).  They are issued from inline assembly so that the
-// compiler does not track them: the compiler cannot tell the LDS stages apart and would wait for
-// every copy in flight before any LDS access.  The only waits for them are the explicit ones
-// before the k-tile barriers.
+// them to LDS byte m0 + 16 l (or 4 l), with m0 = lds + kImm.  They are issued from inline
+// assembly so that the compiler does not track them: it cannot tell the LDS stages apart and
+// would wait for every copy in flight before any LDS access.  The only waits for them are the
+// explicit ones before the k-tile barriers.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "memory", "m0");
+template <int kImm>
+__device__ __forceinline__ void dma16(uint32_t voff, const void* sbase, uint32_t lds) {
+    if constexpr (kImm == 0)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                     : "memory", "m0");
+    else
+        asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds),
+                     "n"(kImm)
+                     : "memory", "m0", "scc");
 }
-__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(m0)
-                 : "memory", "m0");
+template <int kImm>
+__device__ __forceinline__ void dma4(uint32_t voff, const void* sbase, uint32_t lds) {
+    if constexpr (kImm == 0)
+        asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
+                     : "memory", "m0");
+    else
+        asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds),
+                     "n"(kImm)
+                     : "memory", "m0", "scc");
 }
 #pragma clang diagnostic pop
+
+// f(std::integral_constant<int, i>) for i = I .. N-1, so that i can select template arguments.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+// The byte offset of the stage after the one at `off`, for n stages of `size` bytes.
+template <int size, int n>
+__device__ __forceinline__ uint32_t next_stage(uint32_t off) {
+    if constexpr (n == 1) {
+        return 0;
+    } else {
+        off += size;
+        return off == (uint32_t)(size * n) ? 0u : off;
+    }
+}
 
 // s_waitcnt vmcnt(n): at most n of this wave's copies are still in flight.
 template <int n>
@@ -129,30 +173,37 @@ __device__ __forceinline__ void step_schedule(int lead) {
     }
 }
 
-template <int BM, int BN, int WM, int DA, int DB, bool kVec>
+template <int BM, int BN, int WM, int DA, int DB, bool kVec, int KS>
 struct Gemm {
+    // KS groups of 4 waves split each k-tile's four k-steps (KS = 2: two waves per SIMD, so one
+    // hides the other's latencies on short k-tiles); each group holds the whole output tile and
+    // the groups' sums are added at the end.  Within a group the waves form a WM x WN grid.
+    static_assert(KS == 1 || KS == 2, "k groups");
+    static constexpr int kThr = 256 * KS, kWaves = 4 * KS, kOwnSteps = (BK / 16) / KS;
     static constexpr int WN = 4 / WM;
     static constexpr int kWRows = BM / WM, kWCols = BN / WN;  // a wave's output tile
     static constexpr int kMT = kWRows / 32, kNT = kWCols / 32;  // its 32 x 32 MFMA tiles
     static_assert(kMT >= 1 && kNT >= 1 && kWRows % 32 == 0 && kWCols % 32 == 0, "wave tile");
-    static constexpr int kAInst = BM / 32;  // A copies per wave per k-tile (1 KB each)
-    static constexpr int kBInst = kVec ? Smem<BM, BN, DA, DB>::kBpChunks / 256 : 8 * BN / 256;  // packed-word copies
+    using S = Smem<BM, BN, DA, DB, KS>;
+    static constexpr int kAInst = BM / (32 * KS);  // A copies per wave per k-tile (8 rows, 1 KB each)
+    static_assert(kAInst >= 1, "A rows per wave");
+    static constexpr int kBInst = kVec ? S::kBpChunks / kThr : S::kBpDwords / kThr;  // packed-word copies
+    static constexpr int kScInst = 2 / KS;  // scale + minimum copies per wave, when a group starts
     // dequant: kTPC threads per column, each converting kWPT of its 8 packed words per k-tile
-    static constexpr int kTPC = BN <= 128 ? 256 / BN : 1;
+    static constexpr int kTPC = 2 * BN <= kThr ? kThr / BN : 1;
     static constexpr int kWPT = 8 / kTPC;
-    static_assert(BN <= 256 && (BN > 128 || 256 % BN == 0), "dequant split");
-    using S = Smem<BM, BN, DA, DB>;
+    static_assert(BN <= kThr && (2 * BN > kThr || kThr % BN == 0) && kWPT >= 1, "dequant split");
     static_assert(S::kTotal <= 160 * 1024, "LDS budget");
     // schedule: kMFMA MFMAs per k-step; the first kLead of k-step 0 carry no dequant (its words
     // are still coming from LDS); kVPM VALU slots after each of the others
     static constexpr int kMFMA = kMT * kNT;
     static constexpr int kLead = kMFMA >= 8 ? 2 : 0;
-    static constexpr int kValuPerStep = 22 * kWPT / (BK / 16) + 2;
+    static constexpr int kValuPerStep = 22 * kWPT / kOwnSteps + 2;
     static constexpr int kVPM = (kValuPerStep + kMFMA - kLead - 1) / (kMFMA - kLead);
 
     // Copies a wave may still have in flight at the end of k-tile t (parity p) once A(t+1) has
     // landed: the rest of k-tile t+1-DA (its words and scales) and all of k-tiles t+2-DA .. t.
-    static constexpr int sc_copies(int u) { return ((u + DB) & 1) == 0 ? 2 : 0; }  // scales at k-tile u
+    static constexpr int sc_copies(int u) { return ((u + DB) & 1) == 0 ? kScInst : 0; }  // scales at k-tile u
     static constexpr int after_a(int p) {
         int n = kBInst + sc_copies(p + 1 - DA);
         for (int u = p + 2 - DA; u <= p; ++u) n += kAInst + kBInst + sc_copies(u);
@@ -170,10 +221,14 @@ struct Gemm {
     // per-lane byte offsets of the copies (constant over the k-loop)
     uint32_t a_off[kAInst];  // from the k-tile's A base
     uint32_t b_off[kBInst > 0 ? kBInst : 1];  // from the k-tile's first packed row
-    uint32_t sc_off[2];      // scale/min dword for even / odd g*N
+    uint32_t sc_off[2];      // scale/min dword for even / odd g*N (the same slot in both arrays)
+    // this wave's copy destinations in stage 0 (wave-uniform LDS addresses) and the array each
+    // of its scale copies reads
+    uint32_t a_lds, b_lds, sc_lds[kScInst];
+    const char* sc_arr[kScInst];
     // this thread's LDS byte offsets (from smem, without the stage)
-    uint32_t a_rd[kMT][BK / 16];  // A fragment (i, k-step)
-    uint32_t b_rd;                // B fragment of j = 0, k-step 0
+    uint32_t a_rd[kMT][kOwnSteps];  // A fragment (i, own k-step j)
+    uint32_t b_rd;                  // B fragment of column tile 0, own k-step 0
     uint32_t bq_wr[2];            // dequantized row segment, per destination stage
     uint32_t bp_rd;               // packed word of this thread's first row, this thread's column
     uint32_t sc_rd[2];            // scale of this thread's column, for even / odd g*N
@@ -181,50 +236,61 @@ struct Gemm {
     __device__ __forceinline__ void init() {
         const int lane = lane_id(), wave = wave_id(), tid = threadIdx.x;
         const int l32 = lane & 31, lh = lane >> 5;
-        const int wm = wave % WM, wn = wave / WM;
+        const int w4 = wave % 4, wm = w4 % WM, wn = w4 / WM;
         sm = lds_addr(smem);
-        // A copies: instruction i of wave w fills rows w*BM/4 + 8i .. +7; lane l lands on chunk
-        // l % 8 of row l / 8 and so reads the global chunk that the swizzle maps there.  Rows past
-        // M repeat row M-1; they only feed outputs that are never stored.
+        // A copies: instruction i of wave w fills rows w*BM/(4 KS) + 8i .. +7; lane l lands on
+        // chunk l % 8 of row l / 8 and so reads the global chunk that the swizzle maps there.
+        // Rows past M repeat row M-1; they only feed outputs that are never stored.
 #pragma unroll
         for (int i = 0; i < kAInst; ++i) {
-            const int r = wave * (BM / 4) + 8 * i + (lane >> 3);
+            const int r = wave * (BM / kWaves) + 8 * i + (lane >> 3);
             const int gr = min(m0 + r, M - 1) - m0;
             a_off[i] = (uint32_t)(((size_t)gr * K + 8 * a_swizzle(r, lane & 7)) * 2);
         }
+        a_lds = sm + S::oA + wave * (BM / kWaves) * BK * 2;
         // Packed words, LDS layout [8 packed rows][BN columns] u32.  Vector copies (N % 4 == 0):
         // 16-byte chunk c = row * BN/4 + column / 4; lanes past the last chunk land in the stage's
         // pad.  Dword copies: dword d = row * BN + column.  Columns past N repeat a valid column.
 #pragma unroll
         for (int i = 0; i < kBInst; ++i) {
-            const int d = (i * 4 + wave) * kWave + lane;
+            const int d = (i * kWaves + wave) * kWave + lane;
             int row, col;
             if (kVec) {
                 const int c = min(d, 2 * BN - 1);
                 row = c / (BN / 4);
                 col = min(n0 + 4 * (c % (BN / 4)), N - 4);
             } else {
-                row = d / BN;
-                col = min(n0 + d % BN, N - 1);
+                const int dd = min(d, 8 * BN - 1);
+                row = dd / BN;
+                col = min(n0 + dd % BN, N - 1);
             }
             b_off[i] = (uint32_t)(((size_t)row * N + col) * 4);
         }
-        // Scales (one copy) and minimums (another): slot w*64 + l receives the aligned dword that
-        // holds the bf16 of column min(n0 + min(w*64 + l, BN-1), N-1) in the group's row; where
-        // the dword starts depends on the parity of g*N, so both offsets are kept.
+        b_lds = sm + S::oBp + wave * (kVec ? 1024 : 256);
+        // Scales and minimums: copy i of wave w covers lanes (i*kWaves + w)*64 .. of 512, the first
+        // 256 scales, the rest minimums; slot (w % 4)*64 + l receives the aligned dword that holds
+        // the bf16 of column min(n0 + min(slot, BN-1), N-1) in the group's row.  Where the dword
+        // starts depends on the parity of g*N, so both offsets are kept.
         {
-            const int c = min(n0 + min(wave * kWave + lane, BN - 1), N - 1);
+            const int c = min(n0 + min(w4 * kWave + lane, BN - 1), N - 1);
             sc_off[0] = (uint32_t)((2 * c) & ~3);
             sc_off[1] = (uint32_t)((2 + 2 * c) & ~3);
         }
 #pragma unroll
+        for (int i = 0; i < kScInst; ++i) {
+            const int arr = (i * kWaves + wave) / 4;  // 0: scales, 1: minimums (wave-uniform)
+            sc_arr[i] = reinterpret_cast<const char*>(arr ? mins : scales);
+            sc_lds[i] = sm + S::oSc + w4 * 256 + arr * 1024;
+        }
+        const int ks0 = (wave / 4) * kOwnSteps;  // this wave's first k-step of each k-tile
+#pragma unroll
         for (int i = 0; i < kMT; ++i)
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
+            for (int j = 0; j < kOwnSteps; ++j) {
                 const int r = wm * kWRows + i * 32 + l32;
-                a_rd[i][ks] = S::oA + (uint32_t)(r * BK + 8 * a_swizzle(r, 2 * ks + lh)) * 2;
+                a_rd[i][j] = S::oA + (uint32_t)(r * BK + 8 * a_swizzle(r, 2 * (ks0 + j) + lh)) * 2;
             }
-        b_rd = S::oBdq + (uint32_t)((wn * kWCols + l32) * LDT + 8 * lh) * 2;
+        b_rd = S::oBdq + (uint32_t)((wn * kWCols + l32) * LDT + 8 * lh) * 2 + ks0 * 32;
         // dequant: thread tid converts words h*kWPT .. of column col (one column per thread when
         // BN > 128, the threads past column BN-1 writing to the sink; else kTPC per column)
         const int col = kTPC > 1 ? tid % BN : min(tid, BN - 1);
@@ -232,7 +298,7 @@ struct Gemm {
 #pragma unroll
         for (int st = 0; st < 2; ++st)
             bq_wr[st] = (kTPC > 1 || tid < BN) ? S::oBdq + st * S::kBdq + col * LDT * 2 + h * kWPT * 16
-                                               : S::oSink + (tid - BN) * 16;
+                                               : S::oSink + (tid - BN) * 16;  // (only when BN < threads)
         bp_rd = S::oBp + col * 4 + h * kWPT * BN * 4;
         // the bf16 of column c in group g is the (g*N + c) & 1 half of its slot
         const int c = min(n0 + col, N - 1);
@@ -240,116 +306,126 @@ struct Gemm {
         sc_rd[1] = S::oSc + col * 4 + 2 * ((c + 1) & 1);
     }
 
-    __device__ __forceinline__ int64_t group_n(int t) const {
-        return (int64_t)((kbeg + min(t, ntiles - 1) * BK) / 128) * N;
+    // A copies i0 .. i1-1 of this wave's share of one k-tile: src = the block's first row at the
+    // k-tile's first column, stage = the LDS stage's byte offset.
+    template <int i0, int i1>
+    __device__ __forceinline__ void issue_a(const char* src, uint32_t stage) const {
+        const uint32_t lds = a_lds + stage;
+        static_for<i0, i1>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            dma16<i * 8 * BK * 2>(a_off[i], src, lds);
+        });
     }
 
-    // Copies i0 .. i1-1 of this wave's share of A of k-tile ta, into stage ta % kAS.  Indices past
-    // the end fetch the last k-tile again (the data is never used; the stage is the one the index
-    // names, which no MFMA is reading).
-    __device__ __forceinline__ void issue_a(int ta, int i0 = 0, int i1 = kAInst) const {
-        const int wave = wave_id();
-        const char* base =
-            reinterpret_cast<const char*>(x) + ((size_t)m0 * K + kbeg + (size_t)min(ta, ntiles - 1) * BK) * 2;
-        const uint32_t dst = sm + S::oA + (ta % S::kAS) * S::kA + wave * (BM / 4) * BK * 2;
-#pragma unroll
-        for (int i = i0; i < i1; ++i) dma16(a_off[i], base, dst + i * 8 * BK * 2);
-    }
-
-    // The packed words of k-tile tb into stage tb % kBS and, if kSc, its group's scales and
-    // minimums into stage (tb / 2) % kSS (tb is then the group's first k-tile).
-    template <bool kSc>
-    __device__ __forceinline__ void issue_b(int tb) const {
-        const int wave = wave_id();
-        const char* base =
-            reinterpret_cast<const char*>(codes) + (size_t)((kbeg + min(tb, ntiles - 1) * BK) / 8) * N * 4;
-        const uint32_t dst = sm + S::oBp + (tb % S::kBS) * S::kBp;
-#pragma unroll
-        for (int i = 0; i < kBInst; ++i) {
-            if (kVec)
-                dma16(b_off[i], base, dst + (i * 4 + wave) * 1024);
+    // The packed words of one k-tile: src = its first packed row at column 0.
+    __device__ __forceinline__ void issue_b(const char* src, uint32_t stage) const {
+        const uint32_t lds = b_lds + stage;
+        static_for<0, kBInst>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (kVec)
+                dma16<i * kWaves * 1024>(b_off[i], src, lds);
             else
-                dma4(b_off[i], base, dst + (i * 4 + wave) * 256);
-        }
-        if (kSc) {
-            const int64_t gN = group_n(tb);
-            const uint32_t off = (gN & 1) ? sc_off[1] : sc_off[0];  // (no dynamic index: keeps it in a register)
-            const uint32_t sdst = sm + S::oSc + ((tb / 2) % S::kSS) * S::kSc + wave * 256;
-            const int64_t row = (2 * gN) & ~(int64_t)3;
-            dma4(off, reinterpret_cast<const char*>(scales) + row, sdst);
-            dma4(off, reinterpret_cast<const char*>(mins) + row, sdst + 1024);
-        }
+                dma4<i * kWaves * 256>(b_off[i], src, lds);
+        });
     }
 
-    // This thread's kWPT packed words of k-tile tn and its group's scale and minimum.
-    __device__ __forceinline__ void read_words(int tn, uint32_t (&w)[kWPT], float& s, float& s16, float& m) const {
-        const uint8_t* bp = smem + bp_rd + (tn % S::kBS) * S::kBp;
+    // The scales and minimums of one group: rb = 2 g N, the byte offset of row g in either array.
+    __device__ __forceinline__ void issue_sc(size_t rb, uint32_t stage) const {
+        const uint32_t off = (rb & 2) ? sc_off[1] : sc_off[0];  // (no dynamic index: keeps it in a register)
+        const size_t row = rb & ~(size_t)3;
+#pragma unroll
+        for (int i = 0; i < kScInst; ++i) dma4<0>(off, sc_arr[i] + row, sc_lds[i] + stage);
+    }
+
+    // This thread's kWPT packed words (words stage bstage) and the bf16 bits of its column's scale
+    // and minimum (scale stage scstage; odd = the parity of g*N for the words' group).
+    __device__ __forceinline__ void read_words(uint32_t bstage, uint32_t scstage, bool odd, uint32_t (&w)[kWPT],
+                                               uint32_t& sb, uint32_t& mb) const {
+        const uint8_t* bp = smem + bp_rd + bstage;
 #pragma unroll
         for (int r = 0; r < kWPT; ++r) w[r] = *reinterpret_cast<const uint32_t*>(bp + r * BN * 4);
-        const uint8_t* sc = smem + ((group_n(tn) & 1) ? sc_rd[1] : sc_rd[0]) + ((tn / 2) % S::kSS) * S::kSc;
-        s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc));
-        m = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sc + 1024));
-        s16 = s * 0.0625f;
+        const uint8_t* sc = smem + (odd ? sc_rd[1] : sc_rd[0]) + scstage;
+        sb = *reinterpret_cast<const uint16_t*>(sc);
+        mb = *reinterpret_cast<const uint16_t*>(sc + 1024);
     }
 
-    __device__ __forceinline__ void dequant_all(int st, const uint32_t (&w)[kWPT], float s, float s16, float m) const {
+    __device__ __forceinline__ void dequant_all(int st, const uint32_t (&w)[kWPT], uint32_t sb, uint32_t mb) const {
+        const float s = bf16_bits_to_f32(sb), m = bf16_bits_to_f32(mb), s16 = s * 0.0625f;
         uint8_t* dst = smem + bq_wr[st];
 #pragma unroll
         for (int r = 0; r < kWPT; ++r)
             *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
     }
 
-    // One k-tile t: MFMAs on A stage t % kAS and dequantized B stage `st` = t & 1 while the words `w` (the next
-    // k-tile) are dequantized into the other B stage, spread evenly over the k-steps.  issue(ks) runs at the
-    // top of each k-step: the copies for later k-tiles are spread over the tile rather than issued
-    // in one burst, which would hold up the wave's first MFMAs behind the load unit.
+    // The LDS reads of the fragments of own k-step ks of a k-tile (A stage at byte offset astage,
+    // dequantized B stage st) into register slot `slot`.
+    __device__ __forceinline__ void read_frags(uint32_t astage, int st, int ks, bf16x8_t (&af)[kMT],
+                                               bf16x8_t (&bfr)[kNT]) const {
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+            af[i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(smem + astage + a_rd[i][ks]));
+#pragma unroll
+        for (int j = 0; j < kNT; ++j)
+            bfr[j] = __builtin_bit_cast(
+                bf16x8_t, *reinterpret_cast<const uint4*>(smem + b_rd + S::kBdq * st + j * 32 * LDT * 2 + ks * 32));
+    }
+
+    // One k-tile of MFMA steps, shifted by one step: own step j reads the fragments of step j of
+    // this k-tile into register slot j & 1 and runs the MFMAs of the step before it, whose
+    // fragments sit in the other slot -- for j = 0, the last step of the previous k-tile, read
+    // before the barrier that ended it.  So the first MFMAs after a barrier never wait for LDS.
+    // Meanwhile the words `w` (the next k-tile) are dequantized into the other B stage, spread
+    // evenly over the steps, and issue(integral_constant j) runs at the top of step j: the
+    // copies for later k-tiles are spread over the tile rather than issued in one burst, which
+    // would hold up the wave's MFMAs behind the load unit.  The MFMA takes the B fragment as its
+    // first operand, so a lane's accumulator holds four adjacent output columns of one row.
     template <int st, typename Issue>
-    __device__ __forceinline__ void mma_tile(int t, f32x16_t (&acc)[kMT][kNT], const uint32_t (&w)[kWPT], float s,
-                                             float s16, float m, Issue&& issue) const {
-        const uint8_t* abase = smem + S::kA * (S::kAS == 2 ? st : t % S::kAS);
-        const uint8_t* bbase = smem + b_rd + S::kBdq * st;
+    __device__ __forceinline__ void mma_tile(uint32_t astage, f32x16_t (&acc)[kMT][kNT], bf16x8_t (&af)[2][kMT],
+                                             bf16x8_t (&bfr)[2][kNT], const uint32_t (&w)[kWPT], uint32_t sb,
+                                             uint32_t mb, Issue&& issue) const {
         uint8_t* dst = smem + bq_wr[st ^ 1];
-        bf16x8_t af[2][kMT], bfr[2][kNT];
-        auto read_frags = [&](int ks, int slot) {
-#pragma unroll
-            for (int i = 0; i < kMT; ++i)
-                af[slot][i] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(abase + a_rd[i][ks]));
-#pragma unroll
-            for (int j = 0; j < kNT; ++j)
-                bfr[slot][j] =
-                    __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(bbase + j * 32 * LDT * 2 + ks * 32));
-        };
-        read_frags(0, 0);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        float s, s16, m;
+        static_for<0, kOwnSteps>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
             __builtin_amdgcn_sched_barrier(0);
-            issue(ks);
-            if (ks + 1 < BK / 16) read_frags(ks + 1, (ks + 1) & 1);
+            issue(jc);
+            if constexpr (j == 0) {
+                // converted inside the scheduled region, so the wait for them follows the first MFMAs
+                s = bf16_bits_to_f32(sb);
+                m = bf16_bits_to_f32(mb);
+                s16 = s * 0.0625f;
+            }
+            read_frags(astage, st, j, af[j & 1], bfr[j & 1]);
 #pragma unroll
             for (int r = 0; r < kWPT; ++r)
-                if (r * (BK / 16) / kWPT == ks)
+                if (r * kOwnSteps / kWPT == j)
                     *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
-#pragma unroll
-            for (int j = 0; j < kNT; ++j)
-#pragma unroll
-                for (int i = 0; i < kMT; ++i)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks & 1][i], bfr[ks & 1][j], acc[i][j], 0,
-                                                                        0, 0);
-            step_schedule<kMFMA, kVPM>(ks == 0 ? kLead : 0);
-        }
+            mma_step(acc, af[(j + 1) & 1], bfr[(j + 1) & 1]);
+            step_schedule<kMFMA, kVPM>(j == 0 ? kLead : 0);
+        });
         __builtin_amdgcn_sched_barrier(0);
+    }
+
+    __device__ __forceinline__ static void mma_step(f32x16_t (&acc)[kMT][kNT], const bf16x8_t (&af)[kMT],
+                                                    const bf16x8_t (&bfr)[kNT]) {
+#pragma unroll
+        for (int jj = 0; jj < kNT; ++jj)
+#pragma unroll
+            for (int i = 0; i < kMT; ++i)
+                acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[jj], af[i], acc[i][jj], 0, 0, 0);
     }
 };
 
-template <int BM, int BN, int WM, int DA, int DB, bool kVec>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, int WM, int DA, int DB, bool kVec, int KS>
+__global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS)))
 void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                       const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
                       uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K, int k_per_split,
                       int splits, uint32_t mask_lo, uint32_t mask_hi) {
-    using G = Gemm<BM, BN, WM, DA, DB, kVec>;
+    using G = Gemm<BM, BN, WM, DA, DB, kVec, KS>;
+    using S = Smem<BM, BN, DA, DB, KS>;
     constexpr int kMT = G::kMT, kNT = G::kNT, kWPT = G::kWPT;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[Smem<BM, BN, DA, DB>::kTotal];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[S::kTotal];
     // XCD-aware tile order: block b runs on XCD b % 8, so XCD x takes the x-th contiguous eighth
     // of the (split, m, n) tile sequence, n fastest -- its blocks share A rows in its own L2.
     const int tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
@@ -375,6 +451,7 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
     g.mlo = mask_lo;
     g.mhi = mask_hi;
     g.init();
+    const int ntiles = g.ntiles;
     // the accumulators stay outside `g`: a local array is kept in registers across the copies'
     // inline assembly, whose memory clobber would otherwise force them out to scratch
     f32x16_t acc[kMT][kNT];
@@ -385,86 +462,208 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
+    // Copy sources, wave-uniform.  k-tile indices past the end fetch the last k-tile again: the
+    // data is never used, and the stage it lands in is one no MFMA or dequant is reading.
+    const char* const a_base = reinterpret_cast<const char*>(x + (size_t)g.m0 * K + g.kbeg);
+    const uint32_t a_lim = (uint32_t)(ntiles - 1) * BK * 2;
+    const size_t b_step = (size_t)8 * N * 4;  // one k-tile of packed rows
+    const char* const b_base = reinterpret_cast<const char*>(codes + (size_t)(g.kbeg / 8) * N);
+    const int glast = ntiles / 2 - 1;  // the split's last group, counted from its first
+    const size_t sc_step = (size_t)2 * N;
+    const size_t sc_base = (size_t)(g.kbeg / 128) * sc_step;
+
     // Prologue: A of k-tiles 0 .. DA-1, the words of 0 .. DB-1 and the scales of their groups;
     // k-tile 0 is then dequantized into B stage 0.
 #pragma unroll
-    for (int t0 = 0; t0 < DA; ++t0) g.issue_a(t0);
+    for (int t0 = 0; t0 < DA; ++t0) g.template issue_a<0, G::kAInst>(a_base + min(t0, ntiles - 1) * BK * 2, t0 * S::kA);
 #pragma unroll
     for (int t0 = 0; t0 < DB; ++t0) {
-        if (t0 % 2 == 0)
-            g.template issue_b<true>(t0);
-        else
-            g.template issue_b<false>(t0);
+        g.issue_b(b_base + (size_t)min(t0, ntiles - 1) * b_step, t0 * S::kBp);
+        if (t0 % 2 == 0) g.issue_sc(sc_base + (size_t)min(t0 / 2, glast) * sc_step, (t0 / 2) * S::kSc);
     }
     wait_vm<0>();
     __syncthreads();
     {
-        uint32_t w[kWPT];
-        float s, s16, m;
-        g.read_words(0, w, s, s16, m);
-        g.dequant_all(0, w, s, s16, m);
+        uint32_t w[kWPT], sb, mb;
+        g.read_words(0, 0, ((g.kbeg / 128) & N & 1) != 0, w, sb, mb);
+        g.dequant_all(0, w, sb, mb);
     }
     __syncthreads();
+
+    // Cursors of the copies still to come (scalar registers, advanced once per k-tile): the A
+    // k-tile copied next (byte offset, clamped), the words of k-tile tb and the scales of group gb
+    // (pointers, clamped).  Stages as byte offsets: A of k-tile t (a_cur) and of t-1 (a_prev,
+    // which is also the stage of t+DA), the words of t (b_cur, also the stage of t+DB), the
+    // scales of group p = t/2 (s_cur) and of p-1 (s_prev).
+    uint32_t a_o = (uint32_t)min(DA, ntiles - 1) * BK * 2;
+    int tb = DB;
+    const char* b_src = b_base + (size_t)min(DB, ntiles - 1) * b_step;
+    int gb = (DB + 1) / 2;  // the first group whose first k-tile is DB or later
+    size_t sc_rb = sc_base + (size_t)min(gb, glast) * sc_step;
+    uint32_t a_cur = 0, a_prev = (S::kAS - 1) * S::kA, b_cur = 0, s_cur = 0, s_prev = (S::kSS - 1) * S::kSc;
+    const uint32_t nodd = (uint32_t)N & 1;
+    uint32_t gpar = (uint32_t)(g.kbeg / 128) & 1;  // parity of group p
 
     // k-tile t: read the words of t+1; run the MFMAs of t while dequantizing t+1 and copying
     // A(t+DA) (spread over the k-steps) and then the words of t+DB (with their group's scales
     // when t+DB starts a group); then wait until A(t+1) and everything issued before it has
     // landed -- the words of t+2 and their scales were requested no later than A(t+1), since
     // DB >= DA + 2 -- and meet at the barrier.
-    constexpr int kSteps = BK / 16;
-    constexpr int kWaitEven = G::after_a(0), kWaitOdd = G::after_a(1);
-    auto issue_a_step = [&](int ta, int ks) {  // the A copies whose turn is k-step ks
+    constexpr int kSteps = G::kOwnSteps;  // k-steps each wave runs per k-tile
+    static_assert(kSteps % 2 == 0, "the last step's fragments sit in slot 1");
+    // fragment registers, two slots; slot 1 starts as zeros, so the "previous step" MFMAs of the
+    // first k-tile add nothing
+    bf16x8_t af[2][kMT], bfr[2][kNT];
 #pragma unroll
-        for (int i = 0; i < G::kAInst; ++i)
-            if (i * kSteps / G::kAInst == ks) g.issue_a(ta, i, i + 1);
+    for (int i = 0; i < kMT; ++i) af[1][i] = bf16x8_t{};
+#pragma unroll
+    for (int j = 0; j < kNT; ++j) bfr[1][j] = bf16x8_t{};
+    constexpr int kWaitEven = G::after_a(0), kWaitOdd = G::after_a(1);
+    auto advance = [&](bool sc_copied) {
+        a_o = min(a_o + BK * 2, a_lim);
+        ++tb;
+        b_src += tb < ntiles ? b_step : 0;
+        if (sc_copied) {
+            ++gb;
+            sc_rb += gb <= glast ? sc_step : 0;
+        }
+        if constexpr (S::kAS > 2) {
+            a_prev = a_cur;
+            a_cur = next_stage<S::kA, S::kAS>(a_cur);
+        }
     };
-    for (int tt = 0; tt < g.ntiles; tt += 2) {
+    for (int tt = 0; tt < ntiles; tt += 2) {
         {
-            uint32_t w[kWPT];
-            float s, s16, m;
-            g.read_words(tt + 1, w, s, s16, m);
-            g.template mma_tile<0>(tt, acc, w, s, s16, m, [&](int ks) {
-                issue_a_step(tt + DA, ks);
-                if (ks == kSteps - 1) g.template issue_b<DB % 2 == 0>(tt + DB);
+            const uint32_t b_next = next_stage<S::kBp, S::kBS>(b_cur);
+            const uint32_t a_rd = S::kAS == 2 ? 0 : a_cur, a_wr = S::kAS == 2 ? S::kA : a_prev;
+            uint32_t w[kWPT], sb, mb;
+            g.read_words(b_next, s_cur, (gpar & nodd) != 0, w, sb, mb);
+            const char* a_src = a_base + a_o;
+            g.template mma_tile<0>(a_rd, acc, af, bfr, w, sb, mb, [&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value;
+                static_for<0, G::kAInst>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (i * kSteps / G::kAInst == ks) g.template issue_a<i, i + 1>(a_src, a_wr);
+                });
+                if constexpr (ks == kSteps - 1) {
+                    g.issue_b(b_src, b_cur);
+                    if constexpr (DB % 2 == 0) g.issue_sc(sc_rb, s_prev);
+                }
             });
+            advance(DB % 2 == 0);
+            b_cur = b_next;
             wait_vm<kWaitEven>();
             __syncthreads();
         }
         {
-            uint32_t w[kWPT];
-            float s, s16, m;
-            g.read_words(tt + 2, w, s, s16, m);
-            g.template mma_tile<1>(tt + 1, acc, w, s, s16, m, [&](int ks) {
-                issue_a_step(tt + 1 + DA, ks);
-                if (ks == kSteps - 1) g.template issue_b<DB % 2 == 1>(tt + 1 + DB);
+            const uint32_t b_next = next_stage<S::kBp, S::kBS>(b_cur);
+            const uint32_t a_rd = S::kAS == 2 ? S::kA : a_cur, a_wr = S::kAS == 2 ? 0 : a_prev;
+            const uint32_t s_next = next_stage<S::kSc, S::kSS>(s_cur);
+            uint32_t w[kWPT], sb, mb;
+            g.read_words(b_next, s_next, ((gpar ^ 1) & nodd) != 0, w, sb, mb);
+            const char* a_src = a_base + a_o;
+            g.template mma_tile<1>(a_rd, acc, af, bfr, w, sb, mb, [&](auto ksc) {
+                constexpr int ks = decltype(ksc)::value;
+                static_for<0, G::kAInst>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (i * kSteps / G::kAInst == ks) g.template issue_a<i, i + 1>(a_src, a_wr);
+                });
+                if constexpr (ks == kSteps - 1) {
+                    g.issue_b(b_src, b_cur);
+                    if constexpr (DB % 2 == 1) g.issue_sc(sc_rb, s_cur);
+                }
             });
+            advance(DB % 2 == 1);
+            b_cur = b_next;
+            s_prev = s_cur;
+            s_cur = s_next;
+            gpar ^= 1;
             wait_vm<kWaitOdd>();
             __syncthreads();
         }
     }
+    G::mma_step(acc, af[1], bfr[1]);  // the last step of the last k-tile
     wait_vm<0>();  // no copy may still be writing this block's LDS when it exits
 
-    // D fragment of a 32 x 32 tile: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+    // D fragment of the MFMA of B tile jj and A tile i: element e of lane l is output row l % 32
+    // of A tile i and column 8 (e / 4) + 4 (l / 32) + e % 4 of B tile jj -- four adjacent columns
+    // for each q = e / 4.
     const int lane = lane_id(), wave = wave_id();
     const int l32 = lane & 31, lh = lane >> 5;
-    const int wm = wave % WM, wn = wave / WM;
+    const int w4 = wave % 4, wm = w4 % WM, wn = w4 / WM;
+    const int row0 = wm * G::kWRows + l32;     // + 32 i
+    const int col0 = wn * G::kWCols + 4 * lh;  // + 32 jj + 8 q
+    if constexpr (KS == 2) {
+        // the second k group hands its sums to the first through LDS (all copies have landed:
+        // every wave waited for its own above, and the barrier covers the others'); rows are
+        // padded by 16 B so the 16-byte writes and reads of a wave are free of bank conflicts
+        constexpr int kPitch = BN + 4;
+        static_assert(BM * kPitch * 4 <= S::kTotal, "partials fit in LDS");
+        float* part = reinterpret_cast<float*>(smem);
+        __syncthreads();
+        if (wave >= 4) {
+#pragma unroll
+            for (int i = 0; i < kMT; ++i)
+#pragma unroll
+                for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4_t v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                           acc[i][j][4 * q + 3]};
+                        *reinterpret_cast<f32x4_t*>(part + (row0 + 32 * i) * kPitch + col0 + 32 * j + 8 * q) = v;
+                    }
+        }
+        __syncthreads();
+        if (wave >= 4) return;
+#pragma unroll
+        for (int i = 0; i < kMT; ++i)
+#pragma unroll
+            for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4_t v =
+                        *reinterpret_cast<const f32x4_t*>(part + (row0 + 32 * i) * kPitch + col0 + 32 * j + 8 * q);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += v[r];
+                }
+    }
+    // Stores: with N % 4 == 0 each lane writes its four adjacent outputs at once (8 bytes of bf16,
+    // or 16 of fp32 partials), unchecked when the whole tile lies inside the output.
     const bool split = splits > 1;
+    const bool interior = g.m0 + BM <= M && g.n0 + BN <= N;
 #pragma unroll
-    for (int i = 0; i < kMT; ++i)
+    for (int i = 0; i < kMT; ++i) {
+        const int row = g.m0 + row0 + 32 * i;
+        const int col = g.n0 + col0;
+        uint16_t* yr = y + (size_t)min(row, M - 1) * N + col;
+        float* wr = ws + ((size_t)split_id * M + min(row, M - 1)) * N + col;
 #pragma unroll
-        for (int j = 0; j < kNT; ++j) {
-            const int col = g.n0 + wn * G::kWCols + j * 32 + l32;
+        for (int j = 0; j < kNT; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int row = g.m0 + wm * G::kWRows + i * 32 + 8 * (e / 4) + 4 * lh + (e % 4);
-                if (row < M && col < N) {
-                    if (split)
-                        ws[((size_t)split_id * M + row) * N + col] = acc[i][j][e];
-                    else
-                        y[(size_t)row * N + col] = f32_to_bf16_bits(acc[i][j][e]);
+            for (int q = 0; q < 4; ++q) {
+                const int c = 32 * j + 8 * q;
+                const float v0 = acc[i][j][4 * q], v1 = acc[i][j][4 * q + 1];
+                const float v2 = acc[i][j][4 * q + 2], v3 = acc[i][j][4 * q + 3];
+                if constexpr (kVec) {
+                    if (interior || (row < M && col + c < N)) {
+                        if (split)
+                            *reinterpret_cast<f32x4_t*>(wr + c) = f32x4_t{v0, v1, v2, v3};
+                        else
+                            *reinterpret_cast<uint2*>(yr + c) = make_uint2(pack2_bf16(v0, v1), pack2_bf16(v2, v3));
+                    }
+                } else {
+                    const float v[4] = {v0, v1, v2, v3};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (row < M && col + c + r < N) {
+                            if (split)
+                                wr[c + r] = v[r];
+                            else
+                                yr[c + r] = f32_to_bf16_bits(v[r]);
+                        }
                 }
             }
-        }
+    }
 }
 
 // y = bf16(sum over splits, in split order) of the fp32 partials.
@@ -505,18 +704,18 @@ GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     return p;
 }
 
-template <int BM, int BN, int WM, int DA, int DB>
+template <int BM, int BN, int WM, int DA, int DB, int KS>
 void launch_cfg(const GemmPlan& p, const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                 const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace, hipStream_t stream) {
     // a 1-D grid of 8 x ceil(tiles / 8) blocks over (split, m, n); the surplus exit at once
     const int64_t tiles = (int64_t)p.tiles_n * p.tiles_m * p.splits;
     const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
     if (N % 4 == 0)
-        hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, true>), grid, dim3(kThreads), 0, stream, x, codes, scales,
+        hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, true, KS>), grid, dim3(256 * KS), 0, stream, x, codes, scales,
                            mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu,
                            0xF0F0F0F0u);
     else
-        hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, false>), grid, dim3(kThreads), 0, stream, x, codes, scales,
+        hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, false, KS>), grid, dim3(256 * KS), 0, stream, x, codes, scales,
                            mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu,
                            0xF0F0F0F0u);
 }
@@ -535,10 +734,10 @@ hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes,
     if (M <= kMidMaxRows) return launch_mid_g128(x, M, codes, scales, mins, N, K, y, stream);
     const GemmPlan p = plan_gemm(M, N, K);
     switch (p.cfg) {
-        case kT64x128: launch_cfg<64, 128, 2, 3, 6>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
-        case kT128x128: launch_cfg<128, 128, 2, 2, 5>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
-        case kT128x256: launch_cfg<128, 256, 2, 1, 4>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
-        case kT256x224: launch_cfg<256, 224, 4, 1, 3>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT64x128: launch_cfg<64, 128, 2, 3, 6, 2>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT128x128: launch_cfg<128, 128, 2, 2, 5, 2>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT128x256: launch_cfg<128, 256, 2, 1, 4, 1>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT256x224: launch_cfg<256, 224, 4, 1, 3, 1>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
