@@ -19,18 +19,20 @@
 //    HBM latency inside the loop;
 //  * while the MFMAs of k-tile t read one dequantized B stage, the threads turn the 8 packed words
 //    of each column of k-tile t+1 into the other (one column per thread, or two or four threads
-//    per column when BN < 256): w_hat = bf16_rne(fmaf(q, s, min)), the
-//    same value as the reference dequant, 22 VALU instructions per word, interleaved with the
-//    MFMAs (about four VALU instructions fit under one 32x32x16 MFMA).  Each word becomes one
-//    16-byte row segment of an [n][k] tile, which is exactly an MFMA B fragment; rows are padded
-//    to 144 B, so fragment reads and dequant writes are free of bank conflicts;
+//    per column when BN < 256): w_hat = bf16_rne(fmaf(q, s, min)), the same value as the
+//    reference dequant.  Two codes at a time become exact fp32 through the fp8 (e4m3)
+//    conversion, in which the bytes 0..15 are exactly the integers times 2^-9: 19 VALU
+//    instructions per word, interleaved with the MFMAs.  Each word becomes one 16-byte row
+//    segment of an [n][k] tile, which is exactly an MFMA B fragment; rows are padded to 144 B,
+//    so fragment reads and dequant writes are free of bank conflicts;
 //  * the MFMA steps run one step behind the fragment reads and across the k-tile boundary: the
 //    first MFMAs after each barrier use fragments read before it, so no k-tile starts with a
 //    wait for LDS.  The copies' sources and LDS stages are kept in scalar cursors advanced
 //    once per k-tile (a handful of scalar instructions instead of per-tile address arithmetic,
 //    since the scalar unit is shared by the CU's waves);
-//  * the MFMA takes the B fragment first, so each lane's accumulators hold runs of four adjacent
-//    output columns, stored as one 8-byte bf16 (or 16-byte fp32) write each;
+//  * the output tile leaves through LDS as whole rows (16 bytes per lane, a wave writing 1 KB of
+//    consecutive bytes per instruction): with every block finishing at the same moment, one
+//    16-byte write request per row and instruction left the epilogue bound by write requests;
 //  * when the tile grid alone cannot fill the chip, K is split in whole groups; fp32 partials go
 //    to the caller's workspace and a second kernel adds them in split order, so the result does
 //    not depend on scheduling.
@@ -141,19 +143,21 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // One dequantized word: 8 k of one column -> 16 bytes of bf16, w_hat = bf16_rne(fmaf(q, s, m)).
-// Codes 0, 2, 4, 6 come from w & 0x0F0F0F0F and codes 1, 3, 5, 7 from w & 0xF0F0F0F0 as 16 q,
-// multiplied by s/16: the product is the same exact value, so the fma rounds identically.  The
-// masks arrive as kernel arguments so that each byte converts with one v_cvt_f32_ubyteN.
-__device__ __forceinline__ uint4 dequant_word(uint32_t w, uint32_t mlo, uint32_t mhi, float s, float s16, float m) {
-    const uint32_t ev = w & mlo, od = w & mhi;
-    const float v0 = __builtin_fmaf((float)(ev & 0xFF), s, m);
-    const float v2 = __builtin_fmaf((float)((ev >> 8) & 0xFF), s, m);
-    const float v4 = __builtin_fmaf((float)((ev >> 16) & 0xFF), s, m);
-    const float v6 = __builtin_fmaf((float)(ev >> 24), s, m);
-    const float v1 = __builtin_fmaf((float)(od & 0xFF), s16, m);
-    const float v3 = __builtin_fmaf((float)((od >> 8) & 0xFF), s16, m);
-    const float v5 = __builtin_fmaf((float)((od >> 16) & 0xFF), s16, m);
-    const float v7 = __builtin_fmaf((float)(od >> 24), s16, m);
+// Each byte of w & 0x0F0F0F0F (codes 0, 2, 4, 6) and of (w >> 4) & 0x0F0F0F0F (codes 1, 3, 5, 7)
+// read as an OCP fp8 e4m3 value is exactly q * 2^-9 (codes 0..7 are the subnormals m * 2^-9,
+// codes 8..15 the normals of exponent field 1, (8 + m) * 2^-9), so one scaled conversion, whose
+// scale applies only its power of two, yields two exact fp32 codes.  The mask arrives as a
+// kernel argument.
+__device__ __forceinline__ uint4 dequant_word(uint32_t w, uint32_t mlo, float s, float m) {
+    const uint32_t ev = w & mlo, od = (w >> 4) & mlo;
+    const f32x2_t q02 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 512.0f, false);
+    const f32x2_t q46 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(ev, 512.0f, true);
+    const f32x2_t q13 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 512.0f, false);
+    const f32x2_t q57 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(od, 512.0f, true);
+    const float v0 = __builtin_fmaf(q02.x, s, m), v2 = __builtin_fmaf(q02.y, s, m);
+    const float v4 = __builtin_fmaf(q46.x, s, m), v6 = __builtin_fmaf(q46.y, s, m);
+    const float v1 = __builtin_fmaf(q13.x, s, m), v3 = __builtin_fmaf(q13.y, s, m);
+    const float v5 = __builtin_fmaf(q57.x, s, m), v7 = __builtin_fmaf(q57.y, s, m);
     return make_uint4(pack2_bf16(v0, v1), pack2_bf16(v2, v3), pack2_bf16(v4, v5), pack2_bf16(v6, v7));
 }
 
@@ -217,7 +221,7 @@ struct Gemm {
     uint8_t* smem;
     uint32_t sm;  // LDS address of smem
     int M, N, K, m0, n0, kbeg, ntiles;
-    uint32_t mlo, mhi;
+    uint32_t mlo;  // 0x0F0F0F0F (a kernel argument, so the compiler keeps it in a register)
     // per-lane byte offsets of the copies (constant over the k-loop)
     uint32_t a_off[kAInst];  // from the k-tile's A base
     uint32_t b_off[kBInst > 0 ? kBInst : 1];  // from the k-tile's first packed row
@@ -350,11 +354,11 @@ struct Gemm {
     }
 
     __device__ __forceinline__ void dequant_all(int st, const uint32_t (&w)[kWPT], uint32_t sb, uint32_t mb) const {
-        const float s = bf16_bits_to_f32(sb), m = bf16_bits_to_f32(mb), s16 = s * 0.0625f;
+        const float s = bf16_bits_to_f32(sb), m = bf16_bits_to_f32(mb);
         uint8_t* dst = smem + bq_wr[st];
 #pragma unroll
         for (int r = 0; r < kWPT; ++r)
-            *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
+            *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, s, m);
     }
 
     // The LDS reads of the fragments of own k-step ks of a k-tile (A stage at byte offset astage,
@@ -384,7 +388,7 @@ struct Gemm {
                                              bf16x8_t (&bfr)[2][kNT], const uint32_t (&w)[kWPT], uint32_t sb,
                                              uint32_t mb, Issue&& issue) const {
         uint8_t* dst = smem + bq_wr[st ^ 1];
-        float s, s16, m;
+        float s, m;
         static_for<0, kOwnSteps>([&](auto jc) {
             constexpr int j = decltype(jc)::value;
             __builtin_amdgcn_sched_barrier(0);
@@ -393,13 +397,12 @@ struct Gemm {
                 // converted inside the scheduled region, so the wait for them follows the first MFMAs
                 s = bf16_bits_to_f32(sb);
                 m = bf16_bits_to_f32(mb);
-                s16 = s * 0.0625f;
             }
             read_frags(astage, st, j, af[j & 1], bfr[j & 1]);
 #pragma unroll
             for (int r = 0; r < kWPT; ++r)
                 if (r * kOwnSteps / kWPT == j)
-                    *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, mhi, s, s16, m);
+                    *reinterpret_cast<uint4*>(dst + r * 16) = dequant_word(w[r], mlo, s, m);
             mma_step(acc, af[(j + 1) & 1], bfr[(j + 1) & 1]);
             step_schedule<kMFMA, kVPM>(j == 0 ? kLead : 0);
         });
@@ -421,7 +424,7 @@ __global__ __launch_bounds__(256 * KS) __attribute__((amdgpu_waves_per_eu(KS, KS
 void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                       const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
                       uint16_t* __restrict__ y, float* __restrict__ ws, int M, int N, int K, int k_per_split,
-                      int splits, uint32_t mask_lo, uint32_t mask_hi) {
+                      int splits, uint32_t mask_lo) {
     using G = Gemm<BM, BN, WM, DA, DB, kVec, KS>;
     using S = Smem<BM, BN, DA, DB, KS>;
     constexpr int kMT = G::kMT, kNT = G::kNT, kWPT = G::kWPT;
@@ -449,7 +452,6 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
     g.kbeg = split_id * k_per_split;
     g.ntiles = (min(K, g.kbeg + k_per_split) - g.kbeg) / BK;  // even: splits are whole groups
     g.mlo = mask_lo;
-    g.mhi = mask_hi;
     g.init();
     const int ntiles = g.ntiles;
     // the accumulators stay outside `g`: a local array is kept in registers across the copies'
@@ -614,22 +616,55 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
                     }
         }
         __syncthreads();
-        if (wave >= 4) return;
+        if (wave < 4) {
 #pragma unroll
-        for (int i = 0; i < kMT; ++i)
+            for (int i = 0; i < kMT; ++i)
 #pragma unroll
-            for (int j = 0; j < kNT; ++j)
+                for (int j = 0; j < kNT; ++j)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4_t v =
-                        *reinterpret_cast<const f32x4_t*>(part + (row0 + 32 * i) * kPitch + col0 + 32 * j + 8 * q);
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(part + (row0 + 32 * i) * kPitch + col0 +
+                                                                             32 * j + 8 * q);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += v[r];
-                }
+                        for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] += v[r];
+                    }
+        }
     }
-    // Stores: with N % 4 == 0 each lane writes its four adjacent outputs at once (8 bytes of bf16,
-    // or 16 of fp32 partials), unchecked when the whole tile lies inside the output.
     const bool split = splits > 1;
+    if (kVec && !split && N % 8 == 0) {
+        // bf16 output through LDS: the first k group writes its tile as rows of bf16 (8 bytes per
+        // lane and q), then every thread stores whole 16-byte chunks of rows, so a wave writes
+        // 1 KB of consecutive row bytes per instruction -- full cache lines instead of one 16-byte
+        // piece per row and instruction, which left the write path, not the kernel, the limit.
+        // Rows are padded by 16 B to spread the banks.
+        constexpr int kOP = 2 * BN + 16;  // staged row pitch, bytes
+        static_assert(BM * kOP <= S::kTotal, "staged output fits in LDS");
+        constexpr int kChunks = BN / 8;   // 16-byte chunks per row
+        __syncthreads();  // (KS = 2: the second group has read its partials back)
+        if (KS == 1 || wave < 4) {
+#pragma unroll
+            for (int i = 0; i < kMT; ++i)
+#pragma unroll
+                for (int j = 0; j < kNT; ++j)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<uint2*>(smem + (row0 + 32 * i) * kOP + (col0 + 32 * j + 8 * q) * 2) =
+                            make_uint2(pack2_bf16(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                       pack2_bf16(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < BM * kChunks; c += G::kThr) {
+            const int r = c / kChunks, cc = c % kChunks;
+            const int row = g.m0 + r, col = g.n0 + 8 * cc;
+            if (row < M && col < N)
+                *reinterpret_cast<uint4*>(y + (size_t)row * N + col) =
+                    *reinterpret_cast<const uint4*>(smem + r * kOP + cc * 16);
+        }
+        return;
+    }
+    if (KS == 2 && wave >= 4) return;
+    // Direct stores: with N % 4 == 0 each lane writes its four adjacent outputs at once (8 bytes
+    // of bf16, or 16 of fp32 partials), unchecked when the whole tile lies inside the output.
     const bool interior = g.m0 + BM <= M && g.n0 + BN <= N;
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
@@ -712,12 +747,10 @@ void launch_cfg(const GemmPlan& p, const uint16_t* x, int64_t M, const uint32_t*
     const dim3 grid((unsigned)(8 * ((tiles + 7) / 8)));
     if (N % 4 == 0)
         hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, true, KS>), grid, dim3(256 * KS), 0, stream, x, codes, scales,
-                           mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu,
-                           0xF0F0F0F0u);
+                           mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu);
     else
         hipLaunchKernelGGL((gemm_g128_kernel<BM, BN, WM, DA, DB, false, KS>), grid, dim3(256 * KS), 0, stream, x, codes, scales,
-                           mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu,
-                           0xF0F0F0F0u);
+                           mins, y, workspace, (int)M, (int)N, (int)K, p.k_per_split, p.splits, 0x0F0F0F0Fu);
 }
 
 }  // namespace
