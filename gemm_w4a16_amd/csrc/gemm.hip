@@ -636,7 +636,8 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
         // lane and q), then every thread stores whole 16-byte chunks of rows, so a wave writes
         // 1 KB of consecutive row bytes per instruction -- full cache lines instead of one 16-byte
         // piece per row and instruction, which left the write path, not the kernel, the limit.
-        // Rows are padded by 16 B to spread the banks.
+        // Rows are padded by 16 B to spread the banks.  The stores are non-temporal: the output is
+        // not read again by this kernel, and lines left dirty in L2 are written back at its end.
         constexpr int kOP = 2 * BN + 16;  // staged row pitch, bytes
         static_assert(BM * kOP <= S::kTotal, "staged output fits in LDS");
         constexpr int kChunks = BN / 8;   // 16-byte chunks per row
@@ -657,8 +658,8 @@ void gemm_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict
             const int r = c / kChunks, cc = c % kChunks;
             const int row = g.m0 + r, col = g.n0 + 8 * cc;
             if (row < M && col < N)
-                *reinterpret_cast<uint4*>(y + (size_t)row * N + col) =
-                    *reinterpret_cast<const uint4*>(smem + r * kOP + cc * 16);
+                __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(smem + r * kOP + cc * 16),
+                                            reinterpret_cast<u32x4_t*>(y + (size_t)row * N + col));
         }
         return;
     }
