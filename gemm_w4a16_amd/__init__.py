@@ -36,7 +36,7 @@ class W4A16Error(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not _LIB_PATH.exists():
-        raise ImportError(f"{_LIB_PATH} is not built; run `python -m gemm_w4a16_amd.build` "
+        raise ImportError(f"{_LIB_PATH} is not built; run `python gemm_w4a16_amd/build.py` "
                           "(hipcc for gfx950). There is no fallback path.")
     # PyTorch ships its own HIP runtime (libamdhip64.so.7).  It must be the one in the process
     # before libw4a16.so is loaded, so that the library's dependency on libamdhip64.so.7 binds to

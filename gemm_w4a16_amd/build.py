@@ -1,6 +1,6 @@
 """Build libw4a16.so (the HIP kernels + C ABI) in-tree for gfx950 with hipcc.
 
-    python -m gemm_w4a16_amd.build          # or gemm_w4a16_amd.build.build()
+    python gemm_w4a16_amd/build.py         # or __graft_entry__.build()
 
 Flags that matter for the numerics:
   -fhip-fp32-correctly-rounded-divide-sqrt  the quantizers use IEEE fp32 division
