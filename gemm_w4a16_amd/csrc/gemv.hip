@@ -5,19 +5,25 @@
 // that page and anrans "Quantization and GEMV", exercise 1, do) and the register dequant of
 // anrans "W4A16: dequantizing in registers", reorganised for CDNA4:
 //
-//  * Nibbles become bf16/fp16 numbers with one AND-OR each pair: (w >> 4j) & 0x000F000F with
-//    exponent bits 0x4300 (bf16) or 0x6400 (fp16) OR-ed in is the pair (B + q_j, B + q_{j+4})
-//    with B = 128 or 1024 (the magic-number trick both pages describe).  v_dot2c_f32_{bf16,f16}
-//    then multiplies two weights per instruction with fp32 accumulation.  The activations are
-//    paired the same way, (x_j, x_{j+4}), so no nibble has to move.
-//  * The offset B and the bias 8 are removed once per block: s * (sum(x*(B+q)) - (B+8)*sum(x)).
+//  * Nibbles become fp16 numbers with one AND-OR per pair (the magic-number trick both pages
+//    describe): with the exponent of 1024 OR-ed in, mask 0x000F000F turns the nibbles of k = 0
+//    and 4 into 1024 + q, and mask 0x00F000F0 turns those of k = 1 and 5 into 1024 + 16q, both
+//    exact in fp16; the word shifted right by 8 gives k = 2, 6 and 3, 7 the same way.  That is
+//    five instructions per 8 codes.  v_dot2c_f32_f16 multiplies two weights per instruction
+//    with fp32 accumulation into two sums (the 1x and the 16x nibbles), against activations
+//    paired the same way, (x_j, x_{j+4}).  The offsets and the bias 8 are removed once per block:
+//    sum (q - 8) x = [sum (1024 + q) x - 1032 sum x] + [sum (1024 + 16q) x - 1152 sum x] / 16.
+//    (bf16 activations, accepted as an extension, use 128 + q from the low nibble of each half
+//    after a shift: seven instructions per 8 codes.)
 //
 // Layout: codes are [N][K/32][16] bytes (a row's blocks contiguous), so 16 lanes read 512 B
 // of one row per pair of 16-byte loads (256 contiguous bytes each) and a wave covers 4 rows per
 // step.  Each lane always handles the same two blocks (64 k) of the row, so its activations
-// are loaded once, kept in VGPRs already
-// paired, and their per-block sums folded into a constant.  The 16 lanes of a row finish with a
-// DPP row reduction; the 16 waves of a 1024-thread block own 16 K-slices and add in LDS.
+// are loaded once, kept in VGPRs already paired, and their per-block sums folded into
+// constants.  Each wave keeps the loads of the next steps in flight while it computes one (a
+// rolling window, issued before the activations are even waited for).  The 16 lanes of a row
+// finish with a DPP row reduction; the 16 waves of a 1024-thread block own 16 K-slices and add
+// in LDS.
 #include "device_common.h"
 #include "launch.h"
 
@@ -26,6 +32,7 @@ namespace w4a16 {
 namespace {
 
 constexpr uint32_t kNibblePairMask = 0x000F000Fu;
+constexpr uint32_t kNibblePairMaskHi = 0x00F000F0u;
 constexpr uint32_t kBf16Magic = 0x43004300u;  // bf16 128.0 in both halves
 constexpr uint32_t kF16Magic = 0x64006400u;   // fp16 1024.0 in both halves
 constexpr uint32_t kBf16OnePair = 0x3F803F80u;
@@ -39,9 +46,15 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a 
 // Q4 block-32: 1024 threads = 16 waves = 16 K-slices of 1024 k; 64 rows per block.
 // ---------------------------------------------------------------------------------------------
 constexpr int kQ4Waves = 16;
-constexpr int kQ4Rows = 64;               // rows per block
+constexpr int kQ4Rows = 64;                // rows per block
 constexpr int kQ4Steps = kQ4Rows / 4;      // a wave step covers 4 rows
-constexpr int kQ4Pair = 4;                 // row steps whose loads are in flight together
+constexpr int kQ4Ahead = 2;                // row steps whose loads are in flight ahead of the math
+
+// One row step's data for one lane: its two 16-byte code blocks and their two scales.
+struct Q4Step {
+    u32x4_t c[2];
+    uint32_t s[2];
+};
 
 template <bool kF16>
 __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __restrict__ x,
@@ -54,8 +67,16 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
     const int rsub = lane >> 4;  // which of the 4 rows of a step
     const int B = K >> 5;        // blocks per row
     const int n0 = blockIdx.x * kQ4Rows;
-    const uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
-    const float offset = kF16 ? 1032.0f : 136.0f;  // B + 8: (q - 8) = (B + q) - (B + 8)
+    const bool full = n0 + kQ4Rows <= N;
+    // this block's first row of codes (16 B per block) and of scales
+    const char* cblk = reinterpret_cast<const char*>(codes) + (size_t)n0 * B * 16;
+    const char* sblk = reinterpret_cast<const char*>(scales) + (size_t)n0 * B * 2;
+    // The masks in SGPRs and the fp16 exponent in a VGPR, opaque to the compiler, so that each
+    // pair is one v_and_or_b32 (VOP3 takes no literal and one scalar operand on gfx9).
+    uint32_t mask_lo, mask_hi, magic_v;
+    asm volatile("s_mov_b32 %0, %1" : "=s"(mask_lo) : "i"(kNibblePairMask));
+    asm volatile("s_mov_b32 %0, %1" : "=s"(mask_hi) : "i"(kNibblePairMaskHi));
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "i"(kF16 ? kF16Magic : kBf16Magic));
 
     // Per-row partial of this wave; each K-slice a wave owns adds into its own LDS slot.
     for (int t = threadIdx.x & 63; t < kQ4Rows; t += 64) part[wave][t] = 0.0f;
@@ -66,78 +87,109 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
         const int b0 = slice * 32 + sub, b1 = b0 + 16;
         const bool has0 = b0 < B, has1 = b1 < B;
         // A block past the row's end is read at a clamped index and its contribution dropped by a
-        // select after the load: no load sits under a branch (a branch would make every load
+        // zero scale after the load: no load sits under a branch (a branch would make every load
         // wait for all earlier ones).
         const int bb0 = min(b0, B - 1), bb1 = min(b1, B - 1);
-        // activations of the two blocks, paired (x_j, x_{j+4}) per 8 k, and their sums
+        // Loads address a wave-uniform base (this block's first row) plus a 32-bit lane offset;
+        // rows past N (last block only) re-read row N - 1, whose result is never stored.
+        auto load = [&](int t, Q4Step& R) {
+            uint32_t r = 4 * t + rsub;
+            if (!full) r = min(r, (uint32_t)(N - 1 - n0));
+            // byte offsets in 32 bits, so that each load is SGPR base + VGPR offset
+            const uint32_t o0 = r * (uint32_t)B + (uint32_t)bb0, o1 = r * (uint32_t)B + (uint32_t)bb1;
+            R.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o0 * 16u));
+            R.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o1 * 16u));
+            const uint32_t s0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + o0 * 2u));
+            const uint32_t s1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + o1 * 2u));
+            R.s[0] = has0 ? s0 : 0u;  // fp16 +0: the block contributes nothing
+            R.s[1] = has1 ? s1 : 0u;
+        };
+        // The first steps' weight loads go out before the activations are waited for.
+        Q4Step r[kQ4Steps];
+#pragma unroll
+        for (int t = 0; t < kQ4Ahead; ++t) load(t, r[t]);
+        // Activations of the two blocks, paired per 8 k, and the per-block constants that remove
+        // the magic offset and the code bias (see the top of this file).
         uint32_t xq[2][16];
-        float cst[2];
+        float cst[2][2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool has = h ? has1 : has0;
             const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * 32);
-            float sum = 0.0f;
+            float sum_a = 0.0f, sum_b = 0.0f;
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const u32x4_t xl = xr[d];
                 const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
+                // (x0,x4) (x1,x5) (x2,x6) (x3,x7) of these 8 k
                 xq[h][4 * d + 0] = pack_lo(xv.x, xv.z);
                 xq[h][4 * d + 1] = pack_hi(xv.x, xv.z);
                 xq[h][4 * d + 2] = pack_lo(xv.y, xv.w);
                 xq[h][4 * d + 3] = pack_hi(xv.y, xv.w);
+                if (kF16) {
+                    // even-position pairs (x0,x4), (x2,x6) meet 1024 + q; odd ones (x1,x5),
+                    // (x3,x7) meet 1024 + 16q
+                    sum_a = dot2_f16(xq[h][4 * d + 0], kF16OnePair, sum_a);
+                    sum_a = dot2_f16(xq[h][4 * d + 2], kF16OnePair, sum_a);
+                    sum_b = dot2_f16(xq[h][4 * d + 1], kF16OnePair, sum_b);
+                    sum_b = dot2_f16(xq[h][4 * d + 3], kF16OnePair, sum_b);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sum = kF16 ? dot2_f16(xq[h][4 * d + e], kF16OnePair, sum)
-                               : dot2_bf16(xq[h][4 * d + e], kBf16OnePair, sum);
+                    for (int e = 0; e < 4; ++e) sum_a = dot2_bf16(xq[h][4 * d + e], kBf16OnePair, sum_a);
+                }
             }
-            cst[h] = -offset * sum;
+            if (kF16) {
+                cst[h][0] = -1032.0f * sum_a;  // sum (1024 + q) x - 1032 sum x = sum (q - 8) x
+                cst[h][1] = -1152.0f * sum_b;  // (sum (1024 + 16q) x - 1152 sum x) / 16 = sum (q - 8) x
+            } else {
+                cst[h][0] = -136.0f * sum_a;   // sum (128 + q) x - 136 sum x = sum (q - 8) x
+                cst[h][1] = 0.0f;
+            }
         }
-        // Row steps of 4 rows, kQ4Pair at a time: all their loads are issued, then the rows are
-        // computed in order as their data arrives.
-        struct Rows {
-            u32x4_t c[kQ4Pair][2];
-            uint32_t s[kQ4Pair][2];
-        };
-        auto load = [&](int t0, Rows& R) {
+        auto compute = [&](int t, const Q4Step& R) {
+            float part_row = 0.0f;
 #pragma unroll
-            for (int u = 0; u < kQ4Pair; ++u) {
-                int n = n0 + 4 * (t0 + u) + rsub;
-                n = n < N ? n : N - 1;
-                const u32x4_t* cr = reinterpret_cast<const u32x4_t*>(codes) + (size_t)n * B;  // 16 B per block
-                R.c[u][0] = cr[bb0];
-                R.c[u][1] = cr[bb1];
-                const uint32_t s0 = scales[(size_t)n * B + bb0], s1 = scales[(size_t)n * B + bb1];
-                R.s[u][0] = has0 ? s0 : 0u;  // fp16 +0: the block contributes nothing
-                R.s[u][1] = has1 ? s1 : 0u;
-            }
-        };
-        auto compute = [&](int t0, const Rows& R) {
-#pragma unroll
-            for (int u = 0; u < kQ4Pair; ++u) {
-                float part_row = 0.0f;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float acc = cst[h];
+            for (int h = 0; h < 2; ++h) {
+                float dot;
+                if (kF16) {
+                    // Nibbles j (bits 4j) of a word hold k = j of its 8 k.  With the fp16 exponent
+                    // of 1024 OR-ed in, mask 0x000F000F keeps k = 0 and 4 as 1024 + q and mask
+                    // 0x00F000F0 keeps k = 1 and 5 as 1024 + 16q, both exact; the word shifted
+                    // by 8 gives k = 2, 6 and 3, 7 the same way: five instructions per 8 codes.
+                    float acc_a = cst[h][0], acc_b = cst[h][1];
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const uint32_t p = ((R.c[u][h][d] >> (4 * e)) & kNibblePairMask) | magic;
-                            acc = kF16 ? dot2_f16(p, xq[h][4 * d + e], acc) : dot2_bf16(p, xq[h][4 * d + e], acc);
-                        }
+                        const uint32_t w = R.c[h][d], w8 = w >> 8;
+                        acc_a = dot2_f16((w & mask_lo) | magic_v, xq[h][4 * d + 0], acc_a);
+                        acc_b = dot2_f16((w & mask_hi) | magic_v, xq[h][4 * d + 1], acc_b);
+                        acc_a = dot2_f16((w8 & mask_lo) | magic_v, xq[h][4 * d + 2], acc_a);
+                        acc_b = dot2_f16((w8 & mask_hi) | magic_v, xq[h][4 * d + 3], acc_b);
                     }
-                    part_row = __builtin_fmaf(f16_bits_to_f32(R.s[u][h]), acc, part_row);
+                    dot = __builtin_fmaf(acc_b, 0.0625f, acc_a);
+                } else {
+                    float acc = cst[h][0];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc = dot2_bf16(((R.c[h][d] >> (4 * e)) & mask_lo) | magic_v, xq[h][4 * d + e], acc);
+                    dot = acc;
                 }
-                // the 16 lanes of a row -> one value, added to this wave's slot for the row
-                const float v = row16_sum(part_row);
-                if (sub == 15) part[wave][4 * (t0 + u) + rsub] += v;
+                part_row = __builtin_fmaf(f16_bits_to_f32(R.s[h]), dot, part_row);
             }
+            // the 16 lanes of a row -> one value, added to this wave's slot for the row
+            const float v = row16_sum(part_row);
+            if (sub == 15) part[wave][4 * t + rsub] += v;
         };
-#pragma unroll 1
-        for (int t0 = 0; t0 < kQ4Steps; t0 += kQ4Pair) {
-            Rows r;
-            load(t0, r);
-            compute(t0, r);
+        // A rolling window: the loads of step t + kQ4Ahead are issued before the math of step t,
+        // so every wave keeps kQ4Ahead steps (8 KiB of codes) in flight while it computes.
+#pragma unroll
+        for (int t = 0; t < kQ4Steps; ++t) {
+            if (t + kQ4Ahead < kQ4Steps) load(t + kQ4Ahead, r[t + kQ4Ahead]);
+            compute(t, r[t]);
+            // keep the window as written: the scheduler would otherwise hoist later steps' loads
+            // past the register budget
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     // the 16 K-slices of each row, added through LDS in a fixed order
