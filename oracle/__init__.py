@@ -12,6 +12,11 @@ passage of the pages it follows:
   section "Step 2: a W4A16 kernel in Triton" (group 128, scale (max-min)/15, code
   round((w-min)/scale), eight codes per int32 along K, K/8 x N packed, K/128 x N bf16 scale and
   minimum, dequant q*s+min, FP64 reference with the same 4-bit weights).
+* ``quantize_g128zp`` / ``dequant_g128zp`` / ``matmul_g128zp`` -- anrans.github.io "Quantization
+  and GEMV", sections "The quantization formulas" (s = (max-min)/15, z = round(-min/s),
+  q = clamp(round(w/s) + z, 0, 15), w_hat = (q - z) s) and "W4A16: dequantizing in registers"
+  (eight codes per word along K, first in the low bits; words [N][K/8]; a scale and a zero point
+  per group of 128, the zero point kept as fp16).
 * ``quantize_q4b32`` / ``dequant_q4b32`` / ``matmul_q4b32`` -- thuongvuho.com "Why My 4-Bit
   CUDA Kernel Wasn't Faster", sections "Why fewer bytes should have helped" and "Loading the
   same bytes differently" (blocks of 32: 16 code bytes + fp16 scale, decode (code-bias)*scale,
@@ -85,7 +90,13 @@ def bind(path) -> ctypes.CDLL:
     L.oracle_matmul_q4b32_f64.argtypes = [P, I, I64, P, P, I64, I64, P]
     L.oracle_matmul_q4b32_f64_at.argtypes = [P, I, I64, P, P, I64, I64, P, P, I64, P]
     L.oracle_matmul_f32w_f64.argtypes = [P, I, I64, P, I64, I64, P]
-    for name in ("oracle_quantize_g128", "oracle_dequant_g128", "oracle_quantize_q4b32",
+    L.oracle_quantize_g128zp.argtypes = [P, I64, I64, P, P, P]
+    L.oracle_dequant_g128zp.argtypes = [P, P, P, I64, I64, I, P]
+    L.oracle_matmul_g128zp_f64.argtypes = [P, I, I64, P, P, P, I64, I64, P]
+    L.oracle_matmul_g128zp_f64_at.argtypes = [P, I, I64, P, P, P, I64, I64, P, P, I64, P]
+    for name in ("oracle_quantize_g128zp", "oracle_dequant_g128zp", "oracle_matmul_g128zp_f64",
+                 "oracle_matmul_g128zp_f64_at",
+                 "oracle_quantize_g128", "oracle_dequant_g128", "oracle_quantize_q4b32",
                  "oracle_dequant_q4b32", "oracle_matmul_g128_f64", "oracle_matmul_g128_f64_at",
                  "oracle_matmul_q4b32_f64", "oracle_matmul_q4b32_f64_at", "oracle_matmul_f32w_f64"):
         getattr(L, name).restype = I
@@ -188,6 +199,64 @@ def matmul_g128_at(x_bits, codes, scales, mins, rows, cols, x_kind: str = "bf16"
     _check(lib().oracle_matmul_g128_f64_at(_ptr(x_bits), 0 if x_kind == "bf16" else 1, M,
                                            _ptr(codes), _ptr(scales), _ptr(mins), N, K, _ptr(rows),
                                            _ptr(cols), len(rows), _ptr(y)), "matmul_g128_at")
+    return y
+
+
+# ---- format G128-ZP: asymmetric, group 128, fp16 scale + fp16 integer zero point ------------
+
+def quantize_g128zp(W: np.ndarray):
+    """W fp32 [N][K] -> (codes uint32 [N][K/8], scales fp16-bits uint16 [N][K/128], zeros same)."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.zeros((N, K // 8), dtype=np.uint32)
+    scales = np.zeros((N, K // 128), dtype=np.uint16)
+    zeros = np.zeros((N, K // 128), dtype=np.uint16)
+    _check(lib().oracle_quantize_g128zp(_ptr(W), N, K, _ptr(codes), _ptr(scales), _ptr(zeros)),
+           "quantize_g128zp")
+    return codes, scales, zeros
+
+
+def dequant_g128zp(codes, scales, zeros, kind: str = "f32") -> np.ndarray:
+    """kind 'f32' (exact (q - z) s), 'bf16' bits, 'f64', 'f16' bits."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    N, K8 = codes.shape
+    K = K8 * 8
+    k_id, dt = {"f32": (0, np.float32), "bf16": (1, np.uint16), "f64": (2, np.float64),
+                "f16": (3, np.uint16)}[kind]
+    out = np.zeros((N, K), dtype=dt)
+    _check(lib().oracle_dequant_g128zp(_ptr(codes), _ptr(scales), _ptr(zeros), N, K, k_id, _ptr(out)),
+           "dequant_g128zp")
+    return out
+
+
+def matmul_g128zp(x_bits: np.ndarray, codes, scales, zeros, x_kind: str = "f16") -> np.ndarray:
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    M, K = x_bits.shape
+    N = codes.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(lib().oracle_matmul_g128zp_f64(_ptr(x_bits), 0 if x_kind == "bf16" else 1, M, _ptr(codes),
+                                          _ptr(scales), _ptr(zeros), N, K, _ptr(y)), "matmul_g128zp")
+    return y
+
+
+def matmul_g128zp_at(x_bits, codes, scales, zeros, rows, cols, x_kind: str = "f16") -> np.ndarray:
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    M, K = x_bits.shape
+    N = codes.shape[0]
+    y = np.zeros(len(rows), dtype=np.float64)
+    _check(lib().oracle_matmul_g128zp_f64_at(_ptr(x_bits), 0 if x_kind == "bf16" else 1, M,
+                                             _ptr(codes), _ptr(scales), _ptr(zeros), N, K, _ptr(rows),
+                                             _ptr(cols), len(rows), _ptr(y)), "matmul_g128zp_at")
     return y
 
 

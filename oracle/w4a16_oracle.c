@@ -18,7 +18,10 @@
  *       nibble of code byte j multiplies x[2j], the high nibble x[2j+1].
  *  [P3] anrans.github.io, "Quantization and GEMV", sections "The quantization formulas" and
  *       "W4A16: dequantizing in registers" -- first element in the low 4 bits of a word,
- *       extraction (word >> 4i) & 0xF, a zero range gives scale 1, FP64 reference sums.
+ *       extraction (word >> 4i) & 0xF, a zero range gives scale 1, FP64 reference sums; and the
+ *       integer-zero-point format: s = (max - min)/15, z = round(-min/s),
+ *       q = clamp(round(w/s) + z, 0, 15), w_hat = (q - z) * s, words [N][K/8] (a row's words
+ *       along K), scales and zero points [N][K/128].
  *
  * Readings where the pages leave a step open (each is listed in the design notes):
  *  - codes are computed from the STORED (rounded) scale and minimum, so encode and decode
@@ -29,7 +32,13 @@
  *  - Q4: bias 8 and scale max|w|/7 rounded to fp16 (a zero block gets scale 1.0);
  *  - Q4 storage is two arrays: codes [N][K/32][16] bytes and scales [N][K/32] fp16;
  *  - the matmul reference is the fp64 sum, in k order, of x times the exactly dequantized
- *    weight q*s + min (or (q - 8)*s), which fp64 holds without rounding at these magnitudes.
+ *    weight q*s + min (or (q - 8)*s), which fp64 holds without rounding at these magnitudes;
+ *  - zero-point format: scale and zero point are stored as fp16 (the page keeps the zero point
+ *    "as fp16" as one of its options); codes use the stored scale and zero point; "round" is the
+ *    page's std::round, half away from zero (roundf), for both z and the codes; z is clamped to
+ *    [-2048, 2048], the integers fp16 holds exactly (only a group whose range is below 1/2048 of
+ *    its distance from zero reaches the clamp); the code is round(w/s) + z as the formula
+ *    writes it (the page's example rounds w/s + z, which differs only at exact ties).
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math -lm
  * Every function returns 0 on success and a nonzero code on a bad argument or a
@@ -302,6 +311,96 @@ static double q4b32_weight_exact(const uint8_t* codes, const uint16_t* scales, i
 }
 
 /* ------------------------------------------------------------------------------------------
+ * Format G128-ZP [P3 "The quantization formulas", "W4A16: dequantizing in registers"]:
+ * asymmetric groups of 128 along k with an fp16 scale and an fp16 integer zero point.
+ *   codes  uint32 [N][K/8]    word (n, r) holds k = 8r..8r+7 of row n, k = 8r lowest
+ *   scales fp16 bits [N][K/128], zeros fp16 bits [N][K/128] (integer values)
+ * For every (n, g):
+ *   lo, hi = min, max of W[n][128g .. 128g+127]              (a zero is taken as +0)
+ *   s = (hi - lo) / 15 in fp32;  s_h = fp16(s), or 1.0 if that is zero
+ *   z = clamp(roundf(-lo / s_h), -2048, 2048)  stored as fp16 (exact)
+ *   q = clamp(roundf(w / s_h) + z, 0, 15)                    (fp32 divide, half away from zero)
+ *   w_hat = (q - z) * s_h, exact in fp32: |q - z| < 2^12 and s_h has 11 significant bits.
+ * ---------------------------------------------------------------------------------------- */
+
+int oracle_quantize_g128zp(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,
+                           uint16_t* zeros)
+{
+    if (!W || !codes || !scales || !zeros || N <= 0 || K <= 0 || K % 128) return ORACLE_BAD_ARG;
+    const int64_t G = K / 128;
+    for (int64_t i = 0; i < N * (K / 8); ++i) codes[i] = 0;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t g = 0; g < G; ++g) {
+            const float* w = W + n * K + g * 128;
+            float lo = w[0], hi = w[0];
+            for (int j = 0; j < 128; ++j) {
+                if (!isfinite(w[j])) return ORACLE_NONFINITE;
+                if (w[j] < lo) lo = w[j];
+                if (w[j] > hi) hi = w[j];
+            }
+            if (lo == 0.0f) lo = 0.0f;
+            if (hi == 0.0f) hi = 0.0f;
+            const float s_zp = (hi - lo) / 15.0f;
+            uint16_t s_h = oracle_f32_to_f16(s_zp);
+            if (s_h == 0 || s_h == 0x8000) s_h = 0x3C00; /* a zero scale becomes 1.0 */
+            if (!isfinite(oracle_f16_to_f64(s_h))) return ORACLE_NONFINITE;
+            const float sf = (float)oracle_f16_to_f64(s_h);
+            float z = roundf(-lo / sf);
+            if (z < -2048.0f) z = -2048.0f;
+            if (z > 2048.0f) z = 2048.0f;
+            if (z == 0.0f) z = 0.0f; /* -0 becomes +0 */
+            const uint16_t z_h = oracle_f32_to_f16(z);
+            scales[n * G + g] = s_h;
+            zeros[n * G + g] = z_h;
+            const float zf = (float)oracle_f16_to_f64(z_h);
+            for (int j = 0; j < 128; ++j) {
+                const float tz = roundf(w[j] / sf) + zf;
+                const int q = tz < 0.0f ? 0 : (tz > 15.0f ? 15 : (int)tz);
+                const int64_t k = g * 128 + j;
+                codes[n * (K / 8) + k / 8] |= (uint32_t)q << (4 * (k % 8));
+            }
+        }
+    return ORACLE_OK;
+}
+
+static int g128zp_code(const uint32_t* codes, int64_t K, int64_t n, int64_t k)
+{
+    uint8_t q[8];
+    oracle_unpack_word(codes[n * (K / 8) + k / 8], q);
+    return q[k & 7];
+}
+
+static double g128zp_weight_exact(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                                  int64_t K, int64_t n, int64_t k)
+{
+    const int64_t gi = n * (K / 128) + k / 128;
+    return ((double)g128zp_code(codes, K, n, k) - oracle_f16_to_f64(zeros[gi])) * oracle_f16_to_f64(scales[gi]);
+}
+
+/* kind 0: fp32 (q - z) * s (exact); kind 1: bf16 of it; kind 2: fp64; kind 3: fp16 of it. */
+int oracle_dequant_g128zp(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                          int64_t K, int kind, void* out)
+{
+    if (!codes || !scales || !zeros || !out || N <= 0 || K <= 0 || K % 128 || kind < 0 || kind > 3)
+        return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t gi = n * (K / 128) + k / 128;
+            const float s = (float)oracle_f16_to_f64(scales[gi]), z = (float)oracle_f16_to_f64(zeros[gi]);
+            const float v = ((float)g128zp_code(codes, K, n, k) - z) * s;
+            if (kind == 0)
+                ((float*)out)[n * K + k] = v;
+            else if (kind == 1)
+                ((uint16_t*)out)[n * K + k] = oracle_f32_to_bf16(v);
+            else if (kind == 2)
+                ((double*)out)[n * K + k] = g128zp_weight_exact(codes, scales, zeros, K, n, k);
+            else
+                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(v);
+        }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------------------------
  * Matmul y = x . W_hat^T in fp64 [P1 Step 2 accuracy reference; P3 FP64 reference sums]:
  *   y[m][n] = sum over k, in k order, of x[m][k] * w_hat_exact[n][k]
  * x is [M][K] of 16-bit activations: x_kind 0 = bf16 bits, 1 = fp16 bits.
@@ -328,6 +427,15 @@ static double q4b32_dot(const uint16_t* x, int x_kind, const uint8_t* codes, con
     double acc = 0.0;
     for (int64_t k = 0; k < K; ++k)
         acc += act_value(x, x_kind, m * K + k) * q4b32_weight_exact(codes, scales, K, n, k);
+    return acc;
+}
+
+static double g128zp_dot(const uint16_t* x, int x_kind, const uint32_t* codes, const uint16_t* scales,
+                         const uint16_t* zeros, int64_t K, int64_t m, int64_t n)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += act_value(x, x_kind, m * K + k) * g128zp_weight_exact(codes, scales, zeros, K, n, k);
     return acc;
 }
 
@@ -378,6 +486,31 @@ int oracle_matmul_q4b32_f64_at(const uint16_t* x, int x_kind, int64_t M, const u
     for (int64_t i = 0; i < count; ++i) {
         if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return ORACLE_BAD_ARG;
         y[i] = q4b32_dot(x, x_kind, codes, scales, K, rows[i], cols[i]);
+    }
+    return ORACLE_OK;
+}
+
+int oracle_matmul_g128zp_f64(const uint16_t* x, int x_kind, int64_t M, const uint32_t* codes,
+                             const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K, double* y)
+{
+    if (!x || !codes || !scales || !zeros || !y || M <= 0 || N <= 0 || K <= 0 || K % 128 ||
+        (x_kind != 0 && x_kind != 1))
+        return ORACLE_BAD_ARG;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) y[m * N + n] = g128zp_dot(x, x_kind, codes, scales, zeros, K, m, n);
+    return ORACLE_OK;
+}
+
+int oracle_matmul_g128zp_f64_at(const uint16_t* x, int x_kind, int64_t M, const uint32_t* codes,
+                                const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
+                                const int64_t* rows, const int64_t* cols, int64_t count, double* y)
+{
+    if (!x || !codes || !scales || !zeros || !rows || !cols || !y || M <= 0 || N <= 0 || K <= 0 ||
+        K % 128 || count < 0 || (x_kind != 0 && x_kind != 1))
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < count; ++i) {
+        if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return ORACLE_BAD_ARG;
+        y[i] = g128zp_dot(x, x_kind, codes, scales, zeros, K, rows[i], cols[i]);
     }
     return ORACLE_OK;
 }

@@ -53,6 +53,23 @@ MUTATIONS = [
     ("Q4 scale divides by 8", "const float s = a / 7.0f;", "const float s = a / 8.0f;"),
     ("Q4 nibbles swapped", "return (k % 2) ? (byte >> 4) : (byte & 0xF);", "return (k % 2) ? (byte & 0xF) : (byte >> 4);"),
     ("Q4 decode bias 7", "const float v = (float)(q - 8) * s;", "const float v = (float)(q - 7) * s;"),
+    ("ZP codes round half to even", "const float tz = roundf(w[j] / sf) + zf;",
+     "const float tz = rintf(w[j] / sf) + zf;"),
+    ("ZP codes round the sum w/s + z", "const float tz = roundf(w[j] / sf) + zf;",
+     "const float tz = roundf(w[j] / sf + zf + 0.25f);"),
+    ("ZP zero point with the wrong sign", "float z = roundf(-lo / sf);", "float z = roundf(lo / sf);"),
+    ("ZP zero point from the maximum", "float z = roundf(-lo / sf);", "float z = roundf(-hi / sf);"),
+    ("ZP zero point rounded half to even", "float z = roundf(-lo / sf);", "float z = rintf(-lo / sf);"),
+    ("ZP zero point not clamped", "if (z < -2048.0f) z = -2048.0f;", ""),
+    ("ZP scale over 16 levels", "const float s_zp = (hi - lo) / 15.0f;", "const float s_zp = (hi - lo) / 16.0f;"),
+    ("ZP words laid out [K/8][N]", "codes[n * (K / 8) + k / 8] |= (uint32_t)q << (4 * (k % 8));",
+     "codes[(k / 8) * N + n] |= (uint32_t)q << (4 * (k % 8));"),
+    ("ZP nibble read from the wrong end", "return q[k & 7];", "return q[7 - (k & 7)];"),
+    ("ZP decode adds the zero point",
+     "return ((double)g128zp_code(codes, K, n, k) - oracle_f16_to_f64(zeros[gi])) * oracle_f16_to_f64(scales[gi]);",
+     "return ((double)g128zp_code(codes, K, n, k) + oracle_f16_to_f64(zeros[gi])) * oracle_f16_to_f64(scales[gi]);"),
+    ("ZP f32 decode ignores the zero point", "const float v = ((float)g128zp_code(codes, K, n, k) - z) * s;",
+     "const float v = ((float)g128zp_code(codes, K, n, k)) * s;"),
 ]
 
 PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction)

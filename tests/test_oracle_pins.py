@@ -490,3 +490,167 @@ def test_q4_matmul_special_cases():
     y_w = oracle.matmul_original(x, W, "f16")
     rel = np.linalg.norm(y - y_w) / np.linalg.norm(y_w)
     assert 0.05 < rel < 0.2                                # symmetric 4-bit, block 32
+
+
+# ---------------------------------------------------------------------------------------------
+# The integer-zero-point format (anrans.github.io "Quantization and GEMV": "The quantization
+# formulas" and "W4A16: dequantizing in registers").
+# ---------------------------------------------------------------------------------------------
+
+def f16_value(bits) -> np.ndarray:
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def half_away(v):
+    """Round half away from zero (the page's std::round), from its definition."""
+    v = np.asarray(v, dtype=np.float64)
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+def _zp_grid_group(rng, s, z, n=128):
+    """A group on the grid (j - z) * s, j = 0..15 all present (s fp16-exact, z an integer)."""
+    j = np.concatenate([np.arange(16), rng.integers(0, 16, size=n - 16)])
+    rng.shuffle(j)
+    vals = [(Fraction(int(k) - z) * Fraction(s)) for k in j]
+    w = np.array([float(v) for v in vals], dtype=np.float32)
+    assert all(Fraction(float(a)) == b for a, b in zip(w, vals)), "grid values must be fp32-exact"
+    return w, j
+
+
+def _zp_codes(codes):
+    """[N][K] codes from [N][K/8] words, nibble j of word r = k = 8r + j (the page's layout)."""
+    N, K8 = codes.shape
+    q = np.zeros((N, K8 * 8), dtype=np.int64)
+    for j in range(8):
+        q[:, j::8] = (codes.astype(np.int64) >> (4 * j)) & 0xF
+    return q
+
+
+def test_zp_layout_is_n_by_k8_and_grid_is_exact():
+    """Words are [N][K/8] with k = 8r + j in nibble j; scales and zero points [N][K/128].  A group
+    on the grid (j - z) s gives codes j, zero point z, scale s, and decodes to W bit for bit."""
+    rng = np.random.default_rng(21)
+    N, K = 3, 256
+    W = np.zeros((N, K), dtype=np.float32)
+    J = np.zeros((N, K), dtype=np.int64)
+    params = {}
+    for n in range(N):
+        for g in range(K // 128):
+            s = 2.0 ** -(5 + n) * (3 if g else 1)
+            z = [0, 5, 15, 8, 2, 11][2 * n + g]
+            w, j = _zp_grid_group(rng, s, z)
+            W[n, 128 * g:128 * (g + 1)] = w
+            J[n, 128 * g:128 * (g + 1)] = j
+            params[(n, g)] = (s, z)
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    assert codes.shape == (N, K // 8) and scales.shape == (N, K // 128) and zeros.shape == (N, K // 128)
+    for n in range(N):
+        for r in range(K // 8):
+            assert int(codes[n, r]) == sum(int(J[n, 8 * r + j]) << (4 * j) for j in range(8))
+    for (n, g), (s, z) in params.items():
+        assert f16_value(scales[n, g]) == s and f16_value(zeros[n, g]) == z
+    np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "f32").view(np.uint32),
+                                  W.view(np.uint32))
+
+
+def test_zp_scale_and_zero_point_definition():
+    """s = fp16((max - min)/15) (numpy's IEEE fp16 rounding), z = round-half-away(-min / s) in
+    fp32 (the page's formulas), on random groups with and without outliers."""
+    W = workloads.weights(64, 1024, outliers=True, seed=22)
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    g = W.reshape(64, 8, 128)
+    lo, hi = g.min(axis=2), g.max(axis=2)
+    s = ((hi - lo) / np.float32(15.0)).astype(np.float32).astype(np.float16)
+    s = np.where(s == 0, np.float16(1.0), s)
+    np.testing.assert_array_equal(scales, s.view(np.uint16))
+    z = half_away((-lo / s.astype(np.float32)).astype(np.float32))
+    np.testing.assert_array_equal(f16_value(zeros), np.clip(z, -2048, 2048))
+
+
+def test_zp_codes_are_nearest_levels_and_bound():
+    """Brute force over the 16 levels (q - z) s in exact fp64: every code is a nearest level, up
+    to the fp32 rounding of w/s at near-ties.  And the error bound that follows from the formulas:
+    the lowest level is within s/2 of the group minimum (z is rounded), the highest within
+    s/2 + 15 |s - s_exact| of the maximum, so |w - w_hat| <= s (1/2 + 15 * 2^-11) everywhere."""
+    W = workloads.weights(48, 2048, outliers=True, seed=23)
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    q = _zp_codes(codes)
+    s = np.repeat(f16_value(scales), 128, axis=1)
+    z = np.repeat(f16_value(zeros), 128, axis=1)
+    levels = (np.arange(16)[None, None, :] - z[..., None]) * s[..., None]
+    dist = np.abs(W.astype(np.float64)[..., None] - levels)
+    mine = np.take_along_axis(dist, q[..., None], axis=-1)[..., 0]
+    assert np.all(mine <= dist.min(axis=-1) + s * 2.0 ** -20), "a code is not the nearest level"
+    err = np.abs(W.astype(np.float64) - oracle.dequant_g128zp(codes, scales, zeros, "f64"))
+    assert np.all(err <= s * (0.5 + 15 * 2.0 ** -11) + 1e-12), float((err / s).max())
+
+
+def test_zp_round_half_away_at_exact_midpoints():
+    """Weights at exact midpoints (i + 1/2) s round away from zero, as the page's std::round does
+    (round-half-to-even would give the even neighbour)."""
+    rng = np.random.default_rng(24)
+    s, z = 2.0 ** -7, 6
+    w, _ = _zp_grid_group(rng, s, z)
+    ties = np.array([(i + 0.5) * s for i in range(-6, 9)], dtype=np.float32)   # inside the range
+    w[16:16 + len(ties)] = ties
+    codes, scales, zeros = oracle.quantize_g128zp(w.reshape(1, 128))
+    assert f16_value(scales[0, 0]) == s and f16_value(zeros[0, 0]) == z
+    q = _zp_codes(codes)[0, 16:16 + len(ties)]
+    np.testing.assert_array_equal(q, half_away(ties.astype(np.float64) / s) + z)
+    assert np.any(q != np.round(ties.astype(np.float64) / s) + z)       # differs from half-to-even
+
+
+def test_zp_degenerate_and_clamped_zero_point():
+    """A constant group gets scale 1 (the page's zero-range rule) and decodes each value to the
+    nearest integer; a group whose range is tiny against its distance from zero reaches the zero
+    point's clamp at -2048, the most negative integer in [-2048, 2048] that fp16 holds exactly."""
+    W = np.zeros((2, 128), dtype=np.float32)
+    W[0, :] = 3.3
+    W[1, :] = 100.0 + np.arange(128, dtype=np.float32) * 1e-4
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    assert f16_value(scales[0, 0]) == 1.0 and f16_value(zeros[0, 0]) == -3.0
+    np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "f64")[0], 3.0)
+    assert f16_value(zeros[1, 0]) == -2048.0 and int(zeros[1, 0]) == 0xE800
+
+
+def test_zp_dequant_f32_is_exact():
+    """(q - z) s has at most 12 + 11 significant bits, so the fp32 decode equals the fp64 one."""
+    W = workloads.weights(16, 512, outliers=True, seed=25)
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "f32").astype(np.float64),
+                                  oracle.dequant_g128zp(codes, scales, zeros, "f64"))
+
+
+def test_zp_matmul_special_cases():
+    W = workloads.weights(64, 512, seed=26)
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    What = oracle.dequant_g128zp(codes, scales, zeros, "f64")
+    x = workloads.activations(3, 512, "f16", seed=4)
+    y = oracle.matmul_g128zp(x, codes, scales, zeros)
+    ref = workloads.bits_to_f32(x, "f16").astype(np.float64) @ What.T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    e = np.zeros((1, 512), dtype=np.uint16)
+    e[0, 130] = 0x3C00                                     # fp16 1.0
+    np.testing.assert_array_equal(oracle.matmul_g128zp(e, codes, scales, zeros)[0], What[:, 130])
+    np.testing.assert_array_equal(oracle.matmul_g128zp_at(x, codes, scales, zeros, [2, 0], [63, 7]),
+                                  [y[2, 63], y[0, 7]])
+    xb = workloads.activations(1, 512, "bf16", seed=4)
+    np.testing.assert_array_equal(oracle.matmul_g128zp(xb, codes, scales, zeros, "bf16")[0],
+                                  workloads.bits_to_f32(xb, "bf16").astype(np.float64)[0] @ What.T)
+    # quantization error of the format: the same grid spacing as the min/scale form (range/15),
+    # so about 10% of the output against the original weights, as for the group-128 format
+    xr = workloads.activations(4, 512, "f16", seed=5)
+    y_q = oracle.matmul_g128zp(xr, codes, scales, zeros)
+    y_w = oracle.matmul_original(xr, W, "f16")
+    rel = np.linalg.norm(y_q - y_w) / np.linalg.norm(y_w)
+    assert 0.07 < rel < 0.13, rel
+
+
+def test_zp_zero_point_rounds_half_away_at_a_tie():
+    """-min / s exactly 2.5 (min = -2.5 s, max = 12.5 s): the zero point is 3 by the page's
+    std::round; round-half-to-even would give 2."""
+    s = 2.0 ** -6
+    w = np.linspace(-2.5 * s, 12.5 * s, 128).astype(np.float32)
+    w[0], w[-1] = -2.5 * s, 12.5 * s
+    codes, scales, zeros = oracle.quantize_g128zp(w.reshape(1, 128))
+    assert f16_value(scales[0, 0]) == s and f16_value(zeros[0, 0]) == 3.0
