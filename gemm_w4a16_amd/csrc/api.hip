@@ -17,10 +17,10 @@ constexpr int64_t kGemvCutoff = 16;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int64_t group_of(w4a16_format_t fmt) { return fmt == W4A16_FMT_G128_ASYM_BF16 ? kGroupG128 : kBlockQ4; }
+int64_t group_of(w4a16_format_t fmt) { return fmt == W4A16_FMT_Q4_B32_SYM_FP16 ? kBlockQ4 : kGroupG128; }
 
 bool valid_format(w4a16_format_t fmt) {
-    return fmt == W4A16_FMT_G128_ASYM_BF16 || fmt == W4A16_FMT_Q4_B32_SYM_FP16;
+    return fmt == W4A16_FMT_G128_ASYM_BF16 || fmt == W4A16_FMT_Q4_B32_SYM_FP16 || fmt == W4A16_FMT_G128_ZP_FP16;
 }
 
 w4a16_status_t check_shape(w4a16_format_t fmt, int64_t N, int64_t K) {
@@ -33,7 +33,7 @@ w4a16_status_t check_shape(w4a16_format_t fmt, int64_t N, int64_t K) {
 // Packed weights: codes and scales always; mins for G128 only (must be NULL for Q4).
 w4a16_status_t check_packed(w4a16_format_t fmt, const void* codes, const void* scales, const void* mins) {
     if (!aligned16(codes) || !aligned16(scales)) return W4A16_ERR_INVALID;
-    if (fmt == W4A16_FMT_G128_ASYM_BF16 && !aligned16(mins)) return W4A16_ERR_INVALID;
+    if (fmt != W4A16_FMT_Q4_B32_SYM_FP16 && !aligned16(mins)) return W4A16_ERR_INVALID;  // minimums or zero points
     if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 && mins != nullptr) return W4A16_ERR_INVALID;
     return W4A16_OK;
 }
@@ -41,7 +41,7 @@ w4a16_status_t check_packed(w4a16_format_t fmt, const void* codes, const void* s
 w4a16_status_t check_act(w4a16_format_t fmt, w4a16_dtype_t act) {
     if (act != W4A16_BF16 && act != W4A16_FP16 && act != W4A16_FP32) return W4A16_ERR_INVALID;
     if (fmt == W4A16_FMT_G128_ASYM_BF16 && act != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
-    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 && act == W4A16_FP32) return W4A16_ERR_UNSUPPORTED;
+    if (fmt != W4A16_FMT_G128_ASYM_BF16 && act == W4A16_FP32) return W4A16_ERR_UNSUPPORTED;
     return W4A16_OK;
 }
 
@@ -82,7 +82,7 @@ w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K, size
     // G128: the GEMM reads scales and minimums as aligned 4-byte words, so an odd element count
     // gets 2 bytes of padding (never written, never used)
     if (fmt == W4A16_FMT_G128_ASYM_BF16) scales = (scales + 3) & ~(size_t)3;
-    const size_t mins = fmt == W4A16_FMT_G128_ASYM_BF16 ? scales : 0;
+    const size_t mins = fmt == W4A16_FMT_Q4_B32_SYM_FP16 ? 0 : scales;  // minimums or zero points
     if (codes_bytes) *codes_bytes = codes;
     if (scales_bytes) *scales_bytes = scales;
     if (mins_bytes) *mins_bytes = mins;
@@ -100,6 +100,10 @@ w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N
     if (fmt == W4A16_FMT_G128_ASYM_BF16)
         return from_hip(w4a16::launch_pack_g128(W, N, K, static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
                                                 static_cast<uint16_t*>(mins), stream));
+    if (fmt == W4A16_FMT_G128_ZP_FP16)
+        return from_hip(w4a16::launch_pack_g128zp(W, N, K, static_cast<uint32_t*>(codes),
+                                                  static_cast<uint16_t*>(scales), static_cast<uint16_t*>(mins),
+                                                  stream));
     return from_hip(w4a16::launch_pack_q4b32(W, N, K, static_cast<uint8_t*>(codes), static_cast<uint16_t*>(scales),
                                              stream));
 }
@@ -118,6 +122,10 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
         return from_hip(w4a16::launch_dequant_g128(static_cast<const uint32_t*>(codes),
                                                    static_cast<const uint16_t*>(scales),
                                                    static_cast<const uint16_t*>(mins), N, K, dt, W_hat, stream));
+    if (fmt == W4A16_FMT_G128_ZP_FP16)
+        return from_hip(w4a16::launch_dequant_g128zp(static_cast<const uint32_t*>(codes),
+                                                     static_cast<const uint16_t*>(scales),
+                                                     static_cast<const uint16_t*>(mins), N, K, dt, W_hat, stream));
     return from_hip(w4a16::launch_dequant_q4b32(static_cast<const uint8_t*>(codes),
                                                 static_cast<const uint16_t*>(scales), N, K, dt, W_hat, stream));
 }
@@ -139,6 +147,11 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
                                                   static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
                                                   stream));
     }
+    if (fmt == W4A16_FMT_G128_ZP_FP16)
+        return from_hip(w4a16::launch_gemv_g128zp(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
+                                                  static_cast<const uint32_t*>(codes), static_cast<const uint16_t*>(scales),
+                                                  static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
+                                                  stream));
     return from_hip(w4a16::launch_gemv_q4b32(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
                                              static_cast<const uint8_t*>(codes), static_cast<const uint16_t*>(scales),
                                              N, K, static_cast<uint16_t*>(y), stream));
@@ -166,7 +179,7 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
                             const void* scales, const void* mins, int64_t N, int64_t K, void* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 || (M > 0 && M <= kGemvCutoff))
+    if (fmt != W4A16_FMT_G128_ASYM_BF16 || (M > 0 && M <= kGemvCutoff))
         return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
     return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
 }

@@ -1,5 +1,10 @@
-// gemv.hip -- the Q4 block-32 GEMV (thuongvuho.com "Why My 4-Bit CUDA Kernel Wasn't Faster":
-// 16 code bytes + one fp16 scale per 32 weights, fp16 activations).
+// gemv.hip -- the row-major 4-bit GEMVs: the Q4 block-32 format (thuongvuho.com "Why My 4-Bit
+// CUDA Kernel Wasn't Faster": 16 code bytes + one fp16 scale per 32 weights, fp16 activations) and
+// the integer-zero-point format (anrans.github.io "Quantization and GEMV": words [N][K/8], an fp16
+// scale and zero point per group of 128, decode (q - z) s).  Their code bytes are laid out alike,
+// 16 bytes per 32 k along each row, so one kernel serves both: the zero-point form takes z * sum(x)
+// off each block's dot product per row, where Q4's constant bias 8 is folded into the per-block
+// constants.
 //
 // It uses the per-block factored form (scale applied once per block after an unscaled dot, as
 // that page and anrans "Quantization and GEMV", exercise 1, do) and the register dequant of
@@ -43,45 +48,59 @@ __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) { return (a 
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------------------------
-// Q4 block-32: 1024 threads = 16 waves = 16 K-slices of 1024 k; 64 rows per block.
+// Row-major 4-bit GEMV: 1024 threads = 16 waves; 64 rows per block.  The 16 waves are kS K-slices
+// of 32 blocks (1024 k) times 16/kS row groups: with K = 16384 all 16 waves split K and each walks
+// the block's 16 row steps; with K = 4096 four waves split K and each walks 4 of the 16 steps.
 // ---------------------------------------------------------------------------------------------
-constexpr int kQ4Waves = 16;
-constexpr int kQ4Rows = 64;                // rows per block
-constexpr int kQ4Steps = kQ4Rows / 4;      // a wave step covers 4 rows
-constexpr int kQ4Ahead = 2;                // row steps whose loads are in flight ahead of the math
+constexpr int kGvWaves = 16;
+constexpr int kGvRows = 64;                // rows per block
+constexpr int kGvSteps = kGvRows / 4;      // a wave step covers 4 rows
+constexpr int kGvAhead = 2;                // row steps whose loads are in flight ahead of the math
 
-// One row step's data for one lane: its two 16-byte code blocks and their two scales.
-struct Q4Step {
+// One row step's data for one lane: its two 16-byte code blocks, their scales and (zero-point
+// format) their zero points.
+struct GvStep {
     u32x4_t c[2];
     uint32_t s[2];
+    uint32_t z[2];
 };
 
-template <bool kF16>
-__global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __restrict__ x,
-                                                          const uint32_t* __restrict__ codes,
-                                                          const uint16_t* __restrict__ scales,
-                                                          uint16_t* __restrict__ y, int N, int K) {
-    __shared__ float part[kQ4Waves][kQ4Rows];
+// kF16: fp16 (else bf16) activations.  kZP: the zero-point format (a scale and an fp16 zero point
+// per group of 4 blocks, decode (q - z) s) -- else Q4 (a scale per block, decode (q - 8) s).  The
+// code bytes of both formats are the same: 16 bytes per 32 k along each row.
+template <bool kF16, bool kZP, int kS>
+__global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __restrict__ x,
+                                                             const uint32_t* __restrict__ codes,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ zeros,
+                                                             uint16_t* __restrict__ y, int N, int K) {
+    constexpr int kR = kGvWaves / kS;         // row groups
+    constexpr int kMySteps = kGvSteps / kR;   // row steps per wave: rg, rg + kR, ...
+    constexpr int kAhead = kGvAhead < kMySteps ? kGvAhead : kMySteps;
+    __shared__ float part[kGvWaves][kGvRows];
     const int lane = lane_id(), wave = wave_id();
     const int sub = lane & 15;   // position along k inside the slice
     const int rsub = lane >> 4;  // which of the 4 rows of a step
+    const int my_slice = wave % kS, rg = wave / kS;
     const int B = K >> 5;        // blocks per row
-    const int n0 = blockIdx.x * kQ4Rows;
-    const bool full = n0 + kQ4Rows <= N;
-    // this block's first row of codes (16 B per block) and of scales
+    const int G = K >> 7;        // groups of 128 per row (zero-point format)
+    const int n0 = blockIdx.x * kGvRows;
+    const bool full = n0 + kGvRows <= N;
+    // this block's first row of codes (16 B per block), of scales and of zero points
     const char* cblk = reinterpret_cast<const char*>(codes) + (size_t)n0 * B * 16;
-    const char* sblk = reinterpret_cast<const char*>(scales) + (size_t)n0 * B * 2;
-    // The masks in SGPRs and the fp16 exponent in a VGPR, opaque to the compiler, so that each
-    // pair is one v_and_or_b32 (VOP3 takes no literal and one scalar operand on gfx9).
+    const char* sblk = reinterpret_cast<const char*>(scales) + (size_t)n0 * (kZP ? G : B) * 2;
+    const char* zblk = kZP ? reinterpret_cast<const char*>(zeros) + (size_t)n0 * G * 2 : nullptr;
+    // The masks in SGPRs and the exponent in a VGPR, opaque to the compiler, so that each pair is
+    // one v_and_or_b32 (VOP3 takes no literal and one scalar operand on gfx9).
     uint32_t mask_lo, mask_hi, magic_v;
     asm volatile("s_mov_b32 %0, %1" : "=s"(mask_lo) : "i"(kNibblePairMask));
     asm volatile("s_mov_b32 %0, %1" : "=s"(mask_hi) : "i"(kNibblePairMaskHi));
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "i"(kF16 ? kF16Magic : kBf16Magic));
 
     // Per-row partial of this wave; each K-slice a wave owns adds into its own LDS slot.
-    for (int t = threadIdx.x & 63; t < kQ4Rows; t += 64) part[wave][t] = 0.0f;
+    for (int t = threadIdx.x & 63; t < kGvRows; t += 64) part[wave][t] = 0.0f;
 
-    for (int slice = wave; slice * 32 < B; slice += kQ4Waves) {
+    for (int slice = my_slice; slice * 32 < B; slice += kS) {
         // this lane's two blocks, 16 apart: each load instruction of a row's 16 lanes then reads
         // 256 contiguous bytes (whole cache lines) rather than every other 16 bytes of 512
         const int b0 = slice * 32 + sub, b1 = b0 + 16;
@@ -92,26 +111,32 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
         const int bb0 = min(b0, B - 1), bb1 = min(b1, B - 1);
         // Loads address a wave-uniform base (this block's first row) plus a 32-bit lane offset;
         // rows past N (last block only) re-read row N - 1, whose result is never stored.
-        auto load = [&](int t, Q4Step& R) {
+        auto load = [&](int t, GvStep& R) {
             uint32_t r = 4 * t + rsub;
             if (!full) r = min(r, (uint32_t)(N - 1 - n0));
             // byte offsets in 32 bits, so that each load is SGPR base + VGPR offset
             const uint32_t o0 = r * (uint32_t)B + (uint32_t)bb0, o1 = r * (uint32_t)B + (uint32_t)bb1;
             R.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o0 * 16u));
             R.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o1 * 16u));
-            const uint32_t s0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + o0 * 2u));
-            const uint32_t s1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + o1 * 2u));
+            const uint32_t p0 = kZP ? r * (uint32_t)G + (uint32_t)(bb0 >> 2) : o0;
+            const uint32_t p1 = kZP ? r * (uint32_t)G + (uint32_t)(bb1 >> 2) : o1;
+            const uint32_t s0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + p0 * 2u));
+            const uint32_t s1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + p1 * 2u));
             R.s[0] = has0 ? s0 : 0u;  // fp16 +0: the block contributes nothing
             R.s[1] = has1 ? s1 : 0u;
+            if constexpr (kZP) {
+                R.z[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zblk + p0 * 2u));
+                R.z[1] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zblk + p1 * 2u));
+            }
         };
         // The first steps' weight loads go out before the activations are waited for.
-        Q4Step r[kQ4Steps];
+        GvStep r[kMySteps];
 #pragma unroll
-        for (int t = 0; t < kQ4Ahead; ++t) load(t, r[t]);
+        for (int i = 0; i < kAhead; ++i) load(rg + kR * i, r[i]);
         // Activations of the two blocks, paired per 8 k, and the per-block constants that remove
-        // the magic offset and the code bias (see the top of this file).
+        // the magic offset (and, for Q4, the code bias; see the top of this file).
         uint32_t xq[2][16];
-        float cst[2][2];
+        float cst[2][2], sx[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool has = h ? has1 : has0;
@@ -138,15 +163,19 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
                     for (int e = 0; e < 4; ++e) sum_a = dot2_bf16(xq[h][4 * d + e], kBf16OnePair, sum_a);
                 }
             }
+            sx[h] = sum_a + sum_b;
             if (kF16) {
-                cst[h][0] = -1032.0f * sum_a;  // sum (1024 + q) x - 1032 sum x = sum (q - 8) x
-                cst[h][1] = -1152.0f * sum_b;  // (sum (1024 + 16q) x - 1152 sum x) / 16 = sum (q - 8) x
+                // Q4: sum (1024 + q) x - 1032 sum x = sum (q - 8) x and
+                //     (sum (1024 + 16q) x - 1152 sum x) / 16 = sum (q - 8) x;
+                // zero point: the offsets 1024 only, z sum x is taken off per row
+                cst[h][0] = (kZP ? -1024.0f : -1032.0f) * sum_a;
+                cst[h][1] = (kZP ? -1024.0f : -1152.0f) * sum_b;
             } else {
-                cst[h][0] = -136.0f * sum_a;   // sum (128 + q) x - 136 sum x = sum (q - 8) x
+                cst[h][0] = (kZP ? -128.0f : -136.0f) * sum_a;  // 128 + q, less 128 (and the bias 8)
                 cst[h][1] = 0.0f;
             }
         }
-        auto compute = [&](int t, const Q4Step& R) {
+        auto compute = [&](int t, const GvStep& R) {
             float part_row = 0.0f;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -175,48 +204,78 @@ __global__ __launch_bounds__(1024) void gemv_q4b32_kernel(const uint16_t* __rest
                             acc = dot2_bf16(((R.c[h][d] >> (4 * e)) & mask_lo) | magic_v, xq[h][4 * d + e], acc);
                     dot = acc;
                 }
+                if constexpr (kZP) dot = __builtin_fmaf(-f16_bits_to_f32(R.z[h]), sx[h], dot);
                 part_row = __builtin_fmaf(f16_bits_to_f32(R.s[h]), dot, part_row);
             }
             // the 16 lanes of a row -> one value, added to this wave's slot for the row
             const float v = row16_sum(part_row);
             if (sub == 15) part[wave][4 * t + rsub] += v;
         };
-        // A rolling window: the loads of step t + kQ4Ahead are issued before the math of step t,
-        // so every wave keeps kQ4Ahead steps (8 KiB of codes) in flight while it computes.
+        // A rolling window: the loads of step i + kAhead are issued before the math of step i.
 #pragma unroll
-        for (int t = 0; t < kQ4Steps; ++t) {
-            if (t + kQ4Ahead < kQ4Steps) load(t + kQ4Ahead, r[t + kQ4Ahead]);
-            compute(t, r[t]);
+        for (int i = 0; i < kMySteps; ++i) {
+            if (i + kAhead < kMySteps) load(rg + kR * (i + kAhead), r[i + kAhead]);
+            compute(rg + kR * i, r[i]);
             // keep the window as written: the scheduler would otherwise hoist later steps' loads
             // past the register budget
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    // the 16 K-slices of each row, added through LDS in a fixed order
+    // the 16 waves' partials of each row (zero where a wave has no part in it), added through LDS
+    // in a fixed order
     __syncthreads();
     const int t = threadIdx.x;
-    if (t < kQ4Rows && n0 + t < N) {
+    if (t < kGvRows && n0 + t < N) {
         float sum = 0.0f;
 #pragma unroll
-        for (int v = 0; v < kQ4Waves; ++v) sum += part[v][t];
+        for (int v = 0; v < kGvWaves; ++v) sum += part[v][t];
         y[n0 + t] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
     }
+}
+
+template <bool kF16, bool kZP>
+void launch_rowmajor(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros,
+                     int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+    const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), block(1024);
+    // K-slices of 1024 k: as many as K has, rounded up to a power of two, at most 16
+    const int64_t slices = (K / 32 + 31) / 32;
+    const int n = (int)N, k = (int)K;
+    if (slices >= 9)
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 16>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+    else if (slices >= 5)
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 8>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+    else if (slices >= 3)
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 4>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+    else if (slices == 2)
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 2>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+    else
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 1>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
 }
 
 }  // namespace
 
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-    const dim3 grid((unsigned)((N + kQ4Rows - 1) / kQ4Rows)), block(1024);
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(codes);
     for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
-        const uint16_t* xm = x + m * K;
-        uint16_t* ym = y + m * N;
         if (act_f16)
-            hipLaunchKernelGGL(gemv_q4b32_kernel<true>, grid, block, 0, stream, xm,
-                               reinterpret_cast<const uint32_t*>(codes), scales, ym, (int)N, (int)K);
+            launch_rowmajor<true, false>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
         else
-            hipLaunchKernelGGL(gemv_q4b32_kernel<false>, grid, block, 0, stream, xm,
-                               reinterpret_cast<const uint32_t*>(codes), scales, ym, (int)N, (int)K);
+            launch_rowmajor<false, false>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_g128zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y,
+                              hipStream_t stream) {
+    for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
+        if (act_f16)
+            launch_rowmajor<true, true>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+        else
+            launch_rowmajor<false, true>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

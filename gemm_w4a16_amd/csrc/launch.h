@@ -24,6 +24,15 @@ hipError_t launch_dequant_g128(const uint32_t* codes, const uint16_t* scales, co
 hipError_t launch_dequant_q4b32(const uint8_t* codes, const uint16_t* scales, int64_t N, int64_t K, int dtype,
                                 void* out, hipStream_t stream);
 
+// Zero-point format (fp16 scale and zero point per group of 128, words [N][K/8]).
+hipError_t launch_pack_g128zp(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,
+                              uint16_t* zeros, hipStream_t stream);
+hipError_t launch_dequant_g128zp(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                                 int64_t K, int dtype, void* out, hipStream_t stream);
+hipError_t launch_gemv_g128zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                              const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y,
+                              hipStream_t stream);
+
 // Small-M G128 path (the skinny MFMA kernel), bf16 activations, M <= kGemvMaxRows.
 constexpr int kGemvMaxRows = 16;
 hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

@@ -8,6 +8,12 @@
 //   same bytes differently"): per (row n, block of 32 k): s = max|w|/7, s_h = fp16(s) (1.0 if
 //   0), q = clamp(rint(w/s_h) + 8, 0, 15), byte j = q[2j] | q[2j+1] << 4.
 //
+// G128-ZP (anrans.github.io "Quantization and GEMV", "The quantization formulas" and "W4A16:
+//   dequantizing in registers"): per (row n, group of 128 k): lo/hi as for G128, s = (hi-lo)/15,
+//   s_h = fp16(s) (1.0 if 0), z = clamp(round(-lo/s_h), -2048, 2048) as fp16, q = clamp(round(w/s_h)
+//   + z, 0, 15) with round half away from zero (the page's std::round), eight codes per word along
+//   k, words stored [N][K/8].
+//
 // The arithmetic is IEEE fp32 with a correctly rounded divide (-fhip-fp32-correctly-rounded-
 // divide-sqrt), rint = round-half-to-even, and no expression here is eligible for FMA
 // contraction, so the codes are bit-identical to any other IEEE implementation of the rule.
@@ -115,6 +121,69 @@ __global__ __launch_bounds__(256) void pack_q4b32_kernel(const float* __restrict
     scales[i] = s_h;
 }
 
+// ---- G128-ZP quantize/pack ----------------------------------------------------------------
+// Four consecutive threads per (row, group of 128): thread p reads k = 32p .. 32p+31 of the
+// group (8 x 16-byte loads), the four combine their min/max with two lane swaps, and each writes
+// its 4 words: the group's 16 words are 64 contiguous bytes of the row.
+__global__ __launch_bounds__(256) void pack_g128zp_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                          uint32_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                          uint16_t* __restrict__ zeros) {
+    const int64_t G = K / 128;
+    const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x >> 2);  // (row, group) index
+    const int p = threadIdx.x & 3;
+    const bool live = i < N * G;
+    const int64_t ii = live ? i : N * G - 1;  // clamped for the loads; dead lanes store nothing
+    const float4* src = reinterpret_cast<const float4*>(W + ii * 128 + p * 32);  // row n = ii / G
+    float w[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float4 v = src[j];
+        w[4 * j] = v.x;
+        w[4 * j + 1] = v.y;
+        w[4 * j + 2] = v.z;
+        w[4 * j + 3] = v.w;
+    }
+    float lo = w[0], hi = w[0];
+#pragma unroll
+    for (int j = 1; j < 32; ++j) {
+        lo = fminf(lo, w[j]);
+        hi = fmaxf(hi, w[j]);
+    }
+    lo = fminf(lo, __shfl_xor(lo, 1));
+    hi = fmaxf(hi, __shfl_xor(hi, 1));
+    lo = fminf(lo, __shfl_xor(lo, 2));
+    hi = fmaxf(hi, __shfl_xor(hi, 2));
+    if (lo == 0.0f) lo = 0.0f;  // -0 -> +0
+    if (hi == 0.0f) hi = 0.0f;
+    const float s = (hi - lo) / 15.0f;
+    uint16_t s_h = f32_to_f16_bits(s);
+    if ((s_h & 0x7FFFu) == 0) s_h = 0x3C00;  // a zero scale becomes 1.0
+    const float sf = f16_bits_to_f32(s_h);
+    float z = __builtin_roundf(-lo / sf);
+    z = fminf(fmaxf(z, -2048.0f), 2048.0f);
+    if (z == 0.0f) z = 0.0f;  // -0 -> +0
+    const uint16_t z_h = f32_to_f16_bits(z);  // exact: an integer of magnitude <= 2048
+    const float zf = f16_bits_to_f32(z_h);
+    if (!live) return;
+    uint32_t out[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float t = __builtin_roundf(w[8 * d + j] / sf) + zf;
+            const uint32_t q = t < 0.0f ? 0u : (t > 15.0f ? 15u : (uint32_t)t);
+            word |= q << (4 * j);
+        }
+        out[d] = word;
+    }
+    *reinterpret_cast<uint4*>(codes + i * 16 + p * 4) = make_uint4(out[0], out[1], out[2], out[3]);
+    if (p == 0) {
+        scales[i] = s_h;
+        zeros[i] = z_h;
+    }
+}
+
 // ---- reference dequant ----------------------------------------------------------------------
 // Eight fp32 values -> out[idx .. idx+7] as bf16 (dtype 0), fp16 (1) or fp32 (2), each rounded
 // to nearest even.
@@ -162,6 +231,37 @@ __global__ __launch_bounds__(256) void dequant_q4b32_kernel(const uint32_t* __re
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = (float)((int)((word >> (4 * j)) & 0xFu) - 8) * s;
     store8(out, i * 8, v, dtype);
+}
+
+// One thread per packed word (n, r): w_hat[n][8r .. 8r+7] = (q - z) * s (exact), then rounded.
+__global__ __launch_bounds__(256) void dequant_g128zp_kernel(const uint32_t* __restrict__ codes,
+                                                             const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ zeros, int64_t N, int64_t K,
+                                                             int dtype, void* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // word index over all rows
+    if (i >= N * (K / 8)) return;
+    const uint32_t word = codes[i];
+    const float s = f16_bits_to_f32(scales[i / 16]), z = f16_bits_to_f32(zeros[i / 16]);  // 16 words per group
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ((float)((word >> (4 * j)) & 0xFu) - z) * s;
+    store8(out, i * 8, v, dtype);
+}
+
+hipError_t launch_pack_g128zp(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,
+                              uint16_t* zeros, hipStream_t stream) {
+    const int64_t groups = N * (K / 128);
+    hipLaunchKernelGGL(pack_g128zp_kernel, dim3((unsigned)((groups + 63) / 64)), dim3(256), 0, stream, W, N, K, codes,
+                       scales, zeros);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_g128zp(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t N,
+                                 int64_t K, int dtype, void* out, hipStream_t stream) {
+    const int64_t blocks = (N * (K / 8) + 255) / 256;
+    hipLaunchKernelGGL(dequant_g128zp_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, zeros, N,
+                       K, dtype, out);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_g128(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,

@@ -67,7 +67,17 @@ typedef enum {
      * scales fp16   [N][K/32]
      * mins   unused (pass NULL)
      * w_hat = (q - 8) * scale (exact in fp32); K % 32 == 0 */
-    W4A16_FMT_Q4_B32_SYM_FP16 = 1
+    W4A16_FMT_Q4_B32_SYM_FP16 = 1,
+    /* anrans.github.io "Quantization and GEMV", "The quantization formulas" and "W4A16:
+     * dequantizing in registers" (an integer zero point per group):
+     * codes  uint32 [N][K/8]  word (n, r) = codes of k = 8r..8r+7 of row n, k = 8r in bits 0..3
+     * scales fp16   [N][K/128]  s = fp16((max - min)/15), 1.0 for a zero range
+     * mins   fp16   [N][K/128]  the zero points z = round(-min/s) (integers, clamped to
+     *                           [-2048, 2048]), passed in the `mins` argument
+     * q = clamp(round(w/s) + z, 0, 15) with round half away from zero (the page's std::round);
+     * w_hat = (q - z) * scale (exact in fp32); K % 128 == 0.  The code bytes of a row are laid
+     * out as those of the Q4 format. */
+    W4A16_FMT_G128_ZP_FP16 = 2
 } w4a16_format_t;
 
 typedef enum {
@@ -110,7 +120,8 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
  * registers, sums x.q per group in fp32 and applies the group scale and minimum once per group
  * (the factored form s * sum(x*q) + min * sum(x) that vidyal.ai's M = 1 kernel uses, section
  * "How the measurements were taken"; P3's one-row-per-warp GEMV, "Writing a GEMV kernel").
- * act: BF16 for G128; FP16 (or BF16) for Q4.  y has the activation dtype, rounded to nearest
+ * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format, which run one pass per
+ * activation row.  y has the activation dtype, rounded to nearest
  * even from fp32.  Row-major x and y; x, y 16-byte aligned. */
 w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                           const void* codes, const void* scales, const void* mins, int64_t N,
@@ -124,7 +135,7 @@ int64_t w4a16_gemv_max_rows(void);
  * two calls that may run at the same time. */
 size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K);
 
-/* Large-M path (G128 only): y [M][N] = x [M][K] . W_hat^T on bf16 MFMA with fp32 accumulation.
+/* Large-M path (G128 only; ERR_UNSUPPORTED for the other formats): y [M][N] = x [M][K] . W_hat^T on bf16 MFMA with fp32 accumulation.
  * Packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai Step 2 builds its
  * B tile) into LDS and fed to v_mfma_f32_16x16x32_bf16.  When a K split is used, partial sums go
  * to `workspace` and are added in a fixed order, so results are bitwise reproducible run to
@@ -137,8 +148,8 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 
 /* Dispatch on M (vidyal.ai "How the measurements were taken": a GEMV kernel for one row, tiles
  * chosen per M; anrans "Exercises": kernels chosen by batch size): M <= w4a16_matmul_gemv_cutoff()
- * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4 always takes the GEMV path and then needs
- * M <= w4a16_gemv_max_rows().  Workspace as for w4a16_gemm (w4a16_gemm_workspace_bytes of the
+ * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4 and the zero-point format always take the
+ * GEMV path and then need M <= w4a16_gemv_max_rows().  Workspace as for w4a16_gemm (w4a16_gemm_workspace_bytes of the
  * same shape is always enough). */
 w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                             const void* codes, const void* scales, const void* mins, int64_t N,

@@ -114,3 +114,26 @@ def test_gemm_validation_and_workspace():
     assert _status(m, Q4, F16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, None, 64, 64, FAKE, None, 0, 0) \
         == w.W4A16_ERR_UNSUPPORTED
     assert 1 <= w.w4a16_matmul_gemv_cutoff() <= w.w4a16_gemv_max_rows()
+
+
+ZP = w.W4A16_FMT_G128_ZP_FP16
+
+
+def test_zero_point_format_sizes_and_validation():
+    # words [N][K/8] plus an fp16 scale and an fp16 zero point per group of 128
+    assert w.w4a16_packed_sizes(ZP, 14336, 4096) == (29_360_128, 917_504, 917_504)
+    assert w.w4a16_packed_sizes(ZP, 1, 128) == (64, 2, 2)
+    for N, K in ((5, 64), (5, 200), (0, 128)):
+        with pytest.raises(w.W4A16Error):
+            w.w4a16_packed_sizes(ZP, N, K)
+    q = w.w4a16_quantize_pack
+    assert _status(q, ZP, FAKE, 4, 128, FAKE, FAKE, None, 0) == w.W4A16_ERR_INVALID        # needs zero points
+    assert _status(q, ZP, FAKE, 4, 96, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID         # K % 128
+    g = w.w4a16_gemv
+    assert _status(g, ZP, F32, FAKE, 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, ZP, F16, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, ZP, F16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) \
+        == w.W4A16_ERR_UNSUPPORTED
+    assert _status(w.w4a16_gemm, ZP, F16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) \
+        == w.W4A16_ERR_UNSUPPORTED
+    assert w.w4a16_gemm_workspace_bytes(ZP, 300, 256, 4096) == 0

@@ -17,7 +17,7 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-G128, Q4 = w.W4A16_FMT_G128_ASYM_BF16, w.W4A16_FMT_Q4_B32_SYM_FP16
+G128, Q4, ZP = w.W4A16_FMT_G128_ASYM_BF16, w.W4A16_FMT_Q4_B32_SYM_FP16, w.W4A16_FMT_G128_ZP_FP16
 BF16, F16, F32 = w.W4A16_BF16, w.W4A16_FP16, w.W4A16_FP32
 TOL = 5e-3
 
@@ -386,4 +386,92 @@ def test_q4_full_pack_and_gemv():
     ref = oracle.matmul_q4b32(x, rc, rs, x_kind="f16")
     err = rel_err(workloads.bits_to_f32(y, "f16"), ref)
     say(f"q4 rel err {err:.3e}")
+    assert err <= TOL
+
+
+# ---------------------------------------------------------------------------------------------
+# The integer-zero-point format: pack and dequant bit-exact, GEMV within the tolerance.
+# ---------------------------------------------------------------------------------------------
+
+ZP_SHAPES = [(1, 128), (3, 384), (65, 1024), (130, 4096), (7, 17408), (200, 640)]
+
+
+@pytest.mark.parametrize("N,K", ZP_SHAPES)
+def test_pack_zp_bit_exact(N, K):
+    say(f"pack_zp N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=N * 5 + K)
+    W[0, :128] = 0.3                      # a degenerate group: scale 1.0, zero point -0
+    if N > 1:
+        W[1, -128:] = 100.0 + np.arange(128, dtype=np.float32) * 1e-4   # zero point clamped
+    W[-1, :128] = np.linspace(-2.5, 12.5, 128, dtype=np.float32) * 2.0 ** -6  # zero-point tie
+    c, s, z = gpu_pack(ZP, W)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    np.testing.assert_array_equal(host(c, np.uint32), rc)
+    np.testing.assert_array_equal(host(s, np.uint16), rs)
+    np.testing.assert_array_equal(host(z, np.uint16), rz)
+
+
+def test_pack_zp_rounding_ties_bit_exact():
+    """Codes at exact midpoints (i + 1/2) s round away from zero, on a grid of scales and zero
+    points (the page's std::round; IEEE division)."""
+    rng = np.random.default_rng(31)
+    rows = []
+    for s_exp in range(-12, 0):
+        for z in (0, 3, 8, 15):
+            s = 2.0 ** s_exp
+            vals = [-z * s, (15 - z) * s] + [(i + 0.5) * s for i in range(-z, 15 - z)]
+            vals += list((rng.integers(0, 31, size=128 - len(vals)) * 0.5 - z) * s)
+            rows.append(np.array(vals, dtype=np.float32))
+    W = np.stack(rows)
+    c, s_, z_ = gpu_pack(ZP, W)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    np.testing.assert_array_equal(host(c, np.uint32), rc)
+    np.testing.assert_array_equal(host(s_, np.uint16), rs)
+    np.testing.assert_array_equal(host(z_, np.uint16), rz)
+
+
+@pytest.mark.parametrize("dtype,kind,np_t", [(F16, "f16", np.uint16), (BF16, "bf16", np.uint16),
+                                             (F32, "f32", np.float32)])
+def test_dequant_zp_bit_exact(dtype, kind, np_t):
+    N, K = 70, 640
+    W = workloads.weights(N, K, outliers=True, seed=41)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    out = torch.empty((N, K), dtype=torch.float32 if dtype == F32 else torch.int16, device="cuda")
+    w.w4a16_dequant(ZP, dev(rc), dev(rs), dev(rz), N, K, dtype, out)
+    np.testing.assert_array_equal(host(out, np_t), oracle.dequant_g128zp(rc, rs, rz, kind))
+
+
+@pytest.mark.parametrize("act", [F16, BF16])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 65, 384), (2, 130, 4096), (3, 257, 2176), (1, 31, 17408),
+                                   (16, 100, 1024), (1, 1000, 640)])
+def test_gemv_zp_parity(act, M, N, K):
+    say(f"gemv_zp act={act} M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=M + N + K)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    kind = "f16" if act == F16 else "bf16"
+    x = workloads.activations(M, K, kind, seed=K)
+    packed = (dev(rc), dev(rs), dev(rz))
+    y = run_matmul(w.w4a16_gemv, ZP, x, packed, N, K, act)
+    ref = oracle.matmul_g128zp(x, rc, rs, rz, x_kind=kind)
+    err = rel_err(workloads.bits_to_f32(y, kind), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    np.testing.assert_array_equal(run_matmul(w.w4a16_matmul, ZP, x, packed, N, K, act), y)
+
+
+def test_zp_decode_shape_full_pack_and_gemv(decode_weights):
+    """The decode shape (K = 4096, N = 14336, with outliers) in the zero-point format, fp16
+    activations: pack bit-exact, GEMV in full against the oracle."""
+    wl = workloads.DECODE
+    say(f"zp decode shape N={wl.N} K={wl.K}")
+    W, _ = decode_weights
+    packed = gpu_pack(ZP, W)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    np.testing.assert_array_equal(host(packed[0], np.uint32), rc)
+    np.testing.assert_array_equal(host(packed[1], np.uint16), rs)
+    np.testing.assert_array_equal(host(packed[2], np.uint16), rz)
+    x = workloads.activations(1, wl.K, "f16", wl.seed_x)
+    y = run_matmul(w.w4a16_matmul, ZP, x, packed, wl.N, wl.K, F16)
+    err = rel_err(workloads.bits_to_f32(y, "f16"), oracle.matmul_g128zp(x, rc, rs, rz))
+    say(f"zp decode rel err {err:.3e}")
     assert err <= TOL

@@ -24,7 +24,8 @@ import numpy as np
 @dataclass(frozen=True)
 class Workload:
     name: str
-    fmt: str          # "g128" (asymmetric group 128, bf16 scale+min) or "q4b32" (symmetric block 32)
+    fmt: str          # "g128" (asymmetric group 128, bf16 scale+min), "q4b32" (symmetric block 32) or
+                      # "g128zp" (group 128, fp16 scale + integer zero point)
     M: int
     N: int
     K: int
@@ -40,6 +41,9 @@ DECODE = Workload("decode_gemv_m1_k4096_n14336", "g128", 1, 14336, 4096, "bf16",
 SWEEP_MS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 Q4 = Workload("q4b32_gemv_m1_k16384_n16384", "q4b32", 1, 16384, 16384, "f16")
 PREFILL = Workload("prefill_gemm_m1024_k4096_n14336", "g128", 1024, 14336, 4096, "bf16", outliers=True)
+# The decode shape in the integer-zero-point format of anrans.github.io "Quantization and GEMV"
+# (its GEMV example uses fp32 activations and notes that real kernels use FP16/BF16).
+ZP_DECODE = Workload("zp_gemv_m1_k4096_n14336", "g128zp", 1, 14336, 4096, "f16", outliers=True)
 
 
 def sweep(M: int) -> Workload:
