@@ -17,6 +17,9 @@ passage of the pages it follows:
   q = clamp(round(w/s) + z, 0, 15), w_hat = (q - z) s) and "W4A16: dequantizing in registers"
   (eight codes per word along K, first in the low bits; words [N][K/8]; a scale and a zero point
   per group of 128, the zero point kept as fp16).
+* ``quantize_w8row`` / ``dequant_w8row`` / ``matmul_w8row`` -- the same page, "Exercises", 1:
+  symmetric per-channel int8, s = max|w|/127 per row, q = clamp(round(w/s), -127, 127), int8
+  [N][K], the row scale applied after the row's sum.
 * ``quantize_q4b32`` / ``dequant_q4b32`` / ``matmul_q4b32`` -- thuongvuho.com "Why My 4-Bit
   CUDA Kernel Wasn't Faster", sections "Why fewer bytes should have helped" and "Loading the
   same bytes differently" (blocks of 32: 16 code bytes + fp16 scale, decode (code-bias)*scale,
@@ -94,7 +97,11 @@ def bind(path) -> ctypes.CDLL:
     L.oracle_dequant_g128zp.argtypes = [P, P, P, I64, I64, I, P]
     L.oracle_matmul_g128zp_f64.argtypes = [P, I, I64, P, P, P, I64, I64, P]
     L.oracle_matmul_g128zp_f64_at.argtypes = [P, I, I64, P, P, P, I64, I64, P, P, I64, P]
-    for name in ("oracle_quantize_g128zp", "oracle_dequant_g128zp", "oracle_matmul_g128zp_f64",
+    L.oracle_quantize_w8row.argtypes = [P, I64, I64, P, P]
+    L.oracle_dequant_w8row.argtypes = [P, P, I64, I64, I, P]
+    L.oracle_matmul_w8row_f64.argtypes = [P, I, I64, P, P, I64, I64, P]
+    for name in ("oracle_quantize_w8row", "oracle_dequant_w8row", "oracle_matmul_w8row_f64",
+                 "oracle_quantize_g128zp", "oracle_dequant_g128zp", "oracle_matmul_g128zp_f64",
                  "oracle_matmul_g128zp_f64_at",
                  "oracle_quantize_g128", "oracle_dequant_g128", "oracle_quantize_q4b32",
                  "oracle_dequant_q4b32", "oracle_matmul_g128_f64", "oracle_matmul_g128_f64_at",
@@ -257,6 +264,42 @@ def matmul_g128zp_at(x_bits, codes, scales, zeros, rows, cols, x_kind: str = "f1
     _check(lib().oracle_matmul_g128zp_f64_at(_ptr(x_bits), 0 if x_kind == "bf16" else 1, M,
                                              _ptr(codes), _ptr(scales), _ptr(zeros), N, K, _ptr(rows),
                                              _ptr(cols), len(rows), _ptr(y)), "matmul_g128zp_at")
+    return y
+
+
+# ---- format W8: symmetric per-row int8, fp32 row scale -----------------------------------
+
+def quantize_w8row(W: np.ndarray):
+    """W fp32 [N][K] -> (codes int8 [N][K], scales fp32 [N])."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    codes = np.zeros((N, K), dtype=np.int8)
+    scales = np.zeros(N, dtype=np.float32)
+    _check(lib().oracle_quantize_w8row(_ptr(W), N, K, _ptr(codes), _ptr(scales)), "quantize_w8row")
+    return codes, scales
+
+
+def dequant_w8row(codes, scales, kind: str = "f32") -> np.ndarray:
+    """kind 'f32' (q*s rounded once), 'bf16' / 'f16' bits of the exact product, 'f64' (exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    N, K = codes.shape
+    k_id, dt = {"f32": (0, np.float32), "bf16": (1, np.uint16), "f64": (2, np.float64),
+                "f16": (3, np.uint16)}[kind]
+    out = np.zeros((N, K), dtype=dt)
+    _check(lib().oracle_dequant_w8row(_ptr(codes), _ptr(scales), N, K, k_id, _ptr(out)), "dequant_w8row")
+    return out
+
+
+def matmul_w8row(x_bits: np.ndarray, codes, scales, x_kind: str = "f16") -> np.ndarray:
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    M, K = x_bits.shape
+    N = codes.shape[0]
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(lib().oracle_matmul_w8row_f64(_ptr(x_bits), 0 if x_kind == "bf16" else 1, M, _ptr(codes),
+                                         _ptr(scales), N, K, _ptr(y)), "matmul_w8row")
     return y
 
 

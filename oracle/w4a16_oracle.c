@@ -21,7 +21,9 @@
  *       extraction (word >> 4i) & 0xF, a zero range gives scale 1, FP64 reference sums; and the
  *       integer-zero-point format: s = (max - min)/15, z = round(-min/s),
  *       q = clamp(round(w/s) + z, 0, 15), w_hat = (q - z) * s, words [N][K/8] (a row's words
- *       along K), scales and zero points [N][K/128].
+ *       along K), scales and zero points [N][K/128]; and, from its first exercise, W8A16:
+ *       per row s = max|w| / 127, q = clamp(round(w/s), -127, 127) stored as int8 [N][K],
+ *       the row's scale applied once after the row's sum.
  *
  * Readings where the pages leave a step open (each is listed in the design notes):
  *  - codes are computed from the STORED (rounded) scale and minimum, so encode and decode
@@ -401,6 +403,55 @@ int oracle_dequant_g128zp(const uint32_t* codes, const uint16_t* scales, const u
 }
 
 /* ------------------------------------------------------------------------------------------
+ * Format W8 [P3 "Exercises", 1]: symmetric per-channel int8.
+ *   codes  int8 [N][K] row-major;  scales fp32 [N], one per row (output channel)
+ * For every row n:  a = max |w|;  s = a / 127 in fp32 (1.0 for an all-zero row);
+ *   q = clamp(roundf(w / s), -127, 127)   (fp32 divide, half away from zero: std::round)
+ *   w_hat = q * s  (exact in fp64; the fp32 product is rounded)
+ * ---------------------------------------------------------------------------------------- */
+
+int oracle_quantize_w8row(const float* W, int64_t N, int64_t K, int8_t* codes, float* scales)
+{
+    if (!W || !codes || !scales || N <= 0 || K <= 0) return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n) {
+        const float* w = W + n * K;
+        float a = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(w[k])) return ORACLE_NONFINITE;
+            if (fabsf(w[k]) > a) a = fabsf(w[k]);
+        }
+        float s8 = a / 127.0f;
+        if (s8 == 0.0f) s8 = 1.0f;
+        scales[n] = s8;
+        for (int64_t k = 0; k < K; ++k) {
+            const float r8 = roundf(w[k] / s8);
+            codes[n * K + k] = (int8_t)(r8 < -127.0f ? -127 : (r8 > 127.0f ? 127 : (int)r8));
+        }
+    }
+    return ORACLE_OK;
+}
+
+/* kind 0: fp32 q * s (one rounding); kind 1: bf16 of the exact product; kind 2: fp64 (exact);
+ * kind 3: fp16 of the exact product.  (The 16-bit kinds round the exact value once.) */
+int oracle_dequant_w8row(const int8_t* codes, const float* scales, int64_t N, int64_t K, int kind, void* out)
+{
+    if (!codes || !scales || !out || N <= 0 || K <= 0 || kind < 0 || kind > 3) return ORACLE_BAD_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const double v = (double)codes[n * K + k] * (double)scales[n];
+            if (kind == 0)
+                ((float*)out)[n * K + k] = (float)codes[n * K + k] * scales[n];
+            else if (kind == 1)
+                ((uint16_t*)out)[n * K + k] = oracle_f32_to_bf16((float)v);
+            else if (kind == 2)
+                ((double*)out)[n * K + k] = v;
+            else
+                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16((float)v);
+        }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------------------------
  * Matmul y = x . W_hat^T in fp64 [P1 Step 2 accuracy reference; P3 FP64 reference sums]:
  *   y[m][n] = sum over k, in k order, of x[m][k] * w_hat_exact[n][k]
  * x is [M][K] of 16-bit activations: x_kind 0 = bf16 bits, 1 = fp16 bits.
@@ -512,6 +563,21 @@ int oracle_matmul_g128zp_f64_at(const uint16_t* x, int x_kind, int64_t M, const 
         if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return ORACLE_BAD_ARG;
         y[i] = g128zp_dot(x, x_kind, codes, scales, zeros, K, rows[i], cols[i]);
     }
+    return ORACLE_OK;
+}
+
+int oracle_matmul_w8row_f64(const uint16_t* x, int x_kind, int64_t M, const int8_t* codes, const float* scales,
+                            int64_t N, int64_t K, double* y)
+{
+    if (!x || !codes || !scales || !y || M <= 0 || N <= 0 || K <= 0 || (x_kind != 0 && x_kind != 1))
+        return ORACLE_BAD_ARG;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += act_value(x, x_kind, m * K + k) * ((double)codes[n * K + k] * (double)scales[n]);
+            y[m * N + n] = acc;
+        }
     return ORACLE_OK;
 }
 

@@ -68,6 +68,15 @@ MUTATIONS = [
     ("ZP decode adds the zero point",
      "return ((double)g128zp_code(codes, K, n, k) - oracle_f16_to_f64(zeros[gi])) * oracle_f16_to_f64(scales[gi]);",
      "return ((double)g128zp_code(codes, K, n, k) + oracle_f16_to_f64(zeros[gi])) * oracle_f16_to_f64(scales[gi]);"),
+    ("W8 scale over 128 levels", "float s8 = a / 127.0f;", "float s8 = a / 128.0f;"),
+    ("W8 codes round half to even", "const float r8 = roundf(w[k] / s8);", "const float r8 = rintf(w[k] / s8);"),
+    ("W8 scale from the maximum, not the largest magnitude", "if (fabsf(w[k]) > a) a = fabsf(w[k]);",
+     "if (w[k] > a) a = w[k];"),
+    ("W8 exact decode drops the scale", "const double v = (double)codes[n * K + k] * (double)scales[n];",
+     "const double v = (double)codes[n * K + k];"),
+    ("W8 matmul reads codes as unsigned",
+     "acc += act_value(x, x_kind, m * K + k) * ((double)codes[n * K + k] * (double)scales[n]);",
+     "acc += act_value(x, x_kind, m * K + k) * ((double)(uint8_t)codes[n * K + k] * (double)scales[n]);"),
     ("ZP f32 decode ignores the zero point", "const float v = ((float)g128zp_code(codes, K, n, k) - z) * s;",
      "const float v = ((float)g128zp_code(codes, K, n, k)) * s;"),
 ]

@@ -654,3 +654,75 @@ def test_zp_zero_point_rounds_half_away_at_a_tie():
     w[0], w[-1] = -2.5 * s, 12.5 * s
     codes, scales, zeros = oracle.quantize_g128zp(w.reshape(1, 128))
     assert f16_value(scales[0, 0]) == s and f16_value(zeros[0, 0]) == 3.0
+
+
+# ---------------------------------------------------------------------------------------------
+# W8A16, symmetric per-channel int8 (anrans.github.io "Quantization and GEMV", "Exercises", 1).
+# ---------------------------------------------------------------------------------------------
+
+def test_w8_grid_row_is_exact():
+    """A row of j * s, j = -127 .. 127, with s a power of two: max|w| / 127 = s exactly, so the
+    codes are j and the decode is W bit for bit."""
+    rng = np.random.default_rng(51)
+    s = 2.0 ** -10
+    j = np.concatenate([np.arange(-127, 128), rng.integers(-127, 128, size=1)])
+    rng.shuffle(j)
+    W = (j * s).astype(np.float32).reshape(1, -1)
+    codes, scales = oracle.quantize_w8row(W)
+    assert scales[0] == np.float32(s)
+    np.testing.assert_array_equal(codes[0].astype(np.int64), j)
+    np.testing.assert_array_equal(oracle.dequant_w8row(codes, scales, "f32"), W)
+
+
+def test_w8_scale_definition_and_nearest_codes():
+    """s = max|w| / 127 (numpy fp32 division) per row; every code is the nearest of the 255
+    levels q s in exact fp64 (up to the fp32 rounding of w/s at near-ties), so |w - w_hat| <= s/2."""
+    W = workloads.weights(24, 1024, outliers=True, seed=52)
+    W[3, :] *= -1.0
+    W[5, 7] = -1.5                                   # the largest magnitude is negative
+    codes, scales = oracle.quantize_w8row(W)
+    a = np.abs(W).max(axis=1)
+    np.testing.assert_array_equal(scales, (a / np.float32(127.0)).astype(np.float32))
+    q = codes.astype(np.int64)
+    s = scales.astype(np.float64)[:, None]
+    levels = np.arange(-127, 128)[None, None, :] * s[..., None]
+    dist = np.abs(W.astype(np.float64)[..., None] - levels)
+    mine = np.take_along_axis(dist, (q + 127)[..., None], axis=-1)[..., 0]
+    assert np.all(mine <= dist.min(axis=-1) + s * 2.0 ** -20)
+    assert np.all(np.abs(W - oracle.dequant_w8row(codes, scales, "f64")) <= s * (0.5 + 2.0 ** -20))
+
+
+def test_w8_ties_zero_row_and_dequant_kinds():
+    s = 2.0 ** -7
+    ties = np.array([(i + 0.5) * s for i in range(-20, 20)], dtype=np.float32)
+    W = np.zeros((2, 128), dtype=np.float32)
+    W[0, :len(ties)] = ties
+    W[0, -1] = 127 * s                               # fixes s exactly
+    codes, scales = oracle.quantize_w8row(W)
+    assert scales[0] == np.float32(s) and scales[1] == 1.0       # an all-zero row gets scale 1
+    np.testing.assert_array_equal(codes[0, :len(ties)].astype(np.float64), half_away(ties.astype(np.float64) / s))
+    np.testing.assert_array_equal(codes[1], 0)
+    W2 = workloads.weights(4, 256, seed=53)
+    c2, s2 = oracle.quantize_w8row(W2)
+    exact = oracle.dequant_w8row(c2, s2, "f64")
+    np.testing.assert_array_equal(exact, c2.astype(np.float64) * s2.astype(np.float64)[:, None])
+    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "f16"),
+                                  exact.astype(np.float32).astype(np.float16).view(np.uint16))
+    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "bf16"), torch_bf16_bits(exact.astype(np.float32)))
+
+
+def test_w8_matmul_special_cases_and_error():
+    W = workloads.weights(64, 4096, seed=54)
+    codes, scales = oracle.quantize_w8row(W)
+    What = oracle.dequant_w8row(codes, scales, "f64")
+    x = workloads.activations(2, 4096, "f16", seed=6)
+    y = oracle.matmul_w8row(x, codes, scales)
+    ref = workloads.bits_to_f32(x, "f16").astype(np.float64) @ What.T
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    e = np.zeros((1, 4096), dtype=np.uint16)
+    e[0, 4095] = 0x3C00
+    np.testing.assert_array_equal(oracle.matmul_w8row(e, codes, scales)[0], What[:, 4095])
+    # closed form: for N(0, sigma) rows of 4096, max|w| ~ 3.9 sigma, so s ~ 0.031 sigma and the
+    # RMS rounding error s / sqrt(12) ~ 0.009 sigma
+    rms = np.sqrt(np.mean((What - W) ** 2)) / 0.02
+    assert 0.0075 <= rms <= 0.0105, rms
