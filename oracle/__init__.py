@@ -280,7 +280,7 @@ def quantize_w8row(W: np.ndarray):
 
 
 def dequant_w8row(codes, scales, kind: str = "f32") -> np.ndarray:
-    """kind 'f32' (q*s rounded once), 'bf16' / 'f16' bits of the exact product, 'f64' (exact)."""
+    """kind 'f32' (q*s rounded once), 'bf16' / 'f16' bits of that fp32 value, 'f64' (exact)."""
     codes = np.ascontiguousarray(codes, dtype=np.int8)
     scales = np.ascontiguousarray(scales, dtype=np.float32)
     N, K = codes.shape

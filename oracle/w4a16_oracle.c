@@ -431,22 +431,24 @@ int oracle_quantize_w8row(const float* W, int64_t N, int64_t K, int8_t* codes, f
     return ORACLE_OK;
 }
 
-/* kind 0: fp32 q * s (one rounding); kind 1: bf16 of the exact product; kind 2: fp64 (exact);
- * kind 3: fp16 of the exact product.  (The 16-bit kinds round the exact value once.) */
+/* kind 0: fp32 q * s (one rounding); kind 1: bf16 of that fp32 value; kind 2: fp64 (exact);
+ * kind 3: fp16 of the fp32 value.  (As for the group-128 format, the reference dequant forms
+ * the fp32 weight first and rounds it to 16 bits.) */
 int oracle_dequant_w8row(const int8_t* codes, const float* scales, int64_t N, int64_t K, int kind, void* out)
 {
     if (!codes || !scales || !out || N <= 0 || K <= 0 || kind < 0 || kind > 3) return ORACLE_BAD_ARG;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t k = 0; k < K; ++k) {
             const double v = (double)codes[n * K + k] * (double)scales[n];
+            const float v32 = (float)codes[n * K + k] * scales[n];
             if (kind == 0)
-                ((float*)out)[n * K + k] = (float)codes[n * K + k] * scales[n];
+                ((float*)out)[n * K + k] = v32;
             else if (kind == 1)
-                ((uint16_t*)out)[n * K + k] = oracle_f32_to_bf16((float)v);
+                ((uint16_t*)out)[n * K + k] = oracle_f32_to_bf16(v32);
             else if (kind == 2)
                 ((double*)out)[n * K + k] = v;
             else
-                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16((float)v);
+                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(v32);
         }
     return ORACLE_OK;
 }

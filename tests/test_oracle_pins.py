@@ -706,9 +706,10 @@ def test_w8_ties_zero_row_and_dequant_kinds():
     c2, s2 = oracle.quantize_w8row(W2)
     exact = oracle.dequant_w8row(c2, s2, "f64")
     np.testing.assert_array_equal(exact, c2.astype(np.float64) * s2.astype(np.float64)[:, None])
-    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "f16"),
-                                  exact.astype(np.float32).astype(np.float16).view(np.uint16))
-    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "bf16"), torch_bf16_bits(exact.astype(np.float32)))
+    f32 = (c2.astype(np.float32) * s2[:, None]).astype(np.float32)       # numpy's IEEE fp32 product
+    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "f32"), f32)
+    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "f16"), f32.astype(np.float16).view(np.uint16))
+    np.testing.assert_array_equal(oracle.dequant_w8row(c2, s2, "bf16"), torch_bf16_bits(f32))
 
 
 def test_w8_matmul_special_cases_and_error():
