@@ -2,7 +2,7 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                    [--only decode|prefill|q4|sweep|zp]
+                    [--only decode|prefill|q4|sweep|zp|w8]
 
 A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one batch of seeded
 synthetic input, with packed weights, activations and output already resident in HBM.  The
@@ -15,8 +15,8 @@ untimed for WARM_SECONDS so that the GPU's clocks have settled, then HIP events 
 stream bracket one replay and give the average duration per launch used for the roofline.
 
 Prints ONE JSON line.  Secondary figures (prefill TFLOPS at M=1024 with a hipBLASLt bf16-weight
-GEMM beside it, the Q4 block-32 GEMV, the decode shape in the zero-point format, the batch sweep)
-go under "extra".
+GEMM beside it, the Q4 block-32 GEMV, the decode shape in the zero-point and W8A16 formats, the batch
+sweep) go under "extra".
 """
 from __future__ import annotations
 
@@ -70,7 +70,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=170)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -225,15 +225,13 @@ def bench_q4(steps, warmup):
     }
 
 
-def bench_zp(steps, warmup, W=None):
-    """The decode shape in the zero-point format (fp16 scale and zero point per 128, fp16 x)."""
-    import gemm_w4a16_amd as w
+def bench_rowfmt(wl, fmt, steps, warmup, W=None):
+    """A decode-shape GEMV in one of the further formats (fp16 activations)."""
     import workloads
-    wl = workloads.ZP_DECODE
     Wn, x = workloads.inputs(wl)
     if W is None:
         W = Wn
-    fmt = w.W4A16_FMT_G128_ZP_FP16
+    import gemm_w4a16_amd as w
     c, s, m = w.w4a16_packed_sizes(fmt, wl.N, wl.K)
     R = copies_for(c + s + m)
     st = Setup(fmt, wl.M, wl.N, wl.K, x, W, R)
@@ -244,6 +242,20 @@ def bench_zp(steps, warmup, W=None):
         "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
         "frac_hbm_peak": st.weight_bytes * steps / ev / 1e9 / HBM_PEAK_GBS,
     }
+
+
+def bench_zp(steps, warmup, W=None):
+    """The decode shape in the zero-point format (fp16 scale and zero point per 128, fp16 x)."""
+    import gemm_w4a16_amd as w
+    import workloads
+    return bench_rowfmt(workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16, steps, warmup, W)
+
+
+def bench_w8(steps, warmup, W=None):
+    """The decode shape as per-row int8 weights (W8A16, fp16 x)."""
+    import gemm_w4a16_amd as w
+    import workloads
+    return bench_rowfmt(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32, steps, warmup, W)
 
 
 def bench_sweep(steps, warmup, W=None):
@@ -318,7 +330,7 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
-        fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp}[args.only]
+        fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp, "w8": bench_w8}[args.only]
         print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
         return
 
@@ -365,6 +377,9 @@ def main():
         torch.cuda.empty_cache()
         log("zero-point format GEMV (decode shape)")
         extra["zp_decode_m1"] = bench_zp(340, 34, W)
+        torch.cuda.empty_cache()
+        log("W8A16 per-row int8 GEMV (decode shape)")
+        extra["w8_decode_m1"] = bench_w8(200, 20, W)
         torch.cuda.empty_cache()
         log("batch sweep")
         extra["sweep"] = bench_sweep(34, 3, W)

@@ -17,7 +17,7 @@ from pathlib import Path
 _LIB_PATH = Path(__file__).resolve().parent / "libw4a16.so"
 
 W4A16_OK, W4A16_ERR_INVALID, W4A16_ERR_UNSUPPORTED, W4A16_ERR_DEVICE = 0, 1, 2, 3
-W4A16_FMT_G128_ASYM_BF16, W4A16_FMT_Q4_B32_SYM_FP16, W4A16_FMT_G128_ZP_FP16 = 0, 1, 2
+W4A16_FMT_G128_ASYM_BF16, W4A16_FMT_Q4_B32_SYM_FP16, W4A16_FMT_G128_ZP_FP16, W4A16_FMT_W8_ROW_FP32 = 0, 1, 2, 3
 W4A16_BF16, W4A16_FP16, W4A16_FP32 = 0, 1, 2
 
 # Every symbol include/w4a16.h declares.
@@ -145,8 +145,8 @@ def w4a16_matmul_gemv_cutoff() -> int:
 # ---- memory plumbing (torch allocations with the ABI's shapes and dtypes) ------------------------
 
 def alloc_packed(fmt: int, N: int, K: int, device="cuda"):
-    """Empty (codes, scales, mins) device tensors for an N x K weight (mins is None for Q4; the
-    zero points for the zero-point format)."""
+    """Empty (codes, scales, mins) device tensors for an N x K weight (mins is None for Q4 and W8;
+    the zero points for the zero-point format)."""
     import torch
     w4a16_packed_sizes(fmt, N, K)  # validates the shape
     if fmt == W4A16_FMT_G128_ASYM_BF16:
@@ -156,6 +156,10 @@ def alloc_packed(fmt: int, N: int, K: int, device="cuda"):
         return (torch.empty((K // 8, N), dtype=torch.int32, device=device),
                 torch.empty(padded, dtype=torch.int16, device=device)[:n].view(K // 128, N),
                 torch.empty(padded, dtype=torch.int16, device=device)[:n].view(K // 128, N))
+    if fmt == W4A16_FMT_W8_ROW_FP32:
+        return (torch.empty((N, K), dtype=torch.int8, device=device),
+                torch.empty(N, dtype=torch.float32, device=device),
+                None)
     if fmt == W4A16_FMT_G128_ZP_FP16:
         return (torch.empty((N, K // 8), dtype=torch.int32, device=device),
                 torch.empty((N, K // 128), dtype=torch.int16, device=device),

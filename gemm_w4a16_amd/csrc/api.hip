@@ -10,6 +10,7 @@ namespace {
 
 constexpr int64_t kGroupG128 = 128;
 constexpr int64_t kBlockQ4 = 32;
+constexpr int64_t kW8RowAlign = 16;  // int8 rows are whole 16-byte loads
 // Largest extents the kernels index with 32-bit ints (element offsets stay 64-bit).
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
 // M at and below which w4a16_matmul uses the GEMV path for G128 (from the batch sweep).
@@ -17,10 +18,16 @@ constexpr int64_t kGemvCutoff = 16;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int64_t group_of(w4a16_format_t fmt) { return fmt == W4A16_FMT_Q4_B32_SYM_FP16 ? kBlockQ4 : kGroupG128; }
+int64_t group_of(w4a16_format_t fmt) {
+    return fmt == W4A16_FMT_Q4_B32_SYM_FP16 ? kBlockQ4 : fmt == W4A16_FMT_W8_ROW_FP32 ? kW8RowAlign : kGroupG128;
+}
+
+// Formats with no third array (Q4, W8): `mins` must be NULL.
+bool has_mins(w4a16_format_t fmt) { return fmt == W4A16_FMT_G128_ASYM_BF16 || fmt == W4A16_FMT_G128_ZP_FP16; }
 
 bool valid_format(w4a16_format_t fmt) {
-    return fmt == W4A16_FMT_G128_ASYM_BF16 || fmt == W4A16_FMT_Q4_B32_SYM_FP16 || fmt == W4A16_FMT_G128_ZP_FP16;
+    return fmt == W4A16_FMT_G128_ASYM_BF16 || fmt == W4A16_FMT_Q4_B32_SYM_FP16 || fmt == W4A16_FMT_G128_ZP_FP16 ||
+           fmt == W4A16_FMT_W8_ROW_FP32;
 }
 
 w4a16_status_t check_shape(w4a16_format_t fmt, int64_t N, int64_t K) {
@@ -30,11 +37,10 @@ w4a16_status_t check_shape(w4a16_format_t fmt, int64_t N, int64_t K) {
     return W4A16_OK;
 }
 
-// Packed weights: codes and scales always; mins for G128 only (must be NULL for Q4).
+// Packed weights: codes and scales always; minimums (G128) or zero points (ZP), NULL otherwise.
 w4a16_status_t check_packed(w4a16_format_t fmt, const void* codes, const void* scales, const void* mins) {
     if (!aligned16(codes) || !aligned16(scales)) return W4A16_ERR_INVALID;
-    if (fmt != W4A16_FMT_Q4_B32_SYM_FP16 && !aligned16(mins)) return W4A16_ERR_INVALID;  // minimums or zero points
-    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16 && mins != nullptr) return W4A16_ERR_INVALID;
+    if (has_mins(fmt) ? !aligned16(mins) : mins != nullptr) return W4A16_ERR_INVALID;
     return W4A16_OK;
 }
 
@@ -42,6 +48,7 @@ w4a16_status_t check_act(w4a16_format_t fmt, w4a16_dtype_t act) {
     if (act != W4A16_BF16 && act != W4A16_FP16 && act != W4A16_FP32) return W4A16_ERR_INVALID;
     if (fmt == W4A16_FMT_G128_ASYM_BF16 && act != W4A16_BF16) return W4A16_ERR_UNSUPPORTED;
     if (fmt != W4A16_FMT_G128_ASYM_BF16 && act == W4A16_FP32) return W4A16_ERR_UNSUPPORTED;
+    if (fmt == W4A16_FMT_W8_ROW_FP32 && act != W4A16_FP16) return W4A16_ERR_UNSUPPORTED;
     return W4A16_OK;
 }
 
@@ -77,12 +84,18 @@ w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K, size
                                   size_t* scales_bytes, size_t* mins_bytes) {
     const w4a16_status_t st = check_shape(fmt, N, K);
     if (st != W4A16_OK) return st;
-    const size_t codes = (size_t)N * (size_t)K / 2;  // 4 bits per weight in both formats
+    if (fmt == W4A16_FMT_W8_ROW_FP32) {  // one byte per weight and an fp32 scale per row
+        if (codes_bytes) *codes_bytes = (size_t)N * (size_t)K;
+        if (scales_bytes) *scales_bytes = (size_t)N * 4;
+        if (mins_bytes) *mins_bytes = 0;
+        return W4A16_OK;
+    }
+    const size_t codes = (size_t)N * (size_t)K / 2;  // 4 bits per weight in the other formats
     size_t scales = (size_t)N * (size_t)(K / group_of(fmt)) * 2;
     // G128: the GEMM reads scales and minimums as aligned 4-byte words, so an odd element count
     // gets 2 bytes of padding (never written, never used)
     if (fmt == W4A16_FMT_G128_ASYM_BF16) scales = (scales + 3) & ~(size_t)3;
-    const size_t mins = fmt == W4A16_FMT_Q4_B32_SYM_FP16 ? 0 : scales;  // minimums or zero points
+    const size_t mins = has_mins(fmt) ? scales : 0;  // minimums or zero points
     if (codes_bytes) *codes_bytes = codes;
     if (scales_bytes) *scales_bytes = scales;
     if (mins_bytes) *mins_bytes = mins;
@@ -100,6 +113,9 @@ w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N
     if (fmt == W4A16_FMT_G128_ASYM_BF16)
         return from_hip(w4a16::launch_pack_g128(W, N, K, static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
                                                 static_cast<uint16_t*>(mins), stream));
+    if (fmt == W4A16_FMT_W8_ROW_FP32)
+        return from_hip(w4a16::launch_pack_w8row(W, N, K, static_cast<int8_t*>(codes), static_cast<float*>(scales),
+                                                 stream));
     if (fmt == W4A16_FMT_G128_ZP_FP16)
         return from_hip(w4a16::launch_pack_g128zp(W, N, K, static_cast<uint32_t*>(codes),
                                                   static_cast<uint16_t*>(scales), static_cast<uint16_t*>(mins),
@@ -122,6 +138,9 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
         return from_hip(w4a16::launch_dequant_g128(static_cast<const uint32_t*>(codes),
                                                    static_cast<const uint16_t*>(scales),
                                                    static_cast<const uint16_t*>(mins), N, K, dt, W_hat, stream));
+    if (fmt == W4A16_FMT_W8_ROW_FP32)
+        return from_hip(w4a16::launch_dequant_w8row(static_cast<const int8_t*>(codes), static_cast<const float*>(scales),
+                                                    N, K, dt, W_hat, stream));
     if (fmt == W4A16_FMT_G128_ZP_FP16)
         return from_hip(w4a16::launch_dequant_g128zp(static_cast<const uint32_t*>(codes),
                                                      static_cast<const uint16_t*>(scales),
@@ -147,6 +166,10 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
                                                   static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
                                                   stream));
     }
+    if (fmt == W4A16_FMT_W8_ROW_FP32)
+        return from_hip(w4a16::launch_gemv_w8row(static_cast<const uint16_t*>(x), M, static_cast<const int8_t*>(codes),
+                                                 static_cast<const float*>(scales), N, K, static_cast<uint16_t*>(y),
+                                                 stream));
     if (fmt == W4A16_FMT_G128_ZP_FP16)
         return from_hip(w4a16::launch_gemv_g128zp(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
                                                   static_cast<const uint32_t*>(codes), static_cast<const uint16_t*>(scales),

@@ -65,15 +65,23 @@ struct GvStep {
     uint32_t z[2];
 };
 
-// kF16: fp16 (else bf16) activations.  kZP: the zero-point format (a scale and an fp16 zero point
-// per group of 4 blocks, decode (q - z) s) -- else Q4 (a scale per block, decode (q - 8) s).  The
-// code bytes of both formats are the same: 16 bytes per 32 k along each row.
-template <bool kF16, bool kZP, int kS>
+// Formats of the row-major kernel.  Q4 and ZP share their code bytes (16 bytes per 32 k along
+// each row); W8 has 16 bytes per 16 k (signed bytes) and one scale per row.
+enum RowFmt { kRowQ4 = 0, kRowZP = 1, kRowW8 = 2 };
+
+// kF16: fp16 (else bf16) activations.  kFmt: kRowQ4 (a scale per block, decode (q - 8) s),
+// kRowZP (a scale and an fp16 zero point per group of 4 blocks, decode (q - z) s) or kRowW8 (int8
+// codes, one fp32 scale per row applied to the row's sum; fp16 activations only).
+template <bool kF16, int kFmt, int kS>
 __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __restrict__ x,
                                                              const uint32_t* __restrict__ codes,
                                                              const uint16_t* __restrict__ scales,
                                                              const uint16_t* __restrict__ zeros,
                                                              uint16_t* __restrict__ y, int N, int K) {
+    constexpr bool kZP = kFmt == kRowZP, kW8 = kFmt == kRowW8;
+    static_assert(!kW8 || kF16, "int8 codes need fp16 activations (1024 + u with u < 256)");
+    constexpr int kBlockK = kW8 ? 16 : 32;    // k per 16-byte block of codes
+    constexpr int kXq = kBlockK / 2;          // paired activation dwords per block
     constexpr int kR = kGvWaves / kS;         // row groups
     constexpr int kMySteps = kGvSteps / kR;   // row steps per wave: rg, rg + kR, ...
     constexpr int kAhead = kGvAhead < kMySteps ? kGvAhead : kMySteps;
@@ -82,18 +90,18 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
     const int sub = lane & 15;   // position along k inside the slice
     const int rsub = lane >> 4;  // which of the 4 rows of a step
     const int my_slice = wave % kS, rg = wave / kS;
-    const int B = K >> 5;        // blocks per row
+    const int B = K / kBlockK;   // blocks per row
     const int G = K >> 7;        // groups of 128 per row (zero-point format)
     const int n0 = blockIdx.x * kGvRows;
     const bool full = n0 + kGvRows <= N;
     // this block's first row of codes (16 B per block), of scales and of zero points
     const char* cblk = reinterpret_cast<const char*>(codes) + (size_t)n0 * B * 16;
-    const char* sblk = reinterpret_cast<const char*>(scales) + (size_t)n0 * (kZP ? G : B) * 2;
+    const char* sblk = reinterpret_cast<const char*>(scales) + (size_t)n0 * (kZP ? G : B) * 2;  // (not W8)
     const char* zblk = kZP ? reinterpret_cast<const char*>(zeros) + (size_t)n0 * G * 2 : nullptr;
     // The masks in SGPRs and the exponent in a VGPR, opaque to the compiler, so that each pair is
     // one v_and_or_b32 (VOP3 takes no literal and one scalar operand on gfx9).
     uint32_t mask_lo, mask_hi, magic_v;
-    asm volatile("s_mov_b32 %0, %1" : "=s"(mask_lo) : "i"(kNibblePairMask));
+    asm volatile("s_mov_b32 %0, %1" : "=s"(mask_lo) : "i"(kW8 ? 0x00FF00FFu : kNibblePairMask));
     asm volatile("s_mov_b32 %0, %1" : "=s"(mask_hi) : "i"(kNibblePairMaskHi));
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "i"(kF16 ? kF16Magic : kBf16Magic));
 
@@ -118,6 +126,7 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
             const uint32_t o0 = r * (uint32_t)B + (uint32_t)bb0, o1 = r * (uint32_t)B + (uint32_t)bb1;
             R.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o0 * 16u));
             R.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o1 * 16u));
+            if constexpr (kW8) return;  // the row's scale is applied to its total
             const uint32_t p0 = kZP ? r * (uint32_t)G + (uint32_t)(bb0 >> 2) : o0;
             const uint32_t p1 = kZP ? r * (uint32_t)G + (uint32_t)(bb1 >> 2) : o1;
             const uint32_t s0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + p0 * 2u));
@@ -135,13 +144,31 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
         for (int i = 0; i < kAhead; ++i) load(rg + kR * i, r[i]);
         // Activations of the two blocks, paired per 8 k, and the per-block constants that remove
         // the magic offset (and, for Q4, the code bias; see the top of this file).
-        uint32_t xq[2][16];
+        uint32_t xq[2][kXq];
         float cst[2][2], sx[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool has = h ? has1 : has0;
-            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * 32);
+            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * kBlockK);
             float sum_a = 0.0f, sum_b = 0.0f;
+            if constexpr (kW8) {
+                // per 4 k of a code dword: (x0, x2) and (x1, x3), which meet the byte pairs below
+#pragma unroll
+                for (int d = 0; d < 2; ++d) {
+                    const u32x4_t xl = xr[d];
+                    const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
+                    xq[h][4 * d + 0] = pack_lo(xv.x, xv.y);
+                    xq[h][4 * d + 1] = pack_hi(xv.x, xv.y);
+                    xq[h][4 * d + 2] = pack_lo(xv.z, xv.w);
+                    xq[h][4 * d + 3] = pack_hi(xv.z, xv.w);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum_a = dot2_f16(xq[h][4 * d + e], kF16OnePair, sum_a);
+                }
+                sx[h] = sum_a;
+                cst[h][0] = -1152.0f * sum_a;  // sum (1024 + 128 + q) x - 1152 sum x = sum q x
+                cst[h][1] = 0.0f;
+                continue;
+            }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 const u32x4_t xl = xr[d];
@@ -180,6 +207,20 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 float dot;
+                if constexpr (kW8) {
+                    // Signed bytes with the top bit flipped are u = q + 128 in 0..255; OR-ed into
+                    // the fp16 exponent of 1024 they are 1024 + u, exact: bytes 0 and 2 of a
+                    // dword with mask 0x00FF00FF, bytes 1 and 3 after a shift by 8.
+                    float acc = cst[h][0];
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t u = R.c[h][d] ^ 0x80808080u;
+                        acc = dot2_f16((u & mask_lo) | magic_v, xq[h][2 * d + 0], acc);
+                        acc = dot2_f16(((u >> 8) & mask_lo) | magic_v, xq[h][2 * d + 1], acc);
+                    }
+                    part_row += acc;
+                    continue;
+                }
                 if (kF16) {
                     // Nibbles j (bits 4j) of a word hold k = j of its 8 k.  With the fp16 exponent
                     // of 1024 OR-ed in, mask 0x000F000F keeps k = 0 and 4 as 1024 + q and mask
@@ -229,27 +270,28 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
         float sum = 0.0f;
 #pragma unroll
         for (int v = 0; v < kGvWaves; ++v) sum += part[v][t];
+        if constexpr (kW8) sum *= reinterpret_cast<const float*>(scales)[n0 + t];
         y[n0 + t] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
     }
 }
 
-template <bool kF16, bool kZP>
+template <bool kF16, int kFmt>
 void launch_rowmajor(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros,
                      int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), block(1024);
-    // K-slices of 1024 k: as many as K has, rounded up to a power of two, at most 16
-    const int64_t slices = (K / 32 + 31) / 32;
+    // K-slices of 32 blocks: as many as K has, rounded up to a power of two, at most 16
+    const int64_t slices = (K / (kFmt == kRowW8 ? 16 : 32) + 31) / 32;
     const int n = (int)N, k = (int)K;
     if (slices >= 9)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 16>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 16>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else if (slices >= 5)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 8>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 8>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else if (slices >= 3)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 4>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 4>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else if (slices == 2)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 2>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 2>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kZP, 1>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 1>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
 }
 
 }  // namespace
@@ -259,9 +301,9 @@ hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const u
     const uint32_t* words = reinterpret_cast<const uint32_t*>(codes);
     for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
         if (act_f16)
-            launch_rowmajor<true, false>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
+            launch_rowmajor<true, kRowQ4>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
         else
-            launch_rowmajor<false, false>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
+            launch_rowmajor<false, kRowQ4>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -273,9 +315,20 @@ hipError_t launch_gemv_g128zp(const uint16_t* x, int64_t M, bool act_f16, const 
                               hipStream_t stream) {
     for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
         if (act_f16)
-            launch_rowmajor<true, true>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+            launch_rowmajor<true, kRowZP>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
         else
-            launch_rowmajor<false, true>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+            launch_rowmajor<false, kRowZP>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_gemv_w8row(const uint16_t* x, int64_t M, const int8_t* codes, const float* scales, int64_t N,
+                             int64_t K, uint16_t* y, hipStream_t stream) {
+    for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
+        launch_rowmajor<true, kRowW8>(x + m * K, reinterpret_cast<const uint32_t*>(codes),
+                                      reinterpret_cast<const uint16_t*>(scales), nullptr, N, K, y + m * N, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -33,6 +33,13 @@ hipError_t launch_gemv_g128zp(const uint16_t* x, int64_t M, bool act_f16, const 
                               const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y,
                               hipStream_t stream);
 
+// W8 format (int8 [N][K], fp32 scale per row).
+hipError_t launch_pack_w8row(const float* W, int64_t N, int64_t K, int8_t* codes, float* scales, hipStream_t stream);
+hipError_t launch_dequant_w8row(const int8_t* codes, const float* scales, int64_t N, int64_t K, int dtype, void* out,
+                                hipStream_t stream);
+hipError_t launch_gemv_w8row(const uint16_t* x, int64_t M, const int8_t* codes, const float* scales, int64_t N,
+                             int64_t K, uint16_t* y, hipStream_t stream);
+
 // Small-M G128 path (the skinny MFMA kernel), bf16 activations, M <= kGemvMaxRows.
 constexpr int kGemvMaxRows = 16;
 hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

@@ -13,6 +13,9 @@
 //   s_h = fp16(s) (1.0 if 0), z = clamp(round(-lo/s_h), -2048, 2048) as fp16, q = clamp(round(w/s_h)
 //   + z, 0, 15) with round half away from zero (the page's std::round), eight codes per word along
 //   k, words stored [N][K/8].
+// W8 (anrans.github.io "Quantization and GEMV", "Exercises", 1): per row n: s = max|w|/127 in
+//   fp32 (1.0 for an all-zero row), q = clamp(round(w/s), -127, 127) as int8 [N][K], round half
+//   away from zero.
 //
 // The arithmetic is IEEE fp32 with a correctly rounded divide (-fhip-fp32-correctly-rounded-
 // divide-sqrt), rint = round-half-to-even, and no expression here is eligible for FMA
@@ -184,6 +187,42 @@ __global__ __launch_bounds__(256) void pack_g128zp_kernel(const float* __restric
     }
 }
 
+// ---- W8 quantize/pack -------------------------------------------------------------------------
+// One 256-thread block per row: a max-|w| reduction over the row (16-byte loads, lane swaps, LDS),
+// then each thread writes 4 codes at a time.  K % 16 == 0.
+__global__ __launch_bounds__(256) void pack_w8row_kernel(const float* __restrict__ W, int64_t N, int64_t K,
+                                                         int8_t* __restrict__ codes, float* __restrict__ scales) {
+    __shared__ float wmax[4];
+    const int64_t n = blockIdx.x;
+    const float4* row = reinterpret_cast<const float4*>(W + n * K);
+    const int64_t K4 = K / 4;
+    float a = 0.0f;
+    for (int64_t i = threadIdx.x; i < K4; i += 256) {
+        const float4 v = row[i];
+        a = fmaxf(a, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+    __syncthreads();
+    a = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    float s = a / 127.0f;
+    if (s == 0.0f) s = 1.0f;
+    uint32_t* out = reinterpret_cast<uint32_t*>(codes + n * K);
+    for (int64_t i = threadIdx.x; i < K4; i += 256) {
+        const float4 v = row[i];
+        const float w4[4] = {v.x, v.y, v.z, v.w};
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float r = fminf(fmaxf(__builtin_roundf(w4[j] / s), -127.0f), 127.0f);
+            word |= ((uint32_t)(int32_t)r & 0xFFu) << (8 * j);
+        }
+        out[i] = word;
+    }
+    if (threadIdx.x == 0) scales[n] = s;
+}
+
 // ---- reference dequant ----------------------------------------------------------------------
 // Eight fp32 values -> out[idx .. idx+7] as bf16 (dtype 0), fp16 (1) or fp32 (2), each rounded
 // to nearest even.
@@ -246,6 +285,33 @@ __global__ __launch_bounds__(256) void dequant_g128zp_kernel(const uint32_t* __r
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = ((float)((word >> (4 * j)) & 0xFu) - z) * s;
     store8(out, i * 8, v, dtype);
+}
+
+// One thread per 8 codes of a row: w_hat = q * s in fp32 (one rounding), then rounded to 16 bits.
+__global__ __launch_bounds__(256) void dequant_w8row_kernel(const int8_t* __restrict__ codes,
+                                                            const float* __restrict__ scales, int64_t N, int64_t K,
+                                                            int dtype, void* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index of 8 codes over all rows
+    if (i >= N * (K / 8)) return;
+    const uint2 c = reinterpret_cast<const uint2*>(codes)[i];
+    const float s = scales[i / (K / 8)];
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (float)(int8_t)(((j < 4 ? c.x : c.y) >> (8 * (j & 3))) & 0xFFu) * s;
+    store8(out, i * 8, v, dtype);
+}
+
+hipError_t launch_pack_w8row(const float* W, int64_t N, int64_t K, int8_t* codes, float* scales, hipStream_t stream) {
+    hipLaunchKernelGGL(pack_w8row_kernel, dim3((unsigned)N), dim3(256), 0, stream, W, N, K, codes, scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_w8row(const int8_t* codes, const float* scales, int64_t N, int64_t K, int dtype, void* out,
+                                hipStream_t stream) {
+    const int64_t blocks = (N * (K / 8) + 255) / 256;
+    hipLaunchKernelGGL(dequant_w8row_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales, N, K, dtype,
+                       out);
+    return hipGetLastError();
 }
 
 hipError_t launch_pack_g128zp(const float* W, int64_t N, int64_t K, uint32_t* codes, uint16_t* scales,

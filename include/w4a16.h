@@ -77,7 +77,13 @@ typedef enum {
      * q = clamp(round(w/s) + z, 0, 15) with round half away from zero (the page's std::round);
      * w_hat = (q - z) * scale (exact in fp32); K % 128 == 0.  The code bytes of a row are laid
      * out as those of the Q4 format. */
-    W4A16_FMT_G128_ZP_FP16 = 2
+    W4A16_FMT_G128_ZP_FP16 = 2,
+    /* anrans.github.io "Quantization and GEMV", "Exercises", 1 (W8A16, symmetric per channel):
+     * codes  int8   [N][K]  q = clamp(round(w/s), -127, 127), round half away from zero
+     * scales fp32   [N]     s = max|w| / 127 per row (1.0 for an all-zero row)
+     * mins   unused (pass NULL)
+     * w_hat = q * s; K % 16 == 0; fp16 activations only.  Packed sizes: N*K and 4*N bytes. */
+    W4A16_FMT_W8_ROW_FP32 = 3
 } w4a16_format_t;
 
 typedef enum {
@@ -90,12 +96,12 @@ typedef enum {
 const char* w4a16_status_string(w4a16_status_t status);
 
 /* Bytes to allocate for the three packed arrays of an N x K weight in `fmt` (mins is 0 for the
- * Q4 format).  For G128 the scale and minimum sizes are the arrays' sizes rounded up to a
+ * Q4 and W8 formats).  For G128 the scale and minimum sizes are the arrays' sizes rounded up to a
  * multiple of 4 bytes: the GEMM reads them as aligned 4-byte words, so when (K/128)*N is odd
  * the last word covers 2 bytes past the last element (read, never written, value unused).
  * Buffers passed to the matmul entry points must have at least these sizes.
  * Pure host arithmetic; any output pointer may be NULL.  ERR_INVALID if N, K <= 0 or K is not a
- * multiple of the format's group (128 or 32). */
+ * multiple of the format's group (128, 32, or 16 for W8). */
 w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K,
                                   size_t* codes_bytes, size_t* scales_bytes, size_t* mins_bytes);
 
@@ -120,8 +126,8 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
  * registers, sums x.q per group in fp32 and applies the group scale and minimum once per group
  * (the factored form s * sum(x*q) + min * sum(x) that vidyal.ai's M = 1 kernel uses, section
  * "How the measurements were taken"; P3's one-row-per-warp GEMV, "Writing a GEMV kernel").
- * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format, which run one pass per
- * activation row.  y has the activation dtype, rounded to nearest
+ * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format; FP16 for W8.  Q4, the
+ * zero-point format and W8 run one pass per activation row.  y has the activation dtype, rounded to nearest
  * even from fp32.  Row-major x and y; x, y 16-byte aligned. */
 w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                           const void* codes, const void* scales, const void* mins, int64_t N,
@@ -148,7 +154,7 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 
 /* Dispatch on M (vidyal.ai "How the measurements were taken": a GEMV kernel for one row, tiles
  * chosen per M; anrans "Exercises": kernels chosen by batch size): M <= w4a16_matmul_gemv_cutoff()
- * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4 and the zero-point format always take the
+ * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4, the zero-point format and W8 always take the
  * GEMV path and then need M <= w4a16_gemv_max_rows().  Workspace as for w4a16_gemm (w4a16_gemm_workspace_bytes of the
  * same shape is always enough). */
 w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,

@@ -137,3 +137,22 @@ def test_zero_point_format_sizes_and_validation():
     assert _status(w.w4a16_gemm, ZP, F16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) \
         == w.W4A16_ERR_UNSUPPORTED
     assert w.w4a16_gemm_workspace_bytes(ZP, 300, 256, 4096) == 0
+
+
+W8 = w.W4A16_FMT_W8_ROW_FP32
+
+
+def test_w8_format_sizes_and_validation():
+    # one byte per weight and an fp32 scale per row
+    assert w.w4a16_packed_sizes(W8, 14336, 4096) == (58_720_256, 57_344, 0)
+    assert w.w4a16_packed_sizes(W8, 3, 16) == (48, 12, 0)
+    for N, K in ((5, 8), (5, 40), (0, 16)):
+        with pytest.raises(w.W4A16Error):
+            w.w4a16_packed_sizes(W8, N, K)
+    q = w.w4a16_quantize_pack
+    assert _status(q, W8, FAKE, 4, 32, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID         # takes no mins
+    g = w.w4a16_gemv
+    assert _status(g, W8, BF16, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, W8, F32, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(w.w4a16_gemm, W8, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) \
+        == w.W4A16_ERR_UNSUPPORTED

@@ -475,3 +475,63 @@ def test_zp_decode_shape_full_pack_and_gemv(decode_weights):
     err = rel_err(workloads.bits_to_f32(y, "f16"), oracle.matmul_g128zp(x, rc, rs, rz))
     say(f"zp decode rel err {err:.3e}")
     assert err <= TOL
+
+
+# ---------------------------------------------------------------------------------------------
+# W8A16 per-row int8: pack and dequant bit-exact, GEMV within the tolerance.
+# ---------------------------------------------------------------------------------------------
+
+W8 = w.W4A16_FMT_W8_ROW_FP32
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (3, 48), (65, 1024), (130, 4096), (5, 17408), (300, 272)])
+def test_pack_w8_bit_exact(N, K):
+    say(f"pack_w8 N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=N * 3 + K)
+    W[0, :] = 0.0                          # an all-zero row: scale 1.0
+    if N > 2:
+        W[1, ::2] = np.float32(2.0 ** -7) * (np.arange(K // 2) % 64 - 32 + 0.5)  # exact ties
+        W[1, 1] = np.float32(2.0 ** -7 * 127)
+    c, s, _ = gpu_pack(W8, W)
+    rc, rs = oracle.quantize_w8row(W)
+    np.testing.assert_array_equal(host(c, np.int8), rc)
+    np.testing.assert_array_equal(host(s, np.float32), rs)
+
+
+@pytest.mark.parametrize("dtype,kind,np_t", [(F16, "f16", np.uint16), (BF16, "bf16", np.uint16),
+                                             (F32, "f32", np.float32)])
+def test_dequant_w8_bit_exact(dtype, kind, np_t):
+    N, K = 70, 528
+    rc, rs = oracle.quantize_w8row(workloads.weights(N, K, outliers=True, seed=61))
+    out = torch.empty((N, K), dtype=torch.float32 if dtype == F32 else torch.int16, device="cuda")
+    w.w4a16_dequant(W8, torch.from_numpy(rc).cuda(), torch.from_numpy(rs).cuda(), None, N, K, dtype, out)
+    np.testing.assert_array_equal(host(out, np_t), oracle.dequant_w8row(rc, rs, kind))
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 16), (1, 65, 496), (2, 130, 4096), (3, 257, 2064), (1, 31, 17408),
+                                   (16, 100, 1024), (1, 1000, 640)])
+def test_gemv_w8_parity(M, N, K):
+    say(f"gemv_w8 M={M} N={N} K={K}")
+    rc, rs = oracle.quantize_w8row(workloads.weights(N, K, outliers=True, seed=M + 2 * N + K))
+    x = workloads.activations(M, K, "f16", seed=K + 1)
+    packed = (torch.from_numpy(rc).cuda(), torch.from_numpy(rs).cuda(), None)
+    y = run_matmul(w.w4a16_gemv, W8, x, packed, N, K, F16)
+    err = rel_err(workloads.bits_to_f32(y, "f16"), oracle.matmul_w8row(x, rc, rs))
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    np.testing.assert_array_equal(run_matmul(w.w4a16_matmul, W8, x, packed, N, K, F16), y)
+
+
+def test_w8_decode_shape_full_pack_and_gemv(decode_weights):
+    wl = workloads.DECODE
+    say(f"w8 decode shape N={wl.N} K={wl.K}")
+    W, _ = decode_weights
+    packed = gpu_pack(W8, W)
+    rc, rs = oracle.quantize_w8row(W)
+    np.testing.assert_array_equal(host(packed[0], np.int8), rc)
+    np.testing.assert_array_equal(host(packed[1], np.float32), rs)
+    x = workloads.activations(1, wl.K, "f16", wl.seed_x)
+    y = run_matmul(w.w4a16_matmul, W8, x, packed, wl.N, wl.K, F16)
+    err = rel_err(workloads.bits_to_f32(y, "f16"), oracle.matmul_w8row(x, rc, rs))
+    say(f"w8 decode rel err {err:.3e}")
+    assert err <= TOL

@@ -25,7 +25,7 @@ import numpy as np
 class Workload:
     name: str
     fmt: str          # "g128" (asymmetric group 128, bf16 scale+min), "q4b32" (symmetric block 32) or
-                      # "g128zp" (group 128, fp16 scale + integer zero point)
+                      # "g128zp" (group 128, fp16 scale + integer zero point) or "w8row" (int8, row scale)
     M: int
     N: int
     K: int
@@ -44,6 +44,8 @@ PREFILL = Workload("prefill_gemm_m1024_k4096_n14336", "g128", 1024, 14336, 4096,
 # The decode shape in the integer-zero-point format of anrans.github.io "Quantization and GEMV"
 # (its GEMV example uses fp32 activations and notes that real kernels use FP16/BF16).
 ZP_DECODE = Workload("zp_gemv_m1_k4096_n14336", "g128zp", 1, 14336, 4096, "f16", outliers=True)
+# ... and in the per-row int8 format of that page's first exercise (W8A16).
+W8_DECODE = Workload("w8_gemv_m1_k4096_n14336", "w8row", 1, 14336, 4096, "f16", outliers=True)
 
 
 def sweep(M: int) -> Workload:
