@@ -34,10 +34,11 @@ constexpr int kGroupsPerPass = 32;  // groups of 128 k a block covers per pass (
 constexpr uint32_t kNibblePairMask = 0x000F000Fu;
 constexpr uint32_t kBf16Magic = 0x43004300u;  // bf16 128.0 in both halves
 
-// Waves per SIMD the register budget is sized for: one block per CU when a block covers 64
-// columns (or stages 16 activation rows, which fills LDS), two when it covers 32.
+// Waves per SIMD the register budget is sized for: one block per CU.  (32-column blocks are
+// used when N is small, so that there are more blocks; two of them per CU would halve the
+// register budget and spill, for a grid that rarely exceeds the CU count.)
 template <int MR, int TPL, int WAVES>
-constexpr int waves_per_eu() { return (TPL == 4 || MR == 16 ? 1 : 2) * WAVES / 4; }
+constexpr int waves_per_eu() { return WAVES / 4; }
 
 // `mask` and `magic` arrive as kernel arguments (0x000F000F and 0x43004300) so that they sit in
 // registers and each pair is one v_and_or_b32 (VOP3 cannot take a literal on gfx9).

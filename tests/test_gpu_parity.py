@@ -535,3 +535,41 @@ def test_w8_decode_shape_full_pack_and_gemv(decode_weights):
     err = rel_err(workloads.bits_to_f32(y, "f16"), oracle.matmul_w8row(x, rc, rs))
     say(f"w8 decode rel err {err:.3e}")
     assert err <= TOL
+
+
+# ---------------------------------------------------------------------------------------------
+# HIP-graph capture (the benchmark replays its steps from a graph): every replay bit-identical
+# to the eager call, with eager work and synchronisations between the replays.
+# ---------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt,act,M,N,K", [(G128, BF16, 1, 1000, 2048), (G128, BF16, 40, 520, 1024),
+                                           (G128, BF16, 300, 256, 4096), (Q4, F16, 2, 300, 1024),
+                                           (ZP, F16, 1, 300, 4096), (W8, F16, 3, 130, 512)])
+def test_graph_replays_match_eager(fmt, act, M, N, K):
+    say(f"graph replay fmt={fmt} M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=71)
+    codes, scales, mins = gpu_pack(fmt, W)
+    kind = "bf16" if act == BF16 else "f16"
+    xd = dev(workloads.activations(M, K, kind, seed=72))
+    ws, nb = w.alloc_workspace(fmt, M, N, K)
+    y_eager = torch.empty((M, N), dtype=torch.int16, device="cuda")
+    w.w4a16_matmul(fmt, act, xd, M, codes, scales, mins, N, K, y_eager, ws, nb)
+    ref = host(y_eager, np.uint16).copy()
+    y = torch.zeros((M, N), dtype=torch.int16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w.w4a16_matmul(fmt, act, xd, M, codes, scales, mins, N, K, y, ws, nb)  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w.w4a16_matmul(fmt, act, xd, M, codes, scales, mins, N, K, y, ws, nb)
+    junk = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+    for r in range(3):
+        y.fill_(0)
+        junk.normal_()                     # unrelated eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y, np.uint16), ref, err_msg=f"replay {r}")
