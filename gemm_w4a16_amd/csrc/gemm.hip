@@ -9,8 +9,9 @@
 //    this shape runs at twice the rate of 16x16x32).  The tile is chosen so that the grid fills
 //    the 256 CUs without splitting K where it can: 256 x 224 (waves stacked along M) at
 //    M = 1024, since 14336 = 64 x 224 and 1024 = 4 x 256 give exactly 256 tiles -- a
-//    power-of-two N tile would leave 1/8 of the chip idle; 128 x 256, 128 x 128 and 64 x 128
-//    (2 x 2 waves) for 512, 256 and 128 rows (224 tiles);
+//    power-of-two N tile would leave 1/8 of the chip idle; 128 x 256 and 128 x 128 (2 x 2 waves)
+//    for 512 and 256 rows, and 128 x 64 (waves along M) up to 128 rows, where one M-tile means
+//    each weight is dequantized once (224 tiles);
 //  * every global read in the k-loop is a direct-to-LDS copy by the load unit (global_load_lds)
 //    issued ahead of its use: the A tile one k-tile ahead (two LDS stages, XOR-swizzled rows),
 //    the packed B words three k-tiles ahead (three stages) and each group's scales and minimums
@@ -713,8 +714,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 }
 
 // Tile shapes by M (see the header comment): each fills the 256 CUs at N = 14336 without a K
-// split, from 128 rows (64 x 128 tiles, 2 x 2 waves) to 1024 rows (256 x 224, waves along M).
-enum TileCfg { kT64x128, kT128x128, kT128x256, kT256x224 };
+// split, from 65..128 rows (128 x 64 tiles, waves along M: each weight dequantized once) to 1024
+// rows (256 x 224, waves along M).
+enum TileCfg { kT128x64, kT128x128, kT128x256, kT256x224 };
 
 struct GemmPlan {
     TileCfg cfg;
@@ -723,7 +725,7 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int64_t M, int64_t N, int64_t K) {
     GemmPlan p;
-    if (M <= 128) p.cfg = kT64x128, p.bm = 64, p.bn = 128;
+    if (M <= 128) p.cfg = kT128x64, p.bm = 128, p.bn = 64;
     else if (M <= 256) p.cfg = kT128x128, p.bm = 128, p.bn = 128;
     else if (M <= 512) p.cfg = kT128x256, p.bm = 128, p.bn = 256;
     else p.cfg = kT256x224, p.bm = 256, p.bn = 224;
@@ -768,7 +770,7 @@ hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes,
     if (M <= kMidMaxRows) return launch_mid_g128(x, M, codes, scales, mins, N, K, y, stream);
     const GemmPlan p = plan_gemm(M, N, K);
     switch (p.cfg) {
-        case kT64x128: launch_cfg<64, 128, 2, 3, 6, 2>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
+        case kT128x64: launch_cfg<128, 64, 4, 3, 6, 1>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
         case kT128x128: launch_cfg<128, 128, 2, 2, 5, 2>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
         case kT128x256: launch_cfg<128, 256, 2, 1, 4, 1>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;
         case kT256x224: launch_cfg<256, 224, 4, 1, 3, 1>(p, x, M, codes, scales, mins, N, K, y, workspace, stream); break;

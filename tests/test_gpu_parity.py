@@ -166,10 +166,11 @@ def test_gemm_g128_parity(M, N, K):
     assert rel_err(bf16_f32(y), ref) <= TOL
 
 
-@pytest.mark.parametrize("M", [100, 200, 400, 600])
+@pytest.mark.parametrize("M", [65, 100, 128, 129, 200, 400, 600])
 @pytest.mark.parametrize("N", [500, 499])
 def test_gemm_every_tile_shape(M, N):
-    """One M in each tile-shape range of the large-M kernel (64x128, 128x128, 128x256, 256x224),
+    """M at the edges and inside each tile-shape range of the large-M kernel (128x64, 128x128,
+    128x256, 256x224),
     with a ragged N that is (500) and is not (499) a multiple of 4 -- the vector and the dword
     copy paths -- and K = 640 (five groups: an odd group count, so some splits are uneven)."""
     K = 640
