@@ -1,12 +1,27 @@
-// mid.hip -- mid-M W4A16 path (17 <= M <= 64) for the [K/8][N] G128 format, on bf16 MFMA.
+// mid.hip -- mid-M W4A16 paths (17 <= M <= 64) for the [K/8][N] G128 format, on bf16 MFMA.
 //
 // The large-M kernel amortizes one dequant of a weight over 256 rows and needs 256 output
 // tiles of 256 x 224 to fill the chip; at a few dozen rows it has neither, and the skinny
-// kernel's trick (all of K's activations resident in LDS) stops fitting past 16 rows.  This
-// kernel streams the weights once per 64-row slice of M, like a GEMV, and does the dequant of
-// vidyal.ai "Low-Precision Kernels", Step 2 (w_hat = bf16_rne(fmaf(q, s, min)), the reference
-// value) straight into MFMA B fragments, with no LDS for the weights:
+// kernel's trick (all of K's activations resident in LDS) stops fitting past 16 rows.  Both
+// kernels here stream the weights once, like a GEMV, with one block per 64 columns.
 //
+// 17..32 rows (mid_rows32_kernel): the factored form of vidyal.ai "Low-Precision Kernels" ("How
+// the measurements were taken": per group s * sum(x*q) + min * sum(x)), as in the skinny kernel,
+// with no LDS for the operands:
+//  * 8 waves; wave w owns the groups g = w (mod 8) and all 32 rows and 64 columns of the block;
+//  * per group a lane loads 16 packed words (4 k-steps x 4 adjacent columns, 16-byte loads),
+//    its bf16 scale/minimum pairs, and its own A fragments straight from global memory (2 row
+//    tiles x 4 k-steps, 16 bytes each; x is small and stays in L2), two groups ahead;
+//  * each word is one lane's B fragment of v_mfma_f32_16x16x32_bf16 after one v_and_or_b32 per
+//    bf16 pair (128 + q_j, 128 + q_{j+4}); the A fragment is put in the same k order by four
+//    v_perm_b32; a fifth MFMA against ones gives sum(x), and the group epilogue is
+//    s * acc + (min - 128 s) * sum(x);
+//  * the 8 waves' sums are added through LDS in wave order (bitwise reproducible).
+// Most of its time is the loads: each block reads all 256 KB of a 32-row x from L2 besides its
+// 128 KB of weights, and a CU's loads complete at ~30 GB/s.
+//
+// 33..64 rows (mid_g128_kernel): dequantizes as vidyal.ai Step 2 builds its B tile (w_hat =
+// bf16_rne(fmaf(q, s, min)), the reference value) straight into MFMA B fragments:
 //  * block = 64 columns x MR rows x all of K; 2*KP waves: wave (h, p) owns the 32 columns of
 //    half h and the groups g = p (mod KP).  With N = 14336 that is 224 blocks per row slice;
 //  * per step the block's threads stage MR rows x KP groups of activations in LDS (two
@@ -25,6 +40,172 @@ namespace w4a16 {
 namespace {
 
 constexpr int kMidCols = 64;
+
+// ---- 17..32 rows ------------------------------------------------------------------------------
+
+constexpr int kR32Waves = 8;
+constexpr int kR32Ahead = 2;  // groups in flight per wave (the register budget of 2 waves/SIMD)
+
+// (w >> 4j) & 0x000F000F | 0x43004300 = bf16 pair (128 + q_j, 128 + q_{j+4}), j = 0..3
+__device__ __forceinline__ bf16x8_t r32_unpack(uint32_t w, uint32_t mask, uint32_t magic) {
+    const u32x4_t p = {(w & mask) | magic, ((w >> 4) & mask) | magic, ((w >> 8) & mask) | magic,
+                       ((w >> 12) & mask) | magic};
+    return __builtin_bit_cast(bf16x8_t, p);
+}
+
+// A fragment (x0..x7) as dwords (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
+__device__ __forceinline__ bf16x8_t r32_pair_up(uint4 v) {
+    const uint4 p = make_uint4(__builtin_amdgcn_perm(v.z, v.x, 0x05040100u), __builtin_amdgcn_perm(v.z, v.x, 0x07060302u),
+                               __builtin_amdgcn_perm(v.w, v.y, 0x05040100u), __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
+    return __builtin_bit_cast(bf16x8_t, p);
+}
+
+// One group's operands in a lane: packed words [k-step][column], scale/minimum pairs, and the A
+// fragments [k-step][row tile] in natural k order.
+struct R32Group {
+    uint32_t w[4][4];
+    uint32_t s[2], m[2];
+    uint4 a[4][2];
+};
+
+template <bool kVec>
+__global__ __launch_bounds__(64 * kR32Waves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
+                       const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
+                       uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic) {
+    __shared__ float part[kR32Waves][32][64];
+    const int lane = lane_id(), wave = wave_id();
+    const int lr = lane & 15, lg = lane >> 4;
+    const int G = K >> 7;
+    const int J = G > wave ? (G - wave + kR32Waves - 1) / kR32Waves : 0;  // this wave's groups
+    const int n0 = blockIdx.x * kMidCols;
+    // this lane's 4 adjacent columns; past N they re-read in-range columns and are never stored
+    int cbase = n0 + 4 * lr;
+    if (kVec) cbase = min(cbase, N - 4);
+    const uint32_t lane_off = ((uint32_t)lg * (uint32_t)N + (uint32_t)cbase) * 4u;
+    // this lane's A rows lr and 16 + lr (clamped: rows past M feed only outputs never stored),
+    // k chunk lg of each 32-k step
+    const uint16_t* xrow0 = x + (size_t)min(lr, M - 1) * K + 8 * lg;
+    const uint16_t* xrow1 = x + (size_t)min(16 + lr, M - 1) * K + 8 * lg;
+
+    auto load = [&](int j, R32Group& o) {
+        const int g = wave + kR32Waves * j;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t* row = codes + (size_t)(16 * g + 4 * s) * N;  // packed rows 16g + 4s + lg
+            if (kVec) {
+                const u32x4_t v = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(reinterpret_cast<const char*>(row) + lane_off));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o.w[s][c] = v[c];
+            } else {
+                const uint32_t* r = row + (size_t)lg * N;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) o.w[s][c] = r[min(cbase + c, N - 1)];
+            }
+            o.a[s][0] = *reinterpret_cast<const uint4*>(xrow0 + g * 128 + 32 * s);
+            o.a[s][1] = *reinterpret_cast<const uint4*>(xrow1 + g * 128 + 32 * s);
+        }
+        const uint16_t* sp = scales + (size_t)g * N;
+        const uint16_t* mp = mins + (size_t)g * N;
+        if (kVec) {
+            const uint2 a = *reinterpret_cast<const uint2*>(sp + cbase), b = *reinterpret_cast<const uint2*>(mp + cbase);
+            o.s[0] = a.x, o.s[1] = a.y, o.m[0] = b.x, o.m[1] = b.y;
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c0 = min(cbase + 2 * h, N - 1), c1 = min(cbase + 2 * h + 1, N - 1);
+                o.s[h] = (uint32_t)sp[c0] | ((uint32_t)sp[c1] << 16);
+                o.m[h] = (uint32_t)mp[c0] | ((uint32_t)mp[c1] << 16);
+            }
+        }
+    };
+
+    // the magic exponent in a VGPR (the mask stays in an SGPR): one v_and_or_b32 per pair
+    uint32_t magic_v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(magic));
+    const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
+
+    // accumulator element e of lane l in a 16x16 tile: row 4 (l / 16) + e, column l % 16; tile c
+    // of a row block holds the columns cbase + c
+    float yacc[4][2][4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yacc[c][rt][e] = 0.0f;
+
+    auto compute = [&](const R32Group& o) {
+        f32x4_t acc[4][2], accs[2];
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            accs[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c][rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            bf16x8_t b[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) b[c] = r32_unpack(o.w[s][c], mask, magic_v);
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const bf16x8_t a = r32_pair_up(o.a[s][rt]);
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    acc[c][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[c], acc[c][rt], 0, 0, 0);
+                accs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, accs[rt], 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const uint32_t sb = (c & 1) ? (o.s[c >> 1] >> 16) : (o.s[c >> 1] & 0xFFFFu);
+            const uint32_t mb = (c & 1) ? (o.m[c >> 1] >> 16) : (o.m[c >> 1] & 0xFFFFu);
+            const float sv = bf16_bits_to_f32(sb), mv = bf16_bits_to_f32(mb);
+            const float cc = __builtin_fmaf(-128.0f, sv, mv);  // min - 128 s
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    yacc[c][rt][e] = __builtin_fmaf(sv, acc[c][rt][e], yacc[c][rt][e]);
+                    yacc[c][rt][e] = __builtin_fmaf(cc, accs[rt][e], yacc[c][rt][e]);
+                }
+        }
+    };
+
+    // groups j, j + 1 in flight while j is used; slot j % 2 is reloaded right after its use
+    R32Group sl[kR32Ahead];
+#pragma unroll
+    for (int d = 0; d < kR32Ahead; ++d)
+        if (d < J) load(d, sl[d]);
+    for (int j0 = 0; j0 < J; j0 += kR32Ahead) {
+#pragma unroll
+        for (int d = 0; d < kR32Ahead; ++d) {
+            if (j0 + d < J) compute(sl[d]);
+            if (j0 + d + kR32Ahead < J) load(j0 + d + kR32Ahead, sl[d]);
+        }
+    }
+
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<float4*>(&part[wave][16 * rt + 4 * lg + e][4 * lr]) =
+                make_float4(yacc[0][rt][e], yacc[1][rt][e], yacc[2][rt][e], yacc[3][rt][e]);
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * kMidCols; idx += 64 * kR32Waves) {
+        const int row = idx / kMidCols, col = idx % kMidCols, n = n0 + col;
+        if (row >= M || n >= N) continue;
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < kR32Waves; ++v) sum += part[v][row][col];
+        y[(size_t)row * N + n] = f32_to_bf16_bits(sum);
+    }
+}
+
+// ---- 33..64 rows ------------------------------------------------------------------------------
 
 // 16-byte chunk c of activation row r sits at chunk c ^ (r & 15) of the row: the 16 rows of a
 // fragment read then hit 16 different 4-bank groups.
@@ -204,8 +385,12 @@ hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, 
                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     const unsigned gx = (unsigned)((N + kMidCols - 1) / kMidCols);
     if (M <= 32) {
-        hipLaunchKernelGGL((mid_g128_kernel<32, 4>), dim3(gx, 1), dim3(128 * 4), 0, stream, x, codes, scales, mins, y,
-                           (int)M, (int)N, (int)K, 0x0F0F0F0Fu, 0xF0F0F0F0u);
+        if (N % 4 == 0)
+            hipLaunchKernelGGL((mid_rows32_kernel<true>), dim3(gx), dim3(64 * kR32Waves), 0, stream, x, codes, scales, mins,
+                               y, (int)M, (int)N, (int)K, 0x000F000Fu, 0x43004300u);
+        else
+            hipLaunchKernelGGL((mid_rows32_kernel<false>), dim3(gx), dim3(64 * kR32Waves), 0, stream, x, codes, scales,
+                               mins, y, (int)M, (int)N, (int)K, 0x000F000Fu, 0x43004300u);
     } else {
         const unsigned gy = (unsigned)((M + 63) / 64);
         hipLaunchKernelGGL((mid_g128_kernel<64, 4>), dim3(gx, gy), dim3(128 * 4), 0, stream, x, codes, scales, mins, y,

@@ -142,11 +142,12 @@ int64_t w4a16_gemv_max_rows(void);
 size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K);
 
 /* Large-M path (G128 only; ERR_UNSUPPORTED for the other formats): y [M][N] = x [M][K] . W_hat^T on bf16 MFMA with fp32 accumulation.
- * Packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai Step 2 builds its
- * B tile) into LDS and fed to v_mfma_f32_16x16x32_bf16.  When a K split is used, partial sums go
- * to `workspace` and are added in a fixed order, so results are bitwise reproducible run to
- * run.  workspace_bytes must be >= w4a16_gemm_workspace_bytes(...); workspace may be NULL if
- * that is 0. */
+ * From 33 rows on, packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai
+ * Step 2 builds its B tile) and fed to the matrix cores; up to 32 rows the factored per-group form
+ * of w4a16_gemv (s * sum(x*(128+q)) + (min - 128 s) * sum(x), fp32) is used instead.  When a K
+ * split is used, partial sums go to `workspace` and are added in a fixed order; every path is
+ * bitwise reproducible run to run.  workspace_bytes must be >= w4a16_gemm_workspace_bytes(...);
+ * workspace may be NULL if that is 0. */
 w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                           const void* codes, const void* scales, const void* mins, int64_t N,
                           int64_t K, void* y, void* workspace, size_t workspace_bytes,

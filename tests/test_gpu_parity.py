@@ -155,7 +155,11 @@ def test_gemv_g128_parity(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(5, 200, 256), (64, 256, 4096), (130, 260, 384), (257, 131, 1024),
                                    (128, 128, 128), (300, 520, 640), (17, 65, 384), (33, 131, 384),
-                                   (513, 230, 1152), (50, 97, 1152), (64, 1000, 640)])
+                                   (513, 230, 1152), (50, 97, 1152), (64, 1000, 640),
+                                   # 17..32 rows: several groups per wave (K = 4224: 33 groups, one
+                                   # wave with 5), waves with no group (K = 128, 256), ragged N
+                                   (24, 1000, 4224), (20, 130, 256), (31, 97, 1152), (32, 64, 128),
+                                   (32, 260, 2048), (18, 4100, 384)])
 def test_gemm_g128_parity(M, N, K):
     say(f"gemm_g128 M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=13)
