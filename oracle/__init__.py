@@ -100,7 +100,11 @@ def bind(path) -> ctypes.CDLL:
     L.oracle_quantize_w8row.argtypes = [P, I64, I64, P, P]
     L.oracle_dequant_w8row.argtypes = [P, P, I64, I64, I, P]
     L.oracle_matmul_w8row_f64.argtypes = [P, I, I64, P, P, I64, I64, P]
-    for name in ("oracle_quantize_w8row", "oracle_dequant_w8row", "oracle_matmul_w8row_f64",
+    L.oracle_quantize_act_i8.argtypes = [P, I64, I64, P, P, P]
+    L.oracle_matmul_w4a8_f64.argtypes = [P, P, I64, P, P, P, I64, I64, P]
+    L.oracle_matmul_w4a8_f64_at.argtypes = [P, P, I64, P, P, P, I64, I64, P, P, I64, P]
+    for name in ("oracle_quantize_act_i8", "oracle_matmul_w4a8_f64", "oracle_matmul_w4a8_f64_at",
+                 "oracle_quantize_w8row", "oracle_dequant_w8row", "oracle_matmul_w8row_f64",
                  "oracle_quantize_g128zp", "oracle_dequant_g128zp", "oracle_matmul_g128zp_f64",
                  "oracle_matmul_g128zp_f64_at",
                  "oracle_quantize_g128", "oracle_dequant_g128", "oracle_quantize_q4b32",
@@ -206,6 +210,54 @@ def matmul_g128_at(x_bits, codes, scales, mins, rows, cols, x_kind: str = "bf16"
     _check(lib().oracle_matmul_g128_f64_at(_ptr(x_bits), 0 if x_kind == "bf16" else 1, M,
                                            _ptr(codes), _ptr(scales), _ptr(mins), N, K, _ptr(rows),
                                            _ptr(cols), len(rows), _ptr(y)), "matmul_g128_at")
+    return y
+
+
+# ---- W4A8: per-row int8 activations with the G128 weights ----------------------------------
+
+def quantize_act_i8(x_bits: np.ndarray):
+    """x_bits uint16 [M][K] bf16 -> (xq int8 [M][K], ascale float32 [M], xsum float32 [K/128][M]).
+
+    Per row a = max|x| / 127 (1.0 for a zero row), xq = clamp(rint(x / a), -127, 127); xsum holds
+    each group's exact integer sum of xq (vidyal.ai "Low-Precision Kernels", "The cost of
+    quantizing activations")."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    M, K = x_bits.shape
+    xq = np.zeros((M, K), dtype=np.int8)
+    ascale = np.zeros(M, dtype=np.float32)
+    xsum = np.zeros((K // 128, M), dtype=np.float32)
+    _check(lib().oracle_quantize_act_i8(_ptr(x_bits), M, K, _ptr(xq), _ptr(ascale), _ptr(xsum)), "quantize_act_i8")
+    return xq, ascale, xsum
+
+
+def matmul_w4a8(xq, ascale, codes, scales, mins) -> np.ndarray:
+    """y float64 [M][N] = (a_m * xq) . (q * s + min)^T in fp64, G128 weights."""
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    ascale = np.ascontiguousarray(ascale, dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    mins = np.ascontiguousarray(mins, dtype=np.uint16)
+    M, K = xq.shape
+    N = codes.shape[1]
+    y = np.zeros((M, N), dtype=np.float64)
+    _check(lib().oracle_matmul_w4a8_f64(_ptr(xq), _ptr(ascale), M, _ptr(codes), _ptr(scales), _ptr(mins), N, K,
+                                        _ptr(y)), "matmul_w4a8")
+    return y
+
+
+def matmul_w4a8_at(xq, ascale, codes, scales, mins, rows, cols) -> np.ndarray:
+    xq = np.ascontiguousarray(xq, dtype=np.int8)
+    ascale = np.ascontiguousarray(ascale, dtype=np.float32)
+    codes = np.ascontiguousarray(codes, dtype=np.uint32)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    mins = np.ascontiguousarray(mins, dtype=np.uint16)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.ascontiguousarray(cols, dtype=np.int64)
+    M, K = xq.shape
+    N = codes.shape[1]
+    y = np.zeros(len(rows), dtype=np.float64)
+    _check(lib().oracle_matmul_w4a8_f64_at(_ptr(xq), _ptr(ascale), M, _ptr(codes), _ptr(scales), _ptr(mins), N, K,
+                                           _ptr(rows), _ptr(cols), len(rows), _ptr(y)), "matmul_w4a8_at")
     return y
 
 

@@ -24,6 +24,11 @@
  *       along K), scales and zero points [N][K/128]; and, from its first exercise, W8A16:
  *       per row s = max|w| / 127, q = clamp(round(w/s), -127, 127) stored as int8 [N][K],
  *       the row's scale applied once after the row's sum.
+ *  [P1'] vidyal.ai, "Low-Precision Kernels", sections "INT8 on a GeForce chip" and "The cost of
+ *       quantizing activations" -- W4A8: the activations quantized to 8-bit integers per row on
+ *       every call (absolute value, maximum per row, divide, round, convert), integer products
+ *       summed in 32 bits, and the activation and weight scales applied to those sums in the
+ *       epilogue.
  *
  * Readings where the pages leave a step open (each is listed in the design notes):
  *  - codes are computed from the STORED (rounded) scale and minimum, so encode and decode
@@ -41,6 +46,9 @@
  *    [-2048, 2048], the integers fp16 holds exactly (only a group whose range is below 1/2048 of
  *    its distance from zero reaches the clamp); the code is round(w/s) + z as the formula
  *    writes it (the page's example rounds w/s + z, which differs only at exact ties).
+ *  - W4A8 activations: symmetric per row, a = max|x| / 127 in fp32 (IEEE division), an all-zero
+ *    row gets a = 1, xq = clamp(rint(x / a), -127, 127) with ties to even; the weights are the
+ *    G128 format unchanged.
  *
  * Build: gcc -O2 -std=c11 -fPIC -shared -ffp-contract=off -fno-fast-math -lm
  * Every function returns 0 on success and a nonzero code on a bad argument or a
@@ -580,6 +588,79 @@ int oracle_matmul_w8row_f64(const uint16_t* x, int x_kind, int64_t M, const int8
                 acc += act_value(x, x_kind, m * K + k) * ((double)codes[n * K + k] * (double)scales[n]);
             y[m * N + n] = acc;
         }
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------------------------
+ * W4A8 with the G128 weights [P1']: per-row int8 activations, integer sums per group.
+ *   x      bf16 bits [M][K], K % 128 == 0
+ *   a_m    = max_k |x[m][k]| / 127 in fp32; 1.0 for an all-zero row       -> ascale fp32 [M]
+ *   xq     = clamp(rint(x / a_m), -127, 127)  (fp32 divide, ties to even)  -> int8 [M][K]
+ *   X[g][m] = sum of xq[m][k] over group g (an exact integer)              -> xsum fp32 [K/128][M]
+ * y[m][n] = sum over k of (a_m * xq[m][k]) * (q * s_b + m_b) in fp64 and k order: the plain
+ * product of the dequantized activations and weights (a kernel computes the same number as
+ * a_m * sum_g (s_b * sum_k xq * q + m_b * X[g][m])).
+ * ---------------------------------------------------------------------------------------- */
+
+int oracle_quantize_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* ascale, float* xsum)
+{
+    if (!x || !xq || !ascale || !xsum || M <= 0 || K <= 0 || K % 128) return ORACLE_BAD_ARG;
+    const int64_t G = K / 128;
+    for (int64_t m = 0; m < M; ++m) {
+        const uint16_t* row = x + m * K;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            const float v = oracle_bf16_to_f32(row[k]);
+            if (!isfinite(v)) return ORACLE_NONFINITE;
+            if (fabsf(v) > amax) amax = fabsf(v);
+        }
+        float a8 = amax / 127.0f;
+        if (a8 == 0.0f) a8 = 1.0f; /* an all-zero row */
+        ascale[m] = a8;
+        for (int64_t g = 0; g < G; ++g) {
+            int64_t sum = 0;
+            for (int64_t k = 128 * g; k < 128 * g + 128; ++k) {
+                const float t8 = rintf(oracle_bf16_to_f32(row[k]) / a8);
+                const int q8 = t8 < -127.0f ? -127 : (t8 > 127.0f ? 127 : (int)t8);
+                xq[m * K + k] = (int8_t)q8;
+                sum += q8;
+            }
+            xsum[g * M + m] = (float)sum; /* |sum| <= 127 * 128: exact */
+        }
+    }
+    return ORACLE_OK;
+}
+
+static double w4a8_dot(const int8_t* xq, const float* ascale, const uint32_t* codes, const uint16_t* scales,
+                       const uint16_t* mins, int64_t N, int64_t K, int64_t m, int64_t n)
+{
+    double acc = 0.0;
+    for (int64_t k = 0; k < K; ++k)
+        acc += ((double)ascale[m] * (double)xq[m * K + k]) * g128_weight_exact(codes, scales, mins, N, n, k);
+    return acc;
+}
+
+int oracle_matmul_w4a8_f64(const int8_t* xq, const float* ascale, int64_t M, const uint32_t* codes,
+                           const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K, double* y)
+{
+    if (!xq || !ascale || !codes || !scales || !mins || !y || M <= 0 || N <= 0 || K <= 0 || K % 128)
+        return ORACLE_BAD_ARG;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) y[m * N + n] = w4a8_dot(xq, ascale, codes, scales, mins, N, K, m, n);
+    return ORACLE_OK;
+}
+
+int oracle_matmul_w4a8_f64_at(const int8_t* xq, const float* ascale, int64_t M, const uint32_t* codes,
+                              const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K,
+                              const int64_t* rows, const int64_t* cols, int64_t count, double* y)
+{
+    if (!xq || !ascale || !codes || !scales || !mins || !rows || !cols || !y || M <= 0 || N <= 0 || K <= 0 ||
+        K % 128 || count < 0)
+        return ORACLE_BAD_ARG;
+    for (int64_t i = 0; i < count; ++i) {
+        if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N) return ORACLE_BAD_ARG;
+        y[i] = w4a8_dot(xq, ascale, codes, scales, mins, N, K, rows[i], cols[i]);
+    }
     return ORACLE_OK;
 }
 

@@ -79,6 +79,17 @@ MUTATIONS = [
      "acc += act_value(x, x_kind, m * K + k) * ((double)(uint8_t)codes[n * K + k] * (double)scales[n]);"),
     ("ZP f32 decode ignores the zero point", "const float v = ((float)g128zp_code(codes, K, n, k) - z) * s;",
      "const float v = ((float)g128zp_code(codes, K, n, k)) * s;"),
+    ("W4A8 activation codes truncate", "const float t8 = rintf(oracle_bf16_to_f32(row[k]) / a8);",
+     "const float t8 = truncf(oracle_bf16_to_f32(row[k]) / a8);"),
+    ("W4A8 activation scale over 128 levels", "float a8 = amax / 127.0f;", "float a8 = amax / 128.0f;"),
+    ("W4A8 zero row keeps scale 0", "if (a8 == 0.0f) a8 = 1.0f; /* an all-zero row */", ""),
+    ("W4A8 activation scale from the signed maximum", "if (fabsf(v) > amax) amax = fabsf(v);",
+     "if (v > amax) amax = v;"),
+    ("W4A8 group sum keeps the last code", "sum += q8;", "sum = q8;"),
+    ("W4A8 group sums laid out [M][K/128]", "xsum[g * M + m] = (float)sum;", "xsum[m * G + g] = (float)sum;"),
+    ("W4A8 product drops the activation scale",
+     "acc += ((double)ascale[m] * (double)xq[m * K + k]) * g128_weight_exact(codes, scales, mins, N, n, k);",
+     "acc += ((double)xq[m * K + k]) * g128_weight_exact(codes, scales, mins, N, n, k);"),
 ]
 
 PIN_TESTS = [f for name, f in inspect.getmembers(pins, inspect.isfunction)

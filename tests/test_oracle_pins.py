@@ -727,3 +727,108 @@ def test_w8_matmul_special_cases_and_error():
     # RMS rounding error s / sqrt(12) ~ 0.009 sigma
     rms = np.sqrt(np.mean((What - W) ** 2)) / 0.02
     assert 0.0075 <= rms <= 0.0105, rms
+
+
+# ---------------------------------------------------------------------------------------------
+# W4A8 (vidyal.ai "Low-Precision Kernels", "INT8 on a GeForce chip" and "The cost of quantizing
+# activations"): per-row int8 activations, a = max|x| / 127, integer sums per group.
+# ---------------------------------------------------------------------------------------------
+
+def _bf16_bits_exact(v):
+    """bf16 bits of values that bf16 holds exactly (checked)."""
+    b = torch_bf16_bits(np.asarray(v, dtype=np.float32))
+    assert np.array_equal(bf16_value(b), np.asarray(v, dtype=np.float32))
+    return b
+
+
+def test_w4a8_grid_rows_quantize_exactly():
+    """Rows of j * 2^e (j = -127..127, with |j| = 127 present): a = 2^e exactly, the codes are j and
+    a * xq reproduces x; the group sums are the sums of j; a zero row gets a = 1 and codes 0."""
+    rng = np.random.default_rng(81)
+    M, K = 4, 384
+    x = np.zeros((M, K), dtype=np.float32)
+    jj = np.zeros((M, K), dtype=np.int64)
+    for m, e in enumerate((-6, 0, 3)):
+        j = rng.integers(-127, 128, size=K)
+        j[rng.integers(0, K)] = 127 if m % 2 else -127
+        jj[m] = j
+        x[m] = j * 2.0 ** e
+    xq, a, xsum = oracle.quantize_act_i8(_bf16_bits_exact(x))
+    np.testing.assert_array_equal(a, np.float32([2.0 ** -6, 1.0, 8.0, 1.0]))
+    np.testing.assert_array_equal(xq.astype(np.int64), jj)
+    np.testing.assert_array_equal(xsum, jj.reshape(M, K // 128, 128).sum(axis=2).T.astype(np.float32))
+    np.testing.assert_array_equal(xq[3], 0)
+
+
+def test_w4a8_ties_go_to_even():
+    """With a = 1 (max|x| = 127), x = j + 1/2 must round to the even neighbour."""
+    halves = np.array([0.5, 1.5, 2.5, 3.5, -0.5, -1.5, -2.5, -3.5, 100.5, -126.5], dtype=np.float32)
+    x = np.zeros((1, 128), dtype=np.float32)
+    x[0, :len(halves)] = halves
+    x[0, -1] = 127.0
+    xq, a, _ = oracle.quantize_act_i8(_bf16_bits_exact(x))
+    assert a[0] == 1.0
+    np.testing.assert_array_equal(xq[0, :len(halves)], [0, 2, 2, 4, 0, -2, -2, -4, 100, -126])
+
+
+def test_w4a8_codes_are_nearest_and_extremes_hit_127():
+    """Random rows: every code is the nearest multiple of a (|x - a xq| <= a/2, up to the fp32
+    rounding of x/a, at most 2^-17 for |x/a| <= 128), the largest magnitude maps to +-127 with its
+    sign, and a is the fp32 quotient max|x| / 127."""
+    x = workloads.activations(16, 1024, "bf16", seed=82)
+    xf = bf16_value(x).astype(np.float64)
+    xq, a, xsum = oracle.quantize_act_i8(x)
+    amax = np.abs(xf).max(axis=1)
+    np.testing.assert_array_equal(a, (amax.astype(np.float32) / np.float32(127.0)).astype(np.float32))
+    err = np.abs(xf - a.astype(np.float64)[:, None] * xq.astype(np.float64))
+    assert np.all(err <= a.astype(np.float64)[:, None] * (0.5 + 2.0 ** -16))
+    arg = np.abs(xf).argmax(axis=1)
+    top = xq[np.arange(16), arg].astype(np.int64)
+    np.testing.assert_array_equal(np.abs(top), 127)
+    np.testing.assert_array_equal(np.sign(top), np.sign(xf[np.arange(16), arg]))
+    assert np.abs(xq.astype(np.int64)).max() == 127
+
+
+def test_w4a8_matmul_equals_w4a16_on_grid_activations():
+    """When every activation is on its row's int8 grid, a * xq == x exactly, so the W4A8 product
+    is the W4A16 reference product bit for bit (same fp64 sums in the same order)."""
+    rng = np.random.default_rng(83)
+    M, N, K = 3, 40, 512
+    x = (rng.integers(-127, 128, size=(M, K)) * 2.0 ** -4).astype(np.float32)
+    x[:, 0] = 127 * 2.0 ** -4
+    bits = _bf16_bits_exact(x)
+    W = workloads.weights(N, K, outliers=True, seed=84)
+    codes, scales, mins = oracle.quantize_g128(W)
+    xq, a, _ = oracle.quantize_act_i8(bits)
+    np.testing.assert_array_equal(oracle.matmul_w4a8(xq, a, codes, scales, mins),
+                                  oracle.matmul_g128(bits, codes, scales, mins))
+
+
+def test_w4a8_matmul_group_form_and_error():
+    """The product equals a_m * sum_g (s * sum(xq q) + min * X_g) (integer group sums, exact), the
+    sampled entry point agrees, and the activation rounding costs about a / sqrt(12) per term:
+    relative error against the W4A16 product well under 2%."""
+    M, N, K = 4, 24, 1024
+    x = workloads.activations(M, K, "bf16", seed=85)
+    W = workloads.weights(N, K, seed=86)
+    codes, scales, mins = oracle.quantize_g128(W)
+    xq, a, xsum = oracle.quantize_act_i8(x)
+    y = oracle.matmul_w4a8(xq, a, codes, scales, mins)
+    q = np.zeros((N, K), dtype=np.int64)
+    for r in range(K // 8):
+        for j in range(8):
+            q[:, 8 * r + j] = (codes[r].astype(np.int64) >> (4 * j)) & 0xF
+    s = bf16_value(scales).astype(np.float64)            # [G][N]
+    mn = bf16_value(mins).astype(np.float64)
+    G = K // 128
+    ref = np.zeros((M, N))
+    for g in range(G):
+        iq = xq[:, 128 * g:128 * g + 128].astype(np.int64) @ q[:, 128 * g:128 * g + 128].T   # exact integers
+        ref += iq * s[g][None, :] + xsum[g][:, None].astype(np.float64) * mn[g][None, :]
+    ref *= a.astype(np.float64)[:, None]
+    assert np.max(np.abs(y - ref)) <= 1e-12 * np.max(np.abs(ref))
+    rows, cols = np.array([0, 3, 1, 2]), np.array([5, 23, 0, 11])
+    np.testing.assert_array_equal(oracle.matmul_w4a8_at(xq, a, codes, scales, mins, rows, cols), y[rows, cols])
+    y16 = oracle.matmul_g128(x, codes, scales, mins)
+    rel = np.max(np.abs(y - y16)) / np.max(np.abs(y16))
+    assert 1e-4 < rel < 2e-2
