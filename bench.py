@@ -2,7 +2,7 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                    [--only decode|prefill|q4|sweep|zp|w8]
+                    [--only decode|prefill|q4|sweep|zp|w8|w4a8]
 
 A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one batch of seeded
 synthetic input, with packed weights, activations and output already resident in HBM.  The
@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
 CACHE_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache (MALL)
 WARM_SECONDS = 0.25            # untimed run-up of each workload before its timed replay
 METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
@@ -70,7 +71,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=170)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -258,6 +259,54 @@ def bench_w8(steps, warmup, W=None):
     return bench_rowfmt(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32, steps, warmup, W)
 
 
+class W4A8Setup:
+    """The prefill shape as W4A8: bf16 activations quantized per row to int8, then the int8-MFMA
+    product with the same packed G128 weights.  A step is both kernels, or the product alone."""
+
+    def __init__(self, wl, W, x_bits, gemm_only: bool):
+        import torch
+        import gemm_w4a16_amd as w
+        self.w, self.wl, self.gemm_only = w, wl, gemm_only
+        fmt = w.W4A16_FMT_G128_ASYM_BF16
+        Wd = torch.from_numpy(W).cuda()
+        self.packed = w.alloc_packed(fmt, wl.N, wl.K)
+        w.w4a16_quantize_pack(fmt, Wd, wl.N, wl.K, *self.packed)
+        del Wd
+        self.x = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).cuda()
+        self.q = w.alloc_act_i8(wl.M, wl.K)
+        w.w4a16_quantize_act_i8(self.x, wl.M, wl.K, *self.q)
+        self.y = torch.empty((wl.M, wl.N), dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+
+    def step(self, i):
+        w, wl = self.w, self.wl
+        if not self.gemm_only:
+            w.w4a16_quantize_act_i8(self.x, wl.M, wl.K, *self.q)
+        w.w4a16_gemm_w4a8(w.W4A16_FMT_G128_ASYM_BF16, *self.q, wl.M, *self.packed, wl.N, wl.K, self.y)
+
+
+def bench_w4a8(steps, warmup):
+    """W4A8 at the prefill shape (M=1024, K=4096, N=14336): quantize + product per step, and the
+    product alone against the int8 matrix-core peak."""
+    import workloads
+    wl = workloads.PREFILL
+    W, x = workloads.inputs(wl)
+    ops = 2.0 * wl.M * wl.N * wl.K
+    out = {"workload": "w4a8_gemm_m1024_k4096_n14336", "M": wl.M, "N": wl.N, "K": wl.K, "steps": steps}
+    for gemm_only in (False, True):
+        st = W4A8Setup(wl, W, x, gemm_only)
+        wall, ev = time_steps(st, steps, warmup)
+        t = ev / steps
+        key = "gemm_only" if gemm_only else "quantize_and_gemm"
+        out[key] = {"us_per_step_events": t * 1e6, "tops": ops / t / 1e12}
+        if gemm_only:
+            out["roofline"] = {"bound": "mfma", "kernel": "w4a8_gemm_kernel", "achieved": ops / t / 1e12,
+                               "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s", "frac": ops / t / 1e12 / MFMA_I8_PEAK_TOPS,
+                               "traffic": None}
+        del st
+    return out
+
+
 def bench_sweep(steps, warmup, W=None):
     import gemm_w4a16_amd as w
     import workloads
@@ -330,7 +379,8 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
-        fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp, "w8": bench_w8}[args.only]
+        fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp, "w8": bench_w8,
+              "w4a8": bench_w4a8}[args.only]
         print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
         return
 
@@ -383,6 +433,9 @@ def main():
         torch.cuda.empty_cache()
         log("batch sweep")
         extra["sweep"] = bench_sweep(34, 3, W)
+        torch.cuda.empty_cache()
+        log("W4A8 at the prefill shape")
+        extra["w4a8_m1024"] = bench_w4a8(20, 3)
         torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline and args.only is None:

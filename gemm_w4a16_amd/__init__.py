@@ -24,7 +24,7 @@ W4A16_BF16, W4A16_FP16, W4A16_FP32 = 0, 1, 2
 EXPORTED = (
     "w4a16_status_string", "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant",
     "w4a16_gemv", "w4a16_gemv_max_rows", "w4a16_gemm_workspace_bytes", "w4a16_gemm",
-    "w4a16_matmul", "w4a16_matmul_gemv_cutoff",
+    "w4a16_matmul", "w4a16_matmul_gemv_cutoff", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
 )
 
 
@@ -56,8 +56,10 @@ def _load() -> ctypes.CDLL:
     L.w4a16_gemm.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P, SZ, P]
     L.w4a16_matmul.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P, SZ, P]
     L.w4a16_matmul_gemv_cutoff.argtypes, L.w4a16_matmul_gemv_cutoff.restype = [], I64
+    L.w4a16_quantize_act_i8.argtypes = [P, I64, I64, P, P, P, P]
+    L.w4a16_gemm_w4a8.argtypes = [I, P, P, P, I64, P, P, P, I64, I64, P, P]
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant", "w4a16_gemv",
-                 "w4a16_gemm", "w4a16_matmul"):
+                 "w4a16_gemm", "w4a16_matmul", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8"):
         getattr(L, name).restype = I
     return L
 
@@ -142,6 +144,17 @@ def w4a16_matmul_gemv_cutoff() -> int:
     return int(lib.w4a16_matmul_gemv_cutoff())
 
 
+def w4a16_quantize_act_i8(x, M: int, K: int, xq, ascale, xsum, stream=None) -> None:
+    _ok(lib.w4a16_quantize_act_i8(_p(x), M, K, _p(xq), _p(ascale), _p(xsum), _stream(stream)),
+        "w4a16_quantize_act_i8")
+
+
+def w4a16_gemm_w4a8(fmt: int, xq, ascale, xsum, M: int, codes, scales, mins, N: int, K: int, y,
+                    stream=None) -> None:
+    _ok(lib.w4a16_gemm_w4a8(fmt, _p(xq), _p(ascale), _p(xsum), M, _p(codes), _p(scales), _p(mins), N, K,
+                            _p(y), _stream(stream)), "w4a16_gemm_w4a8")
+
+
 # ---- memory plumbing (torch allocations with the ABI's shapes and dtypes) ------------------------
 
 def alloc_packed(fmt: int, N: int, K: int, device="cuda"):
@@ -167,6 +180,14 @@ def alloc_packed(fmt: int, N: int, K: int, device="cuda"):
     return (torch.empty((N, K // 32, 16), dtype=torch.uint8, device=device),
             torch.empty((N, K // 32), dtype=torch.int16, device=device),
             None)
+
+
+def alloc_act_i8(M: int, K: int, device="cuda"):
+    """Empty (xq int8 [M][K], ascale fp32 [M], xsum fp32 [K/128][M]) for w4a16_quantize_act_i8."""
+    import torch
+    return (torch.empty((M, K), dtype=torch.int8, device=device),
+            torch.empty(M, dtype=torch.float32, device=device),
+            torch.empty((K // 128, M), dtype=torch.float32, device=device))
 
 
 def alloc_workspace(fmt: int, M: int, N: int, K: int, device="cuda"):

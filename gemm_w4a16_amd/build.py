@@ -24,7 +24,7 @@ LIB = PKG / "libw4a16.so"
 BUILD_DIR = PKG / "_build"
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "skinny.hip", "mid.hip", "gemm.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "skinny.hip", "mid.hip", "gemm.hip", "w4a8.hip"]
 # Per-file extra flags (none at present).
 FILE_FLAGS: dict = {}
 

@@ -207,4 +207,30 @@ w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x
     return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
 }
 
+w4a16_status_t w4a16_quantize_act_i8(const void* x, int64_t M, int64_t K, int8_t* xq, float* ascale, float* xsum,
+                                     hipStream_t stream) {
+    if (M <= 0 || K <= 0 || M > kMaxDim || K > kMaxDim || K % kGroupG128 != 0) return W4A16_ERR_INVALID;
+    if (M * K >= ((int64_t)1 << 31)) return W4A16_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(xq) || !aligned16(ascale) || !aligned16(xsum)) return W4A16_ERR_INVALID;
+    w4a16::clear_stale_error();
+    return from_hip(w4a16::launch_quant_act_i8(static_cast<const uint16_t*>(x), M, K, xq, ascale, xsum, stream));
+}
+
+w4a16_status_t w4a16_gemm_w4a8(w4a16_format_t fmt, const int8_t* xq, const float* ascale, const float* xsum,
+                               int64_t M, const void* codes, const void* scales, const void* mins, int64_t N,
+                               int64_t K, void* y, hipStream_t stream) {
+    if (w4a16_status_t st = check_shape(fmt, N, K); st != W4A16_OK) return st;
+    if (M <= 0 || M > kMaxDim) return W4A16_ERR_INVALID;
+    if (w4a16_status_t st = check_packed(fmt, codes, scales, mins); st != W4A16_OK) return st;
+    if (!aligned16(xq) || !aligned16(ascale) || !aligned16(xsum) || !aligned16(y)) return W4A16_ERR_INVALID;
+    if (fmt != W4A16_FMT_G128_ASYM_BF16 || N % 4 != 0) return W4A16_ERR_UNSUPPORTED;
+    // the kernel's per-lane byte offsets are 32-bit
+    if (M * K >= ((int64_t)1 << 31) || (K / 8) * N * 4 >= ((int64_t)1 << 31) || (K / 128) * M * 4 >= ((int64_t)1 << 31))
+        return W4A16_ERR_UNSUPPORTED;
+    w4a16::clear_stale_error();
+    return from_hip(w4a16::launch_gemm_w4a8(xq, ascale, xsum, M, static_cast<const uint32_t*>(codes),
+                                            static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(mins),
+                                            N, K, static_cast<uint16_t*>(y), stream));
+}
+
 }  // extern "C"

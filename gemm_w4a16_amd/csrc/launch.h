@@ -60,4 +60,12 @@ hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes,
                             const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace,
                             hipStream_t stream);
 
+// W4A8: per-row int8 activations (xq [M][K], ascale [M], xsum [K/128][M]) and the int8-MFMA GEMM
+// against the G128 weights (N % 4 == 0).
+hipError_t launch_quant_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* ascale, float* xsum,
+                               hipStream_t stream);
+hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* xsum, int64_t M,
+                            const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K,
+                            uint16_t* y, hipStream_t stream);
+
 }  // namespace w4a16

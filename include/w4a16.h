@@ -166,6 +166,32 @@ w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x
 /* The M at and below which w4a16_matmul takes the GEMV path for the G128 format. */
 int64_t w4a16_matmul_gemv_cutoff(void);
 
+/* ---- W4A8: int8 activations against the same 4-bit weights ------------------------------------
+ * vidyal.ai "Low-Precision Kernels", "INT8 on a GeForce chip" and "The cost of quantizing
+ * activations": the activations are quantized to int8 per row on every call, the integer
+ * products are summed in 32 bits on the matrix cores, and the activation and weight scales are
+ * applied to those sums in the epilogue. */
+
+/* Per-row symmetric int8 quantization of bf16 activations x [M][K] (K % 128 == 0):
+ *   ascale [M]         a_m = max_k |x[m][k]| / 127 in fp32 (IEEE division); 1.0 for a zero row
+ *   xq     [M][K] int8 clamp(rint(x / a_m), -127, 127), ties to even (IEEE division)
+ *   xsum   [K/128][M]  fp32, the exact integer sum of xq over each group of 128 k (for the
+ *                      minimum term of the G128 weights)
+ * Bit-identical to the CPU definition.  All pointers 16-byte aligned device memory; M*K < 2^31.
+ * x must be finite (non-finite input is undefined). */
+w4a16_status_t w4a16_quantize_act_i8(const void* x, int64_t M, int64_t K, int8_t* xq, float* ascale, float* xsum,
+                                     hipStream_t stream);
+
+/* W4A8 product with G128 weights: y [M][N] bf16 = round_to_nearest_even(
+ *     a_m * sum_g (s[g][n] * sum_{k in g} xq[m][k] q[k][n] + min[g][n] * xsum[g][m])),
+ * the integer sums exact (v_mfma_i32_32x32x32_i8), the rest in fp32.  Inputs as written by
+ * w4a16_quantize_act_i8 for the same M and K.  G128 only (ERR_UNSUPPORTED otherwise); N % 4 == 0
+ * and the 32-bit offset limits M*K, K*N/2, (K/128)*M*4 < 2^31 (ERR_UNSUPPORTED otherwise).  No
+ * workspace; bitwise reproducible run to run. */
+w4a16_status_t w4a16_gemm_w4a8(w4a16_format_t fmt, const int8_t* xq, const float* ascale, const float* xsum,
+                               int64_t M, const void* codes, const void* scales, const void* mins, int64_t N,
+                               int64_t K, void* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -156,3 +156,23 @@ def test_w8_format_sizes_and_validation():
     assert _status(g, W8, F32, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
     assert _status(w.w4a16_gemm, W8, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) \
         == w.W4A16_ERR_UNSUPPORTED
+
+
+def test_w4a8_validation():
+    qa = w.w4a16_quantize_act_i8
+    assert _status(qa, FAKE, 0, 128, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID            # M = 0
+    assert _status(qa, FAKE, 4, 100, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID            # K % 128
+    assert _status(qa, FAKE + 8, 4, 128, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID        # misaligned x
+    assert _status(qa, FAKE, 4, 128, FAKE, None, FAKE, 0) == w.W4A16_ERR_INVALID            # null ascale
+    assert _status(qa, FAKE, 1 << 20, 1 << 12, FAKE, FAKE, FAKE, 0) == w.W4A16_ERR_INVALID  # M*K >= 2^31
+    g = w.w4a16_gemm_w4a8
+    assert _status(g, Q4, FAKE, FAKE, FAKE, 64, FAKE, FAKE, None, 256, 1024, FAKE, 0) \
+        == w.W4A16_ERR_UNSUPPORTED                                                           # G128 only
+    assert _status(g, G128, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 258, 1024, FAKE, 0) \
+        == w.W4A16_ERR_UNSUPPORTED                                                           # N % 4
+    assert _status(g, G128, FAKE, FAKE, FAKE, 64, FAKE, FAKE, None, 256, 1024, FAKE, 0) \
+        == w.W4A16_ERR_INVALID                                                               # no mins
+    assert _status(g, G128, FAKE, FAKE, FAKE + 4, 64, FAKE, FAKE, FAKE, 256, 1024, FAKE, 0) \
+        == w.W4A16_ERR_INVALID                                                               # misaligned xsum
+    assert _status(g, G128, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 256, 1024, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(g, G128, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 256, 1000, FAKE, 0) == w.W4A16_ERR_INVALID
