@@ -13,8 +13,9 @@
 //
 // w4a8_gemm_kernel -- y = a_m * sum_g (s_g,n * sum_k xq q + min_g,n * X_g,m), one group of 128 k
 // per k-tile:
-//  * block tile 128 x 128, 4 waves in a 2 x 2 grid; a wave owns 64 x 64 outputs as 2 x 2
-//    v_mfma_i32_32x32x32_i8 accumulators, restarted at zero every group;
+//  * block tile 128 x 128, 4 waves side by side along N; a wave owns 128 rows x 32 columns as four
+//    v_mfma_i32_32x32x32_i8 accumulators, restarted at zero every group, so each packed word is
+//    unpacked once per block;
 //  * every operand reaches LDS through direct-to-LDS copies issued two k-tiles ahead (three
 //    stages): the 128 x 128-byte activation tile (16-byte chunks XOR-swizzled by row pair, so
 //    the fragment reads are conflict-free), the 16 packed rows x 128 columns of weights as they
@@ -27,7 +28,13 @@
 //    w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F hold the even and odd codes as bytes, and two
 //    v_perm_b32 put them back in k order, matching the activation bytes;
 //  * after a group's 4 k-steps each int32 sum becomes fp32 (exact: |sum| < 2^18) and enters the
-//    fp32 accumulator as s * sum + min * X; the row scale multiplies the total once at the end.
+//    fp32 accumulator as s * sum (one convert and one fma per output); the minimum term
+//    sum_g min_g X_g is a [128 x G] x [G x 128] product of its own, run on v_mfma_f32_32x32x2f32
+//    two groups at a time into the same accumulators, so it costs no VALU work per output;
+//  * the row scale multiplies the total once at the end, and the tile leaves through LDS as
+//    whole rows (16-byte stores of consecutive columns).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -133,12 +140,13 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
                       const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                       const uint16_t* __restrict__ mins, uint16_t* __restrict__ y, int M, int N, int K) {
     __shared__ __attribute__((aligned(16))) char smem[kStages * kStage];
+    __shared__ float arow[kT];  // the block's row scales
     const int lane = lane_id(), wave = wave_id();
-    const int wm = wave & 1, wn = wave >> 1;
     const int l32 = lane & 31, kg = lane >> 5;
     const int n0 = blockIdx.x * kT, m0 = blockIdx.y * kT;
     const int T = K / kT;
     const uint32_t lds0 = w8_lds_addr(smem);
+    const int col = 32 * wave + l32;  // this lane's column in the tile (every row tile)
 
     // Per-lane source offsets of this wave's copies (the k-tile adds a uniform offset):
     //  A: copies j = 4 wave + i, rows 8 j .. 8 j + 7; lane l -> row 8 j + l / 8, LDS slot l % 8,
@@ -182,111 +190,150 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
         for (int i = 0; i < 4; ++i) w8_dma16(a_off[i], xa, sbase + kOffA + 1024u * (4 * wave + i));
         const uint32_t* cb = codes + (size_t)t * 16 * N;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int j = 2 * wave + i;
-            w8_dma16(b_off[i], cb, sbase + kOffB + (uint32_t)(kBCopy * j));
-        }
+        for (int i = 0; i < 2; ++i) w8_dma16(b_off[i], cb, sbase + kOffB + (uint32_t)(kBCopy * (2 * wave + i)));
         const char* sp = (const char*)small_src + (wave < 2 ? (size_t)t * N * 2 : (size_t)t * M * 4);
         w8_dma4(small_off, sp, sbase + small_lds);
     };
 
-    float yacc[2][2][16];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) yacc[rt][ct][e] = 0.0f;
-
-    // one group: 4 k-steps of 2 x 2 int8 MFMAs, then the fp32 epilogue of the group
-    auto compute = [&](int st) {
-        const char* s = smem + st * kStage;
-        i32x16_t acc[2][2];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            i32x4_t a[2], b[2];
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
-                const int r = 64 * wm + 32 * rt + l32;
-                const int c = (2 * ks + kg) ^ ((r >> 1) & 7);
-                a[rt] = *reinterpret_cast<const i32x4_t*>(s + kOffA + 128 * r + 16 * c);
-            }
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int n = 64 * wn + 32 * ct + l32;
-                const int j = 2 * ks + kg;  // the copy that holds packed rows 4 ks + 2 kg, + 1
-                const uint32_t* wp = reinterpret_cast<const uint32_t*>(s + kOffB + kBCopy * j) + n;
-                const uint32_t w0 = wp[0], w1 = wp[128];
-                const uint32_t lo0 = w0 & 0x0F0F0F0Fu, hi0 = (w0 >> 4) & 0x0F0F0F0Fu;
-                const uint32_t lo1 = w1 & 0x0F0F0F0Fu, hi1 = (w1 >> 4) & 0x0F0F0F0Fu;
-                b[ct] = i32x4_t{(int)__builtin_amdgcn_perm(hi0, lo0, 0x05010400u),
-                                (int)__builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
-                                (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u),
-                                (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
-            }
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    if (ks == 0)
-                        acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rt], b[ct], i32x16_t{}, 0, 0, 0);
-                    else
-                        acc[rt][ct] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[rt], b[ct], acc[rt][ct], 0, 0, 0);
-                }
-        }
-        // accumulator element e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4, column l % 32
-        const uint16_t* sc = reinterpret_cast<const uint16_t*>(s + kOffS);
-        const uint16_t* mn = reinterpret_cast<const uint16_t*>(s + kOffMn);
-        const float* X = reinterpret_cast<const float*>(s + kOffX);
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-            const int n = 64 * wn + 32 * ct + l32;
-            const float sv = bf16_bits_to_f32(sc[n]), mv = bf16_bits_to_f32(mn[n]);
-#pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 xs = *reinterpret_cast<const float4*>(X + 64 * wm + 32 * rt + 8 * q + 4 * kg);
-                    const float xv[4] = {xs.x, xs.y, xs.z, xs.w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int e = 4 * q + i;
-                        float v = __builtin_fmaf(sv, (float)acc[rt][ct][e], yacc[rt][ct][e]);
-                        yacc[rt][ct][e] = __builtin_fmaf(mv, xv[i], v);
-                    }
-                }
-        }
-    };
-
-    // Pipeline: k-tile t's copies were issued two k-tiles earlier into stage t % 3.  Before t's
-    // barrier each wave waits until only its 7 copies of t + 1 are in flight; after it, stage
-    // (t + 2) % 3 (read during t - 1) is free for t + 2.
     issue(0, 0);
     if (T > 1) issue(1, 1);
-    for (int t = 0; t < T; ++t) {
+    if (threadIdx.x < kT) arow[threadIdx.x] = ascale[min(m0 + (int)threadIdx.x, M - 1)];
+
+    // Lane offsets inside a stage.  Row 32 rt + l32 of the activation tile keeps its chunk c at
+    // slot c ^ ((l32 >> 1) & 7) (the row tile does not change the swizzle), so k-step ks reads at
+    // a_lane[ks] + 4096 rt; the packed words of copy 2 ks + kg at b_lane + 2 ks kBCopy.
+    uint32_t a_lane[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) a_lane[ks] = kOffA + 128u * l32 + 16u * ((2 * ks + kg) ^ ((l32 >> 1) & 7));
+    const uint32_t b_lane = kOffB + kBCopy * kg + 4u * col;
+
+    // fp32 accumulators, element e of row tile rt: row 32 rt + 8 (e / 4) + 4 kg + e % 4, column col
+    f32x16_t yacc[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) yacc[rt][e] = 0.0f;
+    // the minimum term sum_g min_g X_g on v_mfma_f32_32x32x2f32, two groups per instruction: A
+    // lane l holds X of row l % 32 and group 2 p + l / 32, B lane l the minimum of column l % 32 and
+    // the same group; an even group's values wait in xp / mp for the odd one
+    float xp[4], mp = 0.0f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) xp[rt] = 0.0f;
+
+    // Software pipeline over groups: the int32 sums of group t (acc[t & 1]) are computed while the
+    // previous group's (acc[(t - 1) & 1]) go through the fp32 epilogue, whose scale, minimum and
+    // row sums were read into registers (sv, mv, xc) before their stage could be overwritten.
+    i32x16_t acc[2][4];
+    float sv = 0.0f, mv = 0.0f, xc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto mfma_group = [&](auto par, const char* s) {
+        constexpr int P = decltype(par)::value;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const uint32_t* wp = reinterpret_cast<const uint32_t*>(s + b_lane + 2 * ks * kBCopy);
+            const uint32_t w0 = wp[0], w1 = wp[128];
+            const uint32_t lo0 = w0 & 0x0F0F0F0Fu, hi0 = (w0 >> 4) & 0x0F0F0F0Fu;
+            const uint32_t lo1 = w1 & 0x0F0F0F0Fu, hi1 = (w1 >> 4) & 0x0F0F0F0Fu;
+            const i32x4_t b = {(int)__builtin_amdgcn_perm(hi0, lo0, 0x05010400u),
+                               (int)__builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
+                               (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u),
+                               (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+                const i32x4_t av = *reinterpret_cast<const i32x4_t*>(s + a_lane[ks] + 4096 * rt);
+                if (ks == 0)
+                    acc[P][rt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, i32x16_t{}, 0, 0, 0);
+                else
+                    acc[P][rt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, acc[P][rt], 0, 0, 0);
+            }
+        }
+    };
+    // the epilogue of group g (parity P, odd when g is): s * sum, then the minimum term per pair
+    auto epilogue = [&](auto par) {
+        constexpr int P = decltype(par)::value;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) yacc[rt][e] = __builtin_fmaf(sv, (float)acc[P][rt][e], yacc[rt][e]);
+        if constexpr (P == 1) {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                yacc[rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg ? xc[rt] : xp[rt], kg ? mv : mp, yacc[rt], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) xp[rt] = xc[rt];
+            mp = mv;
+        }
+    };
+    auto read_params = [&](const char* s) {
+        sv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s + kOffS)[col]);
+        mv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s + kOffMn)[col]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) xc[rt] = reinterpret_cast<const float*>(s + kOffX)[32 * rt + l32];
+    };
+
+    // one k-tile t (stage t % 3 and parity t % 2 known at compile time): wait for its copies,
+    // barrier, request t + 2, the MFMAs of t, the epilogue of t - 1, then t's own parameters
+    auto ktile = [&](int t, auto st_c, auto par_c) {
+        constexpr int ST = decltype(st_c)::value, P = decltype(par_c)::value;
         if (t + 1 < T)
             w8_wait_vm<7>();
         else
             w8_wait_vm<0>();
         __syncthreads();
-        if (t + 2 < T) issue(t + 2, (t + 2) % kStages);
-        compute(t % kStages);
+        if (t + 2 < T) issue(t + 2, (ST + 2) % kStages);
+        const char* s = smem + ST * kStage;
+        mfma_group(std::integral_constant<int, P>{}, s);
+        if (t > 0) epilogue(std::integral_constant<int, 1 - P>{});
+        read_params(s);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (int t0 = 0; t0 < T; t0 += 6) {
+        ktile(t0, I0{}, I0{});
+        if (t0 + 1 < T) ktile(t0 + 1, I1{}, I1{});
+        if (t0 + 2 < T) ktile(t0 + 2, I2{}, I0{});
+        if (t0 + 3 < T) ktile(t0 + 3, I0{}, I1{});
+        if (t0 + 4 < T) ktile(t0 + 4, I1{}, I0{});
+        if (t0 + 5 < T) ktile(t0 + 5, I2{}, I1{});
+    }
+    // the last group's epilogue; an unpaired last (even) group pairs with zeros
+    if ((T - 1) & 1) {
+        epilogue(I1{});
+    } else {
+        epilogue(I0{});
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+            yacc[rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg ? 0.0f : xp[rt], kg ? 0.0f : mp, yacc[rt], 0, 0, 0);
     }
 
-    // y = bf16(a_m * acc): rows past M and columns past N are not stored
+    // y = bf16(a_m * acc) through LDS (the stages are free now) as whole rows: 16-byte stores of
+    // consecutive columns; rows past M and columns past N are not stored
+    __syncthreads();
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // [128][128 + 8] bf16
+    constexpr int kPitch = kT + 8;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const int row = m0 + 64 * wm + 32 * rt + 8 * (e / 4) + 4 * kg + (e % 4);
-            if (row >= M) continue;
-            const float am = ascale[row];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int col = n0 + 64 * wn + 32 * ct + l32;
-                if (col < N) y[(size_t)row * N + col] = f32_to_bf16_bits(am * yacc[rt][ct][e]);
-            }
+            const int r = 32 * rt + 8 * (e / 4) + 4 * kg + (e % 4);
+            tile[r * kPitch + col] = f32_to_bf16_bits(arow[r] * yacc[rt][e]);
         }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kT * (kT / 8); idx += 256) {
+        const int r = idx / (kT / 8), c8 = idx % (kT / 8);
+        const int row = m0 + r, c0 = n0 + 8 * c8;
+        if (row >= M || c0 >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kPitch + 8 * c8);
+        uint16_t* dst = y + (size_t)row * N + c0;
+        if ((N & 7) == 0) {
+            *reinterpret_cast<uint4*>(dst) = v;  // N % 8 == 0: in range and 16-byte aligned
+        } else {  // N % 4 == 0: 8-byte aligned halves, the second one only inside the row
+            *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+            if (c0 + 4 < N) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(v.z, v.w);
+        }
+    }
 }
 
 }  // namespace
