@@ -13,17 +13,16 @@
 //
 // w4a8_gemm_kernel -- y = a_m * sum_g (s_g,n * sum_k xq q + min_g,n * X_g,m), one group of 128 k
 // per k-tile:
-//  * block tile 128 x 128, 4 waves side by side along N; a wave owns 128 rows x 32 columns as four
-//    v_mfma_i32_32x32x32_i8 accumulators, restarted at zero every group, so each packed word is
-//    unpacked once per block;
+//  * block tile 128 x 256 (8 waves, one block per CU) where that still gives half the CUs a block,
+//    else 128 x 128 (4 waves, two blocks per CU); the waves sit side by side along N and each owns
+//    128 rows x 32 columns as four v_mfma_i32_32x32x32_i8 accumulators restarted at zero every
+//    group, so each packed word is unpacked once per block;
 //  * every operand reaches LDS through direct-to-LDS copies issued two k-tiles ahead (three
 //    stages): the 128 x 128-byte activation tile (16-byte chunks XOR-swizzled by row pair, so
-//    the fragment reads are conflict-free), the 16 packed rows x 128 columns of weights as they
-//    are stored (each copy of two packed rows 1152 bytes after the previous one, so that the two
-//    copies a k-step reads sit on different banks), the group's 128 scales and minimums, and the
-//    128 row sums X.  Each wave issues
-//    seven copies per k-tile and one `s_waitcnt vmcnt` before the k-tile's barrier waits for
-//    exactly its own copies of that k-tile;
+//    the fragment reads are conflict-free), the 16 packed rows of weights as they are stored (the
+//    pairs of packed rows 128 bytes apart, so that the two pairs a k-step reads sit on different
+//    banks), the group's scales and minimums, and the 128 row sums X.  One `s_waitcnt vmcnt`
+//    before each k-tile's barrier waits for exactly this wave's copies of that k-tile;
 //  * a lane's B fragment (32 k x 32 columns: 16 k of one column) is two consecutive packed words:
 //    w & 0x0F0F0F0F and (w >> 4) & 0x0F0F0F0F hold the even and odd codes as bytes, and two
 //    v_perm_b32 put them back in k order, matching the activation bytes;
@@ -95,16 +94,25 @@ __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __res
 
 // ---- GEMM ------------------------------------------------------------------------------------
 
-constexpr int kT = 128;                                // block tile (rows and columns), and BK
-constexpr int kOffA = 0;                               // 128 rows x 128 bytes
-constexpr int kOffB = kOffA + kT * kT;                 // 8 copies of 2 packed rows x 512 bytes,
-constexpr int kBCopy = 1152;                           //   1152 bytes apart
-constexpr int kOffS = kOffB + 8 * kBCopy;
-constexpr int kOffMn = kOffS + kT * 2;                 // 128 bf16 scales, then 128 bf16 minimums
-constexpr int kOffX = kOffMn + kT * 2;                 // 128 fp32 row sums
-constexpr int kStage = kOffX + kT * 4;                 // 26,624 bytes
+constexpr int kBM = 128;  // block rows, and the k-tile: one group of 128 k
 constexpr int kStages = 3;
-static_assert(kStage % 16 == 0, "stage alignment");
+
+// LDS stage of a 128 x BN block tile.
+template <int BN_>
+struct W8Layout {
+    static constexpr int BN = BN_;
+    static constexpr int OffA = 0;                      // 128 rows x 128 bytes, chunks swizzled
+    static constexpr int BCopy = 2 * BN * 4 + 128;      // packed rows 2j, 2j+1 (BN words each), 128 B apart
+    static constexpr int OffB = OffA + kBM * kBM;       //   from the next pair: the two pairs a k-step reads
+    static constexpr int OffS = OffB + 8 * BCopy;       //   sit on different banks
+    static constexpr int OffMn = OffS + BN * 2;         // BN bf16 scales, BN bf16 minimums
+    static constexpr int OffX = OffMn + BN * 2;         // 128 fp32 row sums
+    static constexpr int Stage = OffX + kBM * 4;
+    static constexpr int RowsPerB = 256 / BN;           // packed rows per 1-KB copy
+    static constexpr int BCopies = BN / 16;             // 1-KB copies of the 16 packed rows
+    static constexpr int NSmall = BN / 64 + 2;          // 256-byte copies: scales, minimums, row sums
+    static_assert(Stage % 16 == 0, "stage alignment");
+};
 
 __device__ __forceinline__ uint32_t w8_lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
@@ -135,156 +143,213 @@ __device__ __forceinline__ void w8_wait_vm() {
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+
+// NW waves side by side along N, each owning 32 columns: the block is 128 x 32 NW.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ ascale, const float* __restrict__ xsum,
                       const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
                       const uint16_t* __restrict__ mins, uint16_t* __restrict__ y, int M, int N, int K) {
-    __shared__ __attribute__((aligned(16))) char smem[kStages * kStage];
-    __shared__ float arow[kT];  // the block's row scales
+    constexpr int WCT = 1;  // 32-column MFMA tiles per wave
+    using L = W8Layout<32 * WCT * NW>;
+    constexpr int BN = L::BN;
+    constexpr int kACopies = 16 / NW, kBCopies = L::BCopies / NW;  // 1-KB copies per wave per k-tile
+    static_assert(kACopies * NW == 16 && kBCopies * NW == L::BCopies, "copies split evenly over the waves");
+    __shared__ __attribute__((aligned(16))) char smem[kStages * L::Stage];
+    __shared__ float arow[kBM];  // the block's row scales
     const int lane = lane_id(), wave = wave_id();
     const int l32 = lane & 31, kg = lane >> 5;
-    const int n0 = blockIdx.x * kT, m0 = blockIdx.y * kT;
-    const int T = K / kT;
+    const int n0 = blockIdx.x * BN, m0 = blockIdx.y * kBM;
+    const int T = K / kBM;
     const uint32_t lds0 = w8_lds_addr(smem);
-    const int col = 32 * wave + l32;  // this lane's column in the tile (every row tile)
 
-    // Per-lane source offsets of this wave's copies (the k-tile adds a uniform offset):
-    //  A: copies j = 4 wave + i, rows 8 j .. 8 j + 7; lane l -> row 8 j + l / 8, LDS slot l % 8,
-    //     which holds chunk (l % 8) ^ ((row >> 1) & 7) of the row's 128 bytes
-    uint32_t a_off[4];
+    // ---- this wave's copies of a k-tile (per-lane source offsets; the k-tile adds a uniform one)
+    //  A: copies j = kACopies wave + i, rows 8 j .. 8 j + 7; lane l -> row 8 j + l / 8, LDS slot
+    //     l % 8, which holds chunk (l % 8) ^ ((row >> 1) & 7) of the row's 128 bytes
+    uint32_t a_off[kACopies];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 8 * (4 * wave + i) + lane / 8;
+    for (int i = 0; i < kACopies; ++i) {
+        const int r = 8 * (kACopies * wave + i) + lane / 8;
         const int c = (lane % 8) ^ ((r >> 1) & 7);
         a_off[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)K + 16u * c;
     }
-    //  B: copies j = 2 wave + i: packed rows 2 j + lane / 32 of the group, columns 4 (lane % 32) ..
-    //     + 3 (past N: the last four columns, never stored)
-    uint32_t b_off[2];
+    //  B: copies j = kBCopies wave + i of 1 KB: packed rows RowsPerB j + lane / (64 / RowsPerB),
+    //     4 columns per lane (past N: the last four columns, never stored)
+    constexpr int kLanesPerRow = 64 / L::RowsPerB;
+    uint32_t b_off[kBCopies], b_lds[kBCopies];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int pr = 2 * (2 * wave + i) + lane / 32;
-        const int n = min(n0 + 4 * l32, N - 4);
+    for (int i = 0; i < kBCopies; ++i) {
+        const int j = kBCopies * wave + i;
+        const int pr0 = L::RowsPerB * j;
+        const int pr = pr0 + lane / kLanesPerRow;
+        const int n = min(n0 + 4 * (lane % kLanesPerRow), N - 4);
         b_off[i] = ((uint32_t)pr * (uint32_t)N + (uint32_t)n) * 4u;
+        b_lds[i] = __builtin_amdgcn_readfirstlane(L::OffB + L::BCopy * (pr0 / 2) + (pr0 % 2) * BN * 4);
     }
-    //  one 4-byte copy: wave 0 the scales, wave 1 the minimums (two columns per lane), waves 2
-    //  and 3 the row sums of rows 64 (wave - 2) + lane
-    const void* small_src;
-    uint32_t small_off, small_lds;
-    if (wave < 2) {
-        small_src = wave == 0 ? (const void*)scales : (const void*)mins;
-        small_off = (uint32_t)min(n0 + 2 * lane, N - 2) * 2u;
-        small_lds = wave == 0 ? kOffS : kOffMn;
-    } else {
-        small_src = xsum;
-        small_off = (uint32_t)min(m0 + 64 * (wave - 2) + lane, M - 1) * 4u;
-        small_lds = kOffX + 256 * (wave - 2);
-    }
-    small_lds = __builtin_amdgcn_readfirstlane(small_lds);
-
-    // the seven copies of k-tile t into stage st
-    auto issue = [&](int t, int st) {
-        const uint32_t sbase = lds0 + (uint32_t)(st * kStage);
-        const int8_t* xa = xq + (size_t)t * kT;
+    //  small 256-byte copies i = wave, wave + NW (of NSmall): the scales (BN / 128 of them, two
+    //  columns per lane), the minimums, then the row sums of rows 64 (i - BN / 64) + lane
+    constexpr int kSC = BN / 128;  // 256-byte copies of the scales (and of the minimums)
+    constexpr int kSmallMax = (L::NSmall + NW - 1) / NW;
+    const void* sm_src[kSmallMax];
+    uint32_t sm_off[kSmallMax], sm_lds[kSmallMax];
+    size_t sm_step[kSmallMax];
+    const int n_small = (L::NSmall - wave + NW - 1) / NW;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w8_dma16(a_off[i], xa, sbase + kOffA + 1024u * (4 * wave + i));
+    for (int u = 0; u < kSmallMax; ++u) {
+        const int i = wave + NW * u;
+        if (i < kSC) {
+            sm_src[u] = scales, sm_step[u] = (size_t)N * 2, sm_lds[u] = L::OffS + 256 * i;
+            sm_off[u] = (uint32_t)min(n0 + 128 * i + 2 * lane, N - 2) * 2u;
+        } else if (i < 2 * kSC) {
+            sm_src[u] = mins, sm_step[u] = (size_t)N * 2, sm_lds[u] = L::OffMn + 256 * (i - kSC);
+            sm_off[u] = (uint32_t)min(n0 + 128 * (i - kSC) + 2 * lane, N - 2) * 2u;
+        } else {
+            sm_src[u] = xsum, sm_step[u] = (size_t)M * 4, sm_lds[u] = L::OffX + 256 * (i - 2 * kSC);
+            sm_off[u] = (uint32_t)min(m0 + 64 * (i - 2 * kSC) + lane, M - 1) * 4u;
+        }
+        sm_lds[u] = __builtin_amdgcn_readfirstlane(sm_lds[u]);
+    }
+
+    auto issue = [&](int t, int st) __attribute__((always_inline)) {
+        const uint32_t sbase = lds0 + (uint32_t)(st * L::Stage);
+        const int8_t* xa = xq + (size_t)t * kBM;
+#pragma unroll
+        for (int i = 0; i < kACopies; ++i) w8_dma16(a_off[i], xa, sbase + L::OffA + 1024u * (kACopies * wave + i));
         const uint32_t* cb = codes + (size_t)t * 16 * N;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) w8_dma16(b_off[i], cb, sbase + kOffB + (uint32_t)(kBCopy * (2 * wave + i)));
-        const char* sp = (const char*)small_src + (wave < 2 ? (size_t)t * N * 2 : (size_t)t * M * 4);
-        w8_dma4(small_off, sp, sbase + small_lds);
+        for (int i = 0; i < kBCopies; ++i) w8_dma16(b_off[i], cb, sbase + b_lds[i]);
+#pragma unroll
+        for (int u = 0; u < kSmallMax; ++u)
+            if (u < n_small) w8_dma4(sm_off[u], (const char*)sm_src[u] + (size_t)t * sm_step[u], sbase + sm_lds[u]);
+    };
+    // copies per wave per k-tile: kACopies + kBCopies + n_small (n_small is 0, 1 or 2, wave-uniform)
+    constexpr int kBase = kACopies + kBCopies;
+    auto wait_next_only = [&]() __attribute__((always_inline)) {  // at most this wave's copies of one k-tile in flight
+        if (n_small == 2)
+            w8_wait_vm<kBase + 2>();
+        else if (n_small == 1)
+            w8_wait_vm<kBase + 1>();
+        else
+            w8_wait_vm<kBase>();
     };
 
     issue(0, 0);
     if (T > 1) issue(1, 1);
-    if (threadIdx.x < kT) arow[threadIdx.x] = ascale[min(m0 + (int)threadIdx.x, M - 1)];
+    if (threadIdx.x < kBM) arow[threadIdx.x] = ascale[min(m0 + (int)threadIdx.x, M - 1)];
 
     // Lane offsets inside a stage.  Row 32 rt + l32 of the activation tile keeps its chunk c at
     // slot c ^ ((l32 >> 1) & 7) (the row tile does not change the swizzle), so k-step ks reads at
-    // a_lane[ks] + 4096 rt; the packed words of copy 2 ks + kg at b_lane + 2 ks kBCopy.
+    // a_lane[ks] + 4096 rt; column tile ct's packed words of k-step ks at b_lane + 2 ks BCopy + 128 ct.
     uint32_t a_lane[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a_lane[ks] = kOffA + 128u * l32 + 16u * ((2 * ks + kg) ^ ((l32 >> 1) & 7));
-    const uint32_t b_lane = kOffB + kBCopy * kg + 4u * col;
+    for (int ks = 0; ks < 4; ++ks) a_lane[ks] = L::OffA + 128u * l32 + 16u * ((2 * ks + kg) ^ ((l32 >> 1) & 7));
+    const int colw = 32 * WCT * wave + l32;  // this lane's column in column tile 0 (tile ct: + 32 ct)
+    const uint32_t b_lane = L::OffB + L::BCopy * kg + 4u * colw;
 
-    // fp32 accumulators, element e of row tile rt: row 32 rt + 8 (e / 4) + 4 kg + e % 4, column col
-    f32x16_t yacc[4];
+    // fp32 accumulators, element e of tile (ct, rt): row 32 rt + 8 (e / 4) + 4 kg + e % 4, column colw + 32 ct
+    f32x16_t yacc[WCT][4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int ct = 0; ct < WCT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) yacc[rt][e] = 0.0f;
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) yacc[ct][rt][e] = 0.0f;
     // the minimum term sum_g min_g X_g on v_mfma_f32_32x32x2f32, two groups per instruction: A
     // lane l holds X of row l % 32 and group 2 p + l / 32, B lane l the minimum of column l % 32 and
     // the same group; an even group's values wait in xp / mp for the odd one
-    float xp[4], mp = 0.0f;
+    float xp[4], mp[WCT];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) xp[rt] = 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct) mp[ct] = 0.0f;
 
     // Software pipeline over groups: the int32 sums of group t (acc[t & 1]) are computed while the
     // previous group's (acc[(t - 1) & 1]) go through the fp32 epilogue, whose scale, minimum and
     // row sums were read into registers (sv, mv, xc) before their stage could be overwritten.
-    i32x16_t acc[2][4];
-    float sv = 0.0f, mv = 0.0f, xc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    i32x16_t acc[2][WCT][4];
+    float sv[WCT], mv[WCT], xc[4];
+#pragma unroll
+    for (int ct = 0; ct < WCT; ++ct) sv[ct] = mv[ct] = 0.0f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) xc[rt] = 0.0f;
 
-    auto mfma_group = [&](auto par, const char* s) {
-        constexpr int P = decltype(par)::value;
+    auto mfma_group = [&](auto slot, const char* s) __attribute__((always_inline)) {
+        constexpr int P = decltype(slot)::value;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const uint32_t* wp = reinterpret_cast<const uint32_t*>(s + b_lane + 2 * ks * kBCopy);
-            const uint32_t w0 = wp[0], w1 = wp[128];
-            const uint32_t lo0 = w0 & 0x0F0F0F0Fu, hi0 = (w0 >> 4) & 0x0F0F0F0Fu;
-            const uint32_t lo1 = w1 & 0x0F0F0F0Fu, hi1 = (w1 >> 4) & 0x0F0F0F0Fu;
-            const i32x4_t b = {(int)__builtin_amdgcn_perm(hi0, lo0, 0x05010400u),
-                               (int)__builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
-                               (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u),
-                               (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
+            i32x4_t b[WCT];
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) {
+                const uint32_t* wp = reinterpret_cast<const uint32_t*>(s + b_lane + 2 * ks * L::BCopy + 128 * ct);
+                const uint32_t w0 = wp[0], w1 = wp[BN];
+                const uint32_t lo0 = w0 & 0x0F0F0F0Fu, hi0 = (w0 >> 4) & 0x0F0F0F0Fu;
+                const uint32_t lo1 = w1 & 0x0F0F0F0Fu, hi1 = (w1 >> 4) & 0x0F0F0F0Fu;
+                b[ct] = i32x4_t{(int)__builtin_amdgcn_perm(hi0, lo0, 0x05010400u),
+                                (int)__builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
+                                (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u),
+                                (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
+            }
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) {
                 const i32x4_t av = *reinterpret_cast<const i32x4_t*>(s + a_lane[ks] + 4096 * rt);
-                if (ks == 0)
-                    acc[P][rt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, i32x16_t{}, 0, 0, 0);
-                else
-                    acc[P][rt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b, acc[P][rt], 0, 0, 0);
+#pragma unroll
+                for (int ct = 0; ct < WCT; ++ct) {
+                    if (ks == 0)
+                        acc[P][ct][rt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b[ct], i32x16_t{}, 0, 0, 0);
+                    else
+                        acc[P][ct][rt] = __builtin_amdgcn_mfma_i32_32x32x32_i8(av, b[ct], acc[P][ct][rt], 0, 0, 0);
+                }
             }
         }
     };
-    // the epilogue of group g (parity P, odd when g is): s * sum, then the minimum term per pair
-    auto epilogue = [&](auto par) {
-        constexpr int P = decltype(par)::value;
+    // the epilogue of a group of parity P whose sums are in acc[A]: s * sum (each int32 sum exact
+    // in fp32: |sum| < 2^18), then the minimum term once per pair of groups
+    auto epilogue = [&](auto slot, auto par) __attribute__((always_inline)) {
+        constexpr int A = decltype(slot)::value, P = decltype(par)::value;
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) yacc[rt][e] = __builtin_fmaf(sv, (float)acc[P][rt][e], yacc[rt][e]);
-        if constexpr (P == 1) {
+        for (int ct = 0; ct < WCT; ++ct)
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
-                yacc[rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg ? xc[rt] : xp[rt], kg ? mv : mp, yacc[rt], 0, 0, 0);
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    yacc[ct][rt][e] = __builtin_fmaf(sv[ct], (float)acc[A][ct][rt][e], yacc[ct][rt][e]);
+        if constexpr (P == 1) {
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct)
+#pragma unroll
+                for (int rt = 0; rt < 4; ++rt)
+                    yacc[ct][rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg ? xc[rt] : xp[rt], kg ? mv[ct] : mp[ct],
+                                                                        yacc[ct][rt], 0, 0, 0);
         } else {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt) xp[rt] = xc[rt];
-            mp = mv;
+#pragma unroll
+            for (int ct = 0; ct < WCT; ++ct) mp[ct] = mv[ct];
         }
     };
-    auto read_params = [&](const char* s) {
-        sv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s + kOffS)[col]);
-        mv = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s + kOffMn)[col]);
+    auto read_params = [&](const char* s) __attribute__((always_inline)) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) xc[rt] = reinterpret_cast<const float*>(s + kOffX)[32 * rt + l32];
+        for (int ct = 0; ct < WCT; ++ct) {
+            sv[ct] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s + L::OffS)[colw + 32 * ct]);
+            mv[ct] = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(s + L::OffMn)[colw + 32 * ct]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) xc[rt] = reinterpret_cast<const float*>(s + L::OffX)[32 * rt + l32];
     };
 
     // one k-tile t (stage t % 3 and parity t % 2 known at compile time): wait for its copies,
     // barrier, request t + 2, the MFMAs of t, the epilogue of t - 1, then t's own parameters
-    auto ktile = [&](int t, auto st_c, auto par_c) {
+    auto ktile = [&](int t, auto st_c, auto par_c) __attribute__((always_inline)) {
         constexpr int ST = decltype(st_c)::value, P = decltype(par_c)::value;
         if (t + 1 < T)
-            w8_wait_vm<7>();
+            wait_next_only();
         else
             w8_wait_vm<0>();
         __syncthreads();
         if (t + 2 < T) issue(t + 2, (ST + 2) % kStages);
-        const char* s = smem + ST * kStage;
+        const char* s = smem + ST * L::Stage;
         mfma_group(std::integral_constant<int, P>{}, s);
-        if (t > 0) epilogue(std::integral_constant<int, 1 - P>{});
+        if (t > 0) epilogue(std::integral_constant<int, 1 - P>{}, std::integral_constant<int, 1 - P>{});
         read_params(s);
     };
     using I0 = std::integral_constant<int, 0>;
@@ -300,29 +365,35 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
     }
     // the last group's epilogue; an unpaired last (even) group pairs with zeros
     if ((T - 1) & 1) {
-        epilogue(I1{});
+        epilogue(I1{}, I1{});
     } else {
-        epilogue(I0{});
+        epilogue(I0{}, I0{});
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
-            yacc[rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg ? 0.0f : xp[rt], kg ? 0.0f : mp, yacc[rt], 0, 0, 0);
+        for (int ct = 0; ct < WCT; ++ct)
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt)
+                yacc[ct][rt] = __builtin_amdgcn_mfma_f32_32x32x2f32(kg ? 0.0f : xp[rt], kg ? 0.0f : mp[ct],
+                                                                    yacc[ct][rt], 0, 0, 0);
     }
 
     // y = bf16(a_m * acc) through LDS (the stages are free now) as whole rows: 16-byte stores of
     // consecutive columns; rows past M and columns past N are not stored
     __syncthreads();
-    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // [128][128 + 8] bf16
-    constexpr int kPitch = kT + 8;
+    constexpr int kPitch = BN + 8;
+    static_assert(kBM * kPitch * 2 <= kStages * L::Stage, "the output tile fits in the stages");
+    uint16_t* tile = reinterpret_cast<uint16_t*>(smem);  // [128][BN + 8] bf16
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
+    for (int ct = 0; ct < WCT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int r = 32 * rt + 8 * (e / 4) + 4 * kg + (e % 4);
-            tile[r * kPitch + col] = f32_to_bf16_bits(arow[r] * yacc[rt][e]);
-        }
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = 32 * rt + 8 * (e / 4) + 4 * kg + (e % 4);
+                tile[r * kPitch + colw + 32 * ct] = f32_to_bf16_bits(arow[r] * yacc[ct][rt][e]);
+            }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < kT * (kT / 8); idx += 256) {
-        const int r = idx / (kT / 8), c8 = idx % (kT / 8);
+    for (int idx = threadIdx.x; idx < kBM * (BN / 8); idx += 64 * NW) {
+        const int r = idx / (BN / 8), c8 = idx % (BN / 8);
         const int row = m0 + r, c0 = n0 + 8 * c8;
         if (row >= M || c0 >= N) continue;
         const uint4 v = *reinterpret_cast<const uint4*>(tile + r * kPitch + 8 * c8);
@@ -348,9 +419,17 @@ hipError_t launch_quant_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* xsum, int64_t M,
                             const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K,
                             uint16_t* y, hipStream_t stream) {
-    const dim3 grid((unsigned)((N + kT - 1) / kT), (unsigned)((M + kT - 1) / kT));
-    hipLaunchKernelGGL(w4a8_gemm_kernel, grid, dim3(256), 0, stream, xq, ascale, xsum, codes, scales, mins, y, (int)M,
-                       (int)N, (int)K);
+    const int64_t mt = (M + kBM - 1) / kBM;
+    // 128 x 256 tiles (8 waves, one block per CU) when they still give half the CUs a block
+    if ((N + 255) / 256 * mt >= 128) {
+        const dim3 grid((unsigned)((N + 255) / 256), (unsigned)mt);
+        hipLaunchKernelGGL((w4a8_gemm_kernel<8>), grid, dim3(512), 0, stream, xq, ascale, xsum, codes, scales, mins,
+                           y, (int)M, (int)N, (int)K);
+    } else {
+        const dim3 grid((unsigned)((N + 127) / 128), (unsigned)mt);
+        hipLaunchKernelGGL((w4a8_gemm_kernel<4>), grid, dim3(256), 0, stream, xq, ascale, xsum, codes, scales, mins,
+                           y, (int)M, (int)N, (int)K);
+    }
     return hipGetLastError();
 }
 

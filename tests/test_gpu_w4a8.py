@@ -75,6 +75,30 @@ def test_gemm_w4a8_parity(M, N, K):
         np.testing.assert_array_equal(y[1], 0)   # the zero row: a = 1, every code 0, y exactly 0
 
 
+@pytest.mark.parametrize("M,N,K", [(1024, 4096, 256), (257, 11268, 128), (520, 8196, 640)])
+def test_gemm_w4a8_wide_tiles(M, N, K):
+    """Shapes that take the 128 x 256 tiles (at least 128 of them): ragged M and N (N % 8 == 4 in
+    the last), one to five groups.  Sampled outputs against the oracle, all outputs against an fp32
+    GPU product of the same quantized activations and the GPU's own dequantized weights."""
+    say(f"gemm_w4a8 wide M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=99)
+    x = _activation_rows(M, K, seed=100)
+    packed = gpu_pack(G128, W)
+    xq, a, xs = gpu_quantize(x)
+    y = bf16_f32(gpu_w4a8(xq, a, xs, packed, M, N, K))
+    rq, ra, _ = oracle.quantize_act_i8(x)
+    rng = np.random.default_rng(101)
+    rows = np.concatenate([rng.integers(0, M, 600), [M - 1] * 4, [0, 1, 2, 3]])
+    cols = np.concatenate([rng.integers(0, N, 600), [N - 1, N - 2, N - 3, N - 4], [N - 1] * 4])
+    ref = oracle.matmul_w4a8_at(rq, ra, *oracle.quantize_g128(W), rows, cols)
+    assert rel_err(y[rows, cols], ref) <= TOL
+    What = torch.empty((N, K), dtype=torch.float32, device="cuda")
+    w.w4a16_dequant(G128, *packed, N, K, w.W4A16_FP32, What)
+    ref_all = ((xq.float() * a[:, None]) @ What.T).double().cpu().numpy()
+    assert rel_err(y, ref_all) <= TOL
+    np.testing.assert_array_equal(y[1], 0)
+
+
 def test_w4a8_end_to_end_and_repeatable():
     """Quantize on the GPU, then the GEMM: equal to the oracle chain, and bit-identical run to run."""
     M, N, K = 96, 384, 1024
