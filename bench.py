@@ -218,12 +218,57 @@ def bench_q4(steps, warmup):
     st = Setup(w.W4A16_FMT_Q4_B32_SYM_FP16, wl.M, wl.N, wl.K, x, W, R)
     del W
     wall, ev = time_steps(st, steps, warmup)
-    return {
+    out = {
         "workload": wl.name, "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R, "steps": steps,
         "weight_bytes": st.weight_bytes, "us_per_launch_events": ev / steps * 1e6,
         "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
         "frac_hbm_peak": st.weight_bytes * steps / ev / 1e9 / HBM_PEAK_GBS,
     }
+    out["fp16_weight_gemv"] = fp16_gemv_comparator(st, wl, steps)
+    return out
+
+
+def fp16_gemv_comparator(st, wl, steps):
+    """Context for the Q4 GEMV (thuongvuho.com, "Why My 4-Bit CUDA Kernel Wasn't Faster", measures
+    its kernels against a GEMV over fp16 weights): the same product with the GPU's own dequantized
+    weights in fp16 (512 MB, larger than the Infinity Cache, so every call reads them from HBM)
+    through torch.matmul."""
+    import torch
+    w = st.w
+    Wh = torch.empty((wl.N, wl.K), dtype=torch.int16, device="cuda")
+    w.w4a16_dequant(w.W4A16_FMT_Q4_B32_SYM_FP16, *st.copies[0], wl.N, wl.K, w.W4A16_FP16, Wh)
+    Wt = Wh.view(torch.float16)
+    xh = st.x.view(torch.float16).reshape(wl.K, 1)
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < WARM_SECONDS:
+        for _ in range(steps):
+            yh = torch.matmul(Wt, xh)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        yh = torch.matmul(Wt, xh)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1e3 / steps
+    nbytes = wl.N * wl.K * 2
+    del Wh, Wt, yh
+    return {"us": t * 1e6, "weight_bytes": nbytes, "gbs": nbytes / t / 1e9}
+
+
+def bench_decode_warm(steps, warmup, W):
+    """The decode GEMV with ONE weight copy, which stays resident in the 256 MB Infinity Cache:
+    a warm number, reported beside (never instead of) the cold, rotated-copy headline."""
+    import gemm_w4a16_amd as w
+    import workloads
+    wl = workloads.DECODE
+    _, x = workloads.inputs(wl)
+    st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, 1)
+    wall, ev = time_steps(st, steps, warmup)
+    return {"workload": wl.name + "_warm", "weight_copies": 1, "steps": steps,
+            "us_per_launch_events": ev / steps * 1e6,
+            "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
+            "cache": "weights resident in the 256 MB Infinity Cache"}
 
 
 def bench_rowfmt(wl, fmt, steps, warmup, W=None):
@@ -419,6 +464,9 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_extra and args.only is None:
         extra = {}
+        log("decode, warm (one weight copy)")
+        extra["decode_warm_m1"] = bench_decode_warm(340, 34, W)
+        torch.cuda.empty_cache()
         log("prefill M=1024")
         extra["prefill_m1024"] = bench_prefill(20, 3)
         torch.cuda.empty_cache()
