@@ -13,6 +13,12 @@ constexpr int64_t kBlockQ4 = 32;
 constexpr int64_t kW8RowAlign = 16;  // int8 rows are whole 16-byte loads
 // Largest extents the kernels index with 32-bit ints (element offsets stay 64-bit).
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
+// Largest N and K this build runs: the kernels address a tile's operands as a 64-bit base plus a
+// 32-bit per-lane byte offset, which spans up to 16 * N bytes of packed words (a lane's rows in
+// the small-M kernels) and 512 * K bytes of activations (a 256-row GEMM tile).  Both limits are
+// far above any layer shape (67 M output columns, 4 M inputs).
+constexpr int64_t kMaxN = (int64_t)1 << 26;
+constexpr int64_t kMaxK = (int64_t)1 << 22;
 // M at and below which w4a16_matmul uses the GEMV path for G128 (from the batch sweep).
 constexpr int64_t kGemvCutoff = 16;
 
@@ -34,6 +40,7 @@ w4a16_status_t check_shape(w4a16_format_t fmt, int64_t N, int64_t K) {
     if (!valid_format(fmt)) return W4A16_ERR_INVALID;
     if (N <= 0 || K <= 0 || N > kMaxDim || K > kMaxDim) return W4A16_ERR_INVALID;
     if (K % group_of(fmt) != 0) return W4A16_ERR_INVALID;
+    if (N > kMaxN || K > kMaxK) return W4A16_ERR_UNSUPPORTED;
     return W4A16_OK;
 }
 

@@ -34,7 +34,10 @@
  *    a call clears the calling thread's pending HIP error (hipGetLastError), which may have
  *    been left by an earlier, unrelated runtime call, so that only its own launches are judged.
  *  - Every pointer must be 16-byte aligned; arrays are dense and row-major as documented.
- *  - Sizes are int64_t; M, N, K must be positive.  N needs no particular multiple.
+ *  - Sizes are int64_t; M, N, K must be positive and at most 2^30 (W4A16_ERR_INVALID otherwise).
+ *    N needs no particular multiple.  N above 2^26 or K above 2^22 returns
+ *    W4A16_ERR_UNSUPPORTED: the kernels address operands as a 64-bit base plus a 32-bit
+ *    per-lane byte offset.
  *  - Weights given to the quantizers must be finite (non-finite input is undefined).
  */
 #ifndef W4A16_H

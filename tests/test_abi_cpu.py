@@ -60,6 +60,26 @@ def test_packed_sizes_rejects_bad_shapes(fmt, N, K):
     assert e.value.status == w.W4A16_ERR_INVALID
 
 
+def test_extents_past_the_32_bit_offsets_are_unsupported():
+    """N above 2^26 or K above 2^22 would overflow the kernels' 32-bit per-lane byte offsets: every
+    entry point refuses them before any launch (the limits themselves are accepted)."""
+    big_n, big_k = (1 << 26) + 64, (1 << 22) + 128
+    assert w.w4a16_packed_sizes(G128, 1 << 26, 128)[0] == (1 << 26) * 64
+    assert w.w4a16_packed_sizes(G128, 64, 1 << 22)[0] == 64 * (1 << 21)
+    for fmt, n, k in [(G128, big_n, 128), (G128, 64, big_k), (Q4, big_n, 32), (Q4, 64, big_k)]:
+        assert _status(w.w4a16_packed_sizes, fmt, n, k) == w.W4A16_ERR_UNSUPPORTED
+    mins = lambda fmt: FAKE if fmt == G128 else None
+    act = lambda fmt: BF16 if fmt == G128 else F16
+    for fmt, n, k in [(G128, big_n, 128), (G128, 64, big_k), (Q4, 64, big_k)]:
+        assert _status(w.w4a16_gemv, fmt, act(fmt), FAKE, 1, FAKE, FAKE, mins(fmt), n, k, FAKE, 0) \
+            == w.W4A16_ERR_UNSUPPORTED
+        assert _status(w.w4a16_quantize_pack, fmt, FAKE, n, k, FAKE, FAKE, mins(fmt), 0) == w.W4A16_ERR_UNSUPPORTED
+        assert _status(w.w4a16_dequant, fmt, FAKE, FAKE, mins(fmt), n, k, BF16, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    for n, k in [(big_n, 128), (64, big_k)]:
+        assert _status(w.w4a16_gemm, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, n, k, FAKE, FAKE, 1 << 40, 0) \
+            == w.W4A16_ERR_UNSUPPORTED
+
+
 def _status(fn, *args):
     try:
         fn(*args)
