@@ -179,7 +179,7 @@ def test_g128_layout_is_k8_by_n():
 
 def test_g128_grid_reconstruction_exact():
     """A group on the grid m + j*s with bf16-exact m, s gives codes j and decodes to W bit for
-    bit; the group min decodes to exactly the stored minimum (survey pin 3)."""
+    bit; the group min decodes to exactly the stored minimum (code 0 gives fma(0, s, m) = m)."""
     rng = np.random.default_rng(7)
     for m_val, s_val in [(-0.125, 2.0 ** -6), (0.5, 2.0 ** -3), (-3.0, 0.375), (0.0, 2.0 ** -10),
                          (-0.0078125, 0.0078125 * 3)]:
@@ -224,7 +224,7 @@ def test_g128_codes_are_nearest_levels_bruteforce():
 def test_g128_codes_clamped_where_bf16_parameters_overshoot():
     """Groups in a narrow band far from zero: bf16(min) can lie more than half a step from the
     true minimum (and bf16(s) slightly off), so (w - m_b)/s_b leaves [0, 15] at the ends.  The
-    clamp of the codes (survey reading o1) must then give the nearest representable level,
+    clamp of the codes (taken with the stored bf16 scale and minimum) must then give the nearest level,
     checked by brute force -- an unclamped or wrapped code would be far from every level."""
     rng = np.random.default_rng(5)
     rows = []
@@ -253,7 +253,7 @@ def test_g128_scale_and_min_definition():
 
 
 def test_g128_error_bound_every_group():
-    """|W - w_hat| <= s/2 up to the bf16 rounding of s and min (survey reading o11), on every group
+    """|W - w_hat| <= s/2 up to the bf16 rounding of s and min (the round-to-nearest bound), on every group
     of the tiny workload and of a slice of the decode workload with its x20 outliers."""
     for W in (workloads.inputs(workloads.TINY)[0], workloads.weights(512, 4096, outliers=True)):
         codes, scales, mins = oracle.quantize_g128(W)
