@@ -2,7 +2,7 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                    [--only decode|prefill|q4|sweep|zp|w8|w4a8]
+                    [--only decode|prefill|q4|sweep|zp|w8|w4a8|w4a8_decode]
 
 A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one batch of seeded
 synthetic input, with packed weights, activations and output already resident in HBM.  The
@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=170)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -352,6 +352,48 @@ def bench_w4a8(steps, warmup):
     return out
 
 
+class W4A8DecodeSetup(Setup):
+    """The decode shape (M=1) as W4A8: the row quantized to int8, then the few-row int8-MFMA
+    product against the same G128 weights, rotated over cold copies like the W4A16 decode."""
+
+    def __init__(self, wl, W, x_bits, copies, gemm_only: bool):
+        import gemm_w4a16_amd as w
+        super().__init__(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x_bits, W, copies)
+        self.gemm_only = gemm_only
+        self.q = w.alloc_act_i8(wl.M, wl.K)
+        w.w4a16_quantize_act_i8(self.x, wl.M, wl.K, *self.q)
+
+    def step(self, i):
+        w = self.w
+        c, s, m = self.copies[i % len(self.copies)]
+        if not self.gemm_only:
+            w.w4a16_quantize_act_i8(self.x, self.M, self.K, *self.q)
+        w.w4a16_gemm_w4a8(self.fmt, *self.q, self.M, c, s, m, self.N, self.K, self.y)
+
+
+def bench_w4a8_decode(steps, warmup, W=None):
+    """W4A8 at the decode shape (M=1, K=4096, N=14336), cold weights: quantize + product per step,
+    and the product alone as effective weight GB/s against the HBM peak."""
+    import workloads
+    wl = workloads.DECODE
+    W0, x = workloads.inputs(wl)
+    W = W0 if W is None else W
+    import gemm_w4a16_amd as w
+    c, s, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl.N, wl.K)
+    R = copies_for(c + s + m)
+    out = {"workload": "w4a8_gemv_m1_k4096_n14336", "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R,
+           "steps": steps}
+    for gemm_only in (False, True):
+        st = W4A8DecodeSetup(wl, W, x, R, gemm_only)
+        wall, ev = time_steps(st, steps, warmup)
+        t = ev / steps
+        key = "gemm_only" if gemm_only else "quantize_and_gemm"
+        out[key] = {"us_per_step_events": t * 1e6, "effective_weight_gbs": st.weight_bytes / t / 1e9,
+                    "frac_hbm_peak": st.weight_bytes / t / 1e9 / HBM_PEAK_GBS}
+        del st
+    return out
+
+
 def bench_sweep(steps, warmup, W=None):
     import gemm_w4a16_amd as w
     import workloads
@@ -425,7 +467,7 @@ def main():
         copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
         fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp, "w8": bench_w8,
-              "w4a8": bench_w4a8}[args.only]
+              "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode}[args.only]
         print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
         return
 
@@ -484,6 +526,9 @@ def main():
         torch.cuda.empty_cache()
         log("W4A8 at the prefill shape")
         extra["w4a8_m1024"] = bench_w4a8(20, 3)
+        torch.cuda.empty_cache()
+        log("W4A8 at the decode shape")
+        extra["w4a8_decode_m1"] = bench_w4a8_decode(340, 34, W)
         torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline and args.only is None:

@@ -32,6 +32,8 @@
 //    two groups at a time into the same accumulators, so it costs no VALU work per output;
 //  * the row scale multiplies the total once at the end, and the tile leaves through LDS as
 //    whole rows (16-byte stores of consecutive columns).
+//
+// w4a8_rows16_kernel -- the same sum for 1..16 rows, where the weight stream sets the time (below).
 #include <type_traits>
 
 #include "device_common.h"
@@ -407,6 +409,153 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
     }
 }
 
+// ---- 1..16 rows: the weights streamed straight into registers -----------------------------------
+//
+// w4a8_rows16_kernel -- the same sum, y = a_m * sum_g (s_g,n * sum_k xq q + min_g,n * X_g,m), for a
+// few rows, where the work is the weight stream (HBM-bound) rather than the products.  A block of 16
+// waves owns 64 columns and all of K, the groups dealt over the waves (two per wave per 4096 k);
+// every load of a pass (16 bytes of 4 adjacent columns of one packed row per lane, the rows' 16-byte
+// activation chunks, the group's scales, minimums and row sums) is issued before any math, in the
+// order it is used.  Per group, a lane's v_mfma_i32_16x16x64_i8 B fragment is 16 k of one column,
+// two packed words unpacked to bytes in k order as in the GEMM, and its A fragment the same 16 k of
+// one row (for a single row staged per wave in LDS: the fragments of all 16 lanes of a lane group
+// are the same bytes, and loading them from memory would request them 16 times); the group
+// epilogue is one convert and two fma per output.  The waves' sums are added
+// through LDS in wave order, so the result is reproducible run to run.
+constexpr int kR16Waves = 16;
+constexpr int kR16Gpp = 2;  // groups per wave per pass: a pass covers 32 groups (4096 k)
+
+// MR: rows the accumulator layout keeps (M <= MR; 1, 4 or 16).  N % 4 == 0.
+template <int MR>
+__global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
+    const int8_t* __restrict__ xq, const float* __restrict__ ascale, const float* __restrict__ xsum,
+    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
+    uint16_t* __restrict__ y, int M, int N, int K) {
+    constexpr int E = MR == 1 ? 1 : 4;  // D rows per lane that can be real (row 4 (lane / 16) + e)
+    constexpr int TPL = 4, COLS = 64;
+    __shared__ float part[kR16Waves][MR][COLS];
+    // one row: each wave stages its groups' 128-byte activation runs in LDS with one 4-byte load
+    // per lane, so that the A fragments cost no vector-memory requests of their own
+    __shared__ __attribute__((aligned(16))) uint32_t xw[MR == 1 ? kR16Waves : 1][kR16Gpp * 32];
+    const int lane = lane_id(), wave = wave_id();
+    const int lr = lane & 15, lg = lane >> 4;
+    const int n0 = blockIdx.x * COLS;
+    const int G = K >> 7;
+    // this lane's 4 adjacent columns; a lane past N re-reads the last 4 and never stores
+    const int cbase = min(n0 + TPL * lr, N - TPL);
+    // A row of this lane (rows past M repeat the last one: their outputs are never stored) and the
+    // D rows it holds
+    const int8_t* xrow = xq + (size_t)min(lr, M - 1) * K + 16 * lg;
+    int drow[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) drow[e] = min(4 * lg + e, M - 1);
+    // lane byte offset inside a pair of packed rows: rows 2 lg, 2 lg + 1 of the k-step's eight
+    const uint32_t lane_off = ((uint32_t)(2 * lg) * (uint32_t)N + (uint32_t)cbase) * 4u;
+
+    float yacc[TPL][E];
+#pragma unroll
+    for (int t = 0; t < TPL; ++t)
+#pragma unroll
+        for (int e = 0; e < E; ++e) yacc[t][e] = 0.0f;
+
+    for (int p0 = 0; p0 < G; p0 += kR16Waves * kR16Gpp) {
+        int gj[kR16Gpp];
+        float live[kR16Gpp];
+#pragma unroll
+        for (int j = 0; j < kR16Gpp; ++j) {
+            const int g = p0 + wave + kR16Waves * j;
+            live[j] = g < G ? 1.0f : 0.0f;  // a clamped duplicate group contributes nothing
+            gj[j] = min(g, G - 1);
+        }
+        // all loads of the pass, in the order they are used
+        i32x4_t xa[kR16Gpp][2];
+        uint2 sf[kR16Gpp], mf[kR16Gpp];
+        float xs[kR16Gpp][E];
+        u32x4_t w[kR16Gpp][2][2];  // [group][k-step][packed row of the pair], 4 columns each
+        uint32_t x1 = 0;
+        if constexpr (MR == 1) {
+            static_assert(kR16Gpp * 32 == 64, "one dword of activations per lane");
+            x1 = *reinterpret_cast<const uint32_t*>(xq + gj[lane >> 5] * 128 + 4 * (lane & 31));
+        }
+#pragma unroll
+        for (int j = 0; j < kR16Gpp; ++j) {
+            if constexpr (MR != 1) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    xa[j][ks] = *reinterpret_cast<const i32x4_t*>(xrow + gj[j] * 128 + 64 * ks);
+            }
+            sf[j] = *reinterpret_cast<const uint2*>(scales + (size_t)gj[j] * N + cbase);
+            mf[j] = *reinterpret_cast<const uint2*>(mins + (size_t)gj[j] * N + cbase);
+#pragma unroll
+            for (int e = 0; e < E; ++e) xs[j][e] = xsum[(size_t)gj[j] * M + drow[e]];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const char* row = reinterpret_cast<const char*>(codes + (size_t)(16 * gj[j] + 8 * ks + h) * N);
+                    w[j][ks][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + lane_off));
+                }
+        }
+        if constexpr (MR == 1) {
+            xw[wave][lane] = x1;  // read back by this wave only, after its own write
+#pragma unroll
+            for (int j = 0; j < kR16Gpp; ++j)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+                    xa[j][ks] = *reinterpret_cast<const i32x4_t*>(&xw[wave][32 * j + 16 * ks + 4 * lg]);
+        }
+#pragma unroll
+        for (int j = 0; j < kR16Gpp; ++j) {
+            i32x4_t acc[TPL];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int t = 0; t < TPL; ++t) {
+                    const uint32_t w0 = w[j][ks][0][t], w1 = w[j][ks][1][t];
+                    const uint32_t lo0 = w0 & 0x0F0F0F0Fu, hi0 = (w0 >> 4) & 0x0F0F0F0Fu;
+                    const uint32_t lo1 = w1 & 0x0F0F0F0Fu, hi1 = (w1 >> 4) & 0x0F0F0F0Fu;
+                    const i32x4_t b = {(int)__builtin_amdgcn_perm(hi0, lo0, 0x05010400u),
+                                       (int)__builtin_amdgcn_perm(hi0, lo0, 0x07030602u),
+                                       (int)__builtin_amdgcn_perm(hi1, lo1, 0x05010400u),
+                                       (int)__builtin_amdgcn_perm(hi1, lo1, 0x07030602u)};
+                    acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa[j][ks], b, ks == 0 ? i32x4_t{} : acc[t], 0, 0, 0);
+                }
+            const uint32_t sv[TPL] = {sf[j].x & 0xFFFFu, sf[j].x >> 16, sf[j].y & 0xFFFFu, sf[j].y >> 16};
+            const uint32_t mv[TPL] = {mf[j].x & 0xFFFFu, mf[j].x >> 16, mf[j].y & 0xFFFFu, mf[j].y >> 16};
+#pragma unroll
+            for (int t = 0; t < TPL; ++t) {
+                const float sc = bf16_bits_to_f32(sv[t]) * live[j], mn = bf16_bits_to_f32(mv[t]) * live[j];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    yacc[t][e] = __builtin_fmaf(sc, (float)acc[t][e], yacc[t][e]);  // |sum| < 2^18: exact in fp32
+                    yacc[t][e] = __builtin_fmaf(mn, xs[j][e], yacc[t][e]);
+                }
+            }
+        }
+    }
+
+    // the waves' sums through LDS, added in wave order; y = bf16(a_m * sum)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int row = 4 * lg + e;
+        if (row < M && row < MR) {
+#pragma unroll
+            for (int t = 0; t < TPL; ++t) part[wave][row][TPL * lr + t] = yacc[t][e];
+        }
+    }
+    __syncthreads();
+    const int rows = min(M, MR);
+    for (int idx = threadIdx.x; idx < rows * COLS; idx += 64 * kR16Waves) {
+        const int row = idx / COLS, c = idx % COLS, n = n0 + c;
+        if (n < N) {
+            float sum = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kR16Waves; ++v) sum += part[v][row][c];
+            y[(size_t)row * N + n] = f32_to_bf16_bits(ascale[row] * sum);
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_quant_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* xq, float* ascale, float* xsum,
@@ -419,6 +568,19 @@ hipError_t launch_quant_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* xsum, int64_t M,
                             const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K,
                             uint16_t* y, hipStream_t stream) {
+    if (M <= 16) {  // a few rows: the weight stream, not the products, sets the time
+        const dim3 grid((unsigned)((N + 63) / 64)), block(64 * kR16Waves);
+        if (M == 1)
+            hipLaunchKernelGGL(w4a8_rows16_kernel<1>, grid, block, 0, stream, xq, ascale, xsum, codes, scales, mins, y,
+                               (int)M, (int)N, (int)K);
+        else if (M <= 4)
+            hipLaunchKernelGGL(w4a8_rows16_kernel<4>, grid, block, 0, stream, xq, ascale, xsum, codes, scales, mins, y,
+                               (int)M, (int)N, (int)K);
+        else
+            hipLaunchKernelGGL(w4a8_rows16_kernel<16>, grid, block, 0, stream, xq, ascale, xsum, codes, scales, mins, y,
+                               (int)M, (int)N, (int)K);
+        return hipGetLastError();
+    }
     const int64_t mt = (M + kBM - 1) / kBM;
     // 128 x 256 tiles (8 waves, one block per CU) when they still give half the CUs a block
     if ((N + 255) / 256 * mt >= 128) {

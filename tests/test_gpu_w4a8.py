@@ -75,6 +75,45 @@ def test_gemm_w4a8_parity(M, N, K):
         np.testing.assert_array_equal(y[1], 0)   # the zero row: a = 1, every code 0, y exactly 0
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 4, 128), (2, 4100, 4224), (4, 1028, 512), (5, 68, 8192), (16, 1156, 1024),
+                                   (16, 20, 384), (7, 132, 4096), (17, 260, 640)])
+def test_gemm_w4a8_few_rows_parity(M, N, K):
+    """Up to 16 rows (the weight-streaming kernel): one and several 4096-k passes, groups past K in
+    the last pass (4224, 8192), ragged N down to 4 columns; 17 rows, the first GEMM shape, beside
+    them.  Full comparison with the oracle on its own quantized activations, then the GPU
+    quantizer's codes through the same product, bit for bit against the first."""
+    say(f"gemm_w4a8 few rows M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=102)
+    x = _activation_rows(M, K, seed=103) if M >= 4 else workloads.activations(M, K, "bf16", seed=103)
+    rq, ra, rs = oracle.quantize_act_i8(x)
+    packed = gpu_pack(G128, W)
+    y = gpu_w4a8(dev(rq), dev(ra), dev(rs), packed, M, N, K)
+    ref = oracle.matmul_w4a8(rq, ra, *oracle.quantize_g128(W))
+    err = rel_err(bf16_f32(y), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= TOL
+    if M >= 4:
+        np.testing.assert_array_equal(y[1], 0)
+    y2 = gpu_w4a8(*gpu_quantize(x), packed, M, N, K)
+    np.testing.assert_array_equal(y2, y)
+
+
+def test_w4a8_decode_full_size():
+    """The decode shape (M=1, K=4096, N=14336) in the launch bench.py times: every output
+    against the oracle."""
+    wl = workloads.DECODE
+    M, N, K = wl.M, wl.N, wl.K
+    say(f"w4a8 decode M={M} N={N} K={K}")
+    W = workloads.weights(N, K, wl.outliers, wl.seed_w)
+    x = workloads.activations(M, K, "bf16", seed=wl.seed_x)
+    packed = gpu_pack(G128, W)
+    y = bf16_f32(gpu_w4a8(*gpu_quantize(x), packed, M, N, K))
+    rq, ra, _ = oracle.quantize_act_i8(x)
+    ref = oracle.matmul_w4a8(rq, ra, *oracle.quantize_g128(W))
+    assert rel_err(y, ref) <= TOL
+    assert np.max(np.abs(y - ref)) <= 2e-2 * np.max(np.abs(ref))
+
+
 @pytest.mark.parametrize("M,N,K", [(1024, 4096, 256), (257, 11268, 128), (520, 8196, 640)])
 def test_gemm_w4a8_wide_tiles(M, N, K):
     """Shapes that take the 128 x 256 tiles (at least 128 of them): ragged M and N (N % 8 == 4 in
