@@ -356,24 +356,28 @@ class W4A8DecodeSetup(Setup):
     """The decode shape (M=1) as W4A8: the row quantized to int8, then the few-row int8-MFMA
     product against the same G128 weights, rotated over cold copies like the W4A16 decode."""
 
-    def __init__(self, wl, W, x_bits, copies, gemm_only: bool):
+    def __init__(self, wl, W, x_bits, copies, mode: str):
         import gemm_w4a16_amd as w
         super().__init__(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x_bits, W, copies)
-        self.gemm_only = gemm_only
+        self.mode = mode  # "quantize_and_gemm", "gemm_only" or "fused" (one launch)
         self.q = w.alloc_act_i8(wl.M, wl.K)
         w.w4a16_quantize_act_i8(self.x, wl.M, wl.K, *self.q)
 
     def step(self, i):
         w = self.w
         c, s, m = self.copies[i % len(self.copies)]
-        if not self.gemm_only:
+        if self.mode == "fused":
+            w.w4a16_matmul_w4a8(self.fmt, self.x, self.M, c, s, m, self.N, self.K, self.y)
+            return
+        if self.mode == "quantize_and_gemm":
             w.w4a16_quantize_act_i8(self.x, self.M, self.K, *self.q)
         w.w4a16_gemm_w4a8(self.fmt, *self.q, self.M, c, s, m, self.N, self.K, self.y)
 
 
 def bench_w4a8_decode(steps, warmup, W=None):
-    """W4A8 at the decode shape (M=1, K=4096, N=14336), cold weights: quantize + product per step,
-    and the product alone as effective weight GB/s against the HBM peak."""
+    """W4A8 at the decode shape (M=1, K=4096, N=14336), cold weights, as effective weight GB/s
+    against the HBM peak: quantize + product (two launches), the product alone, and the fused
+    one-launch form."""
     import workloads
     wl = workloads.DECODE
     W0, x = workloads.inputs(wl)
@@ -383,13 +387,12 @@ def bench_w4a8_decode(steps, warmup, W=None):
     R = copies_for(c + s + m)
     out = {"workload": "w4a8_gemv_m1_k4096_n14336", "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R,
            "steps": steps}
-    for gemm_only in (False, True):
-        st = W4A8DecodeSetup(wl, W, x, R, gemm_only)
+    for mode in ("quantize_and_gemm", "gemm_only", "fused"):
+        st = W4A8DecodeSetup(wl, W, x, R, mode)
         wall, ev = time_steps(st, steps, warmup)
         t = ev / steps
-        key = "gemm_only" if gemm_only else "quantize_and_gemm"
-        out[key] = {"us_per_step_events": t * 1e6, "effective_weight_gbs": st.weight_bytes / t / 1e9,
-                    "frac_hbm_peak": st.weight_bytes / t / 1e9 / HBM_PEAK_GBS}
+        out[mode] = {"us_per_step_events": t * 1e6, "effective_weight_gbs": st.weight_bytes / t / 1e9,
+                     "frac_hbm_peak": st.weight_bytes / t / 1e9 / HBM_PEAK_GBS}
         del st
     return out
 

@@ -25,6 +25,7 @@ EXPORTED = (
     "w4a16_status_string", "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant",
     "w4a16_gemv", "w4a16_gemv_max_rows", "w4a16_gemm_workspace_bytes", "w4a16_gemm",
     "w4a16_matmul", "w4a16_matmul_gemv_cutoff", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
+    "w4a16_matmul_w4a8",
 )
 
 
@@ -58,8 +59,10 @@ def _load() -> ctypes.CDLL:
     L.w4a16_matmul_gemv_cutoff.argtypes, L.w4a16_matmul_gemv_cutoff.restype = [], I64
     L.w4a16_quantize_act_i8.argtypes = [P, I64, I64, P, P, P, P]
     L.w4a16_gemm_w4a8.argtypes = [I, P, P, P, I64, P, P, P, I64, I64, P, P]
+    L.w4a16_matmul_w4a8.argtypes = [I, P, I64, P, P, P, I64, I64, P, P]
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant", "w4a16_gemv",
-                 "w4a16_gemm", "w4a16_matmul", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8"):
+                 "w4a16_gemm", "w4a16_matmul", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
+                 "w4a16_matmul_w4a8"):
         getattr(L, name).restype = I
     return L
 
@@ -153,6 +156,11 @@ def w4a16_gemm_w4a8(fmt: int, xq, ascale, xsum, M: int, codes, scales, mins, N: 
                     stream=None) -> None:
     _ok(lib.w4a16_gemm_w4a8(fmt, _p(xq), _p(ascale), _p(xsum), M, _p(codes), _p(scales), _p(mins), N, K,
                             _p(y), _stream(stream)), "w4a16_gemm_w4a8")
+
+
+def w4a16_matmul_w4a8(fmt: int, x, M: int, codes, scales, mins, N: int, K: int, y, stream=None) -> None:
+    _ok(lib.w4a16_matmul_w4a8(fmt, _p(x), M, _p(codes), _p(scales), _p(mins), N, K, _p(y), _stream(stream)),
+        "w4a16_matmul_w4a8")
 
 
 # ---- memory plumbing (torch allocations with the ABI's shapes and dtypes) ------------------------

@@ -21,6 +21,9 @@ constexpr int64_t kMaxN = (int64_t)1 << 26;
 constexpr int64_t kMaxK = (int64_t)1 << 22;
 // M at and below which w4a16_matmul uses the GEMV path for G128 (from the batch sweep).
 constexpr int64_t kGemvCutoff = 16;
+// Rows the fused W4A8 product quantizes inside its kernel: one, the batch-one case (each wave
+// quantizes every row of its groups, so the work and the registers grow with M).
+constexpr int64_t kW4A8FusedMaxRows = 1;
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -238,6 +241,22 @@ w4a16_status_t w4a16_gemm_w4a8(w4a16_format_t fmt, const int8_t* xq, const float
     return from_hip(w4a16::launch_gemm_w4a8(xq, ascale, xsum, M, static_cast<const uint32_t*>(codes),
                                             static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(mins),
                                             N, K, static_cast<uint16_t*>(y), stream));
+}
+
+w4a16_status_t w4a16_matmul_w4a8(w4a16_format_t fmt, const void* x, int64_t M, const void* codes, const void* scales,
+                                 const void* mins, int64_t N, int64_t K, void* y, hipStream_t stream) {
+    if (w4a16_status_t st = check_shape(fmt, N, K); st != W4A16_OK) return st;
+    if (M <= 0 || M > kMaxDim) return W4A16_ERR_INVALID;
+    if (w4a16_status_t st = check_packed(fmt, codes, scales, mins); st != W4A16_OK) return st;
+    if (!aligned16(x) || !aligned16(y)) return W4A16_ERR_INVALID;
+    if (fmt != W4A16_FMT_G128_ASYM_BF16 || N % 4 != 0 || M > kW4A8FusedMaxRows) return W4A16_ERR_UNSUPPORTED;
+    if ((K / 8) * N * 4 >= ((int64_t)1 << 31)) return W4A16_ERR_UNSUPPORTED;  // as w4a16_gemm_w4a8
+    w4a16::clear_stale_error();
+    return from_hip(w4a16::launch_matmul_w4a8_fused(static_cast<const uint16_t*>(x), M,
+                                                    static_cast<const uint32_t*>(codes),
+                                                    static_cast<const uint16_t*>(scales),
+                                                    static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
+                                                    stream));
 }
 
 }  // extern "C"

@@ -67,5 +67,8 @@ hipError_t launch_quant_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* xsum, int64_t M,
                             const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K,
                             uint16_t* y, hipStream_t stream);
+// The same product for one bf16 row x [K] (M == 1), quantized inside the product's kernel.
+hipError_t launch_matmul_w4a8_fused(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                    const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
 }  // namespace w4a16

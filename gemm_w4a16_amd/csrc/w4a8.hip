@@ -45,6 +45,24 @@ namespace {
 
 // ---- activation quantization ------------------------------------------------------------------
 
+// One activation (bf16 bits) to its int8 code with row scale a: rint(x / a) (IEEE division, ties to
+// even), clamped to [-127, 127].  The quantizer and the fused few-row kernel both use this.
+__device__ __forceinline__ int quant_i8(uint32_t bits, float a) {
+    const float r = rintf(bf16_bits_to_f32(bits) / a);
+    return r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
+}
+
+// max |x| over the 8 bf16 of a 16-byte chunk, folded into m
+__device__ __forceinline__ float absmax8(uint4 v, float m) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)));
+        m = fmaxf(m, fabsf(bf16_bits_to_f32(w[i] >> 16)));
+    }
+    return m;
+}
+
 __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __restrict__ x, int M, int K,
                                                            int8_t* __restrict__ xq, float* __restrict__ ascale,
                                                            float* __restrict__ xsum) {
@@ -55,15 +73,7 @@ __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __res
     const int chunks = K / 8;  // 16-byte chunks of 8 activations; 16 per group
 
     float amax = 0.0f;
-    for (int c = t; c < chunks; c += 256) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + 8 * c);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] & 0xFFFFu)));
-            amax = fmaxf(amax, fabsf(bf16_bits_to_f32(w[i] >> 16)));
-        }
-    }
+    for (int c = t; c < chunks; c += 256) amax = absmax8(*reinterpret_cast<const uint4*>(row + 8 * c), amax);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if ((t & 63) == 0) red[t >> 6] = amax;
@@ -80,9 +90,7 @@ __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __res
         int sum = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const uint32_t bits = (i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu);
-            const float r = rintf(bf16_bits_to_f32(bits) / a);
-            const int q = r < -127.0f ? -127 : (r > 127.0f ? 127 : (int)r);
+            const int q = quant_i8((i & 1) ? (w[i >> 1] >> 16) : (w[i >> 1] & 0xFFFFu), a);
             packed[i >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (i & 3));
             sum += q;
         }
@@ -425,18 +433,35 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
 constexpr int kR16Waves = 16;
 constexpr int kR16Gpp = 2;  // groups per wave per pass: a pass covers 32 groups (4096 k)
 
+// An LDS-only workgroup barrier: this wave's LDS writes complete, then s_barrier.  No memory fence,
+// so the weight loads in flight stay in flight; the memory clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // MR: rows the accumulator layout keeps (M <= MR; 1, 4 or 16).  N % 4 == 0.
-template <int MR>
+// kFused (one row): the block quantizes the bf16 row x itself, with the quantizer's arithmetic:
+// with its first pass's weight loads in flight (requested after one 16-byte chunk of x per thread),
+// the block reduces max|x| (every block reads the whole row, 8 KB at K = 4096, from L2), and each
+// wave then quantizes its own groups into LDS and sums their codes.  Otherwise xq, ascale and xsum
+// come from w4a16_quantize_act_i8.
+template <int MR, bool kFused>
 __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
-    const int8_t* __restrict__ xq, const float* __restrict__ ascale, const float* __restrict__ xsum,
-    const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
-    uint16_t* __restrict__ y, int M, int N, int K) {
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ xq, const float* __restrict__ ascale,
+    const float* __restrict__ xsum, const uint32_t* __restrict__ codes, const uint16_t* __restrict__ scales,
+    const uint16_t* __restrict__ mins, uint16_t* __restrict__ y, int M, int N, int K) {
+    static_assert(!kFused || MR == 1, "the fused form quantizes one row");
     constexpr int E = MR == 1 ? 1 : 4;  // D rows per lane that can be real (row 4 (lane / 16) + e)
     constexpr int TPL = 4, COLS = 64;
+    constexpr bool kStageX = MR == 1 || kFused;  // activation fragments from LDS
     __shared__ float part[kR16Waves][MR][COLS];
-    // one row: each wave stages its groups' 128-byte activation runs in LDS with one 4-byte load
-    // per lane, so that the A fragments cost no vector-memory requests of their own
-    __shared__ __attribute__((aligned(16))) uint32_t xw[MR == 1 ? kR16Waves : 1][kR16Gpp * 32];
+    // each wave's groups' 128-byte activation runs, per row: for one row loaded with one 4-byte
+    // load per lane (the A fragments then cost no vector-memory requests of their own), in the
+    // fused form written by the quantization
+    __shared__ __attribute__((aligned(16))) uint32_t xw[kStageX ? kR16Waves : 1][kStageX ? MR : 1][kR16Gpp * 32];
+    __shared__ float red[kFused ? kR16Waves : 1][MR];
+    float arow[MR];  // fused: the row scales a_m
+#pragma unroll
+    for (int m = 0; m < MR; ++m) arow[m] = 1.0f;
     const int lane = lane_id(), wave = wave_id();
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * COLS;
@@ -445,7 +470,7 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
     const int cbase = min(n0 + TPL * lr, N - TPL);
     // A row of this lane (rows past M repeat the last one: their outputs are never stored) and the
     // D rows it holds
-    const int8_t* xrow = xq + (size_t)min(lr, M - 1) * K + 16 * lg;
+    const int8_t* xrow = kStageX ? nullptr : xq + (size_t)min(lr, M - 1) * K + 16 * lg;
     int drow[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) drow[e] = min(4 * lg + e, M - 1);
@@ -472,22 +497,35 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
         uint2 sf[kR16Gpp], mf[kR16Gpp];
         float xs[kR16Gpp][E];
         u32x4_t w[kR16Gpp][2][2];  // [group][k-step][packed row of the pair], 4 columns each
+        // fused, first pass: each thread's first 16-byte chunk of every row, requested ahead of the
+        // weights so that the max |x| below waits for these loads only (a clamped duplicate chunk
+        // does not change a maximum)
+        uint4 xm[kFused ? MR : 1];
+        if constexpr (kFused) {
+            if (p0 == 0) {
+                const int c0 = min((int)threadIdx.x, (K >> 3) - 1);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) xm[m] = *reinterpret_cast<const uint4*>(x + (size_t)min(m, M - 1) * K + 8 * c0);
+            }
+        }
         uint32_t x1 = 0;
-        if constexpr (MR == 1) {
+        if constexpr (MR == 1 && !kFused) {
             static_assert(kR16Gpp * 32 == 64, "one dword of activations per lane");
             x1 = *reinterpret_cast<const uint32_t*>(xq + gj[lane >> 5] * 128 + 4 * (lane & 31));
         }
 #pragma unroll
         for (int j = 0; j < kR16Gpp; ++j) {
-            if constexpr (MR != 1) {
+            if constexpr (!kStageX) {
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     xa[j][ks] = *reinterpret_cast<const i32x4_t*>(xrow + gj[j] * 128 + 64 * ks);
             }
             sf[j] = *reinterpret_cast<const uint2*>(scales + (size_t)gj[j] * N + cbase);
             mf[j] = *reinterpret_cast<const uint2*>(mins + (size_t)gj[j] * N + cbase);
+            if constexpr (!kFused) {
 #pragma unroll
-            for (int e = 0; e < E; ++e) xs[j][e] = xsum[(size_t)gj[j] * M + drow[e]];
+                for (int e = 0; e < E; ++e) xs[j][e] = xsum[(size_t)gj[j] * M + drow[e]];
+            }
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -496,13 +534,58 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
                     w[j][ks][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + lane_off));
                 }
         }
-        if constexpr (MR == 1) {
-            xw[wave][lane] = x1;  // read back by this wave only, after its own write
+        if constexpr (kFused) {
+            if (p0 == 0) {  // the rows' max |x|, with this pass's weight loads in flight
+                float amx[MR];
+#pragma unroll
+                for (int m = 0; m < MR; ++m) amx[m] = absmax8(xm[m], 0.0f);
+                for (int c = threadIdx.x + 64 * kR16Waves; c < (K >> 3); c += 64 * kR16Waves)
+#pragma unroll
+                    for (int m = 0; m < MR; ++m)
+                        amx[m] = absmax8(*reinterpret_cast<const uint4*>(x + (size_t)min(m, M - 1) * K + 8 * c), amx[m]);
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+#pragma unroll
+                    for (int off = 32; off >= 1; off >>= 1) amx[m] = fmaxf(amx[m], __shfl_xor(amx[m], off));
+                }
+                if (lane == 0) {
+#pragma unroll
+                    for (int m = 0; m < MR; ++m) red[wave][m] = amx[m];
+                }
+                lds_barrier();
+#pragma unroll
+                for (int m = 0; m < MR; ++m) {
+                    float mx = 0.0f;
+#pragma unroll
+                    for (int v = 0; v < kR16Waves; ++v) mx = fmaxf(mx, red[v][m]);
+                    const float a = mx / 127.0f;  // correctly rounded division, as in the quantizer
+                    arow[m] = a == 0.0f ? 1.0f : a;
+                }
+            }
+            // this wave's groups: codes into LDS, and X_g of each row
+            {  // lane: group lane / 32, 4 activations
+                const int j = lane >> 5;
+                const uint2 v = *reinterpret_cast<const uint2*>(x + gj[j] * 128 + 4 * (lane & 31));
+                const int q0 = quant_i8(v.x & 0xFFFFu, arow[0]), q1 = quant_i8(v.x >> 16, arow[0]);
+                const int q2 = quant_i8(v.y & 0xFFFFu, arow[0]), q3 = quant_i8(v.y >> 16, arow[0]);
+                xw[wave][0][lane] = ((uint32_t)q0 & 0xFFu) | (((uint32_t)q1 & 0xFFu) << 8) |
+                                    (((uint32_t)q2 & 0xFFu) << 16) | ((uint32_t)q3 << 24);
+                int sum = q0 + q1 + q2 + q3;
+#pragma unroll
+                for (int off = 16; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+                xs[0][0] = (float)__shfl(sum, 0);  // |X| <= 127 * 128: exact
+                xs[1][0] = (float)__shfl(sum, 32);
+            }
+        } else if constexpr (MR == 1) {
+            xw[wave][0][lane] = x1;  // read back by this wave only, after its own write
+        }
+        if constexpr (kStageX) {
+            const int ar = min(lr, MR - 1);  // A rows past the staged ones repeat one: never stored
 #pragma unroll
             for (int j = 0; j < kR16Gpp; ++j)
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
-                    xa[j][ks] = *reinterpret_cast<const i32x4_t*>(&xw[wave][32 * j + 16 * ks + 4 * lg]);
+                    xa[j][ks] = *reinterpret_cast<const i32x4_t*>(&xw[wave][ar][32 * j + 16 * ks + 4 * lg]);
         }
 #pragma unroll
         for (int j = 0; j < kR16Gpp; ++j) {
@@ -551,7 +634,15 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
             float sum = 0.0f;
 #pragma unroll
             for (int v = 0; v < kR16Waves; ++v) sum += part[v][row][c];
-            y[(size_t)row * N + n] = f32_to_bf16_bits(ascale[row] * sum);
+            float a = 0.0f;
+            if constexpr (kFused) {
+                a = arow[0];
+#pragma unroll
+                for (int m = 1; m < MR; ++m) a = row == m ? arow[m] : a;
+            } else {
+                a = ascale[row];
+            }
+            y[(size_t)row * N + n] = f32_to_bf16_bits(a * sum);
         }
     }
 }
@@ -570,15 +661,16 @@ hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* 
                             uint16_t* y, hipStream_t stream) {
     if (M <= 16) {  // a few rows: the weight stream, not the products, sets the time
         const dim3 grid((unsigned)((N + 63) / 64)), block(64 * kR16Waves);
+        const uint16_t* nox = nullptr;
         if (M == 1)
-            hipLaunchKernelGGL(w4a8_rows16_kernel<1>, grid, block, 0, stream, xq, ascale, xsum, codes, scales, mins, y,
-                               (int)M, (int)N, (int)K);
+            hipLaunchKernelGGL((w4a8_rows16_kernel<1, false>), grid, block, 0, stream, nox, xq, ascale, xsum, codes,
+                               scales, mins, y, (int)M, (int)N, (int)K);
         else if (M <= 4)
-            hipLaunchKernelGGL(w4a8_rows16_kernel<4>, grid, block, 0, stream, xq, ascale, xsum, codes, scales, mins, y,
-                               (int)M, (int)N, (int)K);
+            hipLaunchKernelGGL((w4a8_rows16_kernel<4, false>), grid, block, 0, stream, nox, xq, ascale, xsum, codes,
+                               scales, mins, y, (int)M, (int)N, (int)K);
         else
-            hipLaunchKernelGGL(w4a8_rows16_kernel<16>, grid, block, 0, stream, xq, ascale, xsum, codes, scales, mins, y,
-                               (int)M, (int)N, (int)K);
+            hipLaunchKernelGGL((w4a8_rows16_kernel<16, false>), grid, block, 0, stream, nox, xq, ascale, xsum, codes,
+                               scales, mins, y, (int)M, (int)N, (int)K);
         return hipGetLastError();
     }
     const int64_t mt = (M + kBM - 1) / kBM;
@@ -592,6 +684,17 @@ hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* 
         hipLaunchKernelGGL((w4a8_gemm_kernel<4>), grid, dim3(256), 0, stream, xq, ascale, xsum, codes, scales, mins,
                            y, (int)M, (int)N, (int)K);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_matmul_w4a8_fused(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                    const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+    if (M != 1) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((N + 63) / 64)), block(64 * kR16Waves);
+    const int8_t* noq = nullptr;
+    const float* nof = nullptr;
+    hipLaunchKernelGGL((w4a8_rows16_kernel<1, true>), grid, block, 0, stream, x, noq, nof, nof, codes, scales, mins, y,
+                       (int)M, (int)N, (int)K);
     return hipGetLastError();
 }
 

@@ -197,6 +197,16 @@ w4a16_status_t w4a16_gemm_w4a8(w4a16_format_t fmt, const int8_t* xq, const float
                                int64_t M, const void* codes, const void* scales, const void* mins, int64_t N,
                                int64_t K, void* y, hipStream_t stream);
 
+/* W4A8 with the activation quantization fused into the product, for one activation row:
+ * y [M][N] bf16 = w4a16_gemm_w4a8 of the codes, row scales and group sums that
+ * w4a16_quantize_act_i8 would write for x, bit for bit, in one launch and with no intermediate
+ * buffers (vidyal.ai "Low-Precision Kernels", "The cost of quantizing activations": the
+ * quantization is paid on every call).  x: bf16 [M][K] with M == 1 (ERR_UNSUPPORTED above: use
+ * the two calls).  G128 only, N % 4 == 0, K*N/2 < 2^31 (ERR_UNSUPPORTED otherwise).  No workspace;
+ * bitwise reproducible run to run. */
+w4a16_status_t w4a16_matmul_w4a8(w4a16_format_t fmt, const void* x, int64_t M, const void* codes, const void* scales,
+                                 const void* mins, int64_t N, int64_t K, void* y, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -80,6 +80,17 @@ def test_extents_past_the_32_bit_offsets_are_unsupported():
             == w.W4A16_ERR_UNSUPPORTED
 
 
+def test_matmul_w4a8_validation():
+    f = w.w4a16_matmul_w4a8
+    assert _status(f, G128, FAKE, 0, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_INVALID       # M
+    assert _status(f, G128, FAKE + 2, 1, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_INVALID   # x
+    assert _status(f, G128, FAKE, 1, FAKE, FAKE, None, 256, 128, FAKE, 0) == w.W4A16_ERR_INVALID       # mins
+    assert _status(f, G128, FAKE, 1, FAKE, FAKE, FAKE, 256, 100, FAKE, 0) == w.W4A16_ERR_INVALID       # K % 128
+    assert _status(f, G128, FAKE, 2, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED   # one row
+    assert _status(f, G128, FAKE, 1, FAKE, FAKE, FAKE, 258, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED   # N % 4
+    assert _status(f, Q4, FAKE, 1, FAKE, FAKE, None, 256, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED     # G128 only
+
+
 def _status(fn, *args):
     try:
         fn(*args)

@@ -114,6 +114,30 @@ def test_w4a8_decode_full_size():
     assert np.max(np.abs(y - ref)) <= 2e-2 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("N,K", [(4, 128), (260, 1152), (4100, 4224), (68, 8192), (14336, 4096)])
+def test_matmul_w4a8_fused_one_row(N, K):
+    """The fused one-row entry point: bit for bit the two-call result (same codes, scales and
+    sums, same order of the fp32 epilogue), and within tolerance of the oracle; one and several
+    4096-k passes, groups past K, a zero row, a row whose largest magnitude ties an exact .5."""
+    say(f"matmul_w4a8 fused M=1 N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=104)
+    packed = gpu_pack(G128, W)
+    rows = [workloads.activations(1, K, "bf16", seed=105), np.zeros((1, K), dtype=np.uint16),
+            _activation_rows(4, K, seed=106)[2:3]]
+    for x in rows:
+        y2 = gpu_w4a8(*gpu_quantize(x), packed, 1, N, K)
+        y1 = torch.empty((1, N), dtype=torch.int16, device="cuda")
+        w.w4a16_matmul_w4a8(G128, dev(x), 1, *packed, N, K, y1)
+        y1 = host(y1, np.uint16)
+        np.testing.assert_array_equal(y1, y2)
+        rq, ra, _ = oracle.quantize_act_i8(x)
+        ref = oracle.matmul_w4a8(rq, ra, *oracle.quantize_g128(W))
+        if np.any(ref != 0):
+            assert rel_err(bf16_f32(y1), ref) <= TOL
+        else:
+            np.testing.assert_array_equal(y1, 0)
+
+
 @pytest.mark.parametrize("M,N,K", [(1024, 4096, 256), (257, 11268, 128), (520, 8196, 640)])
 def test_gemm_w4a8_wide_tiles(M, N, K):
     """Shapes that take the 128 x 256 tiles (at least 128 of them): ragged M and N (N % 8 == 4 in
