@@ -497,11 +497,14 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
         uint2 sf[kR16Gpp], mf[kR16Gpp];
         float xs[kR16Gpp][E];
         u32x4_t w[kR16Gpp][2][2];  // [group][k-step][packed row of the pair], 4 columns each
-        // fused, first pass: each thread's first 16-byte chunk of every row, requested ahead of the
-        // weights so that the max |x| below waits for these loads only (a clamped duplicate chunk
-        // does not change a maximum)
+        // fused: this lane's activations of the pass and, in the first pass, each thread's first
+        // 16-byte chunk of the row, requested ahead of the weights so that the max |x| and the
+        // quantization below wait for these loads only (a clamped duplicate chunk does not change
+        // a maximum)
         uint4 xm[kFused ? MR : 1];
+        uint2 xv = make_uint2(0u, 0u);  // fused: this lane's 4 activations of its group (lane / 32)
         if constexpr (kFused) {
+            xv = *reinterpret_cast<const uint2*>(x + gj[lane >> 5] * 128 + 4 * (lane & 31));
             if (p0 == 0) {
                 const int c0 = min((int)threadIdx.x, (K >> 3) - 1);
 #pragma unroll
@@ -564,8 +567,7 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
             }
             // this wave's groups: codes into LDS, and X_g of each row
             {  // lane: group lane / 32, 4 activations
-                const int j = lane >> 5;
-                const uint2 v = *reinterpret_cast<const uint2*>(x + gj[j] * 128 + 4 * (lane & 31));
+                const uint2 v = xv;
                 const int q0 = quant_i8(v.x & 0xFFFFu, arow[0]), q1 = quant_i8(v.x >> 16, arow[0]);
                 const int q2 = quant_i8(v.y & 0xFFFFu, arow[0]), q3 = quant_i8(v.y >> 16, arow[0]);
                 xw[wave][0][lane] = ((uint32_t)q0 & 0xFFu) | (((uint32_t)q1 & 0xFFu) << 8) |
