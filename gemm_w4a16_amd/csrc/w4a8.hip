@@ -71,9 +71,23 @@ __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __res
     const int t = threadIdx.x;
     const uint16_t* row = x + (size_t)m * K;
     const int chunks = K / 8;  // 16-byte chunks of 8 activations; 16 per group
+    // The first kKeep chunks of each thread stay in registers between the two passes (all of a row
+    // up to K = 8192), so the quantization does not wait for a second read of the row.  Chunks are
+    // taken in whole 16-lane groups (chunks is a multiple of 16, 256 of 16), so every lane of a
+    // group is active at the group sum's shuffles.
+    constexpr int kKeep = 4;
+    uint4 keep[kKeep];
 
     float amax = 0.0f;
-    for (int c = t; c < chunks; c += 256) amax = absmax8(*reinterpret_cast<const uint4*>(row + 8 * c), amax);
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i) {
+        const int c = t + 256 * i;
+        if (c < chunks) {
+            keep[i] = *reinterpret_cast<const uint4*>(row + 8 * c);
+            amax = absmax8(keep[i], amax);
+        }
+    }
+    for (int c = t + 256 * kKeep; c < chunks; c += 256) amax = absmax8(*reinterpret_cast<const uint4*>(row + 8 * c), amax);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
     if ((t & 63) == 0) red[t >> 6] = amax;
@@ -83,8 +97,8 @@ __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __res
     if (a == 0.0f) a = 1.0f;
     if (t == 0) ascale[m] = a;
 
-    for (int c = t; c < chunks; c += 256) {
-        const uint4 v = *reinterpret_cast<const uint4*>(row + 8 * c);
+    // codes of chunk c (8 activations), and the exact code sum of its group
+    auto quantize_chunk = [&](uint4 v, int c) __attribute__((always_inline)) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
         uint32_t packed[2] = {0u, 0u};
         int sum = 0;
@@ -95,11 +109,17 @@ __global__ __launch_bounds__(256) void quant_act_i8_kernel(const uint16_t* __res
             sum += q;
         }
         *reinterpret_cast<uint2*>(xq + (size_t)m * K + 8 * c) = make_uint2(packed[0], packed[1]);
-        // the 16 chunks of a group are 16 consecutive threads (256 is a multiple of 16)
+        // the 16 chunks of a group are 16 consecutive threads
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
         if ((c & 15) == 0) xsum[(size_t)(c / 16) * M + m] = (float)sum;  // |sum| <= 127 * 128: exact
+    };
+#pragma unroll
+    for (int i = 0; i < kKeep; ++i) {
+        const int c = t + 256 * i;
+        if (c < chunks) quantize_chunk(keep[i], c);
     }
+    for (int c = t + 256 * kKeep; c < chunks; c += 256) quantize_chunk(*reinterpret_cast<const uint4*>(row + 8 * c), c);
 }
 
 // ---- GEMM ------------------------------------------------------------------------------------
