@@ -430,14 +430,15 @@ def cpu_baseline(W, x):
     weight_bytes = codes.nbytes + scales.nbytes + mins.nbytes
     times = []
     t_start = time.perf_counter()
-    while len(times) < 3 or (time.perf_counter() - t_start < 10.0 and len(times) < 20):
+    # about 10-15 s of CPU work: at least 3 runs, then more until 10 s have passed (at most 100)
+    while len(times) < 3 or (time.perf_counter() - t_start < 10.0 and len(times) < 100):
         t0 = time.perf_counter()
         oracle.matmul_g128(x, codes, scales, mins)
         times.append(time.perf_counter() - t0)
     t = float(np.median(times))
     return {"value": weight_bytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full decode GEMV (M=1, K=4096, N=14336) in fp64, {len(times)} runs, median "
-                      f"{t:.3f} s, on {platform.processor() or platform.machine()}"}
+            "sample": f"the full decode GEMV (M=1, K=4096, N=14336) in fp64, {len(times)} runs "
+                      f"({sum(times):.1f} s), median {t:.3f} s, on {platform.processor() or platform.machine()}"}
 
 
 def copy_calibration(mib: int):
