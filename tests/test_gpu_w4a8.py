@@ -240,3 +240,34 @@ def test_w4a8_graph_replays_match_eager():
         g.replay()
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(y, np.uint16), ref, err_msg=f"replay {r}")
+
+
+def test_w4a8_fused_graph_replays_match_eager():
+    """The fused one-row product (its LDS-only barrier included) captured in a HIP graph: every
+    replay, with other work and synchronizations in between, equals the eager result bit for bit."""
+    N, K = 1028, 4224
+    W = workloads.weights(N, K, seed=107)
+    packed = gpu_pack(G128, W)
+    xd = dev(workloads.activations(1, K, "bf16", seed=108))
+    y_eager = torch.empty((1, N), dtype=torch.int16, device="cuda")
+    w.w4a16_matmul_w4a8(G128, xd, 1, *packed, N, K, y_eager)
+    ref = host(y_eager, np.uint16).copy()
+    y = torch.zeros((1, N), dtype=torch.int16, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        w.w4a16_matmul_w4a8(G128, xd, 1, *packed, N, K, y)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        w.w4a16_matmul_w4a8(G128, xd, 1, *packed, N, K, y)
+    junk = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+    for r in range(3):
+        y.fill_(0)
+        junk.normal_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y, np.uint16), ref, err_msg=f"replay {r}")
+
