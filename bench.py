@@ -2,7 +2,7 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                    [--only decode|prefill|q4|sweep|zp|w8|w4a8|w4a8_decode]
+                    [--only decode|prefill|q4|sweep|zp|w8|w4a8|w4a8_decode|w4a8_sweep]
 
 A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one batch of seeded
 synthetic input, with packed weights, activations and output already resident in HBM.  The
@@ -71,7 +71,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=170)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode", "w4a8_sweep"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -397,6 +397,32 @@ def bench_w4a8_decode(steps, warmup, W=None):
     return out
 
 
+def bench_w4a8_sweep(steps, warmup, W=None):
+    """W4A8 product alone (activations quantized once, before the timed steps) over the batch
+    sweep's M at K=4096, N=14336, cold weights: which kernel each M takes and its time."""
+    import gemm_w4a16_amd as w
+    import workloads
+    wl1 = workloads.DECODE
+    if W is None:
+        W = workloads.weights(wl1.N, wl1.K, wl1.outliers, wl1.seed_w)
+    c, s, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl1.N, wl1.K)
+    R = copies_for(c + s + m)
+    out, base = [], None
+    for M in workloads.SWEEP_MS:
+        wl = workloads.sweep(M)
+        x = workloads.activations(M, wl.K, "bf16", wl.seed_x, rows_drawn=max(workloads.SWEEP_MS))
+        st = W4A8DecodeSetup(wl, W, x, R if base is None else 1, "gemm_only")
+        if base is None:
+            base = st.copies
+        else:
+            st.copies = base  # reuse the rotated weight copies
+        wall, ev = time_steps(st, steps, warmup)
+        t = ev / steps
+        out.append({"M": M, "kernel": "rows16" if M <= 64 else "gemm", "us": t * 1e6,
+                    "effective_weight_gbs": st.weight_bytes / t / 1e9, "tops": 2.0 * M * wl.N * wl.K / t / 1e12})
+    return out
+
+
 def bench_sweep(steps, warmup, W=None):
     import gemm_w4a16_amd as w
     import workloads
@@ -471,7 +497,8 @@ def main():
         copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
         fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp, "w8": bench_w8,
-              "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode}[args.only]
+              "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
+              "w4a8_sweep": bench_w4a8_sweep}[args.only]
         print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
         return
 
@@ -533,6 +560,9 @@ def main():
         torch.cuda.empty_cache()
         log("W4A8 at the decode shape")
         extra["w4a8_decode_m1"] = bench_w4a8_decode(340, 34, W)
+        torch.cuda.empty_cache()
+        log("W4A8 batch sweep")
+        extra["w4a8_sweep"] = bench_w4a8_sweep(34, 3, W)
         torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline and args.only is None:

@@ -33,7 +33,8 @@
 //  * the row scale multiplies the total once at the end, and the tile leaves through LDS as
 //    whole rows (16-byte stores of consecutive columns).
 //
-// w4a8_rows16_kernel -- the same sum for 1..16 rows, where the weight stream sets the time (below).
+// w4a8_rows16_kernel -- the same sum for up to 64 rows, 16 per block, where the weight stream sets
+// the time (below).
 #include <type_traits>
 
 #include "device_common.h"
@@ -437,11 +438,12 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
     }
 }
 
-// ---- 1..16 rows: the weights streamed straight into registers -----------------------------------
+// ---- 1..64 rows: the weights streamed straight into registers -----------------------------------
 //
 // w4a8_rows16_kernel -- the same sum, y = a_m * sum_g (s_g,n * sum_k xq q + min_g,n * X_g,m), for a
 // few rows, where the work is the weight stream (HBM-bound) rather than the products.  A block of 16
-// waves owns 64 columns and all of K, the groups dealt over the waves (two per wave per 4096 k);
+// waves owns 64 columns, up to 16 rows (blockIdx.y) and all of K, the groups dealt over the waves
+// (two per wave per 4096 k);
 // every load of a pass (16 bytes of 4 adjacent columns of one packed row per lane, the rows' 16-byte
 // activation chunks, the group's scales, minimums and row sums) is issued before any math, in the
 // order it is used.  Per group, a lane's v_mfma_i32_16x16x64_i8 B fragment is 16 k of one column,
@@ -451,6 +453,7 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
 // epilogue is one convert and two fma per output.  The waves' sums are added
 // through LDS in wave order, so the result is reproducible run to run.
 constexpr int kR16Waves = 16;
+constexpr int kW4A8Rows16Max = 64;  // rows up to which w4a8_rows16_kernel (16 rows per block) is used
 constexpr int kR16Gpp = 2;  // groups per wave per pass: a pass covers 32 groups (4096 k)
 
 // An LDS-only workgroup barrier: this wave's LDS writes complete, then s_barrier.  No memory fence,
@@ -485,15 +488,17 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
     const int lane = lane_id(), wave = wave_id();
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * COLS;
+    const int m0 = blockIdx.y * MR;       // this block's rows m0 .. m0 + Mb - 1
+    const int Mb = min(M - m0, MR);
     const int G = K >> 7;
     // this lane's 4 adjacent columns; a lane past N re-reads the last 4 and never stores
     const int cbase = min(n0 + TPL * lr, N - TPL);
-    // A row of this lane (rows past M repeat the last one: their outputs are never stored) and the
-    // D rows it holds
-    const int8_t* xrow = kStageX ? nullptr : xq + (size_t)min(lr, M - 1) * K + 16 * lg;
+    // A row of this lane (rows past the block's last repeat it: their outputs are never stored)
+    // and the D rows it holds
+    const int8_t* xrow = kStageX ? nullptr : xq + (size_t)(m0 + min(lr, Mb - 1)) * K + 16 * lg;
     int drow[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) drow[e] = min(4 * lg + e, M - 1);
+    for (int e = 0; e < E; ++e) drow[e] = m0 + min(4 * lg + e, Mb - 1);
     // lane byte offset inside a pair of packed rows: rows 2 lg, 2 lg + 1 of the k-step's eight
     const uint32_t lane_off = ((uint32_t)(2 * lg) * (uint32_t)N + (uint32_t)cbase) * 4u;
 
@@ -643,14 +648,13 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int row = 4 * lg + e;
-        if (row < M && row < MR) {
+        if (row < Mb) {
 #pragma unroll
             for (int t = 0; t < TPL; ++t) part[wave][row][TPL * lr + t] = yacc[t][e];
         }
     }
     __syncthreads();
-    const int rows = min(M, MR);
-    for (int idx = threadIdx.x; idx < rows * COLS; idx += 64 * kR16Waves) {
+    for (int idx = threadIdx.x; idx < Mb * COLS; idx += 64 * kR16Waves) {
         const int row = idx / COLS, c = idx % COLS, n = n0 + c;
         if (n < N) {
             float sum = 0.0f;
@@ -662,9 +666,9 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
 #pragma unroll
                 for (int m = 1; m < MR; ++m) a = row == m ? arow[m] : a;
             } else {
-                a = ascale[row];
+                a = ascale[m0 + row];
             }
-            y[(size_t)row * N + n] = f32_to_bf16_bits(a * sum);
+            y[(size_t)(m0 + row) * N + n] = f32_to_bf16_bits(a * sum);
         }
     }
 }
@@ -681,8 +685,11 @@ hipError_t launch_quant_act_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* 
 hipError_t launch_gemm_w4a8(const int8_t* xq, const float* ascale, const float* xsum, int64_t M,
                             const uint32_t* codes, const uint16_t* scales, const uint16_t* mins, int64_t N, int64_t K,
                             uint16_t* y, hipStream_t stream) {
-    if (M <= 16) {  // a few rows: the weight stream, not the products, sets the time
-        const dim3 grid((unsigned)((N + 63) / 64)), block(64 * kR16Waves);
+    // up to 64 rows, blocks of 16 rows that stream the weights again for each 16 rows (from the
+    // Infinity Cache after the first): at K = 4096, N = 14336 that is 15-16 us at 17-32 rows and
+    // 30 us at 64, against 35 us for the 128-row tiles, which win from ~96 rows on
+    if (M <= kW4A8Rows16Max) {
+        const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 15) / 16)), block(64 * kR16Waves);
         const uint16_t* nox = nullptr;
         if (M == 1)
             hipLaunchKernelGGL((w4a8_rows16_kernel<1, false>), grid, block, 0, stream, nox, xq, ascale, xsum, codes,

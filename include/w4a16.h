@@ -187,8 +187,9 @@ w4a16_status_t w4a16_quantize_act_i8(const void* x, int64_t M, int64_t K, int8_t
 
 /* W4A8 product with G128 weights: y [M][N] bf16 = round_to_nearest_even(
  *     a_m * sum_g (s[g][n] * sum_{k in g} xq[m][k] q[k][n] + min[g][n] * xsum[g][m])),
- * the integer sums exact (on the int8 matrix cores: v_mfma_i32_16x16x64_i8 for up to 16 rows,
- * where the weight stream sets the time, v_mfma_i32_32x32x32_i8 tiles above), the rest in fp32.
+ * the integer sums exact (on the int8 matrix cores: v_mfma_i32_16x16x64_i8 in blocks of 16 rows
+ * for up to 64 rows, where the weight stream sets the time, v_mfma_i32_32x32x32_i8 tiles above),
+ * the rest in fp32.
  * Inputs as written by
  * w4a16_quantize_act_i8 for the same M and K.  G128 only (ERR_UNSUPPORTED otherwise); N % 4 == 0
  * and the 32-bit offset limits M*K, K*N/2, (K/128)*M*4 < 2^31 (ERR_UNSUPPORTED otherwise).  No

@@ -76,11 +76,12 @@ def test_gemm_w4a8_parity(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 4, 128), (2, 4100, 4224), (4, 1028, 512), (5, 68, 8192), (16, 1156, 1024),
-                                   (16, 20, 384), (7, 132, 4096), (17, 260, 640)])
+                                   (16, 20, 384), (7, 132, 4096), (17, 260, 640), (33, 1156, 4224),
+                                   (50, 68, 1024), (64, 516, 256), (65, 260, 640)])
 def test_gemm_w4a8_few_rows_parity(M, N, K):
-    """Up to 16 rows (the weight-streaming kernel): one and several 4096-k passes, groups past K in
-    the last pass (4224, 8192), ragged N down to 4 columns; 17 rows, the first GEMM shape, beside
-    them.  Full comparison with the oracle on its own quantized activations, then the GPU
+    """Up to 64 rows (the weight-streaming kernel, 16 rows per block: one row in the last block at
+    17 and 33): one and several 4096-k passes, groups past K in the last pass (4224, 8192), ragged N
+    down to 4 columns; 65 rows, the first 128-row-tile shape, beside them.  Full comparison with the oracle on its own quantized activations, then the GPU
     quantizer's codes through the same product, bit for bit against the first."""
     say(f"gemm_w4a8 few rows M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=102)
