@@ -562,6 +562,9 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
                     w[j][ks][h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(row + lane_off));
                 }
         }
+        // keep every load of the pass ahead of the math (the scheduler would otherwise sink half of
+        // them between the MFMAs, leaving fewer bytes in flight)
+        __builtin_amdgcn_sched_barrier(0);
         if constexpr (kFused) {
             if (p0 == 0) {  // the rows' max |x|, with this pass's weight loads in flight
                 float amx[MR];
