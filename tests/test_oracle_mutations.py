@@ -79,6 +79,31 @@ MUTATIONS = [
      "acc += act_value(x, x_kind, m * K + k) * ((double)(uint8_t)codes[n * K + k] * (double)scales[n]);"),
     ("ZP f32 decode ignores the zero point", "const float v = ((float)g128zp_code(codes, K, n, k) - z) * s;",
      "const float v = ((float)g128zp_code(codes, K, n, k)) * s;"),
+    ("Q4 bf16 dequant rounds through fp16 first",
+     "oracle_f32_to_bf16(v);\n            else if (kind == 2)\n                ((double*)out)[n * K + k] = (double)(q - 8)",
+     "oracle_f32_to_bf16((float)oracle_f16_to_f64(oracle_f32_to_f16(v)));\n            else if (kind == 2)\n"
+     "                ((double*)out)[n * K + k] = (double)(q - 8)"),
+    ("Q4 fp16 dequant keeps only bf16 precision",
+     "(K / 32) + k / 32]);\n            else\n                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(v);",
+     "(K / 32) + k / 32]);\n            else\n"
+     "                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(oracle_bf16_to_f32(oracle_f32_to_bf16(v)));"),
+    ("Q4 16-bit dequant kinds swapped",
+     "oracle_f32_to_bf16(v);\n            else if (kind == 2)\n                ((double*)out)[n * K + k] = (double)(q - 8)",
+     "oracle_f32_to_f16(v);\n            else if (kind == 2)\n                ((double*)out)[n * K + k] = (double)(q - 8)"),
+    ("ZP bf16 dequant rounds through fp16 first",
+     "oracle_f32_to_bf16(v);\n            else if (kind == 2)\n                ((double*)out)[n * K + k] = g128zp_weight_exact",
+     "oracle_f32_to_bf16((float)oracle_f16_to_f64(oracle_f32_to_f16(v)));\n            else if (kind == 2)\n"
+     "                ((double*)out)[n * K + k] = g128zp_weight_exact"),
+    ("ZP fp16 dequant keeps only bf16 precision",
+     "g128zp_weight_exact(codes, scales, zeros, K, n, k);\n            else\n"
+     "                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(v);",
+     "g128zp_weight_exact(codes, scales, zeros, K, n, k);\n            else\n"
+     "                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(oracle_bf16_to_f32(oracle_f32_to_bf16(v)));"),
+    ("ZP fp16 dequant truncates instead of rounding",
+     "g128zp_weight_exact(codes, scales, zeros, K, n, k);\n            else\n"
+     "                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(v);",
+     "g128zp_weight_exact(codes, scales, zeros, K, n, k);\n            else\n"
+     "                ((uint16_t*)out)[n * K + k] = oracle_f32_to_f16(nextafterf(v, 0.0f));"),
     ("W4A8 activation codes truncate", "const float t8 = rintf(oracle_bf16_to_f32(row[k]) / a8);",
      "const float t8 = truncf(oracle_bf16_to_f32(row[k]) / a8);"),
     ("W4A8 activation scale over 128 levels", "float a8 = amax / 127.0f;", "float a8 = amax / 128.0f;"),

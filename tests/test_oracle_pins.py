@@ -383,6 +383,35 @@ def test_q4_dequant_f32_is_exact():
                                   oracle.dequant_q4b32(codes, scales, "f64"))
 
 
+def _wide_range_weights(N, K, seed):
+    """N(0, 0.02) rows scaled by powers of two from 2^-20 to 2^10, so that 16-bit roundings of the
+    decoded weights reach fp16's subnormal range, its normal range and bf16's wider exponents."""
+    W = workloads.weights(N, K, outliers=True, seed=seed)
+    e = np.random.default_rng(seed + 100).integers(-20, 11, size=(N, 1))
+    return (W * np.exp2(e).astype(np.float32)).astype(np.float32)
+
+
+def test_q4_dequant_16bit_kinds_round_the_exact_decode():
+    """The bf16 and fp16 reference dequants are the round-to-nearest-even of the exact decode
+    (q - 8) * s, here formed by numpy from the packed bytes and converted by torch (bf16) and
+    numpy (fp16), including fp16 subnormals and exact ties."""
+    W = _wide_range_weights(64, 512, seed=7)
+    codes, scales = oracle.quantize_q4b32(W)
+    N, K = W.shape
+    q = np.empty((N, K), dtype=np.int64)
+    q[:, 0::2] = (codes & 0xF).reshape(N, K // 2)
+    q[:, 1::2] = (codes >> 4).reshape(N, K // 2)
+    s = np.repeat(scales.view(np.float16).astype(np.float32), 32, axis=1)
+    exact = ((q - 8).astype(np.float32) * s).astype(np.float32)     # exact: 4 x 11 significant bits
+    assert np.count_nonzero(np.abs(exact) < 2.0 ** -14) > 100          # fp16 subnormal results occur
+    np.testing.assert_array_equal(oracle.dequant_q4b32(codes, scales, "f32"), exact)
+    np.testing.assert_array_equal(oracle.dequant_q4b32(codes, scales, "f16"), exact.astype(np.float16).view(np.uint16))
+    np.testing.assert_array_equal(oracle.dequant_q4b32(codes, scales, "bf16"), torch_bf16_bits(exact))
+    # the two 16-bit kinds differ on most weights: neither is the other's type
+    nz = exact != 0
+    assert np.mean(oracle.dequant_q4b32(codes, scales, "f16")[nz] != torch_bf16_bits(exact)[nz]) > 0.9
+
+
 # ---------------------------------------------------------------------------------------------
 # Byte accounting against the numbers the pages print.
 # ---------------------------------------------------------------------------------------------
@@ -619,6 +648,25 @@ def test_zp_dequant_f32_is_exact():
     codes, scales, zeros = oracle.quantize_g128zp(W)
     np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "f32").astype(np.float64),
                                   oracle.dequant_g128zp(codes, scales, zeros, "f64"))
+
+
+def test_zp_dequant_16bit_kinds_round_the_exact_decode():
+    """The bf16 and fp16 reference dequants of the zero-point format are the round-to-nearest-
+    even of (q - z) * s, formed here by numpy from the packed words and converted by torch (bf16)
+    and numpy (fp16), over a wide exponent range."""
+    W = _wide_range_weights(64, 512, seed=27)
+    codes, scales, zeros = oracle.quantize_g128zp(W)
+    q = _zp_codes(codes)
+    s = np.repeat(scales.view(np.float16).astype(np.float32), 128, axis=1)
+    z = np.repeat(zeros.view(np.float16).astype(np.float32), 128, axis=1)
+    exact = ((q.astype(np.float32) - z) * s).astype(np.float32)
+    assert np.count_nonzero(np.abs(exact) < 2.0 ** -14) > 100
+    np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "f32"), exact)
+    np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "f16"),
+                                  exact.astype(np.float16).view(np.uint16))
+    np.testing.assert_array_equal(oracle.dequant_g128zp(codes, scales, zeros, "bf16"), torch_bf16_bits(exact))
+    nz = exact != 0
+    assert np.mean(oracle.dequant_g128zp(codes, scales, zeros, "f16")[nz] != torch_bf16_bits(exact)[nz]) > 0.9
 
 
 def test_zp_matmul_special_cases():
