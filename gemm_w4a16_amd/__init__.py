@@ -25,7 +25,7 @@ EXPORTED = (
     "w4a16_status_string", "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant",
     "w4a16_gemv", "w4a16_gemv_max_rows", "w4a16_gemm_workspace_bytes", "w4a16_gemm",
     "w4a16_matmul", "w4a16_matmul_gemv_cutoff", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
-    "w4a16_matmul_w4a8",
+    "w4a16_matmul_w4a8", "w4a16_check_weights",
 )
 
 
@@ -51,6 +51,7 @@ def _load() -> ctypes.CDLL:
     L.w4a16_packed_sizes.argtypes = [I, I64, I64, ctypes.POINTER(SZ), ctypes.POINTER(SZ), ctypes.POINTER(SZ)]
     L.w4a16_quantize_pack.argtypes = [I, P, I64, I64, P, P, P, P]
     L.w4a16_dequant.argtypes = [I, P, P, P, I64, I64, I, P, P]
+    L.w4a16_check_weights.argtypes = [I, P, I64, I64]
     L.w4a16_gemv.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P]
     L.w4a16_gemv_max_rows.argtypes, L.w4a16_gemv_max_rows.restype = [], I64
     L.w4a16_gemm_workspace_bytes.argtypes, L.w4a16_gemm_workspace_bytes.restype = [I, I64, I64, I64], SZ
@@ -60,7 +61,7 @@ def _load() -> ctypes.CDLL:
     L.w4a16_quantize_act_i8.argtypes = [P, I64, I64, P, P, P, P]
     L.w4a16_gemm_w4a8.argtypes = [I, P, P, P, I64, P, P, P, I64, I64, P, P]
     L.w4a16_matmul_w4a8.argtypes = [I, P, I64, P, P, P, I64, I64, P, P]
-    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant", "w4a16_gemv",
+    for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_check_weights", "w4a16_dequant", "w4a16_gemv",
                  "w4a16_gemm", "w4a16_matmul", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
                  "w4a16_matmul_w4a8"):
         getattr(L, name).restype = I
@@ -111,6 +112,12 @@ def w4a16_packed_sizes(fmt: int, N: int, K: int):
 def w4a16_quantize_pack(fmt: int, W, N: int, K: int, codes, scales, mins, stream=None) -> None:
     _ok(lib.w4a16_quantize_pack(fmt, _p(W), N, K, _p(codes), _p(scales), _p(mins), _stream(stream)),
         "w4a16_quantize_pack")
+
+
+def w4a16_check_weights(fmt: int, W, N: int, K: int) -> None:
+    """Host-side weight check (W: a C-contiguous float32 numpy array or a host address)."""
+    addr = W if isinstance(W, int) or W is None else W.ctypes.data
+    _ok(lib.w4a16_check_weights(fmt, addr, N, K), "w4a16_check_weights")
 
 
 def w4a16_dequant(fmt: int, codes, scales, mins, N: int, K: int, out_dtype: int, W_hat, stream=None) -> None:

@@ -2,6 +2,10 @@
 // Every check runs on the host before anything is enqueued; see include/w4a16.h for the
 // contract of each entry point.
 #include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
 
 #include "../../include/w4a16.h"
 #include "launch.h"
@@ -64,6 +68,23 @@ w4a16_status_t check_act(w4a16_format_t fmt, w4a16_dtype_t act) {
 
 w4a16_status_t from_hip(hipError_t e) { return e == hipSuccess ? W4A16_OK : W4A16_ERR_DEVICE; }
 
+// Largest fp32 values that still round to a finite 16-bit value under round-to-nearest-even: the
+// midpoints between each format's largest finite value and the next power of two round up (to
+// even, i.e. to infinity).  fp16: 65504 and 65536 -> 65520.  bf16: 0x7F7F and 2^128 -> fp32 bits
+// 0x7F7F8000.
+bool fits_fp16(float v) { return std::fabs(v) < 65520.0f; }
+bool fits_bf16(float v) {
+    uint32_t u;
+    std::memcpy(&u, &v, 4);
+    return (u & 0x7FFFFFFFu) < 0x7F7F8000u;
+}
+
+// W4A16_DEBUG_CHECKS set to anything but "0" turns on the quantizers' host-side weight check.
+bool debug_checks_enabled() {
+    const char* v = std::getenv("W4A16_DEBUG_CHECKS");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
 w4a16_status_t check_matmul_common(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                                    const void* codes, const void* scales, const void* mins, int64_t N, int64_t K,
                                    const void* y) {
@@ -112,6 +133,41 @@ w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K, size
     return W4A16_OK;
 }
 
+w4a16_status_t w4a16_check_weights(w4a16_format_t fmt, const float* W, int64_t N, int64_t K) {
+    const w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    if (W == nullptr) return W4A16_ERR_INVALID;
+    // one pass per row and group: the group's range (G128, zero point) or largest magnitude
+    // (Q4, W8), then the stored parameter the quantizer would form from it
+    const int64_t span = fmt == W4A16_FMT_W8_ROW_FP32 ? K : group_of(fmt);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g0 = 0; g0 < K; g0 += span) {
+            const float* w = W + n * K + g0;
+            float lo = w[0], hi = w[0], amax = 0.0f;
+            for (int64_t j = 0; j < span; ++j) {
+                if (!std::isfinite(w[j])) return W4A16_ERR_INVALID;
+                lo = std::min(lo, w[j]);
+                hi = std::max(hi, w[j]);
+                amax = std::max(amax, std::fabs(w[j]));
+            }
+            switch (fmt) {
+                case W4A16_FMT_G128_ASYM_BF16:
+                    if (!fits_bf16((hi - lo) / 15.0f) || !fits_bf16(lo)) return W4A16_ERR_INVALID;
+                    break;
+                case W4A16_FMT_G128_ZP_FP16:
+                    if (!fits_fp16((hi - lo) / 15.0f)) return W4A16_ERR_INVALID;
+                    break;
+                case W4A16_FMT_Q4_B32_SYM_FP16:
+                    if (!fits_fp16(amax / 7.0f)) return W4A16_ERR_INVALID;
+                    break;
+                default:  // W8: an fp32 scale max|w| / 127 is always finite
+                    break;
+            }
+        }
+    }
+    return W4A16_OK;
+}
+
 w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N, int64_t K, void* codes,
                                    void* scales, void* mins, hipStream_t stream) {
     w4a16_status_t st = check_shape(fmt, N, K);
@@ -120,6 +176,14 @@ w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N
     st = check_packed(fmt, codes, scales, mins);
     if (st != W4A16_OK) return st;
     w4a16::clear_stale_error();
+    if (debug_checks_enabled()) {  // debug only: a synchronous copy of W to the host
+        std::vector<float> host((size_t)N * (size_t)K);
+        if (hipStreamSynchronize(stream) != hipSuccess ||
+            hipMemcpy(host.data(), W, host.size() * sizeof(float), hipMemcpyDeviceToHost) != hipSuccess)
+            return W4A16_ERR_DEVICE;
+        st = w4a16_check_weights(fmt, host.data(), N, K);
+        if (st != W4A16_OK) return st;
+    }
     if (fmt == W4A16_FMT_G128_ASYM_BF16)
         return from_hip(w4a16::launch_pack_g128(W, N, K, static_cast<uint32_t*>(codes), static_cast<uint16_t*>(scales),
                                                 static_cast<uint16_t*>(mins), stream));

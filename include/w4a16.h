@@ -99,7 +99,14 @@ typedef enum {
 const char* w4a16_status_string(w4a16_status_t status);
 
 /* Bytes to allocate for the three packed arrays of an N x K weight in `fmt` (mins is 0 for the
- * Q4 and W8 formats).  For G128 the scale and minimum sizes are the arrays' sizes rounded up to a
+ * Q4 and W8 formats).  G128 and the zero-point format store N*K/2 bytes of codes and two 2-byte
+ * values per group of 128, 4 + 32/128 = 4.25 bits per weight (vidyal.ai "Low-Precision Kernels",
+ * "Step 1": the 4.25 bits per weight behind the 3.76x ceiling over bf16, and "Step 2": a K/8 x N
+ * word matrix with K/128 x N scales and minimums).  Q4 stores 16 code bytes and a 2-byte fp16
+ * scale per block of 32 weights, 18 bytes or 4.5 bits per weight (thuongvuho.com "Why My 4-Bit
+ * CUDA Kernel Wasn't Faster", introduction and "Why fewer bytes should have helped").  W8 stores
+ * one byte per weight and a 4-byte scale per row (anrans.github.io "Quantization and GEMV",
+ * "Exercises", 1).  For G128 the scale and minimum sizes are the arrays' sizes rounded up to a
  * multiple of 4 bytes: the GEMM reads them as aligned 4-byte words, so when (K/128)*N is odd
  * the last word covers 2 bytes past the last element (read, never written, value unused).
  * Buffers passed to the matmul entry points must have at least these sizes.
@@ -113,9 +120,25 @@ w4a16_status_t w4a16_packed_sizes(w4a16_format_t fmt, int64_t N, int64_t K,
  * thuongvuho.com "Why My 4-Bit CUDA Kernel Wasn't Faster", introduction and "Loading the same
  * bytes differently" (Q4: per (n, block) absmax/7 fp16 scale, codes + 8).
  * Output arrays as described by w4a16_format_t, all written in full (mins: G128 only; NULL
- * for Q4).  The result is bit-identical to the CPU definition. */
+ * for Q4).  The result is bit-identical to the CPU definition.  With W4A16_DEBUG_CHECKS set, the
+ * call first synchronizes `stream`, copies W to host memory it allocates and frees, and returns
+ * the status of w4a16_check_weights on it (ERR_INVALID before any launch). */
 w4a16_status_t w4a16_quantize_pack(w4a16_format_t fmt, const float* W, int64_t N, int64_t K,
                                    void* codes, void* scales, void* mins, hipStream_t stream);
+
+/* Debug check of weights before they are quantized, on HOST memory: W [N][K] fp32 row-major.
+ * Returns W4A16_ERR_INVALID if a weight is not finite or if a group's stored parameter would
+ * overflow its storage type: for Q4 a block with max|w| / 7 at or above 65520 (the fp16 scale
+ * would round to infinity, i.e. max|w| > 7 x 65504 in round numbers; thuongvuho.com "Why My 4-Bit
+ * CUDA Kernel Wasn't Faster", introduction: the fp16 block scale); for the zero-point format a
+ * group with (max - min) / 15 at or above 65520 (anrans.github.io "Quantization and GEMV", "The
+ * quantization formulas", the scale kept in fp16); for G128 a scale (max - min) / 15 or minimum
+ * whose bf16 rounding overflows (vidyal.ai "Low-Precision Kernels", "Step 2").  W4A16_OK
+ * otherwise.  Pure host code: no HIP call, no allocation.  Shape checks as w4a16_packed_sizes.
+ * w4a16_quantize_pack runs this check itself (on a host copy of W, after synchronizing `stream`)
+ * when the environment variable W4A16_DEBUG_CHECKS is set to a value other than "0"; without it
+ * the quantizers do not check, and non-finite or overflowing weights give undefined codes. */
+w4a16_status_t w4a16_check_weights(w4a16_format_t fmt, const float* W_host, int64_t N, int64_t K);
 
 /* Reference dequant: W_hat [N][K] (row-major) in `out_dtype` (BF16, FP16 or FP32), each value
  * the round-to-nearest-even of the fp32 dequantized weight (fmaf(q, s, m) for G128,

@@ -207,3 +207,51 @@ def test_w4a8_validation():
         == w.W4A16_ERR_INVALID                                                               # misaligned xsum
     assert _status(g, G128, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, 256, 1024, FAKE, 0) == w.W4A16_ERR_INVALID
     assert _status(g, G128, FAKE, FAKE, FAKE, 64, FAKE, FAKE, FAKE, 256, 1000, FAKE, 0) == w.W4A16_ERR_INVALID
+
+
+def test_check_weights_rejects_what_the_formats_cannot_store():
+    """The debug weight check (host memory, no GPU): every weight finite, and each group's stored
+    parameter representable -- the Q4 fp16 scale max|w|/7 and the zero-point format's fp16 scale
+    (max - min)/15 below 65520 (the rounding midpoint past fp16's largest value, 65504), the G128
+    bf16 scale and minimum below bf16's overflow midpoint."""
+    import numpy as np
+    ZP, W8 = w.W4A16_FMT_G128_ZP_FP16, w.W4A16_FMT_W8_ROW_FP32
+    ok = (np.random.default_rng(0).standard_normal((4, 256)) * 0.02).astype(np.float32)
+    for fmt in (G128, Q4, ZP, W8):
+        w.w4a16_check_weights(fmt, ok, 4, 256)
+    for fmt in (G128, Q4, ZP, W8):
+        bad = ok.copy()
+        bad[2, 200] = np.nan
+        assert _status(w.w4a16_check_weights, fmt, bad, 4, 256) == w.W4A16_ERR_INVALID
+        bad[2, 200] = np.inf
+        assert _status(w.w4a16_check_weights, fmt, bad, 4, 256) == w.W4A16_ERR_INVALID
+    # Q4: max|w| / 7 just below and at the fp16 overflow midpoint, in the last block of a row
+    edge = np.float32(65520.0 * 7)
+    q4 = ok.copy()
+    q4[3, 255] = np.nextafter(edge, np.float32(0))
+    assert np.float32(q4[3, 255]) / np.float32(7) < 65520
+    w.w4a16_check_weights(Q4, q4, 4, 256)
+    q4[3, 255] = -edge
+    assert _status(w.w4a16_check_weights, Q4, q4, 4, 256) == w.W4A16_ERR_INVALID
+    w.w4a16_check_weights(G128, q4, 4, 256)          # bf16 holds that scale; W8's fp32 too
+    w.w4a16_check_weights(W8, q4, 4, 256)
+    # zero-point format: the range sets the scale (a group from -a to +a has scale 2a / 15)
+    zp = ok.copy()
+    zp[1, 0], zp[1, 1] = -4.0e5, 4.0e5             # 8e5 / 15 = 53333: fits
+    w.w4a16_check_weights(ZP, zp, 4, 256)
+    zp[1, 1] = 6.0e5                                # 1e6 / 15 = 66667: overflows fp16
+    assert _status(w.w4a16_check_weights, ZP, zp, 4, 256) == w.W4A16_ERR_INVALID
+    assert _status(w.w4a16_check_weights, Q4, zp, 4, 256) == w.W4A16_ERR_INVALID   # 6e5 / 7
+    w.w4a16_check_weights(G128, zp, 4, 256)
+    # G128: a range that overflows fp32 (and so the bf16 scale), and a minimum past bf16's range
+    g = ok.copy()
+    g[0, 5], g[0, 6] = -3.0e38, 3.0e38
+    assert _status(w.w4a16_check_weights, G128, g, 4, 256) == w.W4A16_ERR_INVALID
+    g = ok.copy()
+    g[0, :128] = np.float32(-3.4e38)                # a constant group: scale 0 (fine), min overflows bf16
+    assert _status(w.w4a16_check_weights, G128, g, 4, 256) == w.W4A16_ERR_INVALID
+    g[0, :128] = np.float32(-3.38e38)              # rounds to bf16's largest finite value
+    w.w4a16_check_weights(G128, g, 4, 256)
+    # shape errors as w4a16_packed_sizes
+    assert _status(w.w4a16_check_weights, G128, ok, 4, 100) == w.W4A16_ERR_INVALID
+    assert _status(w.w4a16_check_weights, G128, None, 4, 256) == w.W4A16_ERR_INVALID
