@@ -77,6 +77,17 @@ __device__ __forceinline__ float wave_sum(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
+// Orders one wave's own LDS accesses where its lanes exchange values through LDS: the writes
+// before the barrier are complete and visible to every lane of the wave before the reads after
+// it (and reads before it complete before later writes).  Wavefront scope: the hardware already
+// runs one wave's LDS operations in order, so this only keeps the compiler from moving LDS
+// accesses across it and costs no instruction.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x / kWave); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 

@@ -15,8 +15,9 @@
 //    LDS in the same order;
 //  * a fifth MFMA against a B fragment of ones gives sum(x) per row and group in the same
 //    accumulator layout, so the group epilogue is s * acc + (min - 128 s) * sum(x);
-//  * the activations a wave needs (its 4 groups x M rows) are staged in its own LDS slice, so no
-//    barrier is needed before the math; lanes whose A row is past M read a zero row.
+//  * the activations a wave needs (its 4 groups x M rows) are staged in its own LDS slice, so only
+//    a wave-scope ordering (no block barrier) is needed before the math; lanes whose A row is past
+//    M read a zero row.
 // The waves' partial sums are added through LDS in a fixed order, so results are bitwise
 // reproducible.  All global loads are issued before the first MFMA and never under a branch.
 #include "device_common.h"
@@ -183,6 +184,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
             const int c = q & 15, m = (q >> 4) % MR, j = q / (16 * MR);
             xs[wave][j][m][c] = m < M ? pair_up(xr[i]) : make_uint4(0, 0, 0, 0);
         }
+        wave_lds_sync();  // the slice is read below by other lanes of this wave
 
         // 5) per group: 4 k-steps of (TPL + 1) MFMAs, then the group epilogue
 #pragma unroll
@@ -211,6 +213,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
                 }
             }
         }
+        wave_lds_sync();  // this pass's reads of the slice precede the next pass's writes
     }
 
     // 6) partial sums through LDS: each wave reuses its own activation slice (it has finished

@@ -610,6 +610,7 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
             xw[wave][0][lane] = x1;  // read back by this wave only, after its own write
         }
         if constexpr (kStageX) {
+            wave_lds_sync();  // the codes just written by this wave's lanes are read across lanes
             const int ar = min(lr, MR - 1);  // A rows past the staged ones repeat one: never stored
 #pragma unroll
             for (int j = 0; j < kR16Gpp; ++j)
@@ -645,6 +646,7 @@ __global__ __launch_bounds__(64 * kR16Waves) void w4a8_rows16_kernel(
                 }
             }
         }
+        if constexpr (kStageX) wave_lds_sync();  // this pass's reads precede the next pass's writes
     }
 
     // the waves' sums through LDS, added in wave order; y = bf16(a_m * sum)
