@@ -8,15 +8,23 @@ A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one ba
 synthetic input, with packed weights, activations and output already resident in HBM.  The
 headline workload is the decode GEMV on the Llama-3-8B up-projection shape (M=1, K=4096,
 N=14336, group-128 asymmetric format); its value is effective weight bytes (codes + scales +
-mins) per second.  To keep the 256 MB Infinity Cache from serving the weights, the steps rotate
-over enough packed copies to exceed 512 MB.  The K timed steps are captured once into a HIP
-graph (so host launch cost does not pace the GPU) and replayed; the graph is first replayed
-untimed for WARM_SECONDS so that the GPU's clocks have settled, then HIP events on the launch
-stream bracket one replay and give the average duration per launch used for the roofline.
+mins) per second over the wall time of the K timed steps.  To keep the 256 MB Infinity Cache
+from serving the weights, the steps rotate over enough packed copies to exceed 512 MB.  The K
+timed steps are captured once into a HIP graph (so host launch cost does not pace the GPU) and
+replayed; the graph is first replayed untimed for WARM_SECONDS so that the GPU's clocks have
+settled.
+
+Kernel durations (the roofline and every secondary figure) follow vidyal.ai "Low-Precision
+Kernels", "How the measurements were taken" (medians over many launches, three rounds, cold
+cache): a HIP graph of at least 100 back-to-back launches rotating over the cold copies is
+replayed three times, each replay bracketed by HIP events on the launch stream, and the median of
+the three per-launch averages is reported with all three.  Beside each figure stand measured
+roofs timed the same way: a plain streaming read of the same bytes and an empty launch
+(libw4a16_roof.so), and for prefill hipBLASLt's bf16-weight GEMM of the same shape.
 
 Prints ONE JSON line.  Secondary figures (prefill TFLOPS at M=1024 with a hipBLASLt bf16-weight
 GEMM beside it, the Q4 block-32 GEMV, the decode shape in the zero-point and W8A16 formats, the batch
-sweep) go under "extra".
+sweep, W4A8) go under "extra".
 """
 from __future__ import annotations
 
@@ -38,6 +46,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 MFMA_I8_PEAK_TOPS = 5000.0     # MI355X dense int8 MFMA, TOP/s
 CACHE_BYTES = 256 * 2 ** 20    # MI355X Infinity Cache (MALL)
 WARM_SECONDS = 0.25            # untimed run-up of each workload before its timed replay
+ROUNDS = 3                     # timed replays of a kernel's graph; the median is reported
+MIN_LAUNCHES = 100             # launches per timed replay (rounded up to whole rotations)
 METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
 DECODE_KERNEL = "skinny_g128_kernel<1, 4, 16, true>"
 PREFILL_KERNEL = "gemm_g128_kernel<256, 224, 4, 1, 3, true, 1>"
@@ -71,7 +81,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=170)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode", "w4a8_sweep"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode", "w4a8_sweep",
+                                       "cpu"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -153,7 +164,105 @@ def copies_for(weight_bytes: int) -> int:
     return max(1, math.ceil(2 * CACHE_BYTES / weight_bytes))
 
 
+def time_rounds(step, copies: int, rounds: int = ROUNDS):
+    """Per-launch duration of `step(i)` (i selects the weight copy i % copies): L >= MIN_LAUNCHES
+    launches in one HIP graph, replayed untimed for WARM_SECONDS, then `rounds` replays each
+    bracketed by HIP events on the launch stream.  Returns {"us": median of the rounds' per-launch
+    averages, "rounds_us": [...], "launches_per_round": L}."""
+    import torch
+    L = copies * math.ceil(MIN_LAUNCHES / copies)
+    for i in range(min(L, 2 * copies)):
+        step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(L):
+            step(i)
+    t_warm = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t_warm >= WARM_SECONDS:
+            break
+    per = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / L)
+    del g
+    return {"us": float(np.median(per)), "rounds_us": [round(v, 4) for v in per], "launches_per_round": L}
+
+
+class Roofs:
+    """The measured roofs of libw4a16_roof.so: a plain 16-byte non-temporal streaming read and an
+    empty launch, timed like the kernels (graph, rotated cold copies, median of three rounds)."""
+
+    def __init__(self):
+        import ctypes
+        import torch
+        path = os.path.join(ROOT, "gemm_w4a16_amd", "libw4a16_roof.so")
+        self.lib = ctypes.CDLL(path)
+        self.lib.roof_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p]
+        self.lib.roof_empty.argtypes = [ctypes.c_void_p]
+        self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+
+    def _stream(self):
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+
+    def empty_launch_us(self):
+        def step(i):
+            assert self.lib.roof_empty(self._stream()) == 0
+        return time_rounds(step, 1)["us"]
+
+    def read(self, nbytes: int, copies: int):
+        """Fastest of a few grid sizes for a cold read of `nbytes` per launch."""
+        import torch
+        bufs = [torch.randint(0, 256, (nbytes,), dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        best = None
+        one_pass = (nbytes // 16 + 1023) // 1024
+        for blocks in (one_pass, 2048, 1024, 512):
+            def step(i, blocks=blocks):
+                assert self.lib.roof_read(bufs[i % copies].data_ptr(), nbytes, self.sink.data_ptr(), blocks,
+                                          self._stream()) == 0
+            r = time_rounds(step, copies)
+            if best is None or r["us"] < best["us"]:
+                best = dict(r, blocks=blocks)
+        del bufs
+        torch.cuda.empty_cache()
+        best["gbs"] = nbytes / best["us"] / 1e3
+        best["bytes"] = nbytes
+        best["kernel"] = "roof_read_kernel (16-byte non-temporal loads, 4 in flight per lane)"
+        return best
+
+
+def time_rounds_eager(step, rounds: int = ROUNDS):
+    """As time_rounds, for library calls kept out of graphs (hipBLASLt through torch.matmul):
+    MIN_LAUNCHES eager launches per round, bracketed by HIP events."""
+    import torch
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < WARM_SECONDS:
+        for i in range(10):
+            step(i)
+        torch.cuda.synchronize()
+    per = []
+    for _ in range(rounds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(MIN_LAUNCHES):
+            step(i)
+        e1.record()
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / MIN_LAUNCHES)
+    return {"us": float(np.median(per)), "rounds_us": [round(v, 4) for v in per], "launches_per_round": MIN_LAUNCHES}
+
+
 def bench_decode(steps, warmup):
+    """The headline: K steps for the wall-clock value, then the kernel's own duration."""
     import gemm_w4a16_amd as w
     import workloads
     wl = workloads.DECODE
@@ -162,53 +271,48 @@ def bench_decode(steps, warmup):
     R = copies_for(c + s + m)
     st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, R)
     wall, ev = time_steps(st, steps, warmup)
+    kt = time_rounds(st.step, R)
     algo_bytes = st.weight_bytes + wl.M * wl.K * 2 + wl.M * wl.N * 2
-    return wl, st, R, wall, ev, algo_bytes, W, x
+    return wl, st, R, wall, ev, kt, algo_bytes, W, x
 
 
-def bench_prefill(steps, warmup):
+def bench_prefill():
     import torch
     import gemm_w4a16_amd as w
     import workloads
     wl = workloads.PREFILL
     W, x = workloads.inputs(wl)
     st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, 1)
-    wall, ev = time_steps(st, steps, warmup)
+    kt = time_rounds(st.step, 1)
     flops = 2.0 * wl.M * wl.N * wl.K
-    # comparator: the same product with bf16 weights (the GPU's own dequantized weights) through
-    # torch.matmul (hipBLASLt)
+    t = kt["us"] * 1e-6
+    # the measured roof: the same product with bf16 weights (the GPU's own dequantized weights)
+    # through torch.matmul (hipBLASLt)
     Wb = torch.empty((wl.N, wl.K), dtype=torch.int16, device="cuda")
     w.w4a16_dequant(w.W4A16_FMT_G128_ASYM_BF16, *st.copies[0], wl.N, wl.K, w.W4A16_BF16, Wb)
     Wt = Wb.view(torch.bfloat16).t().contiguous()   # [K][N]
     xb = st.x.view(torch.bfloat16)
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < WARM_SECONDS:
-        for _ in range(steps):
-            yb = torch.matmul(xb, Wt)
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        yb = torch.matmul(xb, Wt)
-    e1.record()
-    torch.cuda.synchronize()
-    t_bf16 = e0.elapsed_time(e1) / 1e3 / steps
+    yb = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    bt = time_rounds_eager(lambda i: torch.matmul(xb, Wt, out=yb))
     del Wb, Wt, yb
     return {
-        "workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K, "steps": steps,
-        "us_per_step_wall": wall / steps * 1e6, "us_per_launch_events": ev / steps * 1e6,
-        "tflops": flops / (ev / steps) / 1e12,
-        "frac_mfma_bf16_peak": flops / (ev / steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": flops / (ev / steps) / 1e12,
+        "workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
+        "us_per_launch": kt["us"], "us_per_launch_rounds": kt["rounds_us"],
+        "launches_per_round": kt["launches_per_round"],
+        "tflops": flops / t / 1e12,
+        "frac_mfma_bf16_peak": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": flops / t / 1e12,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": flops / (ev / steps) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": recorded_traffic(PREFILL_KERNEL)},
-        "bf16_weight_gemm_hipblaslt_tflops": flops / t_bf16 / 1e12,
-        "bf16_weight_gemm_us": t_bf16 * 1e6,
+                     "frac": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": recorded_traffic(PREFILL_KERNEL),
+                     "measured_roof": {"kernel": "hipBLASLt bf16-weight GEMM (torch.matmul) of the same shape",
+                                       "us": bt["us"], "us_rounds": bt["rounds_us"],
+                                       "tflops": flops / (bt["us"] * 1e-6) / 1e12,
+                                       "frac_of_measured_roof": bt["us"] / kt["us"]}},
     }
 
 
-def bench_q4(steps, warmup):
+def bench_q4(roofs):
     import gemm_w4a16_amd as w
     import workloads
     wl = workloads.Q4
@@ -217,18 +321,25 @@ def bench_q4(steps, warmup):
     R = copies_for(c + s + m)
     st = Setup(w.W4A16_FMT_Q4_B32_SYM_FP16, wl.M, wl.N, wl.K, x, W, R)
     del W
-    wall, ev = time_steps(st, steps, warmup)
+    kt = time_rounds(st.step, R)
+    t = kt["us"] * 1e-6
     out = {
-        "workload": wl.name, "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R, "steps": steps,
-        "weight_bytes": st.weight_bytes, "us_per_launch_events": ev / steps * 1e6,
-        "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
-        "frac_hbm_peak": st.weight_bytes * steps / ev / 1e9 / HBM_PEAK_GBS,
+        "workload": wl.name, "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R,
+        "weight_bytes": st.weight_bytes, "us_per_launch": kt["us"], "us_per_launch_rounds": kt["rounds_us"],
+        "launches_per_round": kt["launches_per_round"],
+        "effective_weight_gbs": st.weight_bytes / t / 1e9,
+        "frac_hbm_peak": st.weight_bytes / t / 1e9 / HBM_PEAK_GBS,
     }
-    out["fp16_weight_gemv"] = fp16_gemv_comparator(st, wl, steps)
+    out["fp16_weight_gemv"] = fp16_gemv_comparator(st, wl)
+    del st
+    import torch
+    torch.cuda.empty_cache()
+    rr = roofs.read(c + s + m, R)
+    out["measured_roof"] = {"read_us": rr["us"], "read_gbs": rr["gbs"], "frac_of_measured_roof": rr["us"] / kt["us"]}
     return out
 
 
-def fp16_gemv_comparator(st, wl, steps):
+def fp16_gemv_comparator(st, wl):
     """Context for the Q4 GEMV (thuongvuho.com, "Why My 4-Bit CUDA Kernel Wasn't Faster", measures
     its kernels against a GEMV over fp16 weights): the same product with the GPU's own dequantized
     weights in fp16 (512 MB, larger than the Infinity Cache, so every call reads them from HBM)
@@ -239,24 +350,14 @@ def fp16_gemv_comparator(st, wl, steps):
     w.w4a16_dequant(w.W4A16_FMT_Q4_B32_SYM_FP16, *st.copies[0], wl.N, wl.K, w.W4A16_FP16, Wh)
     Wt = Wh.view(torch.float16)
     xh = st.x.view(torch.float16).reshape(wl.K, 1)
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < WARM_SECONDS:
-        for _ in range(steps):
-            yh = torch.matmul(Wt, xh)
-        torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(steps):
-        yh = torch.matmul(Wt, xh)
-    e1.record()
-    torch.cuda.synchronize()
-    t = e0.elapsed_time(e1) / 1e3 / steps
+    yh = torch.empty((wl.N, 1), dtype=torch.float16, device="cuda")
+    r = time_rounds_eager(lambda i: torch.matmul(Wt, xh, out=yh))
     nbytes = wl.N * wl.K * 2
     del Wh, Wt, yh
-    return {"us": t * 1e6, "weight_bytes": nbytes, "gbs": nbytes / t / 1e9}
+    return {"us": r["us"], "us_rounds": r["rounds_us"], "weight_bytes": nbytes, "gbs": nbytes / r["us"] / 1e3}
 
 
-def bench_decode_warm(steps, warmup, W):
+def bench_decode_warm(W):
     """The decode GEMV with ONE weight copy, which stays resident in the 256 MB Infinity Cache:
     a warm number, reported beside (never instead of) the cold, rotated-copy headline."""
     import gemm_w4a16_amd as w
@@ -264,14 +365,14 @@ def bench_decode_warm(steps, warmup, W):
     wl = workloads.DECODE
     _, x = workloads.inputs(wl)
     st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, 1)
-    wall, ev = time_steps(st, steps, warmup)
-    return {"workload": wl.name + "_warm", "weight_copies": 1, "steps": steps,
-            "us_per_launch_events": ev / steps * 1e6,
-            "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
+    kt = time_rounds(st.step, 1)
+    return {"workload": wl.name + "_warm", "weight_copies": 1, "us_per_launch": kt["us"],
+            "us_per_launch_rounds": kt["rounds_us"],
+            "effective_weight_gbs": st.weight_bytes / kt["us"] / 1e3,
             "cache": "weights resident in the 256 MB Infinity Cache"}
 
 
-def bench_rowfmt(wl, fmt, steps, warmup, W=None):
+def bench_rowfmt(wl, fmt, W=None):
     """A decode-shape GEMV in one of the further formats (fp16 activations)."""
     import workloads
     Wn, x = workloads.inputs(wl)
@@ -281,27 +382,28 @@ def bench_rowfmt(wl, fmt, steps, warmup, W=None):
     c, s, m = w.w4a16_packed_sizes(fmt, wl.N, wl.K)
     R = copies_for(c + s + m)
     st = Setup(fmt, wl.M, wl.N, wl.K, x, W, R)
-    wall, ev = time_steps(st, steps, warmup)
+    kt = time_rounds(st.step, R)
+    t = kt["us"] * 1e-6
     return {
-        "workload": wl.name, "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R, "steps": steps,
-        "weight_bytes": st.weight_bytes, "us_per_launch_events": ev / steps * 1e6,
-        "effective_weight_gbs": st.weight_bytes * steps / ev / 1e9,
-        "frac_hbm_peak": st.weight_bytes * steps / ev / 1e9 / HBM_PEAK_GBS,
+        "workload": wl.name, "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R,
+        "weight_bytes": st.weight_bytes, "us_per_launch": kt["us"], "us_per_launch_rounds": kt["rounds_us"],
+        "effective_weight_gbs": st.weight_bytes / t / 1e9,
+        "frac_hbm_peak": st.weight_bytes / t / 1e9 / HBM_PEAK_GBS,
     }
 
 
-def bench_zp(steps, warmup, W=None):
+def bench_zp(W=None):
     """The decode shape in the zero-point format (fp16 scale and zero point per 128, fp16 x)."""
     import gemm_w4a16_amd as w
     import workloads
-    return bench_rowfmt(workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16, steps, warmup, W)
+    return bench_rowfmt(workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16, W)
 
 
-def bench_w8(steps, warmup, W=None):
+def bench_w8(W=None):
     """The decode shape as per-row int8 weights (W8A16, fp16 x)."""
     import gemm_w4a16_amd as w
     import workloads
-    return bench_rowfmt(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32, steps, warmup, W)
+    return bench_rowfmt(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32, W)
 
 
 class W4A8Setup:
@@ -330,20 +432,20 @@ class W4A8Setup:
         w.w4a16_gemm_w4a8(w.W4A16_FMT_G128_ASYM_BF16, *self.q, wl.M, *self.packed, wl.N, wl.K, self.y)
 
 
-def bench_w4a8(steps, warmup):
+def bench_w4a8():
     """W4A8 at the prefill shape (M=1024, K=4096, N=14336): quantize + product per step, and the
     product alone against the int8 matrix-core peak."""
     import workloads
     wl = workloads.PREFILL
     W, x = workloads.inputs(wl)
     ops = 2.0 * wl.M * wl.N * wl.K
-    out = {"workload": "w4a8_gemm_m1024_k4096_n14336", "M": wl.M, "N": wl.N, "K": wl.K, "steps": steps}
+    out = {"workload": "w4a8_gemm_m1024_k4096_n14336", "M": wl.M, "N": wl.N, "K": wl.K}
     for gemm_only in (False, True):
         st = W4A8Setup(wl, W, x, gemm_only)
-        wall, ev = time_steps(st, steps, warmup)
-        t = ev / steps
+        kt = time_rounds(st.step, 1)
+        t = kt["us"] * 1e-6
         key = "gemm_only" if gemm_only else "quantize_and_gemm"
-        out[key] = {"us_per_step_events": t * 1e6, "tops": ops / t / 1e12}
+        out[key] = {"us_per_step": kt["us"], "us_rounds": kt["rounds_us"], "tops": ops / t / 1e12}
         if gemm_only:
             out["roofline"] = {"bound": "mfma", "kernel": "w4a8_gemm_kernel", "achieved": ops / t / 1e12,
                                "peak": MFMA_I8_PEAK_TOPS, "unit": "TOP/s", "frac": ops / t / 1e12 / MFMA_I8_PEAK_TOPS,
@@ -374,7 +476,7 @@ class W4A8DecodeSetup(Setup):
         w.w4a16_gemm_w4a8(self.fmt, *self.q, self.M, c, s, m, self.N, self.K, self.y)
 
 
-def bench_w4a8_decode(steps, warmup, W=None):
+def bench_w4a8_decode(W=None):
     """W4A8 at the decode shape (M=1, K=4096, N=14336), cold weights, as effective weight GB/s
     against the HBM peak: quantize + product (two launches), the product alone, and the fused
     one-launch form."""
@@ -385,19 +487,19 @@ def bench_w4a8_decode(steps, warmup, W=None):
     import gemm_w4a16_amd as w
     c, s, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl.N, wl.K)
     R = copies_for(c + s + m)
-    out = {"workload": "w4a8_gemv_m1_k4096_n14336", "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R,
-           "steps": steps}
+    out = {"workload": "w4a8_gemv_m1_k4096_n14336", "M": 1, "N": wl.N, "K": wl.K, "weight_copies": R}
     for mode in ("quantize_and_gemm", "gemm_only", "fused"):
         st = W4A8DecodeSetup(wl, W, x, R, mode)
-        wall, ev = time_steps(st, steps, warmup)
-        t = ev / steps
-        out[mode] = {"us_per_step_events": t * 1e6, "effective_weight_gbs": st.weight_bytes / t / 1e9,
+        kt = time_rounds(st.step, R)
+        t = kt["us"] * 1e-6
+        out[mode] = {"us_per_step": kt["us"], "us_rounds": kt["rounds_us"],
+                     "effective_weight_gbs": st.weight_bytes / t / 1e9,
                      "frac_hbm_peak": st.weight_bytes / t / 1e9 / HBM_PEAK_GBS}
         del st
     return out
 
 
-def bench_w4a8_sweep(steps, warmup, W=None):
+def bench_w4a8_sweep(W=None):
     """W4A8 product alone (activations quantized once, before the timed steps) over the batch
     sweep's M at K=4096, N=14336, cold weights: which kernel each M takes and its time."""
     import gemm_w4a16_amd as w
@@ -416,14 +518,13 @@ def bench_w4a8_sweep(steps, warmup, W=None):
             base = st.copies
         else:
             st.copies = base  # reuse the rotated weight copies
-        wall, ev = time_steps(st, steps, warmup)
-        t = ev / steps
+        t = time_rounds(st.step, R)["us"] * 1e-6
         out.append({"M": M, "kernel": "rows16" if M <= 64 else "gemm", "us": t * 1e6,
                     "effective_weight_gbs": st.weight_bytes / t / 1e9, "tops": 2.0 * M * wl.N * wl.K / t / 1e12})
     return out
 
 
-def bench_sweep(steps, warmup, W=None):
+def bench_sweep(W=None):
     import gemm_w4a16_amd as w
     import workloads
     wl1 = workloads.DECODE
@@ -441,30 +542,105 @@ def bench_sweep(steps, warmup, W=None):
             base = st.copies
         else:
             st.copies = base  # reuse the rotated weight copies
-        wall, ev = time_steps(st, steps, warmup)
-        t = ev / steps
+        kt = time_rounds(st.step, R)
+        t = kt["us"] * 1e-6
         out.append({"M": M, "path": "gemv" if M <= w.w4a16_matmul_gemv_cutoff() else "gemm",
-                    "us": t * 1e6, "effective_weight_gbs": st.weight_bytes / t / 1e9,
+                    "us": kt["us"], "us_rounds": kt["rounds_us"], "effective_weight_gbs": st.weight_bytes / t / 1e9,
                     "tflops": 2.0 * M * wl.N * wl.K / t / 1e12})
     return out
 
 
-def cpu_baseline(W, x):
-    """The oracle as it stands (single-threaded C, fp64) on the full decode GEMV."""
-    import oracle
-    codes, scales, mins = oracle.quantize_g128(W)
-    weight_bytes = codes.nbytes + scales.nbytes + mins.nbytes
-    times = []
-    t_start = time.perf_counter()
-    # about 10-15 s of CPU work: at least 3 runs, then more until 10 s have passed (at most 100)
-    while len(times) < 3 or (time.perf_counter() - t_start < 10.0 and len(times) < 100):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_threads() -> int:
+    """Host threads for the all-cores run: the cores this process may run on
+    (sched_getaffinity), capped by OMP_NUM_THREADS where the host sets it."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(cap)) if cap.isdigit() and int(cap) > 0 else n
+
+
+def oracle_outputs(fn_at, args, M, N, threads):
+    """Every output of an M x N product through the oracle's per-output entry point, split into
+    `threads` contiguous slices run on that many threads (the foreign calls release the GIL).
+    The oracle's arithmetic is unchanged: each output is its k-ordered fp64 sum."""
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.repeat(np.arange(M, dtype=np.int64), N)
+    cols = np.tile(np.arange(N, dtype=np.int64), M)
+    parts = np.array_split(np.arange(M * N), threads)
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda idx: fn_at(*args, rows[idx], cols[idx]), parts))
+
+
+def timed(fn, min_runs, budget_s):
+    times, t_start = [], time.perf_counter()
+    while len(times) < min_runs or (time.perf_counter() - t_start < budget_s and len(times) < 50):
         t0 = time.perf_counter()
-        oracle.matmul_g128(x, codes, scales, mins)
+        fn()
         times.append(time.perf_counter() - t0)
-    t = float(np.median(times))
-    return {"value": weight_bytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"the full decode GEMV (M=1, K=4096, N=14336) in fp64, {len(times)} runs "
-                      f"({sum(times):.1f} s), median {t:.3f} s, on {platform.processor() or platform.machine()}"}
+    return float(np.median(times)), len(times)
+
+
+def cpu_baseline(W, x):
+    """The oracle as it stands (plain C, fp64 sums in k order) on the host, single-threaded and on
+    all the cores this process may use, over bounded samples of the workloads: the full decode
+    GEMV, the full 16384^2 Q4 GEMV, and row slices of prefill."""
+    import oracle
+    import workloads
+    T = cpu_threads()
+    legs = {}
+    codes, scales, mins = oracle.quantize_g128(W)
+    wbytes = codes.nbytes + scales.nbytes + mins.nbytes
+    wl = workloads.DECODE
+    t1, n1 = timed(lambda: oracle.matmul_g128(x, codes, scales, mins), 3, 5.0)
+    tT, nT = timed(lambda: oracle_outputs(oracle.matmul_g128_at, (x, codes, scales, mins), 1, wl.N, T), 3, 1.0)
+    legs["decode_gemv"] = {"workload": wl.name, "weight_bytes": wbytes,
+                           "single_thread": {"s": t1, "runs": n1, "gbs": wbytes / t1 / 1e9},
+                           "all_cores": {"s": tT, "runs": nT, "threads": T, "gbs": wbytes / tT / 1e9}}
+    # prefill (M=1024): the first 8 rows on one thread, the first 64 on all cores
+    pw = workloads.PREFILL
+    _, xp = workloads.inputs(pw)
+    rows1, rowsT = 4, 64
+    t1p, _ = timed(lambda: oracle.matmul_g128(np.ascontiguousarray(xp[:rows1]), codes, scales, mins), 1, 0.0)
+    tTp, _ = timed(lambda: oracle_outputs(oracle.matmul_g128_at, (np.ascontiguousarray(xp[:rowsT]), codes, scales, mins),
+                                          rowsT, pw.N, T), 1, 0.0)
+    legs["prefill_gemm_row_slice"] = {
+        "workload": pw.name, "sample": f"rows 0..{rows1 - 1} on one thread, rows 0..{rowsT - 1} on all cores",
+        "single_thread": {"s": t1p, "rows": rows1, "gflops": 2.0 * rows1 * pw.N * pw.K / t1p / 1e9},
+        "all_cores": {"s": tTp, "rows": rowsT, "threads": T, "gflops": 2.0 * rowsT * pw.N * pw.K / tTp / 1e9},
+        "full_m1024_all_cores_s_extrapolated": tTp * pw.M / rowsT}
+    del xp
+    # Q4 block-32 GEMV, 16384 x 16384 (the oracle quantizes the weights first, untimed)
+    qw = workloads.Q4
+    Wq, xq = workloads.inputs(qw)
+    qc, qs = oracle.quantize_q4b32(Wq)
+    del Wq
+    qbytes = qc.nbytes + qs.nbytes
+    t1q, n1q = timed(lambda: oracle.matmul_q4b32(xq, qc, qs), 1, 0.0)
+    tTq, nTq = timed(lambda: oracle_outputs(oracle.matmul_q4b32_at, (xq, qc, qs), 1, qw.N, T), 3, 0.0)
+    legs["q4b32_gemv"] = {"workload": qw.name, "weight_bytes": qbytes,
+                          "single_thread": {"s": t1q, "runs": n1q, "gbs": qbytes / t1q / 1e9},
+                          "all_cores": {"s": tTq, "runs": nTq, "threads": T, "gbs": qbytes / tTq / 1e9}}
+    dec = legs["decode_gemv"]["all_cores"]
+    return {"value": dec["gbs"], "unit": "GB/s", "cores": T, "kind": "oracle",
+            "sample": (f"the full decode GEMV (M=1, K=4096, N=14336) in fp64 on {T} threads, median of "
+                       f"{dec['runs']} runs ({dec['s'] * 1e3:.1f} ms); single-threaded, the Q4 GEMV and "
+                       f"prefill row slices under 'legs'"),
+            "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0)), "legs": legs}
+
+
+def cpu_baseline_only():
+    import workloads
+    return cpu_baseline(*workloads.inputs(workloads.DECODE))
 
 
 def copy_calibration(mib: int):
@@ -496,17 +672,24 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
-        fn = {"prefill": bench_prefill, "q4": bench_q4, "sweep": bench_sweep, "zp": bench_zp, "w8": bench_w8,
-              "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
-              "w4a8_sweep": bench_w4a8_sweep}[args.only]
-        print(json.dumps({"only": args.only, "result": fn(args.steps, args.warmup)}), flush=True)
+        fn = {"prefill": bench_prefill, "q4": lambda: bench_q4(Roofs()), "sweep": bench_sweep, "zp": bench_zp,
+              "w8": bench_w8, "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
+              "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only}[args.only]
+        print(json.dumps({"only": args.only, "result": fn()}), flush=True)
         return
 
     log(f"decode: {args.warmup} warmup + {args.steps} timed steps")
-    wl, st, R, wall, ev, algo_bytes, W, x = bench_decode(args.steps, args.warmup)
-    per_launch = ev / args.steps
+    wl, st, R, wall, ev, kt, algo_bytes, W, x = bench_decode(args.steps, args.warmup)
+    per_launch = kt["us"] * 1e-6
     value = st.weight_bytes * args.steps / wall / 1e9
     achieved = algo_bytes / per_launch / 1e9
+    weight_bytes = st.weight_bytes
+    del st
+    torch.cuda.empty_cache()
+    log("measured roofs: empty launch, streaming read of the decode weight bytes")
+    roofs = Roofs()
+    empty_us = roofs.empty_launch_us()
+    rr = roofs.read(weight_bytes, R)
     line = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -523,46 +706,51 @@ def main():
         "config": {"workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
                    "format": "int4 codes, group 128 along K, bf16 scale + bf16 min",
                    "weights": "N(0,0.02) fp32 with 0.1% x20 outliers, seed 0", "activations": "bf16 N(0,1)",
-                   "weight_copies_rotated": R, "weight_bytes": st.weight_bytes,
+                   "weight_copies_rotated": R, "weight_bytes": weight_bytes,
                    "timing": "K eager launches" if EAGER else "K steps in one HIP graph replay",
                    "device": props.name,
                    "compute_units": props.multi_processor_count,
                    "frac_hbm_peak_effective_weight": value / HBM_PEAK_GBS},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(DECODE_KERNEL),
-                     "kernel": DECODE_KERNEL, "us_per_launch": per_launch * 1e6,
-                     "algorithmic_bytes_per_launch": algo_bytes},
+                     "kernel": DECODE_KERNEL, "us_per_launch": kt["us"], "us_per_launch_rounds": kt["rounds_us"],
+                     "launches_per_round": kt["launches_per_round"],
+                     "timing": "median of 3 rounds; a round is one HIP-graph replay of back-to-back launches "
+                               "over the rotated cold copies, bracketed by HIP events",
+                     "algorithmic_bytes_per_launch": algo_bytes,
+                     "measured_roof": {"read_us": rr["us"], "read_gbs": rr["gbs"], "read_blocks": rr["blocks"],
+                                       "read_us_rounds": rr["rounds_us"], "kernel": rr["kernel"],
+                                       "empty_launch_us": empty_us,
+                                       "frac_of_measured_roof": rr["us"] / kt["us"]}},
     }
-    del st
-    torch.cuda.empty_cache()
     if not args.no_extra and args.only is None:
         extra = {}
         log("decode, warm (one weight copy)")
-        extra["decode_warm_m1"] = bench_decode_warm(340, 34, W)
+        extra["decode_warm_m1"] = bench_decode_warm(W)
         torch.cuda.empty_cache()
         log("prefill M=1024")
-        extra["prefill_m1024"] = bench_prefill(20, 3)
+        extra["prefill_m1024"] = bench_prefill()
         torch.cuda.empty_cache()
         log("q4 block-32 GEMV")
-        extra["q4b32_m1"] = bench_q4(40, 4)
+        extra["q4b32_m1"] = bench_q4(roofs)
         torch.cuda.empty_cache()
         log("zero-point format GEMV (decode shape)")
-        extra["zp_decode_m1"] = bench_zp(340, 34, W)
+        extra["zp_decode_m1"] = bench_zp(W)
         torch.cuda.empty_cache()
         log("W8A16 per-row int8 GEMV (decode shape)")
-        extra["w8_decode_m1"] = bench_w8(200, 20, W)
+        extra["w8_decode_m1"] = bench_w8(W)
         torch.cuda.empty_cache()
         log("batch sweep")
-        extra["sweep"] = bench_sweep(34, 3, W)
+        extra["sweep"] = bench_sweep(W)
         torch.cuda.empty_cache()
         log("W4A8 at the prefill shape")
-        extra["w4a8_m1024"] = bench_w4a8(20, 3)
+        extra["w4a8_m1024"] = bench_w4a8()
         torch.cuda.empty_cache()
         log("W4A8 at the decode shape")
-        extra["w4a8_decode_m1"] = bench_w4a8_decode(340, 34, W)
+        extra["w4a8_decode_m1"] = bench_w4a8_decode(W)
         torch.cuda.empty_cache()
         log("W4A8 batch sweep")
-        extra["w4a8_sweep"] = bench_w4a8_sweep(34, 3, W)
+        extra["w4a8_sweep"] = bench_w4a8_sweep(W)
         torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline and args.only is None:
