@@ -25,7 +25,7 @@ EXPORTED = (
     "w4a16_status_string", "w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_dequant",
     "w4a16_gemv", "w4a16_gemv_max_rows", "w4a16_gemm_workspace_bytes", "w4a16_gemm",
     "w4a16_matmul", "w4a16_matmul_gemv_cutoff", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
-    "w4a16_matmul_w4a8", "w4a16_check_weights",
+    "w4a16_matmul_w4a8", "w4a16_check_weights", "w4a16_matmul_noalloc", "w4a16_matmul_noalloc_max_scratch_bytes",
 )
 
 
@@ -58,11 +58,14 @@ def _load() -> ctypes.CDLL:
     L.w4a16_gemm.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P, SZ, P]
     L.w4a16_matmul.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P, SZ, P]
     L.w4a16_matmul_gemv_cutoff.argtypes, L.w4a16_matmul_gemv_cutoff.restype = [], I64
+    L.w4a16_matmul_noalloc.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P]
+    L.w4a16_matmul_noalloc_max_scratch_bytes.argtypes = []
+    L.w4a16_matmul_noalloc_max_scratch_bytes.restype = SZ
     L.w4a16_quantize_act_i8.argtypes = [P, I64, I64, P, P, P, P]
     L.w4a16_gemm_w4a8.argtypes = [I, P, P, P, I64, P, P, P, I64, I64, P, P]
     L.w4a16_matmul_w4a8.argtypes = [I, P, I64, P, P, P, I64, I64, P, P]
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_check_weights", "w4a16_dequant", "w4a16_gemv",
-                 "w4a16_gemm", "w4a16_matmul", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
+                 "w4a16_gemm", "w4a16_matmul", "w4a16_matmul_noalloc", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
                  "w4a16_matmul_w4a8"):
         getattr(L, name).restype = I
     return L
@@ -148,6 +151,15 @@ def w4a16_matmul(fmt: int, act: int, x, M: int, codes, scales, mins, N: int, K: 
                  workspace_bytes: int = 0, stream=None) -> None:
     _ok(lib.w4a16_matmul(fmt, act, _p(x), M, _p(codes), _p(scales), _p(mins), N, K, _p(y), _p(workspace),
                          workspace_bytes, _stream(stream)), "w4a16_matmul")
+
+
+def w4a16_matmul_noalloc(fmt: int, act: int, x, M: int, codes, scales, mins, N: int, K: int, y, stream=None) -> None:
+    _ok(lib.w4a16_matmul_noalloc(fmt, act, _p(x), M, _p(codes), _p(scales), _p(mins), N, K, _p(y), _stream(stream)),
+        "w4a16_matmul_noalloc")
+
+
+def w4a16_matmul_noalloc_max_scratch_bytes() -> int:
+    return int(lib.w4a16_matmul_noalloc_max_scratch_bytes())
 
 
 def w4a16_matmul_gemv_cutoff() -> int:

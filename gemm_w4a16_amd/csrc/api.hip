@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/w4a16.h"
@@ -95,6 +96,38 @@ w4a16_status_t check_matmul_common(w4a16_format_t fmt, w4a16_dtype_t act, const 
     st = check_packed(fmt, codes, scales, mins);
     if (st != W4A16_OK) return st;
     return check_act(fmt, act);
+}
+
+// ---- The no-allocation entry point's scratch buffer -------------------------------------------
+// Split-K partial sums of the large-M GEMM for callers that cannot allocate a workspace.  One
+// array per GPU, in the code object's zero-initialised device data, held until the process ends.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+// `scratch` names a host-side stand-in in host code: its device address is looked up once per
+// device, with that device current, and only that address is passed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch address on the device that runs `stream` (the current device for the null stream).
+w4a16_status_t scratch_for_stream(hipStream_t stream, float** out) {
+    int cur = 0, dev = 0;
+    if (hipGetDevice(&cur) != hipSuccess) return W4A16_ERR_DEVICE;
+    dev = cur;
+    if (stream != nullptr && hipStreamGetDevice(stream, &dev) != hipSuccess) return W4A16_ERR_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return W4A16_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        if (dev != cur && hipSetDevice(dev) != hipSuccess) return W4A16_ERR_DEVICE;
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur && hipSetDevice(cur) != hipSuccess) return W4A16_ERR_DEVICE;
+        if (e != hipSuccess || p == nullptr) return W4A16_ERR_DEVICE;
+        g_scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return W4A16_OK;
 }
 
 }  // namespace
@@ -279,6 +312,21 @@ w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x
     if (fmt != W4A16_FMT_G128_ASYM_BF16 || (M > 0 && M <= kGemvCutoff))
         return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
     return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
+}
+
+size_t w4a16_matmul_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+w4a16_status_t w4a16_matmul_noalloc(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                                    const void* codes, const void* scales, const void* mins, int64_t N, int64_t K,
+                                    void* y, hipStream_t stream) {
+    w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
+    if (st != W4A16_OK) return st;
+    const bool gemm = fmt == W4A16_FMT_G128_ASYM_BF16 && M > kGemvCutoff;
+    const size_t need = gemm ? w4a16::gemm_g128_workspace_bytes(M, N, K) : 0;
+    if (need > kScratchBytes) return W4A16_ERR_UNSUPPORTED;
+    float* ws = nullptr;
+    if (need > 0 && (st = scratch_for_stream(stream, &ws)) != W4A16_OK) return st;
+    return w4a16_matmul(fmt, act, x, M, codes, scales, mins, N, K, y, ws, need, stream);
 }
 
 w4a16_status_t w4a16_quantize_act_i8(const void* x, int64_t M, int64_t K, int8_t* xq, float* ascale, float* xsum,

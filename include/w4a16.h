@@ -192,6 +192,24 @@ w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x
 /* The M at and below which w4a16_matmul takes the GEMV path for the G128 format. */
 int64_t w4a16_matmul_gemv_cutoff(void);
 
+/* For callers that cannot allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc: w4a16_matmul with no workspace argument.  Where the
+ * large-M GEMM splits K, its partial sums go to a scratch array inside the library: one per GPU,
+ * w4a16_matmul_noalloc_max_scratch_bytes() (16 MiB) in size, part of the library's device data from
+ * the first call on that GPU until the process ends.  A shape whose split needs more than that
+ * (w4a16_gemm_workspace_bytes of the shape) returns W4A16_ERR_UNSUPPORTED before any launch: use
+ * w4a16_matmul with a workspace.  Every call on one GPU shares that GPU's array, so calls that may
+ * run at the same time on one GPU (different streams, different host threads) race on it and
+ * must not overlap.  No call allocates or frees anything; the first call on each GPU looks up the
+ * array's device address (hipGetSymbolAddress, with that GPU current) and keeps it.  Results are
+ * bit-identical to w4a16_matmul's; other arguments and errors as for w4a16_matmul. */
+w4a16_status_t w4a16_matmul_noalloc(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                                    const void* codes, const void* scales, const void* mins, int64_t N,
+                                    int64_t K, void* y, hipStream_t stream);
+
+/* Size of w4a16_matmul_noalloc's per-GPU scratch array in bytes. */
+size_t w4a16_matmul_noalloc_max_scratch_bytes(void);
+
 /* ---- W4A8: int8 activations against the same 4-bit weights ------------------------------------
  * vidyal.ai "Low-Precision Kernels", "INT8 on a GeForce chip" and "The cost of quantizing
  * activations": the activations are quantized to int8 per row on every call, the integer

@@ -255,3 +255,16 @@ def test_check_weights_rejects_what_the_formats_cannot_store():
     # shape errors as w4a16_packed_sizes
     assert _status(w.w4a16_check_weights, G128, ok, 4, 100) == w.W4A16_ERR_INVALID
     assert _status(w.w4a16_check_weights, G128, None, 4, 256) == w.W4A16_ERR_INVALID
+
+
+def test_matmul_noalloc_validation():
+    """The no-allocation entry point checks like w4a16_matmul, and refuses on the host a shape
+    whose split-K partials exceed its scratch array (no device is touched by any of these)."""
+    f = w.w4a16_matmul_noalloc
+    assert w.w4a16_matmul_noalloc_max_scratch_bytes() == 16 << 20
+    assert _status(f, G128, BF16, FAKE, 0, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(f, G128, BF16, FAKE + 2, 1, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(f, G128, BF16, FAKE, 1, FAKE, FAKE, None, 256, 128, FAKE, 0) == w.W4A16_ERR_INVALID
+    assert _status(f, G128, F16, FAKE, 1, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert w.w4a16_gemm_workspace_bytes(G128, 2048, 520, 1024) > 16 << 20
+    assert _status(f, G128, BF16, FAKE, 2048, FAKE, FAKE, FAKE, 520, 1024, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
