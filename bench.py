@@ -82,7 +82,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode", "w4a8_sweep",
-                                       "cpu"], default=None,
+                                       "cpu", "rowfmt_sweep"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -392,6 +392,34 @@ def bench_rowfmt(wl, fmt, W=None):
     }
 
 
+ROWFMT_SWEEP_MS = (1, 2, 4, 8, 16, 32, 64)
+
+
+def bench_rowfmt_sweep(wl, fmt, W=None, Ms=ROWFMT_SWEEP_MS):
+    """A row-major format over several fp16 activation rows (one weight pass per call up to 64
+    rows), cold weights: the time per M, to show the weight stream's cost staying flat."""
+    import workloads
+    import gemm_w4a16_amd as w
+    if W is None:
+        W = workloads.inputs(wl)[0]
+    c, s, m = w.w4a16_packed_sizes(fmt, wl.N, wl.K)
+    R = copies_for(c + s + m)
+    out, base = [], None
+    for M in Ms:
+        x = workloads.activations(M, wl.K, "f16", wl.seed_x, rows_drawn=max(Ms))
+        st = Setup(fmt, M, wl.N, wl.K, x, W, R if base is None else 1)
+        if base is None:
+            base = st.copies
+        else:
+            st.copies = base
+        kt = time_rounds(st.step, R)
+        t = kt["us"] * 1e-6
+        out.append({"M": M, "us": kt["us"], "us_rounds": kt["rounds_us"],
+                    "effective_weight_gbs": st.weight_bytes / t / 1e9,
+                    "tflops": 2.0 * M * wl.N * wl.K / t / 1e12})
+    return out
+
+
 def bench_zp(W=None):
     """The decode shape in the zero-point format (fp16 scale and zero point per 128, fp16 x)."""
     import gemm_w4a16_amd as w
@@ -672,7 +700,12 @@ def main():
     if args.copy_calibration_mib:
         copy_calibration(args.copy_calibration_mib)
     if args.only and args.only != "decode":
+        import workloads
         fn = {"prefill": bench_prefill, "q4": lambda: bench_q4(Roofs()), "sweep": bench_sweep, "zp": bench_zp,
+              "rowfmt_sweep": lambda: {
+                  "zp": bench_rowfmt_sweep(workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16),
+                  "w8": bench_rowfmt_sweep(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32),
+                  "q4": bench_rowfmt_sweep(workloads.Q4, w.W4A16_FMT_Q4_B32_SYM_FP16, None, (1, 2, 4, 8, 16))},
               "w8": bench_w8, "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
               "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only}[args.only]
         print(json.dumps({"only": args.only, "result": fn()}), flush=True)
@@ -742,6 +775,14 @@ def main():
         torch.cuda.empty_cache()
         log("batch sweep")
         extra["sweep"] = bench_sweep(W)
+        torch.cuda.empty_cache()
+        import workloads
+        log("row-major formats over M (zero point and W8 at the decode shape, Q4 at 16384^2)")
+        extra["zp_sweep"] = bench_rowfmt_sweep(workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16, W)
+        torch.cuda.empty_cache()
+        extra["w8_sweep"] = bench_rowfmt_sweep(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32, W)
+        torch.cuda.empty_cache()
+        extra["q4_sweep"] = bench_rowfmt_sweep(workloads.Q4, w.W4A16_FMT_Q4_B32_SYM_FP16, None, (1, 2, 4, 8, 16))
         torch.cuda.empty_cache()
         log("W4A8 at the prefill shape")
         extra["w4a8_m1024"] = bench_w4a8()

@@ -24,7 +24,7 @@ LIB = PKG / "libw4a16.so"
 BUILD_DIR = PKG / "_build"
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "pack.hip", "gemv.hip", "skinny.hip", "mid.hip", "gemm.hip", "w4a8.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemv.hip", "rowmma.hip", "skinny.hip", "mid.hip", "gemm.hip", "w4a8.hip"]
 # The benchmark's measured roofs (a streaming read, an empty launch): a library of their own, so
 # that nothing in libw4a16 exists only to be timed.
 ROOF_SOURCE, ROOF_LIB = "roof.hip", PKG / "libw4a16_roof.so"

@@ -98,6 +98,24 @@ w4a16_status_t check_matmul_common(w4a16_format_t fmt, w4a16_dtype_t act, const 
     return check_act(fmt, act);
 }
 
+// Q4, the zero-point format and W8 with fp16 activations: every row of x against one weight pass
+// (64 rows at a time) on the fp16 matrix cores.
+w4a16_status_t launch_rowmajor_rows(w4a16_format_t fmt, const void* x, int64_t M, const void* codes,
+                                    const void* scales, const void* mins, int64_t N, int64_t K, void* y,
+                                    hipStream_t stream) {
+    const uint16_t* xa = static_cast<const uint16_t*>(x);
+    uint16_t* ya = static_cast<uint16_t*>(y);
+    if (fmt == W4A16_FMT_Q4_B32_SYM_FP16)
+        return from_hip(w4a16::launch_rowmma_q4b32(xa, M, static_cast<const uint8_t*>(codes),
+                                                   static_cast<const uint16_t*>(scales), N, K, ya, stream));
+    if (fmt == W4A16_FMT_G128_ZP_FP16)
+        return from_hip(w4a16::launch_rowmma_g128zp(xa, M, static_cast<const uint32_t*>(codes),
+                                                    static_cast<const uint16_t*>(scales),
+                                                    static_cast<const uint16_t*>(mins), N, K, ya, stream));
+    return from_hip(w4a16::launch_rowmma_w8row(xa, M, static_cast<const int8_t*>(codes),
+                                               static_cast<const float*>(scales), N, K, ya, stream));
+}
+
 // ---- The no-allocation entry point's scratch buffer -------------------------------------------
 // Split-K partial sums of the large-M GEMM for callers that cannot allocate a workspace.  One
 // array per GPU, in the code object's zero-initialised device data, held until the process ends.
@@ -273,6 +291,7 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
                                                   static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
                                                   stream));
     }
+    if (M > 1 && act == W4A16_FP16) return launch_rowmajor_rows(fmt, x, M, codes, scales, mins, N, K, y, stream);
     if (fmt == W4A16_FMT_W8_ROW_FP32)
         return from_hip(w4a16::launch_gemv_w8row(static_cast<const uint16_t*>(x), M, static_cast<const int8_t*>(codes),
                                                  static_cast<const float*>(scales), N, K, static_cast<uint16_t*>(y),
@@ -297,7 +316,11 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
                           size_t workspace_bytes, hipStream_t stream) {
     const w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
     if (st != W4A16_OK) return st;
-    if (fmt != W4A16_FMT_G128_ASYM_BF16) return W4A16_ERR_UNSUPPORTED;
+    if (fmt != W4A16_FMT_G128_ASYM_BF16) {  // the row-major formats: fp16 activations, no workspace
+        if (act != W4A16_FP16) return W4A16_ERR_UNSUPPORTED;
+        w4a16::clear_stale_error();
+        return launch_rowmajor_rows(fmt, x, M, codes, scales, mins, N, K, y, stream);
+    }
     const size_t need = w4a16::gemm_g128_workspace_bytes(M, N, K);
     if (need > 0 && (workspace_bytes < need || !aligned16(workspace))) return W4A16_ERR_INVALID;
     w4a16::clear_stale_error();
@@ -309,8 +332,10 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
                             const void* scales, const void* mins, int64_t N, int64_t K, void* y, void* workspace,
                             size_t workspace_bytes, hipStream_t stream) {
-    if (fmt != W4A16_FMT_G128_ASYM_BF16 || (M > 0 && M <= kGemvCutoff))
-        return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
+    // G128 by the cutoff; the row-major formats take the GEMV up to its row limit, and above it
+    // w4a16_gemm (fp16 activations)
+    const int64_t cut = fmt == W4A16_FMT_G128_ASYM_BF16 ? kGemvCutoff : w4a16::kGemvMaxRows;
+    if (M > 0 && M <= cut) return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
     return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
 }
 

@@ -48,6 +48,14 @@ hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* code
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
+// Row-major formats on fp16 MFMA for any number of fp16 activation rows (64 per weight pass).
+hipError_t launch_rowmma_q4b32(const uint16_t* x, int64_t M, const uint8_t* codes, const uint16_t* scales, int64_t N,
+                               int64_t K, uint16_t* y, hipStream_t stream);
+hipError_t launch_rowmma_g128zp(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+hipError_t launch_rowmma_w8row(const uint16_t* x, int64_t M, const int8_t* codes, const float* scales, int64_t N,
+                               int64_t K, uint16_t* y, hipStream_t stream);
+
 // Mid-M G128 path (kGemvMaxRows < M <= kMidMaxRows): weights streamed once per 64-row slice,
 // dequantized straight into MFMA fragments; no workspace.
 constexpr int kMidMaxRows = 64;  // measured: beyond 64 rows the large-M kernel is faster

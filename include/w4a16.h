@@ -152,9 +152,13 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
  * registers, sums x.q per group in fp32 and applies the group scale and minimum once per group
  * (the factored form s * sum(x*q) + min * sum(x) that vidyal.ai's M = 1 kernel uses, section
  * "How the measurements were taken"; P3's one-row-per-warp GEMV, "Writing a GEMV kernel").
- * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format; FP16 for W8.  Q4, the
- * zero-point format and W8 run one pass per activation row.  y has the activation dtype, rounded to nearest
- * even from fp32.  Row-major x and y; x, y 16-byte aligned. */
+ * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format; FP16 for W8.  For Q4,
+ * the zero-point format and W8, one row of fp16 activations takes the one-row GEMV (dot2 with the
+ * scale applied once per block); two or more fp16 rows share one weight pass on the fp16 matrix
+ * cores, the weights dequantized to fp16 in registers ((q - 8) s, (q - z) s or q, each rounded
+ * once) and the W8 row scale applied to each total; bf16 activations run one pass per row.  y has
+ * the activation dtype, rounded to nearest even from fp32.  Row-major x and y; x, y 16-byte
+ * aligned. */
 w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                           const void* codes, const void* scales, const void* mins, int64_t N,
                           int64_t K, void* y, hipStream_t stream);
@@ -167,7 +171,11 @@ int64_t w4a16_gemv_max_rows(void);
  * two calls that may run at the same time. */
 size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K);
 
-/* Large-M path (G128 only; ERR_UNSUPPORTED for the other formats): y [M][N] = x [M][K] . W_hat^T on bf16 MFMA with fp32 accumulation.
+/* Large-M path: y [M][N] = x [M][K] . W_hat^T on the matrix cores with fp32 accumulation.
+ * Q4, the zero-point format and W8 (fp16 activations only; ERR_UNSUPPORTED for bf16): any M, each
+ * 64 rows against one pass over the weights, dequantized to fp16 in registers as for w4a16_gemv's
+ * rows (anrans.github.io "Quantization and GEMV", "The quantization formulas": the zero-point
+ * format's (q - z) s); no workspace.  G128 as follows, on bf16 MFMA.
  * From 33 rows on, packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai
  * Step 2 builds its B tile) and fed to the matrix cores; up to 32 rows the factored per-group form
  * of w4a16_gemv (s * sum(x*(128+q)) + (min - 128 s) * sum(x), fp32) is used instead.  When a K
@@ -181,9 +189,9 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 
 /* Dispatch on M (vidyal.ai "How the measurements were taken": a GEMV kernel for one row, tiles
  * chosen per M; anrans "Exercises": kernels chosen by batch size): M <= w4a16_matmul_gemv_cutoff()
- * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4, the zero-point format and W8 always take the
- * GEMV path and then need M <= w4a16_gemv_max_rows().  Workspace as for w4a16_gemm (w4a16_gemm_workspace_bytes of the
- * same shape is always enough). */
+ * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4, the zero-point format and W8 take the GEMV
+ * path up to w4a16_gemv_max_rows() rows and w4a16_gemm above (fp16 activations).  Workspace as for
+ * w4a16_gemm (w4a16_gemm_workspace_bytes of the same shape is always enough). */
 w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                             const void* codes, const void* scales, const void* mins, int64_t N,
                             int64_t K, void* y, void* workspace, size_t workspace_bytes,

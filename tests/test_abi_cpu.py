@@ -140,9 +140,10 @@ def test_gemm_validation_and_workspace():
     g = w.w4a16_gemm
     assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, FAKE, need - 4, 0) == w.W4A16_ERR_INVALID
     assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_INVALID
-    assert _status(g, Q4, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_UNSUPPORTED
+    # the row-major formats reach the large-M path with fp16 activations only
+    assert _status(g, Q4, BF16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_UNSUPPORTED
     m = w.w4a16_matmul
-    assert _status(m, Q4, F16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, None, 64, 64, FAKE, None, 0, 0) \
+    assert _status(m, Q4, BF16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, None, 64, 64, FAKE, None, 0, 0) \
         == w.W4A16_ERR_UNSUPPORTED
     assert 1 <= w.w4a16_matmul_gemv_cutoff() <= w.w4a16_gemv_max_rows()
 
@@ -165,8 +166,11 @@ def test_zero_point_format_sizes_and_validation():
     assert _status(g, ZP, F16, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_INVALID
     assert _status(g, ZP, F16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, FAKE, FAKE, 8, 128, FAKE, 0) \
         == w.W4A16_ERR_UNSUPPORTED
-    assert _status(w.w4a16_gemm, ZP, F16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) \
+    # the large-M path: fp16 activations only, and no workspace
+    assert _status(w.w4a16_gemm, ZP, BF16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) \
         == w.W4A16_ERR_UNSUPPORTED
+    assert _status(w.w4a16_gemm, ZP, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) \
+        == w.W4A16_ERR_INVALID
     assert w.w4a16_gemm_workspace_bytes(ZP, 300, 256, 4096) == 0
 
 
@@ -185,8 +189,10 @@ def test_w8_format_sizes_and_validation():
     g = w.w4a16_gemv
     assert _status(g, W8, BF16, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
     assert _status(g, W8, F32, FAKE, 1, FAKE, FAKE, None, 8, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
-    assert _status(w.w4a16_gemm, W8, F16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) \
+    assert _status(w.w4a16_gemm, W8, BF16, FAKE, 64, FAKE, FAKE, None, 256, 4096, FAKE, None, 0, 0) \
         == w.W4A16_ERR_UNSUPPORTED
+    assert _status(w.w4a16_gemm, W8, F16, FAKE, 64, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) \
+        == w.W4A16_ERR_INVALID                                                             # takes no mins
 
 
 def test_w4a8_validation():

@@ -641,13 +641,87 @@ def test_w8_decode_shape_full_pack_and_gemv(decode_weights):
 
 
 # ---------------------------------------------------------------------------------------------
+# The row-major formats (Q4, zero point, W8) with several fp16 activation rows: one weight pass
+# for up to 64 rows on the fp16 matrix cores, through w4a16_gemv (up to 16 rows) and w4a16_gemm.
+# ---------------------------------------------------------------------------------------------
+
+def _rowfmt_pack(fmt, W):
+    if fmt == Q4:
+        rc, rs = oracle.quantize_q4b32(W)
+        return (dev(rc), dev(rs), None), (lambda x: refcheck.q4b32(x, rc, rs))
+    if fmt == ZP:
+        rc, rs, rz = oracle.quantize_g128zp(W)
+        return (dev(rc), dev(rs), dev(rz)), (lambda x: refcheck.g128zp(x, rc, rs, rz))
+    rc, rs = oracle.quantize_w8row(W)
+    return (torch.from_numpy(rc).cuda(), torch.from_numpy(rs).cuda(), None), (lambda x: refcheck.w8row(x, rc, rs))
+
+
+@pytest.mark.parametrize("fmt", [Q4, ZP, W8])
+@pytest.mark.parametrize("M,N,K", [(2, 1000, 1152), (3, 65, 4224), (8, 1000, 1152), (16, 130, 2048), (17, 1000, 1152),
+                                   (33, 200, 640), (64, 1000, 1152), (65, 70, 1152), (130, 300, 512)])
+def test_rowmajor_formats_many_rows(fmt, M, N, K):
+    """Ragged N (64-row blocks), K with a partial last unit of 4 blocks for Q4 and W8 (1152 = 36
+    Q4 blocks, 72 W8 blocks; 4224 = 132 and 264), one to three activation tiles of 16 rows, and
+    above 64 rows two passes over the weights.  Every output element-wise against the oracle."""
+    say(f"rowmajor many rows fmt={fmt} M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=300 + M + fmt)
+    x = workloads.activations(M, K, "f16", seed=301 + M)
+    packed, ref = _rowfmt_pack(fmt, W)
+    fn = w.w4a16_gemv if M <= w.w4a16_gemv_max_rows() else w.w4a16_gemm
+    y = run_matmul(fn, fmt, x, packed, N, K, F16)
+    err, worst = refcheck.check(workloads.bits_to_f32(y, "f16"), ref(x), "f16", f"fmt={fmt} M={M}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+    np.testing.assert_array_equal(run_matmul(w.w4a16_matmul, fmt, x, packed, N, K, F16), y)   # same kernel
+
+
+@pytest.mark.parametrize("fmt,M", [(Q4, 5), (W8, 5), (Q4, 40), (W8, 40)])
+def test_rowmajor_ragged_last_unit(fmt, M):
+    """K = 1120: 35 Q4 blocks (70 W8 blocks), so the last unit of 4 blocks is partial and its
+    missing blocks meet zero activations."""
+    N, K = 130, 1120
+    say(f"rowmajor ragged unit fmt={fmt} M={M}")
+    W = workloads.weights(N, K, outliers=True, seed=320 + fmt)
+    x = workloads.activations(M, K, "f16", seed=321)
+    packed, ref = _rowfmt_pack(fmt, W)
+    y = run_matmul(w.w4a16_matmul, fmt, x, packed, N, K, F16)
+    refcheck.check(workloads.bits_to_f32(y, "f16"), ref(x), "f16", f"ragged fmt={fmt} M={M}")
+
+
+@pytest.mark.parametrize("fmt,M", [(ZP, 2), (ZP, 8), (ZP, 16), (ZP, 64), (W8, 16), (Q4, 16)])
+def test_rowmajor_decode_shape_many_rows(decode_weights, fmt, M):
+    """The decode weights (K = 4096, N = 14336, with outliers) in the zero-point and W8 formats,
+    and Q4, with 2 to 64 rows of fp16 activations, as the benchmark runs them."""
+    wl = workloads.DECODE
+    say(f"rowmajor decode shape fmt={fmt} M={M}")
+    W, _ = decode_weights
+    packed, ref = _rowfmt_pack(fmt, W)
+    x = workloads.activations(M, wl.K, "f16", wl.seed_x, rows_drawn=max(workloads.SWEEP_MS))
+    y = run_matmul(w.w4a16_matmul, fmt, x, packed, wl.N, wl.K, F16)
+    err, worst = refcheck.check(workloads.bits_to_f32(y, "f16"), ref(x), "f16", f"decode fmt={fmt} M={M}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+
+
+def test_rowmajor_bf16_rows_rejected_above_gemv():
+    """bf16 activations with the row-major formats run one GEMV pass per row up to 16 rows; the
+    large-M path takes fp16 activations only."""
+    N, K = 64, 128
+    W = workloads.weights(N, K, seed=310)
+    packed, _ = _rowfmt_pack(ZP, W)
+    x = workloads.activations(17, K, "bf16", seed=311)
+    with pytest.raises(w.W4A16Error) as e:
+        run_matmul(w.w4a16_gemm, ZP, x, packed, N, K, BF16)
+    assert e.value.status == w.W4A16_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------------------------------------
 # HIP-graph capture (the benchmark replays its steps from a graph): every replay bit-identical
 # to the eager call, with eager work and synchronisations between the replays.
 # ---------------------------------------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt,act,M,N,K", [(G128, BF16, 1, 1000, 2048), (G128, BF16, 40, 520, 1024),
                                            (G128, BF16, 300, 256, 4096), (Q4, F16, 2, 300, 1024),
-                                           (ZP, F16, 1, 300, 4096), (W8, F16, 3, 130, 512)])
+                                           (ZP, F16, 1, 300, 4096), (W8, F16, 3, 130, 512),
+                                           (ZP, F16, 40, 300, 1024), (Q4, F16, 9, 200, 1024)])
 def test_graph_replays_match_eager(fmt, act, M, N, K):
     say(f"graph replay fmt={fmt} M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=71)
