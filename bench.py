@@ -174,6 +174,17 @@ def time_rounds(step, copies: int, rounds: int = ROUNDS):
     for i in range(min(L, 2 * copies)):
         step(i)
     torch.cuda.synchronize()
+    if EAGER:  # counter runs: direct launches, no graph
+        per = []
+        for _ in range(rounds):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(L):
+                step(i)
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3 / L)
+        return {"us": float(np.median(per)), "rounds_us": [round(v, 4) for v in per], "launches_per_round": L}
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         for i in range(L):
