@@ -2,7 +2,7 @@
 """Benchmark of the W4A16 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                    [--only decode|prefill|q4|sweep|zp|w8|w4a8|w4a8_decode|w4a8_sweep]
+                    [--only decode|prefill|q4|sweep|zp|zp_prepared|w8|w4a8|w4a8_decode|w4a8_sweep]
 
 A step is one w4a16_matmul call (dispatch by M -> GEMV or MFMA GEMM) over one batch of seeded
 synthetic input, with packed weights, activations and output already resident in HBM.  The
@@ -81,8 +81,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=170)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "w8", "w4a8", "w4a8_decode", "w4a8_sweep",
-                                       "cpu", "rowfmt_sweep"], default=None,
+    ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "zp_prepared", "w8", "w4a8",
+                                       "w4a8_decode", "w4a8_sweep", "cpu", "rowfmt_sweep"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -693,6 +693,43 @@ def copy_calibration(mib: int):
     log(f"copy calibration: 5 x {mib} MiB device-to-device")
 
 
+def bench_zp_prepared(W=None, Ms=(1, 4, 16)):
+    """The zero-point format from its prepared copy (w4a16_prepare once, then w4a16_gemv_prepared)
+    at the decode shape, cold copies, fp16 activations; rates over the prepared copy's bytes and,
+    for comparison with the canonical GEMV, over the format's own bytes."""
+    import torch
+    import gemm_w4a16_amd as w
+    import workloads
+    wl, fmt = workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16
+    if W is None:
+        W = workloads.inputs(wl)[0]
+    c, s, m = w.w4a16_packed_sizes(fmt, wl.N, wl.K)
+    nb = w.w4a16_prepared_bytes(fmt, wl.N, wl.K)
+    R = copies_for(nb)
+    st = Setup(fmt, 1, wl.N, wl.K, workloads.activations(1, wl.K, "f16", wl.seed_x), W, 1)
+    preps = []
+    for _ in range(R):
+        p = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        w.w4a16_prepare(fmt, *st.copies[0], wl.N, wl.K, p, nb)
+        preps.append(p)
+    del st
+    out = []
+    for M in Ms:
+        x = torch.from_numpy(workloads.activations(M, wl.K, "f16", wl.seed_x, rows_drawn=max(Ms)).view(np.int16)).cuda()
+        y = torch.empty((M, wl.N), dtype=torch.int16, device="cuda")
+        torch.cuda.synchronize()
+
+        def step(i, x=x, y=y, M=M):
+            w.w4a16_gemv_prepared(fmt, w.W4A16_FP16, x, M, preps[i % R], wl.N, wl.K, y)
+
+        kt = time_rounds(step, R)
+        t = kt["us"] * 1e-6
+        out.append({"M": M, "us": kt["us"], "us_rounds": kt["rounds_us"], "prepared_bytes": nb,
+                    "prepared_gbs": nb / t / 1e9, "format_bytes": c + s + m,
+                    "effective_weight_gbs": (c + s + m) / t / 1e9, "frac_hbm_peak_prepared": nb / t / 1e9 / HBM_PEAK_GBS})
+    return {"workload": wl.name + "_prepared", "weight_copies": R, "rows": out}
+
+
 def main():
     global EAGER
     args = parse()
@@ -717,7 +754,7 @@ def main():
                   "zp": bench_rowfmt_sweep(workloads.ZP_DECODE, w.W4A16_FMT_G128_ZP_FP16),
                   "w8": bench_rowfmt_sweep(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32),
                   "q4": bench_rowfmt_sweep(workloads.Q4, w.W4A16_FMT_Q4_B32_SYM_FP16, None, (1, 2, 4, 8, 16))},
-              "w8": bench_w8, "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
+              "w8": bench_w8, "zp_prepared": bench_zp_prepared, "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
               "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only}[args.only]
         print(json.dumps({"only": args.only, "result": fn()}), flush=True)
         return
@@ -780,6 +817,9 @@ def main():
         torch.cuda.empty_cache()
         log("zero-point format GEMV (decode shape)")
         extra["zp_decode_m1"] = bench_zp(W)
+        torch.cuda.empty_cache()
+        log("zero-point format from its prepared copy (decode shape)")
+        extra["zp_prepared"] = bench_zp_prepared(W)
         torch.cuda.empty_cache()
         log("W8A16 per-row int8 GEMV (decode shape)")
         extra["w8_decode_m1"] = bench_w8(W)

@@ -26,6 +26,7 @@ EXPORTED = (
     "w4a16_gemv", "w4a16_gemv_max_rows", "w4a16_gemm_workspace_bytes", "w4a16_gemm",
     "w4a16_matmul", "w4a16_matmul_gemv_cutoff", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
     "w4a16_matmul_w4a8", "w4a16_check_weights", "w4a16_matmul_noalloc", "w4a16_matmul_noalloc_max_scratch_bytes",
+    "w4a16_prepared_bytes", "w4a16_prepare", "w4a16_gemv_prepared",
 )
 
 
@@ -61,12 +62,15 @@ def _load() -> ctypes.CDLL:
     L.w4a16_matmul_noalloc.argtypes = [I, I, P, I64, P, P, P, I64, I64, P, P]
     L.w4a16_matmul_noalloc_max_scratch_bytes.argtypes = []
     L.w4a16_matmul_noalloc_max_scratch_bytes.restype = SZ
+    L.w4a16_prepared_bytes.argtypes, L.w4a16_prepared_bytes.restype = [I, I64, I64], SZ
+    L.w4a16_prepare.argtypes = [I, P, P, P, I64, I64, P, SZ, P]
+    L.w4a16_gemv_prepared.argtypes = [I, I, P, I64, P, I64, I64, P, P]
     L.w4a16_quantize_act_i8.argtypes = [P, I64, I64, P, P, P, P]
     L.w4a16_gemm_w4a8.argtypes = [I, P, P, P, I64, P, P, P, I64, I64, P, P]
     L.w4a16_matmul_w4a8.argtypes = [I, P, I64, P, P, P, I64, I64, P, P]
     for name in ("w4a16_packed_sizes", "w4a16_quantize_pack", "w4a16_check_weights", "w4a16_dequant", "w4a16_gemv",
                  "w4a16_gemm", "w4a16_matmul", "w4a16_matmul_noalloc", "w4a16_quantize_act_i8", "w4a16_gemm_w4a8",
-                 "w4a16_matmul_w4a8"):
+                 "w4a16_matmul_w4a8", "w4a16_prepare", "w4a16_gemv_prepared"):
         getattr(L, name).restype = I
     return L
 
@@ -160,6 +164,20 @@ def w4a16_matmul_noalloc(fmt: int, act: int, x, M: int, codes, scales, mins, N: 
 
 def w4a16_matmul_noalloc_max_scratch_bytes() -> int:
     return int(lib.w4a16_matmul_noalloc_max_scratch_bytes())
+
+
+def w4a16_prepared_bytes(fmt: int, N: int, K: int) -> int:
+    return int(lib.w4a16_prepared_bytes(fmt, N, K))
+
+
+def w4a16_prepare(fmt: int, codes, scales, mins, N: int, K: int, prepared, prepared_bytes: int, stream=None) -> None:
+    _ok(lib.w4a16_prepare(fmt, _p(codes), _p(scales), _p(mins), N, K, _p(prepared), prepared_bytes,
+                             _stream(stream)), "w4a16_prepare")
+
+
+def w4a16_gemv_prepared(fmt: int, act: int, x, M: int, prepared, N: int, K: int, y, stream=None) -> None:
+    _ok(lib.w4a16_gemv_prepared(fmt, act, _p(x), M, _p(prepared), N, K, _p(y), _stream(stream)),
+        "w4a16_gemv_prepared")
 
 
 def w4a16_matmul_gemv_cutoff() -> int:

@@ -339,6 +339,60 @@ w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x
     return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
 }
 
+// The prepared copy's three parts, each starting 16-byte aligned: words, fp32 scales, fp32 minimums.
+struct PreparedLayout {
+    size_t words, scales, mins, total;
+};
+static PreparedLayout prepared_layout(int64_t N, int64_t K) {
+    auto a16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
+    PreparedLayout L;
+    L.words = 0;
+    L.scales = a16((size_t)(K / 8) * (size_t)N * 4);
+    L.mins = L.scales + a16((size_t)(K / 128) * (size_t)N * 4);
+    L.total = L.mins + a16((size_t)(K / 128) * (size_t)N * 4);
+    return L;
+}
+
+size_t w4a16_prepared_bytes(w4a16_format_t fmt, int64_t N, int64_t K) {
+    if (fmt != W4A16_FMT_G128_ZP_FP16 || check_shape(fmt, N, K) != W4A16_OK) return 0;
+    return prepared_layout(N, K).total;
+}
+
+w4a16_status_t w4a16_prepare(w4a16_format_t fmt, const void* codes, const void* scales, const void* mins, int64_t N,
+                             int64_t K, void* prepared, size_t prepared_bytes, hipStream_t stream) {
+    w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    if (fmt != W4A16_FMT_G128_ZP_FP16) return W4A16_ERR_UNSUPPORTED;
+    if ((st = check_packed(fmt, codes, scales, mins)) != W4A16_OK) return st;
+    const PreparedLayout L = prepared_layout(N, K);
+    if (!aligned16(prepared) || prepared_bytes < L.total) return W4A16_ERR_INVALID;
+    char* base = static_cast<char*>(prepared);
+    w4a16::clear_stale_error();
+    return from_hip(w4a16::launch_prepare_zp(static_cast<const uint32_t*>(codes), static_cast<const uint16_t*>(scales),
+                                             static_cast<const uint16_t*>(mins), N, K,
+                                             reinterpret_cast<uint32_t*>(base + L.words),
+                                             reinterpret_cast<float*>(base + L.scales),
+                                             reinterpret_cast<float*>(base + L.mins), stream));
+}
+
+w4a16_status_t w4a16_gemv_prepared(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
+                                   const void* prepared, int64_t N, int64_t K, void* y, hipStream_t stream) {
+    w4a16_status_t st = check_shape(fmt, N, K);
+    if (st != W4A16_OK) return st;
+    if (M <= 0 || M > kMaxDim) return W4A16_ERR_INVALID;
+    if (!aligned16(x) || !aligned16(y) || !aligned16(prepared)) return W4A16_ERR_INVALID;
+    if (act != W4A16_BF16 && act != W4A16_FP16 && act != W4A16_FP32) return W4A16_ERR_INVALID;
+    if (fmt != W4A16_FMT_G128_ZP_FP16 || act == W4A16_FP32 || M > w4a16::kGemvMaxRows) return W4A16_ERR_UNSUPPORTED;
+    const PreparedLayout L = prepared_layout(N, K);
+    const char* base = static_cast<const char*>(prepared);
+    w4a16::clear_stale_error();
+    return from_hip(w4a16::launch_skinny_prepared_zp(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
+                                                     reinterpret_cast<const uint32_t*>(base + L.words),
+                                                     reinterpret_cast<const float*>(base + L.scales),
+                                                     reinterpret_cast<const float*>(base + L.mins), N, K,
+                                                     static_cast<uint16_t*>(y), stream));
+}
+
 size_t w4a16_matmul_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
 
 w4a16_status_t w4a16_matmul_noalloc(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,

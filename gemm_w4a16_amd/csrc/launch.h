@@ -48,6 +48,14 @@ hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* code
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
+// The zero-point format's prepared copy: words [K/8][N], fp32 s and m = -z s per group [K/128][N];
+// and the small-M kernel over it (fp16 or bf16 activations, M <= kGemvMaxRows).
+hipError_t launch_prepare_zp(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
+                             uint32_t* words, float* s_out, float* m_out, hipStream_t stream);
+hipError_t launch_skinny_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                                     const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
+                                     hipStream_t stream);
+
 // Row-major formats on fp16 MFMA for any number of fp16 activation rows (64 per weight pass).
 hipError_t launch_rowmma_q4b32(const uint16_t* x, int64_t M, const uint8_t* codes, const uint16_t* scales, int64_t N,
                                int64_t K, uint16_t* y, hipStream_t stream);

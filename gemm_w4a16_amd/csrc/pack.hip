@@ -360,4 +360,44 @@ hipError_t launch_dequant_q4b32(const uint8_t* codes, const uint16_t* scales, in
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// The prepared copy of the zero-point format: its words reordered into the [K/8][N] column order
+// the small-M kernel streams (word (r, n) of the copy is word (n, r) of the format), with each
+// group's parameters as fp32 s and m = -z s.  (q - z) s = q s + m exactly in fp32: |q - z| needs
+// at most 12 bits and s 11, so q s, z s and their sum are all exact, and fmaf(q, s, m) is the
+// format's decode bit for bit.
+// ---------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prepare_zp_words_kernel(const uint32_t* __restrict__ codes, int64_t N, int64_t K8,
+                                                               uint32_t* __restrict__ out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output word (r, n), n fastest
+    if (i >= N * K8) return;
+    const int64_t r = i / N, n = i % N;
+    out[i] = codes[n * K8 + r];
+}
+
+__global__ __launch_bounds__(256) void prepare_zp_params_kernel(const uint16_t* __restrict__ scales,
+                                                                const uint16_t* __restrict__ zeros, int64_t N,
+                                                                int64_t G, float* __restrict__ s_out,
+                                                                float* __restrict__ m_out) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output (g, n), n fastest
+    if (i >= N * G) return;
+    const int64_t g = i / N, n = i % N;
+    const float s = f16_bits_to_f32(scales[n * G + g]);
+    const float z = f16_bits_to_f32(zeros[n * G + g]);
+    s_out[i] = s;
+    m_out[i] = -z * s;  // exact: an integer of at most 12 bits times 11 significant bits
+}
+
+hipError_t launch_prepare_zp(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
+                             uint32_t* words, float* s_out, float* m_out, hipStream_t stream) {
+    const int64_t K8 = K / 8, G = K / 128;
+    hipLaunchKernelGGL(prepare_zp_words_kernel, dim3((unsigned)((N * K8 + 255) / 256)), dim3(256), 0, stream, codes, N, K8,
+                       words);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prepare_zp_params_kernel, dim3((unsigned)((N * G + 255) / 256)), dim3(256), 0, stream, scales, zeros,
+                       N, G, s_out, m_out);
+    return hipGetLastError();
+}
+
 }  // namespace w4a16

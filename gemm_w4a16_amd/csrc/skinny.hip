@@ -34,6 +34,7 @@ constexpr int kGroupsPerPass = 32;  // groups of 128 k a block covers per pass (
 #endif
 constexpr uint32_t kNibblePairMask = 0x000F000Fu;
 constexpr uint32_t kBf16Magic = 0x43004300u;  // bf16 128.0 in both halves
+constexpr uint32_t kF16Magic = 0x64006400u;   // fp16 1024.0 in both halves
 
 // Waves per SIMD the register budget is sized for: one block per CU.  (32-column blocks are
 // used when N is small, so that there are more blocks; two of them per CU would halve the
@@ -47,6 +48,18 @@ __device__ __forceinline__ bf16x8_t unpack_b_fragment(uint32_t w, uint32_t mask,
     const u32x4_t p = {(w & mask) | magic, ((w >> 4) & mask) | magic, ((w >> 8) & mask) | magic,
                        ((w >> 12) & mask) | magic};
     return __builtin_bit_cast(bf16x8_t, p);
+}
+
+// v_mfma_f32_16x16x32 on bf16 or, with kF16, on fp16 operands (the same bit patterns in registers)
+template <bool kF16>
+__device__ __forceinline__ f32x4_t mfma16_t(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+    if constexpr (kF16) {
+        typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                      0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
 }
 
 // (x0..x7) as four dwords (x0,x1) (x2,x3) (x4,x5) (x6,x7) -> (x0,x4) (x1,x5) (x2,x6) (x3,x7)
@@ -100,15 +113,41 @@ __device__ __forceinline__ float bf16_half(const uint32_t* v, int t) {
     return bf16_bits_to_f32((t & 1) ? (v[t >> 1] >> 16) : (v[t >> 1] & 0xFFFFu));
 }
 
+// The same for fp32 parameters (the prepared copy of the zero-point format): TPL floats.
+template <int TPL, bool kVec>
+__device__ __forceinline__ void load_params32(const float* __restrict__ p, int N, int cbase, float (&out)[TPL]) {
+    if (kVec && TPL == 4) {
+        const float4 v = *reinterpret_cast<const float4*>(p + cbase);
+        out[0] = v.x;
+        out[1 % TPL] = v.y;
+        out[2 % TPL] = v.z;
+        out[3 % TPL] = v.w;
+    } else if (kVec && TPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(p + cbase);
+        out[0] = v.x;
+        out[TPL - 1] = v.y;
+    } else {
+#pragma unroll
+        for (int t = 0; t < TPL; ++t) out[t] = p[min(cbase + t, N - 1)];
+    }
+}
+
 // MR: activation rows staged (M <= MR; 1, 4 or 16).  TPL: adjacent columns per lane (4 or 2),
 // i.e. 16 * TPL columns per block.  WAVES: waves per block; each takes kGroupsPerPass / WAVES
-// groups per pass.  kVec: N % TPL == 0 (vector loads of a lane's columns).
-template <int MR, int TPL, int WAVES, bool kVec>
+// groups per pass.  kVec: N % TPL == 0 (vector loads of a lane's columns).  kF16: fp16
+// activations and output on the fp16 matrix cores, codes as 1024 + q (else bf16 and 128 + q).
+// kP32: scales and minimums are fp32 [K/128][N] (the prepared zero-point copy), else bf16.
+template <int MR, int TPL, int WAVES, bool kVec, bool kF16 = false, bool kP32 = false>
 __global__ __launch_bounds__(64 * WAVES)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<MR, TPL, WAVES>(), waves_per_eu<MR, TPL, WAVES>())))
 void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
-                        const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
+                        const void* __restrict__ scales_v, const void* __restrict__ mins_v,
                         uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic) {
+    const uint16_t* __restrict__ scales = static_cast<const uint16_t*>(scales_v);
+    const uint16_t* __restrict__ mins = static_cast<const uint16_t*>(mins_v);
+    const float* __restrict__ scales32 = static_cast<const float*>(scales_v);
+    const float* __restrict__ mins32 = static_cast<const float*>(mins_v);
+    constexpr float kOffset = kF16 ? 1024.0f : 128.0f;  // the magic number's value at q = 0
     constexpr int E = MR == 1 ? 1 : 4;  // accumulator rows per lane that can hold a real row
     constexpr int COLS = 16 * TPL;
     constexpr int kWaves = WAVES;
@@ -123,6 +162,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     int cbase = n0 + TPL * lr;
     if (kVec) cbase = min(cbase, N - TPL);
     const int arow = min(lr, MR);  // A-fragment row: rows >= M hold zeros, row MR is all zeros
+    auto mfma16 = [](bf16x8_t a, bf16x8_t b, f32x4_t c) { return mfma16_t<kF16>(a, b, c); };
 
 #pragma unroll
     for (int j = 0; j < kGpp; ++j) xs[wave][j][MR][lr] = make_uint4(0, 0, 0, 0);  // the zero row
@@ -137,7 +177,8 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     uint32_t magic_v;
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(magic));
     magic = magic_v;
-    const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;  // 1.0 in both halves
+    const u32x4_t ones_u = {kOne, kOne, kOne, kOne};
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
 
     for (int p0 = 0; p0 < G; p0 += kWaves * kGpp) {
@@ -163,10 +204,16 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
             gj[j] = min(g, G - 1);
         }
         uint32_t sf[kGpp][TPL / 2], mf[kGpp][TPL / 2];
+        float sf32[kGpp][TPL], mf32[kGpp][TPL];
 #pragma unroll
         for (int j = 0; j < kGpp; ++j) {
-            load_params<TPL, kVec>(scales + (size_t)gj[j] * N, N, cbase, sf[j]);
-            load_params<TPL, kVec>(mins + (size_t)gj[j] * N, N, cbase, mf[j]);
+            if constexpr (kP32) {
+                load_params32<TPL, kVec>(scales32 + (size_t)gj[j] * N, N, cbase, sf32[j]);
+                load_params32<TPL, kVec>(mins32 + (size_t)gj[j] * N, N, cbase, mf32[j]);
+            } else {
+                load_params<TPL, kVec>(scales + (size_t)gj[j] * N, N, cbase, sf[j]);
+                load_params<TPL, kVec>(mins + (size_t)gj[j] * N, N, cbase, mf[j]);
+            }
         }
         uint32_t w[kGpp][4][TPL];
         const uint32_t lane_off = ((uint32_t)lg * (uint32_t)N + (uint32_t)cbase) * 4u;
@@ -197,15 +244,14 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
                 const bf16x8_t a = __builtin_bit_cast(bf16x8_t, xs[wave][j][arow][4 * s + lg]);
 #pragma unroll
                 for (int t = 0; t < TPL; ++t)
-                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, unpack_b_fragment(w[j][s][t], mask, magic), acc[t],
-                                                                   0, 0, 0);
-                accs = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, accs, 0, 0, 0);
+                    acc[t] = mfma16(a, unpack_b_fragment(w[j][s][t], mask, magic), acc[t]);
+                accs = mfma16(a, ones, accs);
             }
 #pragma unroll
             for (int t = 0; t < TPL; ++t) {
-                const float sv = bf16_half(sf[j], t), mv = bf16_half(mf[j], t);
+                const float sv = kP32 ? sf32[j][t] : bf16_half(sf[j], t), mv = kP32 ? mf32[j][t] : bf16_half(mf[j], t);
                 const float s = sv * live[j];
-                const float c = __builtin_fmaf(-128.0f, sv, mv) * live[j];  // min - 128 s
+                const float c = __builtin_fmaf(-kOffset, sv, mv) * live[j];  // min - 128 s (or - 1024 s)
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     yacc[t][e] = __builtin_fmaf(s, acc[t][e], yacc[t][e]);
@@ -237,23 +283,24 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
                 sum += reinterpret_cast<const float*>(&xs[v][0][0][0])[row * COLS + c];
-            y[(size_t)row * N + n] = f32_to_bf16_bits(sum);
+            y[(size_t)row * N + n] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
         }
     }
 }
 
-template <int MR, int TPL>
-void launch_mr(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales, const uint16_t* mins,
+template <int MR, int TPL, bool kF16 = false, bool kP32 = false>
+void launch_mr(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
                int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     constexpr int COLS = 16 * TPL;
     constexpr int WAVES = W4A16_SKINNY_WAVES;
+    constexpr uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
     const dim3 grid((unsigned)((N + COLS - 1) / COLS)), block(64 * WAVES);
     if (N % TPL == 0)
-        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, WAVES, true>), grid, block, 0, stream, x, codes, scales, mins, y,
-                           (int)M, (int)N, (int)K, kNibblePairMask, kBf16Magic);
+        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, WAVES, true, kF16, kP32>), grid, block, 0, stream, x, codes, scales,
+                           mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
     else
-        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, WAVES, false>), grid, block, 0, stream, x, codes, scales, mins, y,
-                           (int)M, (int)N, (int)K, kNibblePairMask, kBf16Magic);
+        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, WAVES, false, kF16, kP32>), grid, block, 0, stream, x, codes,
+                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
 }
 
 }  // namespace
@@ -262,19 +309,38 @@ void launch_mr(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16
 #define W4A16_SKINNY_TPL 0  // 0: chosen from N at launch
 #endif
 
-hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
-                              const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+namespace {
+// M rows, the column split chosen from N (the same for every variant).
+template <bool kF16, bool kP32>
+void launch_rows(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins, int64_t N,
+                 int64_t K, uint16_t* y, hipStream_t stream) {
     // 64 columns per block (16-byte loads, measured best) unless that leaves most CUs idle
     const int tpl = W4A16_SKINNY_TPL ? W4A16_SKINNY_TPL : ((N + 63) / 64 >= 192 ? 4 : 2);
     if (tpl == 4) {
-        if (M == 1) launch_mr<1, 4>(x, M, codes, scales, mins, N, K, y, stream);
-        else if (M <= 4) launch_mr<4, 4>(x, M, codes, scales, mins, N, K, y, stream);
-        else launch_mr<16, 4>(x, M, codes, scales, mins, N, K, y, stream);
+        if (M == 1) launch_mr<1, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else if (M <= 4) launch_mr<4, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else launch_mr<16, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
     } else {
-        if (M == 1) launch_mr<1, 2>(x, M, codes, scales, mins, N, K, y, stream);
-        else if (M <= 4) launch_mr<4, 2>(x, M, codes, scales, mins, N, K, y, stream);
-        else launch_mr<16, 2>(x, M, codes, scales, mins, N, K, y, stream);
+        if (M == 1) launch_mr<1, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else if (M <= 4) launch_mr<4, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else launch_mr<16, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
     }
+}
+}  // namespace
+
+hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                              const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+    launch_rows<false, false>(x, M, codes, scales, mins, N, K, y, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_skinny_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                                     const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
+                                     hipStream_t stream) {
+    if (act_f16)
+        launch_rows<true, true>(x, M, codes, scales, mins, N, K, y, stream);
+    else
+        launch_rows<false, true>(x, M, codes, scales, mins, N, K, y, stream);
     return hipGetLastError();
 }
 

@@ -274,3 +274,29 @@ def test_matmul_noalloc_validation():
     assert _status(f, G128, F16, FAKE, 1, FAKE, FAKE, FAKE, 256, 128, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
     assert w.w4a16_gemm_workspace_bytes(G128, 2048, 520, 1024) > 16 << 20
     assert _status(f, G128, BF16, FAKE, 2048, FAKE, FAKE, FAKE, 520, 1024, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+
+
+def test_prepared_copy_sizes_and_validation():
+    """The zero-point format's prepared copy: words [K/8][N] plus fp32 s and m [K/128][N], each part
+    16-byte aligned; no other format has one.  Every call below fails on the host."""
+    assert w.w4a16_prepared_bytes(ZP, 14336, 4096) == 29_360_128 + 2 * 1_835_008
+    assert w.w4a16_prepared_bytes(ZP, 3, 128) == 192 + 16 + 16     # 12-byte fp32 parts padded to 16
+    assert w.w4a16_prepared_bytes(ZP, 3, 100) == 0                  # no such shape
+    for fmt in (G128, Q4, W8):
+        assert w.w4a16_prepared_bytes(fmt, 256, 4096) == 0
+    need = w.w4a16_prepared_bytes(ZP, 256, 4096)
+    p = w.w4a16_prepare
+    assert _status(p, ZP, FAKE, FAKE, FAKE, 256, 4096, FAKE, need - 1, 0) == w.W4A16_ERR_INVALID   # too small
+    assert _status(p, ZP, FAKE, FAKE, FAKE, 256, 4096, FAKE + 8, need, 0) == w.W4A16_ERR_INVALID   # alignment
+    assert _status(p, ZP, FAKE, FAKE, None, 256, 4096, FAKE, need, 0) == w.W4A16_ERR_INVALID       # zero points
+    assert _status(p, ZP, FAKE, FAKE, FAKE, 256, 100, FAKE, need, 0) == w.W4A16_ERR_INVALID        # K % 128
+    assert _status(p, G128, FAKE, FAKE, FAKE, 256, 4096, FAKE, need, 0) == w.W4A16_ERR_UNSUPPORTED
+    g = w.w4a16_gemv_prepared
+    assert _status(g, ZP, F16, FAKE, 0, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_INVALID           # M = 0
+    assert _status(g, ZP, F16, FAKE + 4, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_INVALID       # alignment
+    assert _status(g, ZP, F16, FAKE, 1, None, 256, 4096, FAKE, 0) == w.W4A16_ERR_INVALID           # no copy
+    assert _status(g, ZP, 7, FAKE, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_INVALID             # no such type
+    assert _status(g, ZP, F32, FAKE, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, ZP, BF16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, 256, 4096, FAKE, 0) \
+        == w.W4A16_ERR_UNSUPPORTED
+    assert _status(g, Q4, F16, FAKE, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED

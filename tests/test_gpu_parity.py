@@ -585,6 +585,87 @@ def test_zp_decode_shape_full_pack_and_gemv(decode_weights):
 
 
 # ---------------------------------------------------------------------------------------------
+# The zero-point format's prepared copy: the copy decodes to the oracle's weights bit for bit,
+# and its GEMV meets the same bars as the canonical one.
+# ---------------------------------------------------------------------------------------------
+
+def gpu_prepare(packed, N, K):
+    nb = w.w4a16_prepared_bytes(ZP, N, K)
+    prep = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    w.w4a16_prepare(ZP, *packed, N, K, prep, nb)
+    return prep
+
+
+def unpack_prepared(prep, N, K):
+    """(words [K/8][N], s [K/128][N], m [K/128][N]) of a prepared copy, each part at the next
+    16-byte boundary after the previous one."""
+    raw = host(prep, np.uint8)
+    a16 = lambda b: (b + 15) // 16 * 16
+    nw, ng = K // 8 * N * 4, K // 128 * N * 4
+    words = raw[:nw].view(np.uint32).reshape(K // 8, N)
+    s = raw[a16(nw):a16(nw) + ng].view(np.float32).reshape(K // 128, N)
+    m = raw[a16(nw) + a16(ng):a16(nw) + a16(ng) + ng].view(np.float32).reshape(K // 128, N)
+    return words, s, m
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (3, 384), (65, 1024), (130, 4096), (7, 17408)])
+def test_prepared_copy_decodes_to_the_oracle_weights(N, K):
+    """Every weight q s + m of the copy (exact in fp32, so any rounding order gives it) equals the
+    oracle's fp32 (q - z) s, on weights with degenerate and clamped zero-point groups."""
+    say(f"prepare zp N={N} K={K}")
+    W = edge_weights(N, K, 128, np.float32(4.0), seed=N + K) if N >= 40 else \
+        workloads.weights(N, K, outliers=True, seed=N + K)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    words, s, m = unpack_prepared(gpu_prepare((dev(rc), dev(rs), dev(rz)), N, K), N, K)
+    np.testing.assert_array_equal(words, rc.T)                      # [K/8][N] column order
+    q = ((words.T[:, :, None] >> (4 * np.arange(8, dtype=np.uint32))) & 15).reshape(N, K).astype(np.float32)
+    sk = np.repeat(s.T, 128, axis=1)
+    mk = np.repeat(m.T, 128, axis=1)
+    np.testing.assert_array_equal((q * sk + mk).view(np.uint32),
+                                  oracle.dequant_g128zp(rc, rs, rz, "f32").view(np.uint32))
+    np.testing.assert_array_equal(s.T, rs.view(np.float16).astype(np.float32))
+
+
+@pytest.mark.parametrize("act", [F16, BF16])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 65, 384), (2, 130, 4096), (3, 257, 2176), (1, 31, 17408),
+                                   (4, 1000, 640), (5, 1000, 1152), (16, 100, 1024), (16, 13001, 256)])
+def test_gemv_prepared_zp_parity(act, M, N, K):
+    say(f"gemv_prepared act={act} M={M} N={N} K={K}")
+    W = edge_weights(N, K, 128, np.float32(4.0), seed=M + N + K)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    kind = "f16" if act == F16 else "bf16"
+    x = edge_activations(M, K, kind, seed=K + 1)
+    prep = gpu_prepare((dev(rc), dev(rs), dev(rz)), N, K)
+    xd = dev(x)
+    ys = []
+    for _ in range(2):
+        y = torch.full((M, N), NAN16, dtype=torch.int16, device="cuda")
+        w.w4a16_gemv_prepared(ZP, act, xd, M, prep, N, K, y)
+        ys.append(host(y, np.uint16))
+    np.testing.assert_array_equal(ys[0], ys[1])                     # bitwise reproducible
+    err, worst = refcheck.check(workloads.bits_to_f32(ys[0], kind), refcheck.g128zp(x, rc, rs, rz, x_kind=kind),
+                                kind, f"prepared M={M} N={N} K={K}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_gemv_prepared_zp_decode_shape(decode_weights, M):
+    """The decode shape (K = 4096, N = 14336) from the prepared copy, fp16 activations, in full."""
+    wl = workloads.ZP_DECODE
+    say(f"prepared zp decode M={M}")
+    W, _ = decode_weights
+    packed = gpu_pack(ZP, W)
+    rc, rs, rz = oracle.quantize_g128zp(W)
+    prep = gpu_prepare(packed, wl.N, wl.K)
+    x = workloads.activations(M, wl.K, "f16", wl.seed_x)
+    y = torch.full((M, wl.N), NAN16, dtype=torch.int16, device="cuda")
+    w.w4a16_gemv_prepared(ZP, F16, dev(x), M, prep, wl.N, wl.K, y)
+    y = workloads.bits_to_f32(host(y, np.uint16), "f16")
+    err, worst = refcheck.check(y, refcheck.g128zp(x, rc, rs, rz), "f16", f"prepared zp decode M={M}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+
+
+# ---------------------------------------------------------------------------------------------
 # W8A16 per-row int8: pack and dequant bit-exact, GEMV within the tolerance.
 # ---------------------------------------------------------------------------------------------
 
