@@ -39,6 +39,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace w4a16 {
 
@@ -145,32 +146,6 @@ struct W8Layout {
     static_assert(Stage % 16 == 0, "stage alignment");
 };
 
-__device__ __forceinline__ uint32_t w8_lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
-// Direct-to-LDS copies from inline assembly, so that the compiler does not track them (it cannot
-// tell the LDS stages apart and would wait for every copy in flight before any LDS read): lane l
-// reads 16 (or 4) bytes at sbase + voff, and the load unit writes them to LDS byte m0 + 16 l
-// (or 4 l).  The only waits for them are the explicit ones before each k-tile's barrier.
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void w8_dma16(uint32_t voff, const void* sbase, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void w8_dma4(uint32_t voff, const void* sbase, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds)
-                 : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int n>
-__device__ __forceinline__ void w8_wait_vm() {
-    static_assert(n >= 0 && n < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | 0x0F70 /* expcnt, lgkmcnt: no wait */);
-}
-
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
 
@@ -192,7 +167,7 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
     const int l32 = lane & 31, kg = lane >> 5;
     const int n0 = blockIdx.x * BN, m0 = blockIdx.y * kBM;
     const int T = K / kBM;
-    const uint32_t lds0 = w8_lds_addr(smem);
+    const uint32_t lds0 = lds_addr(smem);
 
     // ---- this wave's copies of a k-tile (per-lane source offsets; the k-tile adds a uniform one)
     //  A: copies j = kACopies wave + i, rows 8 j .. 8 j + 7; lane l -> row 8 j + l / 8, LDS slot
@@ -245,23 +220,23 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
         const uint32_t sbase = lds0 + (uint32_t)(st * L::Stage);
         const int8_t* xa = xq + (size_t)t * kBM;
 #pragma unroll
-        for (int i = 0; i < kACopies; ++i) w8_dma16(a_off[i], xa, sbase + L::OffA + 1024u * (kACopies * wave + i));
+        for (int i = 0; i < kACopies; ++i) dma16(a_off[i], xa, sbase + L::OffA + 1024u * (kACopies * wave + i));
         const uint32_t* cb = codes + (size_t)t * 16 * N;
 #pragma unroll
-        for (int i = 0; i < kBCopies; ++i) w8_dma16(b_off[i], cb, sbase + b_lds[i]);
+        for (int i = 0; i < kBCopies; ++i) dma16(b_off[i], cb, sbase + b_lds[i]);
 #pragma unroll
         for (int u = 0; u < kSmallMax; ++u)
-            if (u < n_small) w8_dma4(sm_off[u], (const char*)sm_src[u] + (size_t)t * sm_step[u], sbase + sm_lds[u]);
+            if (u < n_small) dma4(sm_off[u], (const char*)sm_src[u] + (size_t)t * sm_step[u], sbase + sm_lds[u]);
     };
     // copies per wave per k-tile: kACopies + kBCopies + n_small (n_small is 0, 1 or 2, wave-uniform)
     constexpr int kBase = kACopies + kBCopies;
     auto wait_next_only = [&]() __attribute__((always_inline)) {  // at most this wave's copies of one k-tile in flight
         if (n_small == 2)
-            w8_wait_vm<kBase + 2>();
+            wait_vm<kBase + 2>();
         else if (n_small == 1)
-            w8_wait_vm<kBase + 1>();
+            wait_vm<kBase + 1>();
         else
-            w8_wait_vm<kBase>();
+            wait_vm<kBase>();
     };
 
     issue(0, 0);
@@ -375,7 +350,7 @@ void w4a8_gemm_kernel(const int8_t* __restrict__ xq, const float* __restrict__ a
         if (t + 1 < T)
             wait_next_only();
         else
-            w8_wait_vm<0>();
+            wait_vm<0>();
         __syncthreads();
         if (t + 2 < T) issue(t + 2, (ST + 2) % kStages);
         const char* s = smem + ST * L::Stage;
