@@ -645,7 +645,7 @@ def cpu_baseline(W, x):
     legs["decode_gemv"] = {"workload": wl.name, "weight_bytes": wbytes,
                            "single_thread": {"s": t1, "runs": n1, "gbs": wbytes / t1 / 1e9},
                            "all_cores": {"s": tT, "runs": nT, "threads": T, "gbs": wbytes / tT / 1e9}}
-    # prefill (M=1024): the first 8 rows on one thread, the first 64 on all cores
+    # prefill (M=1024): the first 4 rows on one thread, the first 64 on all cores
     pw = workloads.PREFILL
     _, xp = workloads.inputs(pw)
     rows1, rowsT = 4, 64

@@ -99,7 +99,7 @@ w4a16_status_t check_matmul_common(w4a16_format_t fmt, w4a16_dtype_t act, const 
 }
 
 // Q4, the zero-point format and W8 with fp16 activations: every row of x against one weight pass
-// (64 rows at a time) on the fp16 matrix cores.
+// (16 rows per pass over the weights) on the fp16 matrix cores.
 w4a16_status_t launch_rowmajor_rows(w4a16_format_t fmt, const void* x, int64_t M, const void* codes,
                                     const void* scales, const void* mins, int64_t N, int64_t K, void* y,
                                     hipStream_t stream) {

@@ -56,7 +56,7 @@ hipError_t launch_skinny_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
                                      const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
                                      hipStream_t stream);
 
-// Row-major formats on fp16 MFMA for any number of fp16 activation rows (64 per weight pass).
+// Row-major formats on fp16 MFMA for any number of fp16 activation rows (16 per weight pass).
 hipError_t launch_rowmma_q4b32(const uint16_t* x, int64_t M, const uint8_t* codes, const uint16_t* scales, int64_t N,
                                int64_t K, uint16_t* y, hipStream_t stream);
 hipError_t launch_rowmma_g128zp(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

@@ -1,6 +1,6 @@
 // rowmma.hip -- the row-major weight formats (Q4 block-32, the integer-zero-point format, W8 per
-// row) against up to 64 rows of fp16 activations on the fp16 matrix cores, with every weight read
-// once per call.
+// row) against fp16 activations on the fp16 matrix cores, 16 activation rows per pass over the
+// weights.
 //
 // The pages' GEMV for these formats takes one activation row (thuongvuho.com "Why My 4-Bit CUDA
 // Kernel Wasn't Faster"; anrans.github.io "Quantization and GEMV", "W4A16: dequantizing in

@@ -173,7 +173,7 @@ size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int6
 
 /* Large-M path: y [M][N] = x [M][K] . W_hat^T on the matrix cores with fp32 accumulation.
  * Q4, the zero-point format and W8 (fp16 activations only; ERR_UNSUPPORTED for bf16): any M, each
- * 64 rows against one pass over the weights, dequantized to fp16 in registers as for w4a16_gemv's
+ * 16 rows against one pass over the weights, dequantized to fp16 in registers as for w4a16_gemv's
  * rows (anrans.github.io "Quantization and GEMV", "The quantization formulas": the zero-point
  * format's (q - z) s); no workspace.  G128 as follows, on bf16 MFMA.
  * From 33 rows on, packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai
