@@ -82,7 +82,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "zp_prepared", "w8", "w4a8",
-                                       "w4a8_decode", "w4a8_sweep", "cpu", "rowfmt_sweep"], default=None,
+                                       "w4a8_decode", "w4a8_sweep", "cpu", "rowfmt_sweep", "l2_patterns"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -219,7 +219,9 @@ class Roofs:
         self.lib.roof_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_void_p]
         self.lib.roof_empty.argtypes = [ctypes.c_void_p]
-        self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        self.lib.roof_shared_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p]
+        self.sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
 
     def _stream(self):
         import torch
@@ -249,6 +251,33 @@ class Roofs:
         best["bytes"] = nbytes
         best["kernel"] = "roof_read_kernel (16-byte non-temporal loads, 4 in flight per lane)"
         return best
+
+
+    def shared_read(self, M: int, K: int, blocks: int = 224):
+        """Every one of `blocks` blocks reads all of one shared bf16 [M][K] (L2-resident after the
+        first) in each wave-load shape: the per-CU rates behind the mid-M kernels' designs."""
+        import torch
+        x = torch.randint(-2 ** 15, 2 ** 15, (M, K), dtype=torch.int16, device="cuda")
+        shapes = ("1 KB of one row", "16 rows x 64 B (16x16x32 A fragments)", "32 rows x 32 B (32x32x16 A fragments)",
+                  "4 rows x 256 B")
+        out = []
+        for pat, shape in enumerate(shapes):
+            def step(i, pat=pat):
+                assert self.lib.roof_shared_read(x.data_ptr(), M, K, pat, blocks, self.sink.data_ptr(),
+                                                 self._stream()) == 0
+            r = time_rounds(step, 1)
+            out.append({"pattern": pat, "shape": shape, "us": r["us"], "us_rounds": r["rounds_us"],
+                        "per_cu_gbs": M * K * 2 / r["us"] / 1e3})
+        del x
+        return out
+
+
+def bench_l2_patterns():
+    """roof_shared_read at K = 4096 for 32, 64 and 128 rows, 224 blocks (one per 64 columns of the
+    decode shape), beside the empty launch that every figure includes."""
+    roofs = Roofs()
+    return {"blocks": 224, "K": 4096, "empty_launch_us": roofs.empty_launch_us(),
+            "rows": {M: roofs.shared_read(M, 4096) for M in (32, 64, 128)}}
 
 
 def time_rounds_eager(step, rounds: int = ROUNDS):
@@ -755,7 +784,7 @@ def main():
                   "w8": bench_rowfmt_sweep(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32),
                   "q4": bench_rowfmt_sweep(workloads.Q4, w.W4A16_FMT_Q4_B32_SYM_FP16, None, (1, 2, 4, 8, 16))},
               "w8": bench_w8, "zp_prepared": bench_zp_prepared, "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
-              "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only}[args.only]
+              "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only, "l2_patterns": bench_l2_patterns}[args.only]
         print(json.dumps({"only": args.only, "result": fn()}), flush=True)
         return
 
