@@ -722,7 +722,7 @@ def copy_calibration(mib: int):
     log(f"copy calibration: 5 x {mib} MiB device-to-device")
 
 
-def bench_zp_prepared(W=None, Ms=(1, 4, 16)):
+def bench_zp_prepared(W=None, Ms=(1, 4, 16, 32, 64)):
     """The zero-point format from its prepared copy (w4a16_prepare once, then w4a16_gemv_prepared)
     at the decode shape, cold copies, fp16 activations; rates over the prepared copy's bytes and,
     for comparison with the canonical GEMV, over the format's own bytes."""

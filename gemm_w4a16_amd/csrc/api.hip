@@ -382,15 +382,21 @@ w4a16_status_t w4a16_gemv_prepared(w4a16_format_t fmt, w4a16_dtype_t act, const 
     if (M <= 0 || M > kMaxDim) return W4A16_ERR_INVALID;
     if (!aligned16(x) || !aligned16(y) || !aligned16(prepared)) return W4A16_ERR_INVALID;
     if (act != W4A16_BF16 && act != W4A16_FP16 && act != W4A16_FP32) return W4A16_ERR_INVALID;
-    if (fmt != W4A16_FMT_G128_ZP_FP16 || act == W4A16_FP32 || M > w4a16::kGemvMaxRows) return W4A16_ERR_UNSUPPORTED;
+    if (fmt != W4A16_FMT_G128_ZP_FP16 || act == W4A16_FP32) return W4A16_ERR_UNSUPPORTED;
     const PreparedLayout L = prepared_layout(N, K);
     const char* base = static_cast<const char*>(prepared);
     w4a16::clear_stale_error();
-    return from_hip(w4a16::launch_skinny_prepared_zp(static_cast<const uint16_t*>(x), M, act == W4A16_FP16,
-                                                     reinterpret_cast<const uint32_t*>(base + L.words),
-                                                     reinterpret_cast<const float*>(base + L.scales),
-                                                     reinterpret_cast<const float*>(base + L.mins), N, K,
-                                                     static_cast<uint16_t*>(y), stream));
+    // passes of up to kGemvMaxRows rows; after the first, the copy is read from the Infinity Cache
+    // when it fits there
+    for (int64_t m0 = 0; m0 < M; m0 += w4a16::kGemvMaxRows) {
+        const int64_t mc = M - m0 < w4a16::kGemvMaxRows ? M - m0 : w4a16::kGemvMaxRows;
+        const w4a16_status_t st = from_hip(w4a16::launch_skinny_prepared_zp(
+            static_cast<const uint16_t*>(x) + m0 * K, mc, act == W4A16_FP16, reinterpret_cast<const uint32_t*>(base + L.words),
+            reinterpret_cast<const float*>(base + L.scales), reinterpret_cast<const float*>(base + L.mins), N, K,
+            static_cast<uint16_t*>(y) + m0 * N, stream));
+        if (st != W4A16_OK) return st;
+    }
+    return W4A16_OK;
 }
 
 size_t w4a16_matmul_noalloc_max_scratch_bytes(void) { return kScratchBytes; }

@@ -211,8 +211,8 @@ int64_t w4a16_matmul_gemv_cutoff(void);
  * m[g][n] = -zeros[n][g] * s[g][n] as fp32 [K/128][N], each part starting 16-byte aligned.
  * With z an integer of magnitude at most 2048 (as the quantizer stores it), (q - z) s = q s + m is
  * exact in fp32 (|q - z| has at most 12 significant bits and s 11), so fmaf(q, s, m) reproduces
- * the format's decode bit for bit.  The copy costs
- * 4 + 64/128 = 4.5 bits per weight against the canonical 4 + 32/128 = 4.25.
+ * the format's decode bit for bit.  The copy costs 4 + 64/128 = 4.5 bits per weight against the
+ * canonical 4 + 32/128 = 4.25.
  * Only W4A16_FMT_G128_ZP_FP16 has a prepared form; the others return 0 / W4A16_ERR_UNSUPPORTED
  * (the G128 format is already stored in that order, so a copy would change nothing). */
 
@@ -222,19 +222,20 @@ size_t w4a16_prepared_bytes(w4a16_format_t fmt, int64_t N, int64_t K);
 /* Write the prepared copy of the packed weights (codes, scales, mins = zero points, as
  * w4a16_quantize_pack wrote them) into `prepared` (device, caller-owned, 16-byte aligned,
  * prepared_bytes >= w4a16_prepared_bytes(fmt, N, K)).  Asynchronous on `stream`; the copy is a
- * pure function of the packed arrays and is valid until they change.  Errors: ERR_SHAPE,
- * ERR_INVALID (alignment, size), ERR_UNSUPPORTED (a format with no prepared form), ERR_HIP. */
+ * pure function of the packed arrays and is valid until they change.  Errors: ERR_INVALID (shape,
+ * alignment, size), ERR_UNSUPPORTED (a format with no prepared form, N or K past the limits),
+ * ERR_DEVICE. */
 w4a16_status_t w4a16_prepare(w4a16_format_t fmt, const void* codes, const void* scales, const void* mins,
                              int64_t N, int64_t K, void* prepared, size_t prepared_bytes,
                              hipStream_t stream);
 
-/* y [M][N] = x [M][K] . W_hat^T from the prepared copy, 1 <= M <= w4a16_gemv_max_rows(), for bf16
- * or fp16 activations; y has the activations' type.  The kernel is w4a16_gemv's G128 one: the
- * inner sums run on the matrix cores against 128 + q (bf16) or 1024 + q (fp16), and each group
- * adds s * sum(x (offset + q)) + (m - offset s) * sum(x) in fp32.  Up to the order of fp32
- * additions this is w4a16_gemv's product on the canonical zero-point arrays; it is bitwise
- * reproducible run to run.  Errors: ERR_SHAPE, ERR_INVALID (M, alignment, act),
- * ERR_UNSUPPORTED (fp32 activations, M above the maximum, other formats), ERR_HIP. */
+/* y [M][N] = x [M][K] . W_hat^T from the prepared copy, any M >= 1, for bf16 or fp16 activations;
+ * y has the activations' type.  The kernel is w4a16_gemv's G128 one, one pass over the copy per
+ * w4a16_gemv_max_rows() rows: the inner sums run on the matrix cores against 128 + q (bf16) or
+ * 1024 + q (fp16), and each group adds s * sum(x (offset + q)) + (m - offset s) * sum(x) in fp32.
+ * Up to the order of fp32 additions this is the product on the canonical zero-point arrays; it is
+ * bitwise reproducible run to run.  Errors: ERR_INVALID (shape, M, alignment, act),
+ * ERR_UNSUPPORTED (fp32 activations, other formats, N or K past the limits), ERR_DEVICE. */
 w4a16_status_t w4a16_gemv_prepared(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                                    const void* prepared, int64_t N, int64_t K, void* y,
                                    hipStream_t stream);

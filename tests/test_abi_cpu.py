@@ -297,6 +297,4 @@ def test_prepared_copy_sizes_and_validation():
     assert _status(g, ZP, F16, FAKE, 1, None, 256, 4096, FAKE, 0) == w.W4A16_ERR_INVALID           # no copy
     assert _status(g, ZP, 7, FAKE, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_INVALID             # no such type
     assert _status(g, ZP, F32, FAKE, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
-    assert _status(g, ZP, BF16, FAKE, w.w4a16_gemv_max_rows() + 1, FAKE, 256, 4096, FAKE, 0) \
-        == w.W4A16_ERR_UNSUPPORTED
     assert _status(g, Q4, F16, FAKE, 1, FAKE, 256, 4096, FAKE, 0) == w.W4A16_ERR_UNSUPPORTED
