@@ -100,10 +100,13 @@ def bind(path) -> ctypes.CDLL:
     L.oracle_quantize_w8row.argtypes = [P, I64, I64, P, P]
     L.oracle_dequant_w8row.argtypes = [P, P, I64, I64, I, P]
     L.oracle_matmul_w8row_f64.argtypes = [P, I, I64, P, P, I64, I64, P]
+    L.oracle_quantize_pack.argtypes = [I, P, I64, I64, P, P, P]
+    L.oracle_dequant.argtypes = [I, P, P, P, I64, I64, I, P]
+    L.oracle_matmul_f64.argtypes = [I, P, I, I64, P, P, P, I64, I64, P]
     L.oracle_quantize_act_i8.argtypes = [P, I64, I64, P, P, P]
     L.oracle_matmul_w4a8_f64.argtypes = [P, P, I64, P, P, P, I64, I64, P]
     L.oracle_matmul_w4a8_f64_at.argtypes = [P, P, I64, P, P, P, I64, I64, P, P, I64, P]
-    for name in ("oracle_quantize_act_i8", "oracle_matmul_w4a8_f64", "oracle_matmul_w4a8_f64_at",
+    for name in ("oracle_quantize_pack", "oracle_dequant", "oracle_matmul_f64", "oracle_quantize_act_i8", "oracle_matmul_w4a8_f64", "oracle_matmul_w4a8_f64_at",
                  "oracle_quantize_w8row", "oracle_dequant_w8row", "oracle_matmul_w8row_f64",
                  "oracle_quantize_g128zp", "oracle_dequant_g128zp", "oracle_matmul_g128zp_f64",
                  "oracle_matmul_g128zp_f64_at",

@@ -679,3 +679,45 @@ int oracle_matmul_f32w_f64(const uint16_t* x, int x_kind, int64_t M, const float
         }
     return ORACLE_OK;
 }
+
+/* ------------------------------------------------------------------------------------------
+ * The format-generic calls, dispatching on fmt: 0 = G128, 1 = Q4 block-32, 2 = zero-point,
+ * 3 = W8 per row (the library's numbering of its formats).  `mins` holds the minimums (G128) or
+ * the zero points (zero-point format) and must be NULL for Q4 and W8, whose scales are fp16 and
+ * fp32 respectively.  Each call forwards to the format's own function above, with its layouts,
+ * its kinds and its argument checks.
+ * ---------------------------------------------------------------------------------------- */
+int oracle_quantize_pack(int fmt, const float* W, int64_t N, int64_t K, void* codes, void* scales, void* mins)
+{
+    switch (fmt) {
+    case 0: return oracle_quantize_g128(W, N, K, codes, scales, mins);
+    case 1: return mins ? ORACLE_BAD_ARG : oracle_quantize_q4b32(W, N, K, codes, scales);
+    case 2: return oracle_quantize_g128zp(W, N, K, codes, scales, mins);
+    case 3: return mins ? ORACLE_BAD_ARG : oracle_quantize_w8row(W, N, K, codes, scales);
+    default: return ORACLE_BAD_ARG;
+    }
+}
+
+int oracle_dequant(int fmt, const void* codes, const void* scales, const void* mins, int64_t N, int64_t K,
+                   int kind, void* out)
+{
+    switch (fmt) {
+    case 0: return oracle_dequant_g128(codes, scales, mins, N, K, kind, out);
+    case 1: return mins ? ORACLE_BAD_ARG : oracle_dequant_q4b32(codes, scales, N, K, kind, out);
+    case 2: return oracle_dequant_g128zp(codes, scales, mins, N, K, kind, out);
+    case 3: return mins ? ORACLE_BAD_ARG : oracle_dequant_w8row(codes, scales, N, K, kind, out);
+    default: return ORACLE_BAD_ARG;
+    }
+}
+
+int oracle_matmul_f64(int fmt, const uint16_t* x, int x_kind, int64_t M, const void* codes, const void* scales,
+                      const void* mins, int64_t N, int64_t K, double* y)
+{
+    switch (fmt) {
+    case 0: return oracle_matmul_g128_f64(x, x_kind, M, codes, scales, mins, N, K, y);
+    case 1: return mins ? ORACLE_BAD_ARG : oracle_matmul_q4b32_f64(x, x_kind, M, codes, scales, N, K, y);
+    case 2: return oracle_matmul_g128zp_f64(x, x_kind, M, codes, scales, mins, N, K, y);
+    case 3: return mins ? ORACLE_BAD_ARG : oracle_matmul_w8row_f64(x, x_kind, M, codes, scales, N, K, y);
+    default: return ORACLE_BAD_ARG;
+    }
+}

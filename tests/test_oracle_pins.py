@@ -880,3 +880,41 @@ def test_w4a8_matmul_group_form_and_error():
     y16 = oracle.matmul_g128(x, codes, scales, mins)
     rel = np.max(np.abs(y - y16)) / np.max(np.abs(y16))
     assert 1e-4 < rel < 2e-2
+
+
+def test_format_generic_calls_forward_to_each_format():
+    """oracle_quantize_pack / oracle_dequant / oracle_matmul_f64 (fmt 0 G128, 1 Q4, 2 zero-point,
+    3 W8) return exactly what each format's own pinned function returns, and refuse a third array
+    for the formats that have none and an unknown format."""
+    L = oracle.lib()
+    N, K, M = 5, 256, 3
+    W = workloads.weights(N, K, outliers=True, seed=77)
+    x16 = workloads.activations(M, K, "f16", seed=78)
+    xbf = workloads.activations(M, K, "bf16", seed=79)
+    cases = {0: (oracle.quantize_g128(W), xbf, 0), 1: (oracle.quantize_q4b32(W), x16, 1),
+             2: (oracle.quantize_g128zp(W), x16, 1), 3: (oracle.quantize_w8row(W), x16, 1)}
+    ptr = lambda a: None if a is None else a.ctypes.data
+    for fmt, (packed, x, xk) in cases.items():
+        packed = tuple(np.ascontiguousarray(a) for a in packed)
+        mine = tuple(np.zeros_like(a) for a in packed)
+        mins_out = ptr(mine[2]) if len(mine) > 2 else None
+        assert L.oracle_quantize_pack(fmt, W.ctypes.data, N, K, ptr(mine[0]), ptr(mine[1]), mins_out) == 0
+        for a, b in zip(packed, mine):
+            np.testing.assert_array_equal(a, b)
+        mins_in = ptr(packed[2]) if len(packed) > 2 else None
+        for kind, dt in ((0, np.float32), (2, np.float64)):
+            out = np.zeros((N, K), dtype=dt)
+            assert L.oracle_dequant(fmt, ptr(packed[0]), ptr(packed[1]), mins_in, N, K, kind, out.ctypes.data) == 0
+            ref = {0: oracle.dequant_g128, 1: oracle.dequant_q4b32, 2: oracle.dequant_g128zp,
+                   3: oracle.dequant_w8row}[fmt](*packed, "f32" if kind == 0 else "f64")
+            np.testing.assert_array_equal(out, ref)
+        y = np.zeros((M, N))
+        assert L.oracle_matmul_f64(fmt, x.ctypes.data, xk, M, ptr(packed[0]), ptr(packed[1]), mins_in, N, K,
+                                   y.ctypes.data) == 0
+        xkind = "bf16" if xk == 0 else "f16"
+        ref = {0: oracle.matmul_g128, 1: oracle.matmul_q4b32, 2: oracle.matmul_g128zp,
+               3: oracle.matmul_w8row}[fmt](x, *packed, x_kind=xkind)
+        np.testing.assert_array_equal(y, ref)
+        if fmt in (1, 3):   # no third array
+            assert L.oracle_quantize_pack(fmt, W.ctypes.data, N, K, ptr(mine[0]), ptr(mine[1]), ptr(mine[0])) != 0
+    assert L.oracle_quantize_pack(7, W.ctypes.data, N, K, None, None, None) != 0
