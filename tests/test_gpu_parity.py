@@ -584,6 +584,29 @@ def test_zp_decode_shape_full_pack_and_gemv(decode_weights):
     say(f"zp decode rel err {err:.3e}")
 
 
+def test_debug_checks_refuse_unstorable_weights(monkeypatch):
+    """W4A16_DEBUG_CHECKS makes w4a16_quantize_pack check a host copy of the weights first: good
+    weights pack exactly as without it; a NaN, or a Q4 block whose fp16 scale would overflow, is
+    refused with ERR_INVALID before anything is written."""
+    N, K = 64, 256
+    W = workloads.weights(N, K, outliers=True, seed=501)
+    plain = [host(t, np.uint32 if i == 0 else np.uint16) for i, t in enumerate(gpu_pack(G128, W))]
+    monkeypatch.setenv("W4A16_DEBUG_CHECKS", "1")
+    checked = [host(t, np.uint32 if i == 0 else np.uint16) for i, t in enumerate(gpu_pack(G128, W))]
+    for a, b in zip(plain, checked):
+        np.testing.assert_array_equal(a, b)
+    for fmt, bad in ((G128, np.float32(np.nan)), (Q4, np.float32(1e6)), (ZP, np.float32(np.inf))):
+        Wb = W.copy()
+        Wb[3, 40] = bad
+        codes, scales, mins = w.alloc_packed(fmt, N, K)
+        codes.fill_(0x34)
+        with pytest.raises(w.W4A16Error) as e:
+            w.w4a16_quantize_pack(fmt, dev(Wb), N, K, codes, scales, mins)
+        assert e.value.status == w.W4A16_ERR_INVALID
+        torch.cuda.synchronize()
+        assert bool((codes == 0x34).all())   # refused before any launch
+
+
 # ---------------------------------------------------------------------------------------------
 # The zero-point format's prepared copy: the copy decodes to the oracle's weights bit for bit,
 # and its GEMV meets the same bars as the canonical one.
