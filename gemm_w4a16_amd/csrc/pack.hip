@@ -367,12 +367,27 @@ hipError_t launch_dequant_q4b32(const uint8_t* codes, const uint16_t* scales, in
 // at most 12 bits and s 11, so q s, z s and their sum are all exact, and fmaf(q, s, m) is the
 // format's decode bit for bit.
 // ---------------------------------------------------------------------------------------------
+// The word transpose goes through a 64 x 64-word LDS tile, so that both the reads (256 bytes of
+// one weight row per 64 lanes) and the writes (256 bytes of one packed row) are whole lines.
+constexpr int kTr = 64;
 __global__ __launch_bounds__(256) void prepare_zp_words_kernel(const uint32_t* __restrict__ codes, int64_t N, int64_t K8,
                                                                uint32_t* __restrict__ out) {
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // output word (r, n), n fastest
-    if (i >= N * K8) return;
-    const int64_t r = i / N, n = i % N;
-    out[i] = codes[n * K8 + r];
+    __shared__ uint32_t tile[kTr][kTr + 1];  // [n][r], padded: column reads hit distinct banks
+    const int64_t n0 = (int64_t)blockIdx.x * kTr, r0 = (int64_t)blockIdx.y * kTr;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 lanes x 4 rows per step
+#pragma unroll
+    for (int i = 0; i < kTr / 4; ++i) {
+        const int nn = 4 * i + ty;
+        const int64_t n = n0 + nn, r = r0 + tx;
+        if (n < N && r < K8) tile[nn][tx] = codes[n * K8 + r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kTr / 4; ++i) {
+        const int rr = 4 * i + ty;
+        const int64_t r = r0 + rr, n = n0 + tx;
+        if (n < N && r < K8) out[r * N + n] = tile[tx][rr];
+    }
 }
 
 __global__ __launch_bounds__(256) void prepare_zp_params_kernel(const uint16_t* __restrict__ scales,
@@ -391,8 +406,8 @@ __global__ __launch_bounds__(256) void prepare_zp_params_kernel(const uint16_t* 
 hipError_t launch_prepare_zp(const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K,
                              uint32_t* words, float* s_out, float* m_out, hipStream_t stream) {
     const int64_t K8 = K / 8, G = K / 128;
-    hipLaunchKernelGGL(prepare_zp_words_kernel, dim3((unsigned)((N * K8 + 255) / 256)), dim3(256), 0, stream, codes, N, K8,
-                       words);
+    hipLaunchKernelGGL(prepare_zp_words_kernel, dim3((unsigned)((N + kTr - 1) / kTr), (unsigned)((K8 + kTr - 1) / kTr)),
+                       dim3(256), 0, stream, codes, N, K8, words);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prepare_zp_params_kernel, dim3((unsigned)((N * G + 255) / 256)), dim3(256), 0, stream, scales, zeros,
