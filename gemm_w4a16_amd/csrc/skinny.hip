@@ -132,7 +132,7 @@ __device__ __forceinline__ void load_params32(const float* __restrict__ p, int N
     }
 }
 
-// MR: activation rows staged (M <= MR; 1, 4 or 16).  TPL: adjacent columns per lane (4 or 2),
+// MR: activation rows staged (M <= MR; 1, 4, 8 or 16).  TPL: adjacent columns per lane (4 or 2),
 // i.e. 16 * TPL columns per block.  WAVES: waves per block; each takes kGroupsPerPass / WAVES
 // groups per pass.  kVec: N % TPL == 0 (vector loads of a lane's columns).  kF16: fp16
 // activations and output on the fp16 matrix cores, codes as 1024 + q (else bf16 and 128 + q).
@@ -319,10 +319,12 @@ void launch_rows(const uint16_t* x, int64_t M, const uint32_t* codes, const void
     if (tpl == 4) {
         if (M == 1) launch_mr<1, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else if (M <= 4) launch_mr<4, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else if (M <= 8) launch_mr<8, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else launch_mr<16, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
     } else {
         if (M == 1) launch_mr<1, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else if (M <= 4) launch_mr<4, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else if (M <= 8) launch_mr<8, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else launch_mr<16, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
     }
 }

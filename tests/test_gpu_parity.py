@@ -148,7 +148,7 @@ def test_dequant_q4_bit_exact(dtype, kind, np_t):
 # Matmul parity at sizes the oracle runs in full.
 # ---------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 2, 3, 4])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 6, 8])
 @pytest.mark.parametrize("N,K", [(256, 512), (1, 128), (63, 256), (65, 384), (1000, 2048), (300, 4224)])
 def test_gemv_g128_parity(M, N, K):
     say(f"gemv_g128 M={M} N={N} K={K}")
@@ -326,7 +326,7 @@ def test_row_major_formats_edge_groups(fmt, M):
     # bound above holds it to 2^-20 B)
 
 
-@pytest.mark.parametrize("M", [1, 3, 9])
+@pytest.mark.parametrize("M", [1, 3, 6, 9])
 def test_gemv_wide_odd_n_two_passes(M):
     """N = 12289 takes the 64-column blocks of the small-M kernel (chosen from 12225 columns up)
     with scalar column loads (N odd); K = 8192 is two passes of 32 groups."""
