@@ -386,15 +386,22 @@ w4a16_status_t w4a16_gemv_prepared(w4a16_format_t fmt, w4a16_dtype_t act, const 
     const PreparedLayout L = prepared_layout(N, K);
     const char* base = static_cast<const char*>(prepared);
     w4a16::clear_stale_error();
-    // passes of up to kGemvMaxRows rows; after the first, the copy is read from the Infinity Cache
-    // when it fits there
-    for (int64_t m0 = 0; m0 < M; m0 += w4a16::kGemvMaxRows) {
-        const int64_t mc = M - m0 < w4a16::kGemvMaxRows ? M - m0 : w4a16::kGemvMaxRows;
-        const w4a16_status_t st = from_hip(w4a16::launch_skinny_prepared_zp(
-            static_cast<const uint16_t*>(x) + m0 * K, mc, act == W4A16_FP16, reinterpret_cast<const uint32_t*>(base + L.words),
-            reinterpret_cast<const float*>(base + L.scales), reinterpret_cast<const float*>(base + L.mins), N, K,
-            static_cast<uint16_t*>(y) + m0 * N, stream));
+    const bool f16 = act == W4A16_FP16;
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(base + L.words);
+    const float* sp = reinterpret_cast<const float*>(base + L.scales);
+    const float* mp = reinterpret_cast<const float*>(base + L.mins);
+    // one pass over the copy per 32 rows (the 17..32-row kernel), the last 1..16 rows on the
+    // small-M kernel; after the first pass the copy is read from the Infinity Cache when it fits
+    for (int64_t m0 = 0; m0 < M;) {
+        const int64_t rem = M - m0;
+        const int64_t mc = rem <= w4a16::kGemvMaxRows ? rem : (rem < 32 ? rem : 32);
+        const uint16_t* xa = static_cast<const uint16_t*>(x) + m0 * K;
+        uint16_t* ya = static_cast<uint16_t*>(y) + m0 * N;
+        const w4a16_status_t st =
+            from_hip(mc <= w4a16::kGemvMaxRows ? w4a16::launch_skinny_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream)
+                                               : w4a16::launch_rows32_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream));
         if (st != W4A16_OK) return st;
+        m0 += mc;
     }
     return W4A16_OK;
 }

@@ -55,6 +55,10 @@ hipError_t launch_prepare_zp(const uint32_t* codes, const uint16_t* scales, cons
 hipError_t launch_skinny_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
                                      const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
                                      hipStream_t stream);
+// ... and the 17..32-row kernel over it.
+hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                                     const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
+                                     hipStream_t stream);
 
 // Row-major formats on fp16 MFMA for any number of fp16 activation rows (16 per weight pass).
 hipError_t launch_rowmma_q4b32(const uint16_t* x, int64_t M, const uint8_t* codes, const uint16_t* scales, int64_t N,

@@ -32,6 +32,8 @@
 //  * the packed words, scales and minimums of the next step are loaded while this step runs; a
 //    wave whose group lies past K skips the step;
 //  * the KP partial sums of each output are added through LDS in a fixed order.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -60,19 +62,44 @@ __device__ __forceinline__ bf16x8_t r32_pair_up(uint4 v) {
     return __builtin_bit_cast(bf16x8_t, p);
 }
 
-// One group's operands in a lane: packed words [k-step][column], scale/minimum pairs, and the A
-// fragments [k-step][row tile] in natural k order.
+// One group's operands in a lane: packed words [k-step][column], scale/minimum pairs (bf16 pairs,
+// or fp32 for the zero-point format's prepared copy), and the A fragments [k-step][row tile] in
+// natural k order.
+template <bool kP32>
 struct R32Group {
     uint32_t w[4][4];
     uint32_t s[2], m[2];
     uint4 a[4][2];
 };
+template <>
+struct R32Group<true> {
+    uint32_t w[4][4];
+    float s[4], m[4];
+    uint4 a[4][2];
+};
 
-template <bool kVec>
+// kF16: fp16 activations and output on the fp16 matrix cores, codes as 1024 + q (the prepared
+// zero-point copy), else bf16 and 128 + q.  kP32: fp32 scales and minimums [K/128][N].
+template <bool kVec, bool kF16 = false, bool kP32 = false>
 __global__ __launch_bounds__(64 * kR32Waves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
-                       const uint16_t* __restrict__ scales, const uint16_t* __restrict__ mins,
+                       const void* __restrict__ scales_v, const void* __restrict__ mins_v,
                        uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic) {
+    const uint16_t* __restrict__ scales = static_cast<const uint16_t*>(scales_v);
+    const uint16_t* __restrict__ mins = static_cast<const uint16_t*>(mins_v);
+    const float* __restrict__ scales32 = static_cast<const float*>(scales_v);
+    const float* __restrict__ mins32 = static_cast<const float*>(mins_v);
+    using Group = R32Group<kP32>;
+    constexpr float kOffset = kF16 ? 1024.0f : 128.0f;  // the magic number's value at q = 0
+    auto mfma = [](bf16x8_t a, bf16x8_t b, f32x4_t c) {
+        if constexpr (kF16) {
+            typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                          0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+        }
+    };
     __shared__ float part[kR32Waves][32][64];
     const int lane = lane_id(), wave = wave_id();
     const int lr = lane & 15, lg = lane >> 4;
@@ -88,7 +115,7 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
     const uint16_t* xrow0 = x + (size_t)min(lr, M - 1) * K + 8 * lg;
     const uint16_t* xrow1 = x + (size_t)min(16 + lr, M - 1) * K + 8 * lg;
 
-    auto load = [&](int j, R32Group& o) {
+    auto load = [&](int j, Group& o) {
         const int g = wave + kR32Waves * j;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -105,6 +132,22 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
             }
             o.a[s][0] = *reinterpret_cast<const uint4*>(xrow0 + g * 128 + 32 * s);
             o.a[s][1] = *reinterpret_cast<const uint4*>(xrow1 + g * 128 + 32 * s);
+        }
+        if constexpr (kP32) {
+            const float* sp = scales32 + (size_t)g * N;
+            const float* mp = mins32 + (size_t)g * N;
+            if (kVec) {
+                const float4 a = *reinterpret_cast<const float4*>(sp + cbase), b = *reinterpret_cast<const float4*>(mp + cbase);
+                o.s[0] = a.x, o.s[1] = a.y, o.s[2] = a.z, o.s[3] = a.w;
+                o.m[0] = b.x, o.m[1] = b.y, o.m[2] = b.z, o.m[3] = b.w;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    o.s[c] = sp[min(cbase + c, N - 1)];
+                    o.m[c] = mp[min(cbase + c, N - 1)];
+                }
+            }
+            return;
         }
         const uint16_t* sp = scales + (size_t)g * N;
         const uint16_t* mp = mins + (size_t)g * N;
@@ -124,7 +167,8 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
     // the magic exponent in a VGPR (the mask stays in an SGPR): one v_and_or_b32 per pair
     uint32_t magic_v;
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(magic));
-    const u32x4_t ones_u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;  // 1.0 in both halves
+    const u32x4_t ones_u = {kOne, kOne, kOne, kOne};
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
 
     // accumulator element e of lane l in a 16x16 tile: row 4 (l / 16) + e, column l % 16; tile c
@@ -137,7 +181,7 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
 #pragma unroll
             for (int e = 0; e < 4; ++e) yacc[c][rt][e] = 0.0f;
 
-    auto compute = [&](const R32Group& o) {
+    auto compute = [&](const Group& o) {
         f32x4_t acc[4][2], accs[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
@@ -155,16 +199,21 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
                 const bf16x8_t a = r32_pair_up(o.a[s][rt]);
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    acc[c][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[c], acc[c][rt], 0, 0, 0);
-                accs[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ones, accs[rt], 0, 0, 0);
+                    acc[c][rt] = mfma(a, b[c], acc[c][rt]);
+                accs[rt] = mfma(a, ones, accs[rt]);
             }
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const uint32_t sb = (c & 1) ? (o.s[c >> 1] >> 16) : (o.s[c >> 1] & 0xFFFFu);
-            const uint32_t mb = (c & 1) ? (o.m[c >> 1] >> 16) : (o.m[c >> 1] & 0xFFFFu);
-            const float sv = bf16_bits_to_f32(sb), mv = bf16_bits_to_f32(mb);
-            const float cc = __builtin_fmaf(-128.0f, sv, mv);  // min - 128 s
+            float sv, mv;
+            if constexpr (kP32) {
+                sv = o.s[c], mv = o.m[c];
+            } else {
+                const uint32_t sb = (c & 1) ? (o.s[c >> 1] >> 16) : (o.s[c >> 1] & 0xFFFFu);
+                const uint32_t mb = (c & 1) ? (o.m[c >> 1] >> 16) : (o.m[c >> 1] & 0xFFFFu);
+                sv = bf16_bits_to_f32(sb), mv = bf16_bits_to_f32(mb);
+            }
+            const float cc = __builtin_fmaf(-kOffset, sv, mv);  // min - 128 s (or - 1024 s)
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
@@ -176,7 +225,7 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
     };
 
     // groups j, j + 1 in flight while j is used; slot j % 2 is reloaded right after its use
-    R32Group sl[kR32Ahead];
+    Group sl[kR32Ahead];
 #pragma unroll
     for (int d = 0; d < kR32Ahead; ++d)
         if (d < J) load(d, sl[d]);
@@ -201,7 +250,7 @@ void mid_rows32_kernel(const uint16_t* __restrict__ x, const uint32_t* __restric
         float sum = 0.0f;
 #pragma unroll
         for (int v = 0; v < kR32Waves; ++v) sum += part[v][row][col];
-        y[(size_t)row * N + n] = f32_to_bf16_bits(sum);
+        y[(size_t)row * N + n] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
     }
 }
 
@@ -380,6 +429,26 @@ __global__ __launch_bounds__(128 * KP) void mid_g128_kernel(const uint16_t* __re
 }
 
 }  // namespace
+
+hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                                     const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
+                                     hipStream_t stream) {
+    const unsigned gx = (unsigned)((N + kMidCols - 1) / kMidCols);
+    const uint32_t magic = act_f16 ? 0x64006400u : 0x43004300u;  // 1024 (fp16) or 128 (bf16), both halves
+    auto go = [&](auto vec, auto f16) {
+        hipLaunchKernelGGL((mid_rows32_kernel<decltype(vec)::value, decltype(f16)::value, true>), dim3(gx),
+                           dim3(64 * kR32Waves), 0, stream, x, codes, scales, mins, y, (int)M, (int)N, (int)K,
+                           0x000F000Fu, magic);
+    };
+    using T = std::true_type;
+    using F = std::false_type;
+    if (N % 4 == 0) {
+        if (act_f16) go(T{}, T{}); else go(T{}, F{});
+    } else {
+        if (act_f16) go(F{}, T{}); else go(F{}, F{});
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {

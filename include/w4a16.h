@@ -230,9 +230,10 @@ w4a16_status_t w4a16_prepare(w4a16_format_t fmt, const void* codes, const void* 
                              hipStream_t stream);
 
 /* y [M][N] = x [M][K] . W_hat^T from the prepared copy, any M >= 1, for bf16 or fp16 activations;
- * y has the activations' type.  The kernel is w4a16_gemv's G128 one, one pass over the copy per
- * w4a16_gemv_max_rows() rows: the inner sums run on the matrix cores against 128 + q (bf16) or
- * 1024 + q (fp16), and each group adds s * sum(x (offset + q)) + (m - offset s) * sum(x) in fp32.
+ * y has the activations' type.  The kernels are the G128 ones for up to 16 and for 17..32 rows (one
+ * pass over the copy per 32 rows, the last 1..16 rows in a pass of their own): the inner sums run on
+ * the matrix cores against 128 + q (bf16) or 1024 + q (fp16), and each group adds
+ * s * sum(x (offset + q)) + (m - offset s) * sum(x) in fp32.
  * Up to the order of fp32 additions this is the product on the canonical zero-point arrays; it is
  * bitwise reproducible run to run.  Errors: ERR_INVALID (shape, M, alignment, act),
  * ERR_UNSUPPORTED (fp32 activations, other formats, N or K past the limits), ERR_DEVICE. */

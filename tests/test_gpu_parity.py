@@ -652,7 +652,7 @@ def test_prepared_copy_decodes_to_the_oracle_weights(N, K):
 @pytest.mark.parametrize("act", [F16, BF16])
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 65, 384), (2, 130, 4096), (3, 257, 2176), (1, 31, 17408),
                                    (4, 1000, 640), (5, 1000, 1152), (16, 100, 1024), (16, 13001, 256),
-                                   (17, 300, 1024), (40, 1000, 640)])
+                                   (17, 300, 1024), (40, 1000, 640), (32, 129, 384), (49, 62, 256)])
 def test_gemv_prepared_zp_parity(act, M, N, K):
     say(f"gemv_prepared act={act} M={M} N={N} K={K}")
     W = edge_weights(N, K, 128, np.float32(4.0), seed=M + N + K)
@@ -672,7 +672,7 @@ def test_gemv_prepared_zp_parity(act, M, N, K):
     say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
 
 
-@pytest.mark.parametrize("M", [1, 16, 64])
+@pytest.mark.parametrize("M", [1, 16, 32, 64])
 def test_gemv_prepared_zp_decode_shape(decode_weights, M):
     """The decode shape (K = 4096, N = 14336) from the prepared copy, fp16 activations, in full."""
     wl = workloads.ZP_DECODE
