@@ -316,6 +316,63 @@ def bench_decode(steps, warmup):
     return wl, st, R, wall, ev, kt, algo_bytes, W, x
 
 
+class ClockSampler:
+    """Records the GPU clocks while a timing runs: a background thread reads the driver's
+    current shader (sclk) and memory (mclk) clock levels from sysfs every `period` seconds.  The
+    clocks are not set here; a compute-bound kernel runs at what the power limit allows, which is
+    why the figures carry them."""
+
+    def __init__(self, period: float = 0.05):
+        import glob
+        self.period = period
+        self.files = {k: sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{k}")) for k in ("sclk", "mclk")}
+        self.samples = {k: {f: [] for f in fs} for k, fs in self.files.items()}
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _current_mhz(path: str):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return int(line.split(":", 1)[1].strip().split("M")[0].split("m")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, fs in self.files.items():
+                for f in fs:
+                    v = self._current_mhz(f)
+                    if v is not None:
+                        self.samples[k][f].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+        return False
+
+    def summary(self):
+        out = {}
+        for k, per in self.samples.items():
+            for f, vals in per.items():
+                if vals:
+                    card = f.split("/")[4]
+                    out.setdefault(k + "_mhz", {})[card] = {"min": min(vals), "median": float(np.median(vals)),
+                                                           "max": max(vals), "samples": len(vals)}
+        return out or {"unavailable": "no readable pp_dpm_sclk / pp_dpm_mclk under /sys/class/drm"}
+
+
 def bench_prefill():
     import torch
     import gemm_w4a16_amd as w
@@ -323,7 +380,8 @@ def bench_prefill():
     wl = workloads.PREFILL
     W, x = workloads.inputs(wl)
     st = Setup(w.W4A16_FMT_G128_ASYM_BF16, wl.M, wl.N, wl.K, x, W, 1)
-    kt = time_rounds(st.step, 1)
+    with ClockSampler() as clocks:
+        kt = time_rounds(st.step, 1)
     flops = 2.0 * wl.M * wl.N * wl.K
     t = kt["us"] * 1e-6
     # the measured roof: the same product with bf16 weights (the GPU's own dequantized weights)
@@ -339,6 +397,7 @@ def bench_prefill():
         "workload": wl.name, "M": wl.M, "N": wl.N, "K": wl.K,
         "us_per_launch": kt["us"], "us_per_launch_rounds": kt["rounds_us"],
         "launches_per_round": kt["launches_per_round"],
+        "clocks_during_timing": clocks.summary(),
         "tflops": flops / t / 1e12,
         "frac_mfma_bf16_peak": flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "roofline": {"bound": "mfma", "kernel": PREFILL_KERNEL, "achieved": flops / t / 1e12,
@@ -666,8 +725,12 @@ def cpu_baseline(W, x):
     import workloads
     T = cpu_threads()
     legs = {}
+    tpack, npack = timed(lambda: oracle.quantize_g128(W), 1, 0.0)
     codes, scales, mins = oracle.quantize_g128(W)
     wbytes = codes.nbytes + scales.nbytes + mins.nbytes
+    legs["quantize_pack_g128"] = {"workload": workloads.DECODE.name, "weights": int(W.size),
+                                  "single_thread": {"s": tpack, "runs": npack,
+                                                    "mweights_per_s": W.size / tpack / 1e6}}
     wl = workloads.DECODE
     t1, n1 = timed(lambda: oracle.matmul_g128(x, codes, scales, mins), 3, 5.0)
     tT, nT = timed(lambda: oracle_outputs(oracle.matmul_g128_at, (x, codes, scales, mins), 1, wl.N, T), 3, 1.0)
@@ -701,8 +764,8 @@ def cpu_baseline(W, x):
     dec = legs["decode_gemv"]["all_cores"]
     return {"value": dec["gbs"], "unit": "GB/s", "cores": T, "kind": "oracle",
             "sample": (f"the full decode GEMV (M=1, K=4096, N=14336) in fp64 on {T} threads, median of "
-                       f"{dec['runs']} runs ({dec['s'] * 1e3:.1f} ms); single-threaded, the Q4 GEMV and "
-                       f"prefill row slices under 'legs'"),
+                       f"{dec['runs']} runs ({dec['s'] * 1e3:.1f} ms); single-threaded, the Q4 GEMV, "
+                       f"prefill row slices and the quantize/pack under 'legs'"),
             "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0)), "legs": legs}
 
 
