@@ -753,7 +753,10 @@ def cpu_baseline(W, x):
     # Q4 block-32 GEMV, 16384 x 16384 (the oracle quantizes the weights first, untimed)
     qw = workloads.Q4
     Wq, xq = workloads.inputs(qw)
+    tpq, npq = timed(lambda: oracle.quantize_q4b32(Wq), 1, 0.0)
     qc, qs = oracle.quantize_q4b32(Wq)
+    legs["quantize_pack_q4b32"] = {"workload": qw.name, "weights": int(Wq.size),
+                                   "single_thread": {"s": tpq, "runs": npq, "mweights_per_s": Wq.size / tpq / 1e6}}
     del Wq
     qbytes = qc.nbytes + qs.nbytes
     t1q, n1q = timed(lambda: oracle.matmul_q4b32(xq, qc, qs), 1, 0.0)
@@ -767,6 +770,24 @@ def cpu_baseline(W, x):
                        f"{dec['runs']} runs ({dec['s'] * 1e3:.1f} ms); single-threaded, the Q4 GEMV, "
                        f"prefill row slices and the quantize/pack under 'legs'"),
             "cpu_model": cpu_model(), "cores_available": len(os.sched_getaffinity(0)), "legs": legs}
+
+
+def gpu_over_oracle(line):
+    """The GPU kernel's rate over the oracle's, per workload timed on both (the kernel's own
+    per-launch time against the oracle on one thread and on all cores)."""
+    legs = line["cpu_baseline"]["legs"]
+    out = {}
+
+    def ratio(gpu_rate, leg, key):
+        return {"single_thread": gpu_rate / leg["single_thread"][key], "all_cores": gpu_rate / leg["all_cores"][key]}
+
+    out["decode_gemv"] = ratio(line["roofline"]["achieved"], legs["decode_gemv"], "gbs")
+    extra = line.get("extra", {})
+    if "q4b32_m1" in extra:
+        out["q4b32_gemv"] = ratio(extra["q4b32_m1"]["effective_weight_gbs"], legs["q4b32_gemv"], "gbs")
+    if "prefill_m1024" in extra:
+        out["prefill_gemm"] = ratio(extra["prefill_m1024"]["tflops"] * 1e3, legs["prefill_gemm_row_slice"], "gflops")
+    return out
 
 
 def cpu_baseline_only():
@@ -940,6 +961,7 @@ def main():
     if not args.no_cpu_baseline and args.only is None:
         log("cpu baseline (oracle)")
         line["cpu_baseline"] = cpu_baseline(W, x)
+        line["cpu_baseline"]["gpu_over_oracle"] = gpu_over_oracle(line)
     print(json.dumps(line), flush=True)
 
 
