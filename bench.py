@@ -652,6 +652,11 @@ def bench_w4a8_sweep(W=None):
 
 
 def bench_sweep(W=None):
+    """The G128 matmul over M = 1 .. 256 (cold rotated weight copies), and beside each M
+    hipBLASLt's product of the same shape with bf16 weights (the GPU's own dequantized weights,
+    also cold: enough rotated bf16 copies to exceed twice the Infinity Cache) -- the pages'
+    speedup-over-BF16 profile ([P1] Step 3)."""
+    import torch
     import gemm_w4a16_amd as w
     import workloads
     wl1 = workloads.DECODE
@@ -661,6 +666,7 @@ def bench_sweep(W=None):
     R = copies_for(c + s + m)
     out = []
     base = None
+    wts = None
     for M in workloads.SWEEP_MS:
         wl = workloads.sweep(M)
         x = workloads.activations(M, wl.K, "bf16", wl.seed_x, rows_drawn=max(workloads.SWEEP_MS))
@@ -669,11 +675,25 @@ def bench_sweep(W=None):
             base = st.copies
         else:
             st.copies = base  # reuse the rotated weight copies
+        if wts is None:
+            Wb = torch.empty((wl.N, wl.K), dtype=torch.int16, device="cuda")
+            w.w4a16_dequant(w.W4A16_FMT_G128_ASYM_BF16, *base[0], wl.N, wl.K, w.W4A16_BF16, Wb)
+            Wt = Wb.view(torch.bfloat16).t().contiguous()  # [K][N]
+            del Wb
+            wts = [Wt] + [Wt.clone() for _ in range(copies_for(Wt.numel() * 2) - 1)]
         kt = time_rounds(st.step, R)
         t = kt["us"] * 1e-6
+        xb = st.x.view(torch.bfloat16)
+        yb = torch.empty((M, wl.N), dtype=torch.bfloat16, device="cuda")
+        bt = time_rounds_eager(lambda i: torch.matmul(xb, wts[i % len(wts)], out=yb))
         out.append({"M": M, "path": "gemv" if M <= w.w4a16_matmul_gemv_cutoff() else "gemm",
                     "us": kt["us"], "us_rounds": kt["rounds_us"], "effective_weight_gbs": st.weight_bytes / t / 1e9,
-                    "tflops": 2.0 * M * wl.N * wl.K / t / 1e12})
+                    "tflops": 2.0 * M * wl.N * wl.K / t / 1e12,
+                    "hipblaslt_bf16_us": bt["us"], "hipblaslt_bf16_us_rounds": bt["rounds_us"],
+                    "speedup_vs_bf16": bt["us"] / kt["us"]})
+        del yb
+    del wts
+    torch.cuda.empty_cache()
     return out
 
 
