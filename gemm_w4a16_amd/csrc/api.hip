@@ -390,16 +390,20 @@ w4a16_status_t w4a16_gemv_prepared(w4a16_format_t fmt, w4a16_dtype_t act, const 
     const uint32_t* words = reinterpret_cast<const uint32_t*>(base + L.words);
     const float* sp = reinterpret_cast<const float*>(base + L.scales);
     const float* mp = reinterpret_cast<const float*>(base + L.mins);
-    // one pass over the copy per 32 rows (the 17..32-row kernel), the last 1..16 rows on the
-    // small-M kernel; after the first pass the copy is read from the Infinity Cache when it fits
+    // one pass over the copy per 64 rows (the 64-row kernel, where the shape fits) or 32 rows (the
+    // 17..32-row kernel), the last 1..16 rows on the small-M kernel; after the first pass the copy
+    // is read from the Infinity Cache when it fits
+    const bool rows64 = w4a16::mid64_fits(N, K);
     for (int64_t m0 = 0; m0 < M;) {
         const int64_t rem = M - m0;
-        const int64_t mc = rem <= w4a16::kGemvMaxRows ? rem : (rem < 32 ? rem : 32);
+        const int64_t mc = rem <= 32 ? rem : (rows64 ? std::min<int64_t>(rem, 64) : 32);
         const uint16_t* xa = static_cast<const uint16_t*>(x) + m0 * K;
         uint16_t* ya = static_cast<uint16_t*>(y) + m0 * N;
-        const w4a16_status_t st =
-            from_hip(mc <= w4a16::kGemvMaxRows ? w4a16::launch_skinny_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream)
-                                               : w4a16::launch_rows32_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream));
+        hipError_t e;
+        if (mc <= w4a16::kGemvMaxRows) e = w4a16::launch_skinny_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream);
+        else if (mc <= 32) e = w4a16::launch_rows32_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream);
+        else e = w4a16::launch_rows64_prepared_zp(xa, mc, f16, words, sp, mp, N, K, ya, stream);
+        const w4a16_status_t st = from_hip(e);
         if (st != W4A16_OK) return st;
         m0 += mc;
     }

@@ -36,6 +36,7 @@
 
 #include "device_common.h"
 #include "launch.h"
+#include "lds_dma.h"
 
 namespace w4a16 {
 
@@ -428,6 +429,158 @@ __global__ __launch_bounds__(128 * KP) void mid_g128_kernel(const uint16_t* __re
     }
 }
 
+
+// ---- 33..64 rows, factored, every operand by direct-to-LDS copies ----------------------------
+
+constexpr int kM64X = 64 * 512;               // x: 64 rows x 256 k (a group pair), 16-byte chunks XOR-swizzled
+constexpr int kM64W = 32 * 256;               // packed words: 32 rows x 64 columns
+constexpr int kM64P = 1024;                   // per group: scales (256 B slot), then minimums (256 B slot)
+constexpr int kM64S = kM64X + kM64W + kM64P;  // one stage: a group pair
+constexpr int kM64Stages = 3;                 // the copies run two stages ahead
+
+// kF16: fp16 activations and output on the fp16 matrix cores, codes as 1024 + q, else bf16 and
+// 128 + q.  kP32: fp32 scales and minimums [K/128][N] (the prepared zero-point copy), else bf16.
+// N % 4 == 0 and an even group count (K % 256 == 0); 1 <= M <= 64.
+template <bool kF16, bool kP32>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void mid64_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes, const void* __restrict__ scales_v,
+                  const void* __restrict__ mins_v, uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask,
+                  uint32_t magic) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[kM64Stages * kM64S];
+    constexpr float kOffset = kF16 ? 1024.0f : 128.0f;  // the magic number's value at q = 0
+    constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
+    const int lane = lane_id(), wave = wave_id();
+    const int half = wave >> 2, w4 = wave & 3;  // half h runs the groups g = h (mod 2)
+    const int wm = w4 & 1, wn = w4 >> 1;        // rows 32 wm .. +31, columns 32 wn .. +31 of the block
+    const int l32 = lane & 31, lh = lane >> 5;
+    const int n0 = blockIdx.x * kMidCols;
+    const int G = K >> 7;
+    const int P = G >> 1;  // group pairs
+    const uint32_t sm = lds_addr(smem);
+
+    // Copy offsets (constant over the pairs).  x: copy i of wave w fills rows 8 w + 2 i, +1 of the
+    // pair's 256 k; lane l lands on 16-byte position l % 32 of row r = 8 w + 2 i + l / 32 and reads
+    // the chunk (l % 32) ^ (r % 16) of that row's 256 k (rows past M repeat row M - 1; they feed
+    // only outputs that are never stored).
+    uint32_t xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 8 * wave + 2 * i + (lane >> 5);
+        xoff[i] = (uint32_t)(((size_t)min(r, M - 1) * K + 8 * ((lane & 31) ^ (r & 15))) * 2);
+    }
+    // words: packed rows 4 w4 .. +3 of group 2 p + w / 4; lane l the 4 columns at 4 (l % 16) of
+    // row 4 w4 + l / 16 (the last block's columns past N repeat the last 4)
+    const uint32_t woff = (uint32_t)(((size_t)(lane >> 4) * N + min(n0 + 4 * (lane & 15), N - 4)) * 4);
+    // scales (even waves) or minimums (odd waves) of group 2 p + w / 4: bf16, lane l the dword of
+    // columns n0 + 2 l, +1 (lanes past 31 repeat dword 31), or fp32, lane l column n0 + l
+    const uint32_t poff = kP32 ? (uint32_t)(min(n0 + lane, N - 1) * 4) : (uint32_t)(min(n0 / 2 + min(lane, 31), N / 2 - 1) * 4);
+    const char* const parr = static_cast<const char*>((wave & 1) ? mins_v : scales_v);
+    constexpr size_t kPBytes = kP32 ? 4 : 2;
+
+    // this wave's six copies of pair p into stage st (a pair past the last repeats it)
+    auto issue = [&](int p, int st) {
+        const int gx = min(2 * p, G - 2);  // first group of the pair
+        const int gg = gx + half;
+        const uint32_t base = sm + (uint32_t)(st * kM64S);
+        const char* xs = reinterpret_cast<const char*>(x + (size_t)gx * 128);
+        dma16<0>(xoff[0], xs, base + 4096u * wave);
+        dma16<1024>(xoff[1], xs, base + 4096u * wave);
+        dma16<2048>(xoff[2], xs, base + 4096u * wave);
+        dma16<3072>(xoff[3], xs, base + 4096u * wave);
+        dma16<kM64X>(woff, codes + (size_t)(16 * gg + 4 * w4) * N, base + 1024u * wave);
+        dma4<kM64X + kM64W>(poff, parr + (size_t)gg * N * kPBytes, base + 512u * half + 256u * (wave & 1));
+    };
+
+    uint32_t magic_v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(magic));
+    const u32x4_t ones_u = {kOne, kOne, kOne, kOne};
+    const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
+    auto mfma = [](bf16x8_t a, bf16x8_t b, f32x16_t c) {
+        if constexpr (kF16) {
+            typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c,
+                                                          0, 0, 0);
+        } else {
+            return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+        }
+    };
+    const int col = 32 * wn + l32;   // this lane's column of the block
+    const int arow = 32 * wm + l32;  // this lane's A row
+    float yacc[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) yacc[e] = 0.0f;
+
+    issue(0, 0);
+    issue(1, 1);
+    int cur = 0;  // the stage of pair p
+    for (int p = 0; p < P; ++p) {
+        wait_vm<6>();     // this wave's copies of pair p have landed (those of p + 1 may not have)
+        __syncthreads();  // ... and every wave's; all are done with pair p - 1, whose stage is refilled next
+        issue(p + 2, cur == 0 ? kM64Stages - 1 : cur - 1);
+        const uint8_t* sx = smem + cur * kM64S;
+        const uint8_t* sw = sx + kM64X + half * 4096;
+        const uint8_t* sp = sx + kM64X + kM64W + half * 512;
+        cur = cur + 1 == kM64Stages ? 0 : cur + 1;
+        // the group's 8 A fragments and 8 words, read from LDS at once
+        uint4 av[8];
+        uint32_t wv[8];
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int ch = 2 * ks + lh;  // 16-byte chunk of the group's 128 k (the word row of the k-step)
+            av[ks] = *reinterpret_cast<const uint4*>(sx + arow * 512 + (((16 * half + ch) ^ (arow & 15)) * 16));
+            wv[ks] = *reinterpret_cast<const uint32_t*>(sw + ch * 256 + col * 4);
+        }
+        float s, mn;
+        if constexpr (kP32) {
+            s = *reinterpret_cast<const float*>(sp + 4 * col);
+            mn = *reinterpret_cast<const float*>(sp + 256 + 4 * col);
+        } else {
+            s = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sp + 2 * col));
+            mn = bf16_bits_to_f32(*reinterpret_cast<const uint16_t*>(sp + 256 + 2 * col));
+        }
+        f32x16_t acc, accs;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] = accs[e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8_t a = r32_pair_up(av[ks]);
+            acc = mfma(a, r32_unpack(wv[ks], mask, magic_v), acc);
+            accs = mfma(a, ones, accs);
+        }
+        const float c = __builtin_fmaf(-kOffset, s, mn);  // min - 128 s (or - 1024 s)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            yacc[e] = __builtin_fmaf(s, acc[e], yacc[e]);
+            yacc[e] = __builtin_fmaf(c, accs[e], yacc[e]);
+        }
+    }
+    wait_vm<0>();     // no copy may still be writing this block's LDS
+    __syncthreads();  // every wave is done reading the stages, which now take half 1's sums
+    float* part = reinterpret_cast<float*>(smem);
+    if (half == 1) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) part[(w4 * 16 + e) * 64 + lane] = yacc[e];
+    }
+    __syncthreads();
+    if (half == 0) {
+        // element e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4 of the wave's 32, column l % 32
+        const int n = n0 + col;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float v = yacc[e] + part[(w4 * 16 + e) * 64 + lane];  // half 0, then half 1
+            const int m = 32 * wm + 8 * (e / 4) + 4 * lh + (e % 4);
+            if (m < M && n < N) y[(size_t)m * N + n] = kF16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+        }
+    }
+}
+
+template <bool kF16, bool kP32>
+void launch_mid64(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins, int64_t N,
+                  int64_t K, uint16_t* y, hipStream_t stream) {
+    hipLaunchKernelGGL((mid64_kernel<kF16, kP32>), dim3((unsigned)((N + kMidCols - 1) / kMidCols)), dim3(512), 0, stream,
+                       x, codes, scales, mins, y, (int)M, (int)N, (int)K, 0x000F000Fu, kF16 ? 0x64006400u : 0x43004300u);
+}
+
 }  // namespace
 
 hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
@@ -450,6 +603,14 @@ hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
     return hipGetLastError();
 }
 
+hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
+                                     const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
+                                     hipStream_t stream) {
+    if (act_f16) launch_mid64<true, true>(x, M, codes, scales, mins, N, K, y, stream);
+    else launch_mid64<false, true>(x, M, codes, scales, mins, N, K, y, stream);
+    return hipGetLastError();
+}
+
 hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     const unsigned gx = (unsigned)((N + kMidCols - 1) / kMidCols);
@@ -460,6 +621,8 @@ hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, 
         else
             hipLaunchKernelGGL((mid_rows32_kernel<false>), dim3(gx), dim3(64 * kR32Waves), 0, stream, x, codes, scales,
                                mins, y, (int)M, (int)N, (int)K, 0x000F000Fu, 0x43004300u);
+    } else if (mid64_fits(N, K)) {
+        launch_mid64<false, false>(x, M, codes, scales, mins, N, K, y, stream);
     } else {
         const unsigned gy = (unsigned)((M + 63) / 64);
         hipLaunchKernelGGL((mid_g128_kernel<64, 4>), dim3(gx, gy), dim3(128 * 4), 0, stream, x, codes, scales, mins, y,

@@ -165,7 +165,10 @@ def test_gemv_g128_parity(M, N, K):
                                    # 17..32 rows: several groups per wave (K = 4224: 33 groups, one
                                    # wave with 5), waves with no group (K = 128, 256), ragged N
                                    (24, 1000, 4224), (20, 130, 256), (31, 97, 1152), (32, 64, 128),
-                                   (32, 260, 2048), (18, 4100, 384)])
+                                   (32, 260, 2048), (18, 4100, 384),
+                                   # 33..64 rows on the 64-row kernel (N % 4 == 0, K % 256 == 0):
+                                   # one group pair, ragged last column block, many pairs
+                                   (40, 68, 256), (48, 1000, 1024), (63, 4100, 512), (33, 64, 4096)])
 def test_gemm_g128_parity(M, N, K):
     say(f"gemm_g128 M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=13)
@@ -376,9 +379,9 @@ def test_gemv_one_hot_within_one_bf16_ulp():
         assert np.all(np.abs(y - What[:, k]) <= ulp)
 
 
-@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("path", ["gemv", "gemm", "gemm48"])
 def test_power_of_two_scaling_is_exact_and_runs_repeat_bitwise(path):
-    M, N, K = (3, 300, 1024) if path == "gemv" else (70, 300, 1024)
+    M, N, K = {"gemv": (3, 300, 1024), "gemm": (70, 300, 1024), "gemm48": (48, 300, 1024)}[path]
     fn = w.w4a16_gemv if path == "gemv" else w.w4a16_gemm
     W = workloads.weights(N, K, seed=19)
     x = workloads.activations(M, K, "bf16", seed=20)
@@ -652,7 +655,10 @@ def test_prepared_copy_decodes_to_the_oracle_weights(N, K):
 @pytest.mark.parametrize("act", [F16, BF16])
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (1, 65, 384), (2, 130, 4096), (3, 257, 2176), (1, 31, 17408),
                                    (4, 1000, 640), (5, 1000, 1152), (16, 100, 1024), (16, 13001, 256),
-                                   (17, 300, 1024), (40, 1000, 640), (32, 129, 384), (49, 62, 256)])
+                                   (17, 300, 1024), (40, 1000, 640), (32, 129, 384), (49, 62, 256),
+                                   # one 64-row pass; 64 + 20 rows (the 32-row kernel); 64 + 64 + 8
+                                   # rows (the small-M kernel last)
+                                   (64, 260, 1024), (40, 1000, 512), (84, 68, 256), (136, 260, 512)])
 def test_gemv_prepared_zp_parity(act, M, N, K):
     say(f"gemv_prepared act={act} M={M} N={N} K={K}")
     W = edge_weights(N, K, 128, np.float32(4.0), seed=M + N + K)
