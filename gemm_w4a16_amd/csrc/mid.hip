@@ -2,7 +2,7 @@
 //
 // The large-M kernel amortizes one dequant of a weight over 256 rows and needs 256 output
 // tiles of 256 x 224 to fill the chip; at a few dozen rows it has neither, and the skinny
-// kernel's trick (all of K's activations resident in LDS) stops fitting past 16 rows.  Both
+// kernel's trick (all of K's activations resident in LDS) stops fitting past 16 rows.  The
 // kernels here stream the weights once, like a GEMV, with one block per 64 columns.
 //
 // 17..32 rows (mid_rows32_kernel): the factored form of vidyal.ai "Low-Precision Kernels" ("How
@@ -20,7 +20,20 @@
 // Most of its time is the loads: each block reads all 256 KB of a 32-row x from L2 besides its
 // 128 KB of weights, and a CU's loads complete at ~30 GB/s.
 //
-// 33..64 rows (mid_g128_kernel): dequantizes as vidyal.ai Step 2 builds its B tile (w_hat =
+// 33..64 rows, N % 4 == 0 and K % 256 == 0 (mid64_kernel): the same factored form on
+// v_mfma_f32_32x32x16, with every operand brought in by direct-to-LDS copies:
+//  * 8 waves in two halves; half h runs the groups g = h (mod 2), and within a half wave w owns
+//    output rows 32 (w % 2) .. +31 and columns 32 (w / 2) .. +31 of the block's 64, over all of K,
+//    so a lane's word is its own B fragment and no word is unpacked twice by a wave;
+//  * a stage holds a group pair: x (64 rows x 256 k, rows XOR-swizzled in 16-byte chunks so the
+//    fragment reads are conflict-free, each copy 2 rows x 512 B), the 32 packed rows and the two
+//    groups' parameters; three stages, the copies two pairs ahead, one barrier per pair;
+//  * each wave reads its group's 8 A fragments and 8 words at once, then 8 k-steps of two MFMAs
+//    (the second against ones gives sum(x)) and the group epilogue s * acc + (min - 128 s) * sum(x);
+//  * the halves' sums are added through LDS in half order (bitwise reproducible).
+// The same kernel reads the zero-point format's prepared copy (fp16 operands, fp32 parameters).
+//
+// 33..64 rows otherwise (mid_g128_kernel): dequantizes as vidyal.ai Step 2 builds its B tile (w_hat =
 // bf16_rne(fmaf(q, s, min)), the reference value) straight into MFMA B fragments:
 //  * block = 64 columns x MR rows x all of K; 2*KP waves: wave (h, p) owns the 32 columns of
 //    half h and the groups g = p (mod KP).  With N = 14336 that is 224 blocks per row slice;

@@ -176,9 +176,10 @@ size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int6
  * 16 rows against one pass over the weights, dequantized to fp16 in registers as for w4a16_gemv's
  * rows (anrans.github.io "Quantization and GEMV", "The quantization formulas": the zero-point
  * format's (q - z) s); no workspace.  G128 as follows, on bf16 MFMA.
- * From 33 rows on, packed B tiles are dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai
- * Step 2 builds its B tile) and fed to the matrix cores; up to 32 rows the factored per-group form
- * of w4a16_gemv (s * sum(x*(128+q)) + (min - 128 s) * sum(x), fp32) is used instead.  When a K
+ * From 65 rows on (and at 33..64 rows when N % 4 != 0 or K % 256 != 0), packed B tiles are
+ * dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai Step 2 builds its B tile) and fed to the
+ * matrix cores; otherwise, up to 64 rows, the factored per-group form of w4a16_gemv
+ * (s * sum(x*(128+q)) + (min - 128 s) * sum(x), fp32) is used instead.  When a K
  * split is used, partial sums go to `workspace` and are added in a fixed order; every path is
  * bitwise reproducible run to run.  workspace_bytes must be >= w4a16_gemm_workspace_bytes(...);
  * workspace may be NULL if that is 0. */
@@ -230,8 +231,9 @@ w4a16_status_t w4a16_prepare(w4a16_format_t fmt, const void* codes, const void* 
                              hipStream_t stream);
 
 /* y [M][N] = x [M][K] . W_hat^T from the prepared copy, any M >= 1, for bf16 or fp16 activations;
- * y has the activations' type.  The kernels are the G128 ones for up to 16 and for 17..32 rows (one
- * pass over the copy per 32 rows, the last 1..16 rows in a pass of their own): the inner sums run on
+ * y has the activations' type.  The kernels are the G128 ones for up to 16, 17..32 and 33..64 rows
+ * (one pass over the copy per 64 rows where N % 4 == 0 and K % 256 == 0, else per 32 rows; the last
+ * 1..16 rows in a pass of their own): the inner sums run on
  * the matrix cores against 128 + q (bf16) or 1024 + q (fp16), and each group adds
  * s * sum(x (offset + q)) + (m - offset s) * sum(x) in fp32.
  * Up to the order of fp32 additions this is the product on the canonical zero-point arrays; it is
