@@ -393,7 +393,7 @@ w4a16_status_t w4a16_gemv_prepared(w4a16_format_t fmt, w4a16_dtype_t act, const 
     // one pass over the copy per 64 rows (the 64-row kernel, where the shape fits) or 32 rows (the
     // 17..32-row kernel), the last 1..16 rows on the small-M kernel; after the first pass the copy
     // is read from the Infinity Cache when it fits
-    const bool rows64 = w4a16::mid64_fits(N, K);
+    const bool rows64 = w4a16::midr_fits(64, N, K);
     for (int64_t m0 = 0; m0 < M;) {
         const int64_t rem = M - m0;
         const int64_t mc = rem <= 32 ? rem : (rows64 ? std::min<int64_t>(rem, 64) : 32);

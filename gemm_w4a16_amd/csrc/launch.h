@@ -55,15 +55,16 @@ hipError_t launch_prepare_zp(const uint32_t* codes, const uint16_t* scales, cons
 hipError_t launch_skinny_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
                                      const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
                                      hipStream_t stream);
-// ... and the 17..32-row kernel over it, and the 64-row one (mid64_fits(N, K), M <= 64).
+// ... and the 17..32-row kernel over it, and the 64-row one (midr_fits(64, N, K), M <= 64).
 hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
                                      const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
                                      hipStream_t stream);
 hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
                                      const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
                                      hipStream_t stream);
-// Shapes the 64-row kernel takes (4-column copies, groups in pairs); others use the general kernels.
-inline bool mid64_fits(int64_t N, int64_t K) { return N % 4 == 0 && (K / 128) % 2 == 0; }
+// Shapes the R-row kernels take (R = 64: groups in pairs, R = 32: in fours; 4-column copies);
+// others use the general kernels.
+inline bool midr_fits(int R, int64_t N, int64_t K) { return N % 4 == 0 && (K / 128) % (R == 64 ? 2 : 4) == 0; }
 
 // Row-major formats on fp16 MFMA for any number of fp16 activation rows (16 per weight pass).
 hipError_t launch_rowmma_q4b32(const uint16_t* x, int64_t M, const uint8_t* codes, const uint16_t* scales, int64_t N,

@@ -20,20 +20,21 @@
 // Most of its time is the loads: each block reads all 256 KB of a 32-row x from L2 besides its
 // 128 KB of weights, and a CU's loads complete at ~30 GB/s.
 //
-// 33..64 rows, N % 4 == 0 and K % 256 == 0 (mid64_kernel): the same factored form on
-// v_mfma_f32_32x32x16, with every operand brought in by direct-to-LDS copies:
-//  * 8 waves in two halves; half h runs the groups g = h (mod 2), and within a half wave w owns
-//    output rows 32 (w % 2) .. +31 and columns 32 (w / 2) .. +31 of the block's 64, over all of K,
-//    so a lane's word is its own B fragment and no word is unpacked twice by a wave;
-//  * a stage holds a group pair: x (64 rows x 256 k, rows XOR-swizzled in 16-byte chunks so the
-//    fragment reads are conflict-free, each copy 2 rows x 512 B), the 32 packed rows and the two
-//    groups' parameters; three stages, the copies two pairs ahead, one barrier per pair;
+// 17..32 and 33..64 rows where N % 4 == 0 and K is a multiple of 512 or 256 (midr_kernel<R> with
+// R = 32 or 64 rows per block): the same factored form on v_mfma_f32_32x32x16, with every operand
+// brought in by direct-to-LDS copies:
+//  * 8 waves in sets (R = 64: two sets of 4, R = 32: four sets of 2); set s runs the groups
+//    g = s (mod sets), and within a set a wave owns a 32 x 32 output tile of the block's R x 64,
+//    over all of K, so a lane's word is its own B fragment and no wave unpacks a word twice;
+//  * a stage holds one group per set: x (R rows x 128 k per group, rows XOR-swizzled in 16-byte
+//    chunks so the fragment reads are conflict-free, each copy 1 KB of x), the groups' packed rows
+//    and parameters; three stages, the copies two stages ahead, one barrier per stage;
 //  * each wave reads its group's 8 A fragments and 8 words at once, then 8 k-steps of two MFMAs
 //    (the second against ones gives sum(x)) and the group epilogue s * acc + (min - 128 s) * sum(x);
-//  * the halves' sums are added through LDS in half order (bitwise reproducible).
+//  * the sets' sums are added through LDS in set order (bitwise reproducible).
 // The same kernel reads the zero-point format's prepared copy (fp16 operands, fp32 parameters).
 //
-// 33..64 rows otherwise (mid_g128_kernel): dequantizes as vidyal.ai Step 2 builds its B tile (w_hat =
+// 17..32 rows otherwise: mid_rows32_kernel above.  33..64 rows otherwise (mid_g128_kernel): dequantizes as vidyal.ai Step 2 builds its B tile (w_hat =
 // bf16_rne(fmaf(q, s, min)), the reference value) straight into MFMA B fragments:
 //  * block = 64 columns x MR rows x all of K; 2*KP waves: wave (h, p) owns the 32 columns of
 //    half h and the groups g = p (mod KP).  With N = 14336 that is 224 blocks per row slice;
@@ -56,6 +57,15 @@ namespace w4a16 {
 namespace {
 
 constexpr int kMidCols = 64;
+
+// f(std::integral_constant<int, i>) for i = I .. N-1, so that i can select template arguments.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 // ---- 17..32 rows ------------------------------------------------------------------------------
 
@@ -443,65 +453,91 @@ __global__ __launch_bounds__(128 * KP) void mid_g128_kernel(const uint16_t* __re
 }
 
 
-// ---- 33..64 rows, factored, every operand by direct-to-LDS copies ----------------------------
+// ---- 17..64 rows, factored, every operand by direct-to-LDS copies ----------------------------
 
-constexpr int kM64X = 64 * 512;               // x: 64 rows x 256 k (a group pair), 16-byte chunks XOR-swizzled
-constexpr int kM64W = 32 * 256;               // packed words: 32 rows x 64 columns
-constexpr int kM64P = 1024;                   // per group: scales (256 B slot), then minimums (256 B slot)
-constexpr int kM64S = kM64X + kM64W + kM64P;  // one stage: a group pair
-constexpr int kM64Stages = 3;                 // the copies run two stages ahead
+// R rows per block (64 or 32).  The 8 waves form kGS sets of 8 / kGS waves (R = 64: 2 sets of 4;
+// R = 32: 4 sets of 2); set s runs the groups g = s (mod kGS), and within a set wave j owns output
+// rows 32 (j % (R / 32)) .. +31 and columns 32 (j / (R / 32)) .. +31 of the block's 64, over all of
+// K.  A stage holds kGS consecutive groups: x (R rows x kGS * 128 k, each row's 16-byte chunks
+// XOR-swizzled by row so the fragment reads are conflict-free; each copy is 1 KB of x: 2 rows x
+// 512 B, or 1 KB of one row), their 16 kGS packed rows and parameters; three stages, the copies two
+// stages ahead, one barrier per stage.
+template <int R>
+struct MidR {
+    static constexpr int kGS = R == 64 ? 2 : 4;        // groups per stage
+    static constexpr int kWPG = 8 / kGS;               // waves per group
+    static constexpr int kRB = kGS * 256;              // bytes of one x row in a stage
+    static constexpr int kX = R * kRB;                 // 32 KB
+    static constexpr int kW = kGS * 16 * 256;          // packed words
+    static constexpr int kP = kGS * 512;               // per group: scales (256 B slot), minimums (256 B slot)
+    static constexpr int kS = kX + kW + kP;            // one stage
+    static constexpr int kRPI = 1024 / kRB;            // x rows per copy instruction
+    static constexpr int kWI = kGS / 2;                // word copies per wave and stage
+    static constexpr int kCopies = 4 + kWI + 1;        // copies per wave and stage
+    static constexpr int kStages = 3;
+    static_assert(kStages * kS <= 160 * 1024, "LDS");
+};
 
 // kF16: fp16 activations and output on the fp16 matrix cores, codes as 1024 + q, else bf16 and
 // 128 + q.  kP32: fp32 scales and minimums [K/128][N] (the prepared zero-point copy), else bf16.
-// N % 4 == 0 and an even group count (K % 256 == 0); 1 <= M <= 64.
-template <bool kF16, bool kP32>
+// N % 4 == 0, K / 128 a multiple of kGS, 1 <= M <= R.
+template <int R, bool kF16, bool kP32>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void mid64_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes, const void* __restrict__ scales_v,
-                  const void* __restrict__ mins_v, uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask,
-                  uint32_t magic) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[kM64Stages * kM64S];
+void midr_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes, const void* __restrict__ scales_v,
+                 const void* __restrict__ mins_v, uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask,
+                 uint32_t magic) {
+    using L = MidR<R>;
+    constexpr int kGS = L::kGS, kWPG = L::kWPG, kRB = L::kRB, kRPI = L::kRPI;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[L::kStages * L::kS];
     constexpr float kOffset = kF16 ? 1024.0f : 128.0f;  // the magic number's value at q = 0
     constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;
     const int lane = lane_id(), wave = wave_id();
-    const int half = wave >> 2, w4 = wave & 3;  // half h runs the groups g = h (mod 2)
-    const int wm = w4 & 1, wn = w4 >> 1;        // rows 32 wm .. +31, columns 32 wn .. +31 of the block
+    const int set = wave / kWPG, wj = wave % kWPG;
+    const int wm = wj % (R / 32), wn = wj / (R / 32);
     const int l32 = lane & 31, lh = lane >> 5;
     const int n0 = blockIdx.x * kMidCols;
     const int G = K >> 7;
-    const int P = G >> 1;  // group pairs
+    const int P = G / kGS;  // stages' worth of groups
     const uint32_t sm = lds_addr(smem);
 
-    // Copy offsets (constant over the pairs).  x: copy i of wave w fills rows 8 w + 2 i, +1 of the
-    // pair's 256 k; lane l lands on 16-byte position l % 32 of row r = 8 w + 2 i + l / 32 and reads
-    // the chunk (l % 32) ^ (r % 16) of that row's 256 k (rows past M repeat row M - 1; they feed
-    // only outputs that are never stored).
+    // Copy offsets (constant over the stages).  x: copy i of wave w fills the kRPI rows from
+    // (4 w + i) kRPI; lane l lands on 16-byte position p = l % (64 / kRPI) of row
+    // r = (4 w + i) kRPI + l / (64 / kRPI) and reads the chunk p ^ (r % 16) of that row's kGS * 128 k
+    // (rows past M repeat row M - 1; they feed only outputs that are never stored).
     uint32_t xoff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int r = 8 * wave + 2 * i + (lane >> 5);
-        xoff[i] = (uint32_t)(((size_t)min(r, M - 1) * K + 8 * ((lane & 31) ^ (r & 15))) * 2);
+        const int r = (4 * wave + i) * kRPI + lane / (64 / kRPI);
+        const int p = lane % (64 / kRPI);
+        xoff[i] = (uint32_t)(((size_t)min(r, M - 1) * K + 8 * (p ^ (r & 15))) * 2);
     }
-    // words: packed rows 4 w4 .. +3 of group 2 p + w / 4; lane l the 4 columns at 4 (l % 16) of
-    // row 4 w4 + l / 16 (the last block's columns past N repeat the last 4)
+    // words: wave w copies the stage's packed rows 2 kGS w .. +2 kGS - 1, four per copy; lane l the
+    // 4 columns at 4 (l % 16) of the copy's row l / 16 (the last block's columns past N repeat the
+    // last 4)
     const uint32_t woff = (uint32_t)(((size_t)(lane >> 4) * N + min(n0 + 4 * (lane & 15), N - 4)) * 4);
-    // scales (even waves) or minimums (odd waves) of group 2 p + w / 4: bf16, lane l the dword of
-    // columns n0 + 2 l, +1 (lanes past 31 repeat dword 31), or fp32, lane l column n0 + l
+    // parameters: wave w copies the scales (w even) or minimums (w odd) of the stage's group
+    // (w / 2) % kGS: bf16, lane l the dword of columns n0 + 2 l, +1 (lanes past 31 repeat dword 31),
+    // or fp32, lane l column n0 + l
     const uint32_t poff = kP32 ? (uint32_t)(min(n0 + lane, N - 1) * 4) : (uint32_t)(min(n0 / 2 + min(lane, 31), N / 2 - 1) * 4);
     const char* const parr = static_cast<const char*>((wave & 1) ? mins_v : scales_v);
     constexpr size_t kPBytes = kP32 ? 4 : 2;
+    const int pgi = (wave >> 1) % kGS;
 
-    // this wave's six copies of pair p into stage st (a pair past the last repeats it)
+    // this wave's copies of stage p into LDS stage st (a stage past the last repeats it)
     auto issue = [&](int p, int st) {
-        const int gx = min(2 * p, G - 2);  // first group of the pair
-        const int gg = gx + half;
-        const uint32_t base = sm + (uint32_t)(st * kM64S);
-        const char* xs = reinterpret_cast<const char*>(x + (size_t)gx * 128);
+        const int g0 = min(p, P - 1) * kGS;  // first group of the stage
+        const uint32_t base = sm + (uint32_t)(st * L::kS);
+        const char* xs = reinterpret_cast<const char*>(x + (size_t)g0 * 128);
         dma16<0>(xoff[0], xs, base + 4096u * wave);
         dma16<1024>(xoff[1], xs, base + 4096u * wave);
         dma16<2048>(xoff[2], xs, base + 4096u * wave);
         dma16<3072>(xoff[3], xs, base + 4096u * wave);
-        dma16<kM64X>(woff, codes + (size_t)(16 * gg + 4 * w4) * N, base + 1024u * wave);
-        dma4<kM64X + kM64W>(poff, parr + (size_t)gg * N * kPBytes, base + 512u * half + 256u * (wave & 1));
+        static_for<0, L::kWI>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            dma16<L::kX + 1024 * j>(woff, codes + (size_t)(16 * g0 + 2 * kGS * wave + 4 * j) * N,
+                                    base + (uint32_t)(2 * kGS * 256) * wave);
+        });
+        dma4<L::kX + L::kW>(poff, parr + (size_t)(g0 + pgi) * N * kPBytes, base + 512u * pgi + 256u * (wave & 1));
     };
 
     uint32_t magic_v;
@@ -525,22 +561,22 @@ void mid64_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ c
 
     issue(0, 0);
     issue(1, 1);
-    int cur = 0;  // the stage of pair p
+    int cur = 0;  // the LDS stage of stage p
     for (int p = 0; p < P; ++p) {
-        wait_vm<6>();     // this wave's copies of pair p have landed (those of p + 1 may not have)
-        __syncthreads();  // ... and every wave's; all are done with pair p - 1, whose stage is refilled next
-        issue(p + 2, cur == 0 ? kM64Stages - 1 : cur - 1);
-        const uint8_t* sx = smem + cur * kM64S;
-        const uint8_t* sw = sx + kM64X + half * 4096;
-        const uint8_t* sp = sx + kM64X + kM64W + half * 512;
-        cur = cur + 1 == kM64Stages ? 0 : cur + 1;
+        wait_vm<L::kCopies>();  // this wave's copies of stage p have landed (those of p + 1 may not have)
+        __syncthreads();        // ... and every wave's; all are done with stage p - 1, which is refilled next
+        issue(p + 2, cur == 0 ? L::kStages - 1 : cur - 1);
+        const uint8_t* sx = smem + cur * L::kS;
+        const uint8_t* sw = sx + L::kX + set * 4096;
+        const uint8_t* sp = sx + L::kX + L::kW + set * 512;
+        cur = cur + 1 == L::kStages ? 0 : cur + 1;
         // the group's 8 A fragments and 8 words, read from LDS at once
         uint4 av[8];
         uint32_t wv[8];
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const int ch = 2 * ks + lh;  // 16-byte chunk of the group's 128 k (the word row of the k-step)
-            av[ks] = *reinterpret_cast<const uint4*>(sx + arow * 512 + (((16 * half + ch) ^ (arow & 15)) * 16));
+            av[ks] = *reinterpret_cast<const uint4*>(sx + arow * kRB + (((16 * set + ch) ^ (arow & 15)) * 16));
             wv[ks] = *reinterpret_cast<const uint32_t*>(sw + ch * 256 + col * 4);
         }
         float s, mn;
@@ -568,30 +604,33 @@ void mid64_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ c
         }
     }
     wait_vm<0>();     // no copy may still be writing this block's LDS
-    __syncthreads();  // every wave is done reading the stages, which now take half 1's sums
+    __syncthreads();  // every wave is done reading the stages, which now take the other sets' sums
     float* part = reinterpret_cast<float*>(smem);
-    if (half == 1) {
+    if (set > 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) part[(w4 * 16 + e) * 64 + lane] = yacc[e];
+        for (int e = 0; e < 16; ++e) part[(wave * 16 + e) * 64 + lane] = yacc[e];
     }
     __syncthreads();
-    if (half == 0) {
+    if (set == 0) {
         // element e of lane l: row 8 (e / 4) + 4 (l / 32) + e % 4 of the wave's 32, column l % 32
         const int n = n0 + col;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-            const float v = yacc[e] + part[(w4 * 16 + e) * 64 + lane];  // half 0, then half 1
+            float v = yacc[e];
+#pragma unroll
+            for (int t = 1; t < kGS; ++t) v += part[((t * kWPG + wj) * 16 + e) * 64 + lane];  // sets in order
             const int m = 32 * wm + 8 * (e / 4) + 4 * lh + (e % 4);
             if (m < M && n < N) y[(size_t)m * N + n] = kF16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
         }
     }
 }
 
-template <bool kF16, bool kP32>
-void launch_mid64(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins, int64_t N,
-                  int64_t K, uint16_t* y, hipStream_t stream) {
-    hipLaunchKernelGGL((mid64_kernel<kF16, kP32>), dim3((unsigned)((N + kMidCols - 1) / kMidCols)), dim3(512), 0, stream,
-                       x, codes, scales, mins, y, (int)M, (int)N, (int)K, 0x000F000Fu, kF16 ? 0x64006400u : 0x43004300u);
+template <int R, bool kF16, bool kP32>
+void launch_midr(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins, int64_t N,
+                 int64_t K, uint16_t* y, hipStream_t stream) {
+    hipLaunchKernelGGL((midr_kernel<R, kF16, kP32>), dim3((unsigned)((N + kMidCols - 1) / kMidCols)), dim3(512), 0,
+                       stream, x, codes, scales, mins, y, (int)M, (int)N, (int)K, 0x000F000Fu,
+                       kF16 ? 0x64006400u : 0x43004300u);
 }
 
 }  // namespace
@@ -608,7 +647,10 @@ hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
     };
     using T = std::true_type;
     using F = std::false_type;
-    if (N % 4 == 0) {
+    if (midr_fits(32, N, K)) {
+        if (act_f16) launch_midr<32, true, true>(x, M, codes, scales, mins, N, K, y, stream);
+        else launch_midr<32, false, true>(x, M, codes, scales, mins, N, K, y, stream);
+    } else if (N % 4 == 0) {
         if (act_f16) go(T{}, T{}); else go(T{}, F{});
     } else {
         if (act_f16) go(F{}, T{}); else go(F{}, F{});
@@ -619,23 +661,25 @@ hipError_t launch_rows32_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
 hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
                                      const float* scales, const float* mins, int64_t N, int64_t K, uint16_t* y,
                                      hipStream_t stream) {
-    if (act_f16) launch_mid64<true, true>(x, M, codes, scales, mins, N, K, y, stream);
-    else launch_mid64<false, true>(x, M, codes, scales, mins, N, K, y, stream);
+    if (act_f16) launch_midr<64, true, true>(x, M, codes, scales, mins, N, K, y, stream);
+    else launch_midr<64, false, true>(x, M, codes, scales, mins, N, K, y, stream);
     return hipGetLastError();
 }
 
 hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                            const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     const unsigned gx = (unsigned)((N + kMidCols - 1) / kMidCols);
-    if (M <= 32) {
+    if (M <= 32 && midr_fits(32, N, K)) {
+        launch_midr<32, false, false>(x, M, codes, scales, mins, N, K, y, stream);
+    } else if (M <= 32) {
         if (N % 4 == 0)
             hipLaunchKernelGGL((mid_rows32_kernel<true>), dim3(gx), dim3(64 * kR32Waves), 0, stream, x, codes, scales, mins,
                                y, (int)M, (int)N, (int)K, 0x000F000Fu, 0x43004300u);
         else
             hipLaunchKernelGGL((mid_rows32_kernel<false>), dim3(gx), dim3(64 * kR32Waves), 0, stream, x, codes, scales,
                                mins, y, (int)M, (int)N, (int)K, 0x000F000Fu, 0x43004300u);
-    } else if (mid64_fits(N, K)) {
-        launch_mid64<false, false>(x, M, codes, scales, mins, N, K, y, stream);
+    } else if (midr_fits(64, N, K)) {
+        launch_midr<64, false, false>(x, M, codes, scales, mins, N, K, y, stream);
     } else {
         const unsigned gy = (unsigned)((M + 63) / 64);
         hipLaunchKernelGGL((mid_g128_kernel<64, 4>), dim3(gx, gy), dim3(128 * 4), 0, stream, x, codes, scales, mins, y,

@@ -168,7 +168,9 @@ def test_gemv_g128_parity(M, N, K):
                                    (32, 260, 2048), (18, 4100, 384),
                                    # 33..64 rows on the 64-row kernel (N % 4 == 0, K % 256 == 0):
                                    # one group pair, ragged last column block, many pairs
-                                   (40, 68, 256), (48, 1000, 1024), (63, 4100, 512), (33, 64, 4096)])
+                                   (40, 68, 256), (48, 1000, 1024), (63, 4100, 512), (33, 64, 4096),
+                                   # 17..32 rows on the 32-row one (N % 4 == 0, K % 512 == 0)
+                                   (17, 68, 512), (25, 1000, 1024), (32, 4100, 2048)])
 def test_gemm_g128_parity(M, N, K):
     say(f"gemm_g128 M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=13)
@@ -657,8 +659,9 @@ def test_prepared_copy_decodes_to_the_oracle_weights(N, K):
                                    (4, 1000, 640), (5, 1000, 1152), (16, 100, 1024), (16, 13001, 256),
                                    (17, 300, 1024), (40, 1000, 640), (32, 129, 384), (49, 62, 256),
                                    # one 64-row pass; 64 + 20 rows (the 32-row kernel); 64 + 64 + 8
-                                   # rows (the small-M kernel last)
-                                   (64, 260, 1024), (40, 1000, 512), (84, 68, 256), (136, 260, 512)])
+                                   # rows (the small-M kernel last); 17..32 rows on the R = 32 kernel
+                                   (64, 260, 1024), (40, 1000, 512), (84, 68, 256), (136, 260, 512),
+                                   (32, 260, 512), (20, 1000, 2048)])
 def test_gemv_prepared_zp_parity(act, M, N, K):
     say(f"gemv_prepared act={act} M={M} N={N} K={K}")
     W = edge_weights(N, K, 128, np.float32(4.0), seed=M + N + K)
