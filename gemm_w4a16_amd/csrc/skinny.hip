@@ -27,20 +27,14 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kGroupsPerPass = 32;  // groups of 128 k a block covers per pass (all of K = 4096)
-
-#ifndef W4A16_SKINNY_WAVES
-#define W4A16_SKINNY_WAVES 16
-#endif
+constexpr int kSkinnyWaves = 16;  // waves per block: one block per CU, four waves per SIMD
 constexpr uint32_t kNibblePairMask = 0x000F000Fu;
 constexpr uint32_t kBf16Magic = 0x43004300u;  // bf16 128.0 in both halves
 constexpr uint32_t kF16Magic = 0x64006400u;   // fp16 1024.0 in both halves
 
-// Waves per SIMD the register budget is sized for: one block per CU.  (32-column blocks are
-// used when N is small, so that there are more blocks; two of them per CU would halve the
-// register budget and spill, for a grid that rarely exceeds the CU count.)
-template <int MR, int TPL, int WAVES>
-constexpr int waves_per_eu() { return WAVES / 4; }
+// The register budget is sized for one block per CU.  (32-column blocks are used when N is
+// small, so that there are more blocks; two of them per CU would halve the register budget and
+// spill, for a grid that rarely exceeds the CU count.)
 
 // `mask` and `magic` arrive as kernel arguments (0x000F000F and 0x43004300) so that they sit in
 // registers and each pair is one v_and_or_b32 (VOP3 cannot take a literal on gfx9).
@@ -133,13 +127,15 @@ __device__ __forceinline__ void load_params32(const float* __restrict__ p, int N
 }
 
 // MR: activation rows staged (M <= MR; 1, 4, 8 or 16).  TPL: adjacent columns per lane (4 or 2),
-// i.e. 16 * TPL columns per block.  WAVES: waves per block; each takes kGroupsPerPass / WAVES
+// i.e. 16 * TPL columns per block.  GPP: groups of 128 k per wave and pass (a pass of the 16 waves
+// covers 16 * GPP groups: 2 for K > 2048, where one pass covers K = 4096; 1 up to K = 2048, where
+// a second group per wave would only repeat a clamped one)
 // groups per pass.  kVec: N % TPL == 0 (vector loads of a lane's columns).  kF16: fp16
 // activations and output on the fp16 matrix cores, codes as 1024 + q (else bf16 and 128 + q).
 // kP32: scales and minimums are fp32 [K/128][N] (the prepared zero-point copy), else bf16.
-template <int MR, int TPL, int WAVES, bool kVec, bool kF16 = false, bool kP32 = false>
-__global__ __launch_bounds__(64 * WAVES)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<MR, TPL, WAVES>(), waves_per_eu<MR, TPL, WAVES>())))
+template <int MR, int TPL, int GPP, bool kVec, bool kF16 = false, bool kP32 = false>
+__global__ __launch_bounds__(64 * kSkinnyWaves)
+__attribute__((amdgpu_waves_per_eu(kSkinnyWaves / 4, kSkinnyWaves / 4)))
 void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                         const void* __restrict__ scales_v, const void* __restrict__ mins_v,
                         uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic) {
@@ -150,8 +146,8 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     constexpr float kOffset = kF16 ? 1024.0f : 128.0f;  // the magic number's value at q = 0
     constexpr int E = MR == 1 ? 1 : 4;  // accumulator rows per lane that can hold a real row
     constexpr int COLS = 16 * TPL;
-    constexpr int kWaves = WAVES;
-    constexpr int kGpp = kGroupsPerPass / WAVES;  // groups per wave per pass
+    constexpr int kWaves = kSkinnyWaves;
+    constexpr int kGpp = GPP;  // groups per wave per pass
     // per wave: [group][row 0..MR-1 staged, row MR zeros][8-k chunk] of 16 B
     __shared__ uint4 xs[kWaves][kGpp][MR + 1][16];
     const int lane = lane_id(), wave = wave_id();
@@ -275,7 +271,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     }
     __syncthreads();
     const int rows = min(M, 16);
-    for (int idx = threadIdx.x; idx < rows * COLS; idx += 64 * WAVES) {
+    for (int idx = threadIdx.x; idx < rows * COLS; idx += 64 * kWaves) {
         const int row = idx / COLS, c = idx % COLS;
         const int n = n0 + c;
         if (n < N) {
@@ -288,19 +284,27 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     }
 }
 
+template <int MR, int TPL, int GPP, bool kF16, bool kP32>
+void launch_gpp(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
+                int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+    constexpr int COLS = 16 * TPL;
+    constexpr uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
+    const dim3 grid((unsigned)((N + COLS - 1) / COLS)), block(64 * kSkinnyWaves);
+    if (N % TPL == 0)
+        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, true, kF16, kP32>), grid, block, 0, stream, x, codes, scales,
+                           mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
+    else
+        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, false, kF16, kP32>), grid, block, 0, stream, x, codes,
+                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
+}
+
 template <int MR, int TPL, bool kF16 = false, bool kP32 = false>
 void launch_mr(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
                int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-    constexpr int COLS = 16 * TPL;
-    constexpr int WAVES = W4A16_SKINNY_WAVES;
-    constexpr uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
-    const dim3 grid((unsigned)((N + COLS - 1) / COLS)), block(64 * WAVES);
-    if (N % TPL == 0)
-        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, WAVES, true, kF16, kP32>), grid, block, 0, stream, x, codes, scales,
-                           mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
+    if (K <= 128 * kSkinnyWaves)
+        launch_gpp<MR, TPL, 1, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
     else
-        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, WAVES, false, kF16, kP32>), grid, block, 0, stream, x, codes,
-                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
+        launch_gpp<MR, TPL, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
 }
 
 }  // namespace

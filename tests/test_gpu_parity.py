@@ -346,6 +346,22 @@ def test_gemv_wide_odd_n_two_passes(M):
     say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 14336, 1024), (16, 14336, 2048), (5, 12289, 2048), (1, 12289, 1536),
+                                   (3, 14336, 2176), (9, 12289, 128)])
+def test_gemv_wide_short_k(M, N, K):
+    """Up to K = 2048 (16 groups) the small-M kernel's waves take one group each per pass; from
+    17 groups two, the second pass partial (K = 2176).  64-column blocks, vector (N = 14336) and
+    scalar (N odd) column loads."""
+    say(f"gemv wide short K M={M} N={N} K={K}")
+    W = workloads.weights(N, K, outliers=True, seed=107)
+    x = workloads.activations(M, K, "bf16", seed=108)
+    rc, rs, rm = oracle.quantize_g128(W)
+    packed = (dev(rc), dev(rs), dev(rm))
+    y = bf16_f32(run_matmul(w.w4a16_gemv, G128, x, packed, N, K, BF16))
+    err, worst = refcheck.check(y, refcheck.g128(x, rc, rs, rm), "bf16", f"wide short K M={M} K={K}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+
+
 # ---------------------------------------------------------------------------------------------
 # Special cases.
 # ---------------------------------------------------------------------------------------------
