@@ -20,6 +20,8 @@
 //    M read a zero row.
 // The waves' partial sums are added through LDS in a fixed order, so results are bitwise
 // reproducible.  All global loads are issued before the first MFMA and never under a branch.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -177,9 +179,11 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     const u32x4_t ones_u = {kOne, kOne, kOne, kOne};
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
 
-    for (int p0 = 0; p0 < G; p0 += kWaves * kGpp) {
+    // One pass over CNT groups per wave: wave w takes groups p0 + w + 16 j, j < CNT.
+    auto pass = [&](int p0, auto cnt_c) {
+        constexpr int CNT = decltype(cnt_c)::value;
         // 1) activation chunks of this wave's groups: chunk q = (j * MR + m) * 16 + c
-        constexpr int kChunks = kGpp * MR * 16;  // 16-byte chunks of x this wave stages per pass
+        constexpr int kChunks = CNT * MR * 16;  // 16-byte chunks of x this wave stages per pass
         constexpr int kNI = (kChunks + 63) / 64;
         uint4 xr[kNI];
 #pragma unroll
@@ -191,18 +195,18 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
             xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)mm * K + (size_t)g * 128 + c * 8);
         }
         // 2) group parameters and 3) packed words, in the order they are used
-        int gj[kGpp];
-        float live[kGpp];
+        int gj[CNT];
+        float live[CNT];
 #pragma unroll
-        for (int j = 0; j < kGpp; ++j) {
+        for (int j = 0; j < CNT; ++j) {
             const int g = p0 + wave + kWaves * j;
             live[j] = g < G ? 1.0f : 0.0f;  // a clamped duplicate group contributes nothing
             gj[j] = min(g, G - 1);
         }
-        uint32_t sf[kGpp][TPL / 2], mf[kGpp][TPL / 2];
-        float sf32[kGpp][TPL], mf32[kGpp][TPL];
+        uint32_t sf[CNT][TPL / 2], mf[CNT][TPL / 2];
+        float sf32[CNT][TPL], mf32[CNT][TPL];
 #pragma unroll
-        for (int j = 0; j < kGpp; ++j) {
+        for (int j = 0; j < CNT; ++j) {
             if constexpr (kP32) {
                 load_params32<TPL, kVec>(scales32 + (size_t)gj[j] * N, N, cbase, sf32[j]);
                 load_params32<TPL, kVec>(mins32 + (size_t)gj[j] * N, N, cbase, mf32[j]);
@@ -211,10 +215,10 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
                 load_params<TPL, kVec>(mins + (size_t)gj[j] * N, N, cbase, mf[j]);
             }
         }
-        uint32_t w[kGpp][4][TPL];
+        uint32_t w[CNT][4][TPL];
         const uint32_t lane_off = ((uint32_t)lg * (uint32_t)N + (uint32_t)cbase) * 4u;
 #pragma unroll
-        for (int j = 0; j < kGpp; ++j)
+        for (int j = 0; j < CNT; ++j)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 load_cols<TPL, kVec>(codes + (size_t)(16 * gj[j] + 4 * s) * N, lane_off,
@@ -231,7 +235,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
 
         // 5) per group: 4 k-steps of (TPL + 1) MFMAs, then the group epilogue
 #pragma unroll
-        for (int j = 0; j < kGpp; ++j) {
+        for (int j = 0; j < CNT; ++j) {
             f32x4_t acc[TPL], accs = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int t = 0; t < TPL; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -256,6 +260,13 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
             }
         }
         wave_lds_sync();  // this pass's reads of the slice precede the next pass's writes
+    };
+    for (int p0 = 0; p0 < G; p0 += kWaves * kGpp) {
+        // a last pass of 16 groups or fewer: one group per wave, none repeated
+        if (kGpp > 1 && G - p0 <= kWaves)
+            pass(p0, std::integral_constant<int, 1>{});
+        else
+            pass(p0, std::integral_constant<int, kGpp>{});
     }
 
     // 6) partial sums through LDS: each wave reuses its own activation slice (it has finished
