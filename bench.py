@@ -221,6 +221,7 @@ class Roofs:
         self.lib.roof_empty.argtypes = [ctypes.c_void_p]
         self.lib.roof_shared_read.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.roof_copy_pipeline.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int] * 3 + [ctypes.c_void_p]
         self.sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
 
     def _stream(self):
@@ -259,7 +260,10 @@ class Roofs:
         import torch
         x = torch.randint(-2 ** 15, 2 ** 15, (M, K), dtype=torch.int16, device="cuda")
         shapes = ("1 KB of one row", "16 rows x 64 B (16x16x32 A fragments)", "32 rows x 32 B (32x32x16 A fragments)",
-                  "4 rows x 256 B")
+                  "4 rows x 256 B", "1 KB of one row, direct-to-LDS copies, 4 in flight per wave",
+                  "1 KB of one row, direct-to-LDS copies, 8 in flight per wave",
+                  "2 rows x 512 B, direct-to-LDS copies, 4 in flight per wave",
+                  "2 rows x 512 B, chunks XOR-swizzled by row, direct-to-LDS copies, 4 in flight per wave")
         out = []
         for pat, shape in enumerate(shapes):
             def step(i, pat=pat):
@@ -272,12 +276,41 @@ class Roofs:
         return out
 
 
+    def copy_pipeline(self, copies, N: int, K: int):
+        """The 64-row factored kernel's operand copies alone (roof_copy_pipeline), over the rotated
+        cold weight copies: x only, the weights only, both, and both with the two streams on
+        separate waves."""
+        import torch
+        x = torch.randint(-2 ** 15, 2 ** 15, (64, K), dtype=torch.int16, device="cuda")
+        modes = ("x only (64 rows, from L2)", "packed words and parameters only (from HBM)", "both",
+                 "both, x and weights copied by separate waves")
+        out = []
+        for mode, what in enumerate(modes):
+            def step(i, mode=mode):
+                c, sc, mn = copies[i % len(copies)]
+                assert self.lib.roof_copy_pipeline(x.data_ptr(), c.data_ptr(), sc.data_ptr(), mn.data_ptr(), N, K, mode,
+                                                   self._stream()) == 0
+            r = time_rounds(step, len(copies))
+            out.append({"mode": mode, "copies": what, "us": r["us"], "us_rounds": r["rounds_us"]})
+        del x
+        return out
+
+
 def bench_l2_patterns():
     """roof_shared_read at K = 4096 for 32, 64 and 128 rows, 224 blocks (one per 64 columns of the
-    decode shape), beside the empty launch that every figure includes."""
+    decode shape), beside the empty launch that every figure includes; and roof_copy_pipeline over
+    the decode shape's weights."""
+    import gemm_w4a16_amd as w
+    import workloads
     roofs = Roofs()
-    return {"blocks": 224, "K": 4096, "empty_launch_us": roofs.empty_launch_us(),
-            "rows": {M: roofs.shared_read(M, 4096) for M in (32, 64, 128)}}
+    out = {"blocks": 224, "K": 4096, "empty_launch_us": roofs.empty_launch_us(),
+           "rows": {M: roofs.shared_read(M, 4096) for M in (32, 64, 128)}}
+    wl = workloads.DECODE
+    W = workloads.weights(wl.N, wl.K, wl.outliers, wl.seed_w)
+    c, s_, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl.N, wl.K)
+    st = Setup(w.W4A16_FMT_G128_ASYM_BF16, 1, wl.N, wl.K, np.zeros((1, wl.K), np.uint16), W, copies_for(c + s_ + m))
+    out["copy_pipeline"] = {"N": wl.N, "K": wl.K, "rows": 64, "modes": roofs.copy_pipeline(st.copies, wl.N, wl.K)}
+    return out
 
 
 def time_rounds_eager(step, rounds: int = ROUNDS):
