@@ -261,9 +261,11 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
         }
         wave_lds_sync();  // this pass's reads of the slice precede the next pass's writes
     };
+    // a last pass of 16 groups or fewer: one group per wave, none repeated (not in the instances
+    // where the second pass body costs registers: 16 rows with fp32 parameters, scalar columns)
+    constexpr bool kShortLast = kGpp > 1 && kVec && !(kP32 && MR == 16);
     for (int p0 = 0; p0 < G; p0 += kWaves * kGpp) {
-        // a last pass of 16 groups or fewer: one group per wave, none repeated
-        if (kGpp > 1 && G - p0 <= kWaves)
+        if (kShortLast && G - p0 <= kWaves)
             pass(p0, std::integral_constant<int, 1>{});
         else
             pass(p0, std::integral_constant<int, kGpp>{});
