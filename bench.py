@@ -283,7 +283,9 @@ class Roofs:
         import torch
         x = torch.randint(-2 ** 15, 2 ** 15, (64, K), dtype=torch.int16, device="cuda")
         modes = ("x only (64 rows, from L2)", "packed words and parameters only (from HBM)", "both",
-                 "both, x and weights copied by separate waves")
+                 "both, x and weights copied by separate waves", "both, the word copies non-temporal (nt)",
+                 "both, the word copies at system scope (sc0 sc1)", "both, the word copies at device scope (sc1)",
+                 "words and parameters only, nt", "words and parameters only, sc0 sc1")
         out = []
         for mode, what in enumerate(modes):
             def step(i, mode=mode):

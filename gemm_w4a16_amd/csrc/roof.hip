@@ -127,11 +127,32 @@ __global__ __launch_bounds__(kSharedThreads) void roof_shared_dma_kernel(const c
     }
 }
 
+// A direct-to-LDS copy of the weights with cache-policy bits: 0 none, 1 nt, 2 sc0 sc1, 3 sc1.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <int kPol, int kImm>
+__device__ __forceinline__ void dma16_pol(uint32_t voff, const void* sbase, uint32_t lds) {
+    if constexpr (kPol == 0) {
+        w4a16::dma16<kImm>(voff, sbase, lds);
+    } else if constexpr (kPol == 1) {
+        asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds), "n"(kImm)
+                     : "memory", "m0", "scc");
+    } else if constexpr (kPol == 2) {
+        asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1 sc0 sc1" ::"v"(voff), "s"(sbase), "s"(lds),
+                     "n"(kImm)
+                     : "memory", "m0", "scc");
+    } else {
+        asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(sbase), "s"(lds), "n"(kImm)
+                     : "memory", "m0", "scc");
+    }
+}
+#pragma clang diagnostic pop
+
 // roof_copy_pipeline's geometry: 64 rows, 64 columns per block, one group per stage.
 constexpr int kCpRows = 64, kCpX = kCpRows * 256, kCpW = 4096, kCpS = kCpX + kCpW + 512;
 constexpr int kCpStages = (160 * 1024) / kCpS;  // 7
 
-template <int kMode>
+template <int kMode, int kPol = 0>
 __global__ __launch_bounds__(512) void roof_copy_pipeline_kernel(const uint16_t* __restrict__ x,
                                                                  const uint32_t* __restrict__ codes,
                                                                  const uint16_t* __restrict__ scales,
@@ -174,8 +195,8 @@ __global__ __launch_bounds__(512) void roof_copy_pipeline_kernel(const uint16_t*
             }
         }
         if (copies_w) {
-            if (kSplit) w4a16::dma16<kCpX>(woff, codes + (size_t)16 * g * N, base + 1024u * wave);
-            else if (lane < 32) w4a16::dma16<kCpX>(woff, codes + (size_t)16 * g * N, base + 512u * wave);
+            if (kSplit) dma16_pol<kPol, kCpX>(woff, codes + (size_t)16 * g * N, base + 1024u * wave);
+            else if (lane < 32) dma16_pol<kPol, kCpX>(woff, codes + (size_t)16 * g * N, base + 512u * wave);
         }
         if (copies_p) w4a16::dma4<kCpX + kCpW>(poff, parr + (size_t)g * N * 2, base + 256u * wave);
     };
@@ -254,6 +275,11 @@ int roof_copy_pipeline(const void* x, const void* codes, const void* scales, con
         case 1: hipLaunchKernelGGL(roof_copy_pipeline_kernel<1>, grid, block, 0, stream, xs, c, sc, mn, N, K); break;
         case 2: hipLaunchKernelGGL(roof_copy_pipeline_kernel<2>, grid, block, 0, stream, xs, c, sc, mn, N, K); break;
         case 3: hipLaunchKernelGGL(roof_copy_pipeline_kernel<3>, grid, block, 0, stream, xs, c, sc, mn, N, K); break;
+        case 4: hipLaunchKernelGGL((roof_copy_pipeline_kernel<2, 1>), grid, block, 0, stream, xs, c, sc, mn, N, K); break;
+        case 5: hipLaunchKernelGGL((roof_copy_pipeline_kernel<2, 2>), grid, block, 0, stream, xs, c, sc, mn, N, K); break;
+        case 6: hipLaunchKernelGGL((roof_copy_pipeline_kernel<2, 3>), grid, block, 0, stream, xs, c, sc, mn, N, K); break;
+        case 7: hipLaunchKernelGGL((roof_copy_pipeline_kernel<1, 1>), grid, block, 0, stream, xs, c, sc, mn, N, K); break;
+        case 8: hipLaunchKernelGGL((roof_copy_pipeline_kernel<1, 2>), grid, block, 0, stream, xs, c, sc, mn, N, K); break;
         default: return 1;
     }
     return hipGetLastError() == hipSuccess ? 0 : 3;
