@@ -15,12 +15,15 @@
 //    has to agree between A and B.  The 8 k of chunk c of lane group g's block are
 //    k = 32(4u + g) + 8c + 0..7, so each lane's B fragment for MFMA c is chunk c of its own block,
 //    and its A fragment is the same 8 k of its activation row.  No data crosses lanes.
-//  * Dequant is exact up to one rounding: the nibble pair (q_t, q_{t+4}) of a code dword becomes
+//  * Q4 dequant is exact up to one rounding: the nibble pair (q_t, q_{t+4}) of a code dword becomes
 //    the fp16 pair (1024 + q) with one AND-OR (the magic-number trick of both pages); subtracting
-//    1032 (Q4: the offset and the bias 8) or 1024 and then z (zero-point format) is exact, and one
-//    packed multiply by the scale rounds (q - 8) s or (q - z) s to fp16.  W8 bytes become 1024 + u,
-//    u = q + 128, and then q exactly; the row's fp32 scale multiplies the row's total once (the
-//    exercise's scale after accumulation).  Packed fp16 arithmetic, no packed fp32.
+//    1032 (the offset and the bias 8) is exact, and one packed multiply by the scale rounds
+//    (q - 8) s to fp16.  W8 bytes become 1024 + u, u = q + 128, and then q exactly; the row's fp32
+//    scale multiplies the row's total once (the exercise's scale after accumulation).  Packed fp16
+//    arithmetic, no packed fp32.  The zero-point format is factored per group instead (its scale
+//    and zero point change only every 128 k): the MFMAs run on 1024 + q itself, a chain against
+//    ones gives sum(x), and each group adds s acc - (1024 + z) s sum(x) in fp32 -- a quarter of the
+//    exact dequant's VALU work per code word.
 //  * Per wave, the activations of its units stay in registers while it walks the block's row
 //    tiles; waves split K, and their partial tiles are added through LDS in a fixed order, so
 //    results are bitwise reproducible run to run.
@@ -191,7 +194,72 @@ __global__ __launch_bounds__(1024) void rowmma_kernel(const uint16_t* __restrict
 
     // 2) per unit and row tile: dequantize each chunk into a B fragment and multiply it with every
     //    activation tile
+    // The zero-point format, factored per unit (one group of 128 k) as the small-M kernel does:
+    // the B fragments are the exact fp16 1024 + q (one AND-OR per pair), a fifth MFMA chain
+    // against ones gives sum(x) per activation row, and the group's epilogue adds
+    // s acc + c sum(x) with c = -(1024 + z) s.  An all-zero weight row still gives exact zeros:
+    // acc is 1024 sum(x) from the same MFMA order.
+    auto compute_zp = [&](const Pass& R) {
+        const u32x4_t ones_u = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};  // fp16 1.0 pairs
+        const f16x8_t ones = __builtin_bit_cast(f16x8_t, ones_u);
+#pragma unroll
+        for (int p = 0; p < UP; ++p) {
+            f32x4_t au[kMyTiles][MT], sx[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                sx[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int r = 0; r < kMyTiles; ++r) au[r][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c) {
+                f16x8_t a[MT];
+#pragma unroll
+                for (int t = 0; t < MT; ++t) {
+                    const u32x4_t xv = pair_nibble_order(R.xa[p][t][c]);
+                    a[t] = __builtin_bit_cast(f16x8_t, R.live[p][t] ? xv : u32x4_t{0u, 0u, 0u, 0u});
+                    sx[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], ones, sx[t], 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < kMyTiles; ++r) {
+                    const uint32_t wd = R.w[p][r][c];
+                    const u32x4_t bf = {(wd & mask) | magic, ((wd >> 4) & mask) | magic, ((wd >> 8) & mask) | magic,
+                                        ((wd >> 12) & mask) | magic};
+#pragma unroll
+                    for (int t = 0; t < MT; ++t)
+                        au[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(f16x8_t, bf),
+                                                                          au[r][t], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < kMyTiles; ++r) {
+                const int rowl = min(16 * (rg + kR * r) + j, rows - 1);
+                uint32_t sv, zv;
+                if constexpr (kStage > 0) {
+                    sv = prm[rowl * PB + R.u[p]];
+                    zv = prm[kParamElems / 2 + rowl * PB + R.u[p]];
+                } else {
+                    sv = R.sc[p][r];
+                    zv = R.zc[p][r];
+                }
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sv);
+                const float cf = -(1024.0f + (float)__builtin_bit_cast(_Float16, (uint16_t)zv)) * sf;
+#pragma unroll
+                for (int t = 0; t < MT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[r][t][e] = __builtin_fmaf(sf, au[r][t][e], acc[r][t][e]);
+                        acc[r][t][e] = __builtin_fmaf(cf, sx[t][e], acc[r][t][e]);
+                    }
+            }
+        }
+    };
+
     auto compute = [&](const Pass& R) {
+        if constexpr (kZP) {
+            compute_zp(R);
+            return;
+        }
 #pragma unroll
         for (int p = 0; p < UP; ++p)
 #pragma unroll
