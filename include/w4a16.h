@@ -155,8 +155,9 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
  * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format; FP16 for W8.  For Q4,
  * the zero-point format and W8, one row of fp16 activations takes the one-row GEMV (dot2 with the
  * scale applied once per block); two or more fp16 rows share one weight pass on the fp16 matrix
- * cores, the weights dequantized to fp16 in registers ((q - 8) s, (q - z) s or q, each rounded
- * once) and the W8 row scale applied to each total; bf16 activations run one pass per row.  y has
+ * cores: Q4 and W8 dequantized to fp16 in registers ((q - 8) s rounded once, or q exactly, the W8
+ * row scale applied to each total), the zero-point format in the factored per-group form
+ * s * sum(x*(1024+q)) - (1024 + z) s * sum(x) in fp32; bf16 activations run one pass per row.  y has
  * the activation dtype, rounded to nearest even from fp32.  Row-major x and y; x, y 16-byte
  * aligned. */
 w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
@@ -173,9 +174,9 @@ size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int6
 
 /* Large-M path: y [M][N] = x [M][K] . W_hat^T on the matrix cores with fp32 accumulation.
  * Q4, the zero-point format and W8 (fp16 activations only; ERR_UNSUPPORTED for bf16): any M, each
- * 16 rows against one pass over the weights, dequantized to fp16 in registers as for w4a16_gemv's
- * rows (anrans.github.io "Quantization and GEMV", "The quantization formulas": the zero-point
- * format's (q - z) s); no workspace.  G128 as follows, on bf16 MFMA.
+ * 16 rows against one pass over the weights, as for w4a16_gemv's rows (anrans.github.io
+ * "Quantization and GEMV", "The quantization formulas": the zero-point format's (q - z) s, in its
+ * factored per-group form); no workspace.  G128 as follows, on bf16 MFMA.
  * From 65 rows on (and at 33..64 rows when N % 4 != 0 or K % 256 != 0), packed B tiles are
  * dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai Step 2 builds its B tile) and fed to the
  * matrix cores; otherwise, up to 64 rows, the factored per-group form of w4a16_gemv
