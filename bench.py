@@ -276,10 +276,10 @@ class Roofs:
         return out
 
 
-    def copy_pipeline(self, copies, N: int, K: int):
+    def copy_pipeline(self, copies, N: int, K: int, nmodes: int = 9):
         """The 64-row factored kernel's operand copies alone (roof_copy_pipeline), over the rotated
         cold weight copies: x only, the weights only, both, and both with the two streams on
-        separate waves."""
+        separate waves (then the cache-policy variants of the weight copies)."""
         import torch
         x = torch.randint(-2 ** 15, 2 ** 15, (64, K), dtype=torch.int16, device="cuda")
         modes = ("x only (64 rows, from L2)", "packed words and parameters only (from HBM)", "both",
@@ -287,7 +287,7 @@ class Roofs:
                  "both, the word copies at system scope (sc0 sc1)", "both, the word copies at device scope (sc1)",
                  "words and parameters only, nt", "words and parameters only, sc0 sc1")
         out = []
-        for mode, what in enumerate(modes):
+        for mode, what in enumerate(modes[:nmodes]):
             def step(i, mode=mode):
                 c, sc, mn = copies[i % len(copies)]
                 assert self.lib.roof_copy_pipeline(x.data_ptr(), c.data_ptr(), sc.data_ptr(), mn.data_ptr(), N, K, mode,
@@ -296,6 +296,21 @@ class Roofs:
             out.append({"mode": mode, "copies": what, "us": r["us"], "us_rounds": r["rounds_us"]})
         del x
         return out
+
+
+def bench_copy_floor(W=None):
+    """What the 64-row kernel's operand copies alone take at the decode shape (x from L2, the
+    weights from HBM, cold rotated copies): the floor under the sweep's M = 64 figure."""
+    import gemm_w4a16_amd as w
+    import workloads
+    wl = workloads.DECODE
+    if W is None:
+        W = workloads.weights(wl.N, wl.K, wl.outliers, wl.seed_w)
+    c, s_, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, wl.N, wl.K)
+    st = Setup(w.W4A16_FMT_G128_ASYM_BF16, 1, wl.N, wl.K, np.zeros((1, wl.K), np.uint16), W, copies_for(c + s_ + m))
+    modes = Roofs().copy_pipeline(st.copies, wl.N, wl.K, nmodes=4)
+    return {"workload": "decode-shape weights, 64 activation rows", "kernel": "roof_copy_pipeline (libw4a16_roof.so)",
+            "modes": modes}
 
 
 def bench_l2_patterns():
@@ -994,6 +1009,9 @@ def main():
         torch.cuda.empty_cache()
         log("batch sweep")
         extra["sweep"] = bench_sweep(W)
+        torch.cuda.empty_cache()
+        log("copy floor of the 64-row kernel (roof_copy_pipeline)")
+        extra["copy_floor_m64"] = bench_copy_floor(W)
         torch.cuda.empty_cache()
         import workloads
         log("row-major formats over M (zero point and W8 at the decode shape, Q4 at 16384^2)")
