@@ -308,7 +308,8 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 
 size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K) {
     if (fmt != W4A16_FMT_G128_ASYM_BF16 || check_shape(fmt, N, K) != W4A16_OK || M <= 0 || M > kMaxDim) return 0;
-    return w4a16::gemm_g128_workspace_bytes(M, N, K);
+    // the large-M GEMM's split-K partials, or w4a16_matmul's small-M K split
+    return std::max(w4a16::gemm_g128_workspace_bytes(M, N, K), w4a16::skinny_split_workspace_bytes(M, N, K));
 }
 
 w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
@@ -335,7 +336,21 @@ w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x
     // G128 by the cutoff; the row-major formats take the GEMV up to its row limit, and above it
     // w4a16_gemm (fp16 activations)
     const int64_t cut = fmt == W4A16_FMT_G128_ASYM_BF16 ? kGemvCutoff : w4a16::kGemvMaxRows;
-    if (M > 0 && M <= cut) return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
+    if (M > 0 && M <= cut) {
+        // G128 with a workspace: the small-M kernel with K split over blocks where its column
+        // blocks alone would leave CUs idle; without one (or short of it), the GEMV
+        const size_t need = fmt == W4A16_FMT_G128_ASYM_BF16 ? w4a16::skinny_split_workspace_bytes(M, N, K) : 0;
+        if (need > 0 && workspace_bytes >= need && aligned16(workspace)) {
+            const w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
+            if (st != W4A16_OK) return st;
+            w4a16::clear_stale_error();
+            return from_hip(w4a16::launch_skinny_g128_split(
+                static_cast<const uint16_t*>(x), M, static_cast<const uint32_t*>(codes),
+                static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
+                static_cast<float*>(workspace), w4a16::skinny_splits(M, N, K), stream));
+        }
+        return w4a16_gemv(fmt, act, x, M, codes, scales, mins, N, K, y, stream);
+    }
     return w4a16_gemm(fmt, act, x, M, codes, scales, mins, N, K, y, workspace, workspace_bytes, stream);
 }
 
@@ -417,8 +432,7 @@ w4a16_status_t w4a16_matmul_noalloc(w4a16_format_t fmt, w4a16_dtype_t act, const
                                     void* y, hipStream_t stream) {
     w4a16_status_t st = check_matmul_common(fmt, act, x, M, codes, scales, mins, N, K, y);
     if (st != W4A16_OK) return st;
-    const bool gemm = fmt == W4A16_FMT_G128_ASYM_BF16 && M > kGemvCutoff;
-    const size_t need = gemm ? w4a16::gemm_g128_workspace_bytes(M, N, K) : 0;
+    const size_t need = w4a16_gemm_workspace_bytes(fmt, M, N, K);
     if (need > kScratchBytes) return W4A16_ERR_UNSUPPORTED;
     float* ws = nullptr;
     if (need > 0 && (st = scratch_for_stream(stream, &ws)) != W4A16_OK) return st;

@@ -730,9 +730,11 @@ hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes,
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.splits == 1) return e;
-    const int64_t MN = M * N;
-    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream, workspace, y,
-                       MN, p.splits);
+    return launch_splitk_reduce(workspace, M * N, p.splits, y, stream);
+}
+
+hipError_t launch_splitk_reduce(const float* ws, int64_t MN, int splits, uint16_t* y, hipStream_t stream) {
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, stream, ws, y, MN, splits);
     return hipGetLastError();
 }
 

@@ -44,6 +44,28 @@ hipError_t launch_gemv_w8row(const uint16_t* x, int64_t M, const int8_t* codes, 
 constexpr int kGemvMaxRows = 16;
 hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                               const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+// The same with K split over `splits` blocks per 64 columns, the fp32 partials in ws
+// [splits][M][N], then summed in split order into y (two launches).
+hipError_t launch_skinny_g128_split(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                    const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* ws, int splits,
+                                    hipStream_t stream);
+// K splits for the small-M kernel (1: none): where even its 32-column blocks would leave CUs idle
+// (fewer than 192 of them) and the codes (at least 16 MiB) pay for the second launch, 64-column
+// blocks times enough splits to fill 256 CUs, 2..8, each at least 16 groups of K.  Measured: at
+// N = 4096, K = 14336 11.6 / 18.5 us -> 10.1 / 13.0 us for 1 / 16 rows; at N = 2048, K = 16384
+// 12.1 / 20.0 -> 8.4 / 10.4 us; at N = 8192 (256 blocks of 32 columns) the split lost.
+inline int skinny_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t nb = (N + 63) / 64, G = K / 128;
+    if (M < 1 || M > kGemvMaxRows || (N + 31) / 32 >= 192 || N * K / 2 < ((int64_t)16 << 20)) return 1;
+    int s = (int)(256 / nb);
+    s = s < 2 ? 2 : (s > 8 ? 8 : s);
+    while (s > 1 && G / s < 16) --s;
+    return s;
+}
+inline size_t skinny_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const int s = skinny_splits(M, N, K);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4 : 0;
+}
 // Q4 path, one activation row per pass; act_f16: fp16 (true) or bf16 (false) activations.
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
@@ -82,6 +104,8 @@ hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, 
 
 // Large-M G128 path on bf16 MFMA (the mid path below kMidMaxRows rows).
 size_t gemm_g128_workspace_bytes(int64_t M, int64_t N, int64_t K);
+// y [MN] = bf16 of the sum over `splits` fp32 partial arrays ws [splits][MN], in split order.
+hipError_t launch_splitk_reduce(const float* ws, int64_t MN, int splits, uint16_t* y, hipStream_t stream);
 hipError_t launch_gemm_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                             const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* workspace,
                             hipStream_t stream);

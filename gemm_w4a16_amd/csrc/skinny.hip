@@ -140,7 +140,8 @@ __global__ __launch_bounds__(64 * kSkinnyWaves)
 __attribute__((amdgpu_waves_per_eu(kSkinnyWaves / 4, kSkinnyWaves / 4)))
 void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                         const void* __restrict__ scales_v, const void* __restrict__ mins_v,
-                        uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic) {
+                        uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic,
+                        float* __restrict__ ws, int gps) {
     const uint16_t* __restrict__ scales = static_cast<const uint16_t*>(scales_v);
     const uint16_t* __restrict__ mins = static_cast<const uint16_t*>(mins_v);
     const float* __restrict__ scales32 = static_cast<const float*>(scales_v);
@@ -155,7 +156,9 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     const int lane = lane_id(), wave = wave_id();
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * COLS;
-    const int G = K >> 7;
+    // K split over blockIdx.y: this block's groups gs .. G - 1 (all of K when gridDim.y == 1)
+    const int gs = blockIdx.y * gps;
+    const int G = min(K >> 7, gs + gps);
     // this lane's TPL adjacent columns; a lane past N re-reads in-range columns, never stores
     int cbase = n0 + TPL * lr;
     if (kVec) cbase = min(cbase, N - TPL);
@@ -264,7 +267,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     // a last pass of 16 groups or fewer: one group per wave, none repeated (not in the instances
     // where the second pass body costs registers: 16 rows with fp32 parameters, scalar columns)
     constexpr bool kShortLast = kGpp > 1 && kVec && !(kP32 && MR == 16);
-    for (int p0 = 0; p0 < G; p0 += kWaves * kGpp) {
+    for (int p0 = gs; p0 < G; p0 += kWaves * kGpp) {
         if (kShortLast && G - p0 <= kWaves)
             pass(p0, std::integral_constant<int, 1>{});
         else
@@ -292,32 +295,37 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
                 sum += reinterpret_cast<const float*>(&xs[v][0][0][0])[row * COLS + c];
-            y[(size_t)row * N + n] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
+            if (ws != nullptr)  // a K split's fp32 partial sums, [split][M][N]
+                ws[((size_t)blockIdx.y * M + row) * N + n] = sum;
+            else
+                y[(size_t)row * N + n] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
         }
     }
 }
 
+// splits > 1: K split over gridDim.y, fp32 partial sums to ws [splits][M][N] (y untouched).
 template <int MR, int TPL, int GPP, bool kF16, bool kP32>
 void launch_gpp(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
-                int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+                int64_t N, int64_t K, uint16_t* y, float* ws, int splits, int gps, hipStream_t stream) {
     constexpr int COLS = 16 * TPL;
     constexpr uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
-    const dim3 grid((unsigned)((N + COLS - 1) / COLS)), block(64 * kSkinnyWaves);
+    const dim3 grid((unsigned)((N + COLS - 1) / COLS), (unsigned)splits), block(64 * kSkinnyWaves);
     if (N % TPL == 0)
         hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, true, kF16, kP32>), grid, block, 0, stream, x, codes, scales,
-                           mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
+                           mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
     else
         hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, false, kF16, kP32>), grid, block, 0, stream, x, codes,
-                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic);
+                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
 }
 
 template <int MR, int TPL, bool kF16 = false, bool kP32 = false>
 void launch_mr(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
-               int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-    if (K <= 128 * kSkinnyWaves)
-        launch_gpp<MR, TPL, 1, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+               int64_t N, int64_t K, uint16_t* y, hipStream_t stream, float* ws = nullptr, int splits = 1) {
+    const int G = (int)(K >> 7), gps = (G + splits - 1) / splits;  // groups per split
+    if (gps <= kSkinnyWaves)
+        launch_gpp<MR, TPL, 1, kF16, kP32>(x, M, codes, scales, mins, N, K, y, ws, splits, gps, stream);
     else
-        launch_gpp<MR, TPL, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        launch_gpp<MR, TPL, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, ws, splits, gps, stream);
 }
 
 }  // namespace
@@ -351,6 +359,19 @@ hipError_t launch_skinny_g128(const uint16_t* x, int64_t M, const uint32_t* code
                               const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     launch_rows<false, false>(x, M, codes, scales, mins, N, K, y, stream);
     return hipGetLastError();
+}
+
+hipError_t launch_skinny_g128_split(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                    const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* ws, int splits,
+                                    hipStream_t stream) {
+    // 64-column blocks times `splits` K-slices, then the partials summed in split order
+    if (M == 1) launch_mr<1, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
+    else if (M <= 4) launch_mr<4, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
+    else if (M <= 8) launch_mr<8, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
+    else launch_mr<16, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce(ws, M * N, splits, y, stream);
 }
 
 hipError_t launch_skinny_prepared_zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,

@@ -167,9 +167,10 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 /* Largest M that w4a16_gemv accepts. */
 int64_t w4a16_gemv_max_rows(void);
 
-/* Bytes of device workspace w4a16_gemm needs for this shape (0 if none).  The workspace holds
- * split-K partial sums; it is caller-owned, needs no initialisation, and must not be shared by
- * two calls that may run at the same time. */
+/* Bytes of device workspace w4a16_gemm needs for this shape (0 if none), or, up to 16 rows of
+ * G128, what w4a16_matmul uses to split K over blocks (below).  The workspace holds split-K
+ * partial sums; it is caller-owned, needs no initialisation, and must not be shared by two calls
+ * that may run at the same time. */
 size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K);
 
 /* Large-M path: y [M][N] = x [M][K] . W_hat^T on the matrix cores with fp32 accumulation.
@@ -193,7 +194,12 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
  * chosen per M; anrans "Exercises": kernels chosen by batch size): M <= w4a16_matmul_gemv_cutoff()
  * goes to w4a16_gemv, larger M to w4a16_gemm.  Q4, the zero-point format and W8 take the GEMV
  * path up to w4a16_gemv_max_rows() rows and w4a16_gemm above (fp16 activations).  Workspace as for
- * w4a16_gemm (w4a16_gemm_workspace_bytes of the same shape is always enough). */
+ * w4a16_gemm (w4a16_gemm_workspace_bytes of the same shape is always enough).  Up to 16 rows of
+ * G128, where N is small enough that the GEMV's column blocks would leave CUs idle (fewer than
+ * 192 blocks of 32 columns) and the codes are at least 16 MiB, a workspace of that size lets the
+ * small-M kernel split K over 2..8 blocks per 64 columns, the fp32 partials summed in split order
+ * by a second launch; without one (NULL or too small) the call runs w4a16_gemv.  Both results
+ * are bitwise reproducible; they differ from each other in fp32 rounding only. */
 w4a16_status_t w4a16_matmul(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,
                             const void* codes, const void* scales, const void* mins, int64_t N,
                             int64_t K, void* y, void* workspace, size_t workspace_bytes,

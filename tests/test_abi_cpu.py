@@ -137,6 +137,15 @@ def test_gemm_validation_and_workspace():
     assert w.w4a16_gemm_workspace_bytes(G128, 64, 256, 4096) == 0
     assert w.w4a16_gemm_workspace_bytes(Q4, 300, 256, 4096) == 0
     assert w.w4a16_gemm_workspace_bytes(G128, 0, 256, 4096) == 0
+    # up to 16 rows, w4a16_matmul splits K over blocks where the 64-column blocks would leave CUs
+    # idle and the codes are at least 16 MiB: 256 / 64 = 4 splits at N = 4096, fp32 partials
+    assert w.w4a16_gemm_workspace_bytes(G128, 16, 4096, 14336) == 4 * 16 * 4096 * 4
+    assert w.w4a16_gemm_workspace_bytes(G128, 1, 2048, 16384) == 8 * 1 * 2048 * 4
+    assert w.w4a16_gemm_workspace_bytes(G128, 1, 8192, 4096) == 0       # 256 blocks of 32 columns
+    assert w.w4a16_gemm_workspace_bytes(G128, 1, 4096, 4096) == 0       # 8 MiB of codes
+    assert w.w4a16_gemm_workspace_bytes(G128, 16, 14336, 4096) == 0     # 224 column blocks
+    assert w.w4a16_gemm_workspace_bytes(G128, 17, 4096, 14336) == 0     # the 32-row kernel
+    assert w.w4a16_gemm_workspace_bytes(ZP, 16, 4096, 14336) == 0
     g = w.w4a16_gemm
     assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, FAKE, need - 4, 0) == w.W4A16_ERR_INVALID
     assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, None, 0, 0) == w.W4A16_ERR_INVALID

@@ -426,6 +426,28 @@ def test_gemm_rows_agree_with_gemv():
         assert rel_err(yg[m], yv.astype(np.float64)) <= TOL
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(1, 4096, 14336, 4), (3, 4096, 14336, 4), (16, 4096, 14336, 4),
+                                          (5, 4104, 8192, 3), (2, 4097, 8192, 3)])
+def test_matmul_small_n_splits_k(M, N, K, splits):
+    """With a workspace, w4a16_matmul splits K over blocks where the small-M kernel's 64-column
+    blocks alone would leave CUs idle (N = 4096: 64 blocks) and sums the fp32 partials in split
+    order: against the oracle, bitwise repeatable; a ragged last split (G = 64 over 3) and ragged
+    column blocks, vector (N = 4104) and scalar (N = 4097) column loads."""
+    say(f"small-N K split M={M} N={N} K={K}")
+    assert w.w4a16_gemm_workspace_bytes(G128, M, N, K) == splits * M * N * 4
+    W = workloads.weights(N, K, outliers=True, seed=109)
+    x = workloads.activations(M, K, "bf16", seed=110)
+    rc, rs, rm = oracle.quantize_g128(W)
+    packed = (dev(rc), dev(rs), dev(rm))
+    y = run_matmul(w.w4a16_matmul, G128, x, packed, N, K, BF16)
+    np.testing.assert_array_equal(y, run_matmul(w.w4a16_matmul, G128, x, packed, N, K, BF16))
+    err, worst = refcheck.check(bf16_f32(y), refcheck.g128(x, rc, rs, rm), "bf16", f"split M={M} N={N}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+    # the unsplit GEMV (w4a16_gemv takes no workspace) meets the same bound
+    yv = bf16_f32(run_matmul(w.w4a16_gemv, G128, x, packed, N, K, BF16))
+    refcheck.check(yv, refcheck.g128(x, rc, rs, rm), "bf16", f"gemv M={M} N={N}")
+
+
 def test_matmul_dispatch_matches_both_paths():
     N, K = 384, 1024
     W = workloads.weights(N, K, seed=24)

@@ -35,13 +35,15 @@ def _with_workspace(x_bits, packed, N, K):
 
 def test_noalloc_matches_matmul_on_two_calls_in_a_row():
     # first: 3 x 1 tiles of 128 x 256 split 32 ways (9.8 MB of partials); second, smaller:
-    # 2 x 2 tiles of 128 x 128 split 16 ways (1.7 MB); then a GEMV-sized call (no scratch)
-    cases = [(300, 256, 4096, 201), (130, 200, 2048, 202), (5, 300, 1024, 203)]
+    # 2 x 2 tiles of 128 x 128 split 16 ways (1.7 MB); then a GEMV-sized call (no scratch), and
+    # two small-M calls with K split over blocks (N = 4096: 4 splits), the second smaller
+    cases = [(300, 256, 4096, 201), (130, 200, 2048, 202), (5, 300, 1024, 203), (6, 4096, 8192, 206),
+             (2, 4096, 8192, 207)]
     for M, N, K, seed in cases:
-        need = w.w4a16_gemm_workspace_bytes(G128, M, N, K) if M > w.w4a16_matmul_gemv_cutoff() else 0
+        need = w.w4a16_gemm_workspace_bytes(G128, M, N, K)
         say(f"noalloc M={M} N={N} K={K}: {need} B of split-K partials")
         assert need <= w.w4a16_matmul_noalloc_max_scratch_bytes()
-        assert (need > 0) == (M > 100)
+        assert (need > 0) == (M > 100 or N == 4096)
         W = workloads.weights(N, K, outliers=True, seed=seed)
         x = workloads.activations(M, K, "bf16", seed=seed + 1)
         packed = gpu_pack(G128, W)
