@@ -82,7 +82,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill", "q4", "sweep", "zp", "zp_prepared", "w8", "w4a8",
-                                       "w4a8_decode", "w4a8_sweep", "cpu", "rowfmt_sweep", "l2_patterns"], default=None,
+                                       "w4a8_decode", "w4a8_sweep", "cpu", "rowfmt_sweep", "l2_patterns", "small_n"], default=None,
                     help="time one workload only (for profiler runs); prints its JSON line")
     ap.add_argument("--eager", action="store_true",
                     help="launch every step directly instead of replaying a HIP graph (counter runs)")
@@ -296,6 +296,35 @@ class Roofs:
             out.append({"mode": mode, "copies": what, "us": r["us"], "us_rounds": r["rounds_us"]})
         del x
         return out
+
+
+def bench_small_n():
+    """The decode GEMV at a small-N shape (N = 4096, K = 14336: the 8B model's down projection), 1
+    and 16 rows, cold rotated copies: w4a16_matmul with its workspace (K split over blocks) and
+    without (the GEMV's 32-column blocks, 128 of them)."""
+    import gemm_w4a16_amd as w
+    import workloads
+    N, K = 4096, 14336
+    W = workloads.weights(N, K, True, 0)
+    c, s_, m = w.w4a16_packed_sizes(w.W4A16_FMT_G128_ASYM_BF16, N, K)
+    R = copies_for(c + s_ + m)
+    out, base = [], None
+    for M in (1, 16):
+        x = workloads.activations(M, K, "bf16", 1, rows_drawn=16)
+        st = Setup(w.W4A16_FMT_G128_ASYM_BF16, M, N, K, x, W, R if base is None else 1)
+        if base is None:
+            base = st.copies
+        else:
+            st.copies = base
+        split = time_rounds(st.step, R)
+        ws_bytes = st.ws_bytes
+        st.ws, st.ws_bytes = None, 0
+        plain = time_rounds(st.step, R)
+        out.append({"M": M, "N": N, "K": K, "workspace_bytes": ws_bytes, "us_k_split": split["us"],
+                    "us_k_split_rounds": split["rounds_us"], "us_no_workspace": plain["us"],
+                    "us_no_workspace_rounds": plain["rounds_us"],
+                    "effective_weight_gbs_k_split": (c + s_ + m) / split["us"] / 1e3})
+    return {"workload": "decode_gemv_k14336_n4096", "weight_bytes": c + s_ + m, "rows": out}
 
 
 def bench_copy_floor(W=None):
@@ -938,7 +967,8 @@ def main():
                   "w8": bench_rowfmt_sweep(workloads.W8_DECODE, w.W4A16_FMT_W8_ROW_FP32),
                   "q4": bench_rowfmt_sweep(workloads.Q4, w.W4A16_FMT_Q4_B32_SYM_FP16, None, (1, 2, 4, 8, 16))},
               "w8": bench_w8, "zp_prepared": bench_zp_prepared, "w4a8": bench_w4a8, "w4a8_decode": bench_w4a8_decode,
-              "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only, "l2_patterns": bench_l2_patterns}[args.only]
+              "w4a8_sweep": bench_w4a8_sweep, "cpu": cpu_baseline_only, "l2_patterns": bench_l2_patterns,
+              "small_n": bench_small_n}[args.only]
         print(json.dumps({"only": args.only, "result": fn()}), flush=True)
         return
 
@@ -1009,6 +1039,9 @@ def main():
         torch.cuda.empty_cache()
         log("batch sweep")
         extra["sweep"] = bench_sweep(W)
+        torch.cuda.empty_cache()
+        log("small-N decode shape (K split over blocks)")
+        extra["decode_small_n"] = bench_small_n()
         torch.cuda.empty_cache()
         log("copy floor of the 64-row kernel (roof_copy_pipeline)")
         extra["copy_floor_m64"] = bench_copy_floor(W)
