@@ -308,8 +308,10 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
 
 size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int64_t K) {
     if (fmt != W4A16_FMT_G128_ASYM_BF16 || check_shape(fmt, N, K) != W4A16_OK || M <= 0 || M > kMaxDim) return 0;
-    // the large-M GEMM's split-K partials, or w4a16_matmul's small-M K split
-    return std::max(w4a16::gemm_g128_workspace_bytes(M, N, K), w4a16::skinny_split_workspace_bytes(M, N, K));
+    // the large-M GEMM's split-K partials, or the optional K split of the small-M (w4a16_matmul)
+    // and 17..64-row kernels
+    return std::max({w4a16::gemm_g128_workspace_bytes(M, N, K), w4a16::skinny_split_workspace_bytes(M, N, K),
+                     w4a16::mid_split_workspace_bytes(M, N, K)});
 }
 
 w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M, const void* codes,
@@ -325,6 +327,15 @@ w4a16_status_t w4a16_gemm(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
     const size_t need = w4a16::gemm_g128_workspace_bytes(M, N, K);
     if (need > 0 && (workspace_bytes < need || !aligned16(workspace))) return W4A16_ERR_INVALID;
     w4a16::clear_stale_error();
+    // 17..64 rows at small N: K split over blocks when the workspace holds the partials (else the
+    // unsplit kernel, which needs none)
+    const size_t mid_need = w4a16::mid_split_workspace_bytes(M, N, K);
+    if (mid_need > 0 && workspace_bytes >= mid_need && aligned16(workspace))
+        return from_hip(w4a16::launch_mid_g128_split(static_cast<const uint16_t*>(x), M,
+                                                     static_cast<const uint32_t*>(codes),
+                                                     static_cast<const uint16_t*>(scales),
+                                                     static_cast<const uint16_t*>(mins), N, K,
+                                                     static_cast<uint16_t*>(y), static_cast<float*>(workspace), stream));
     return from_hip(w4a16::launch_gemm_g128(static_cast<const uint16_t*>(x), M, static_cast<const uint32_t*>(codes),
                                             static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(mins),
                                             N, K, static_cast<uint16_t*>(y), static_cast<float*>(workspace), stream));

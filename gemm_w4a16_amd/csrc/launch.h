@@ -87,6 +87,30 @@ hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
 // Shapes the R-row kernels take (R = 64: groups in pairs, R = 32: in fours; 4-column copies);
 // others use the general kernels.
 inline bool midr_fits(int R, int64_t N, int64_t K) { return N % 4 == 0 && (K / 128) % (R == 64 ? 2 : 4) == 0; }
+// K split for the R-row kernels (17..64 rows, G128; splits 1: none): where their 64-column blocks
+// number fewer than 192 and the codes are at least 8 MiB, enough splits for 256 blocks, 2..8,
+// each a whole number of stages and at least 16 groups of K.
+struct MidSplit {
+    int splits, gps;
+};
+inline MidSplit mid_split(int64_t M, int64_t N, int64_t K) {
+    const int R = M <= 32 ? 32 : 64, gsz = R == 64 ? 2 : 4;  // groups per stage
+    const int64_t nb = (N + 63) / 64, G = K / 128;
+    if (M <= kGemvMaxRows || M > 64 || !midr_fits(R, N, K) || nb >= 192 || N * K / 2 < ((int64_t)8 << 20)) return {1, 0};
+    int s = (int)(256 / nb);
+    s = s < 2 ? 2 : (s > 8 ? 8 : s);
+    while (s > 1 && G / s < 16) --s;
+    if (s <= 1) return {1, 0};
+    const int gps = (int)((G + s - 1) / s + gsz - 1) / gsz * gsz;
+    return {(int)((G + gps - 1) / gps), gps};
+}
+inline size_t mid_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+    const MidSplit sp = mid_split(M, N, K);
+    return sp.splits > 1 ? (size_t)sp.splits * (size_t)M * (size_t)N * 4 : 0;
+}
+// 17..64 rows with K split as mid_split says: fp32 partials in ws, then summed in split order.
+hipError_t launch_mid_g128_split(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* ws, hipStream_t stream);
 
 // Row-major formats on fp16 MFMA for any number of fp16 activation rows (16 per weight pass).
 hipError_t launch_rowmma_q4b32(const uint16_t* x, int64_t M, const uint8_t* codes, const uint16_t* scales, int64_t N,

@@ -485,7 +485,7 @@ template <int R, bool kF16, bool kP32>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void midr_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes, const void* __restrict__ scales_v,
                  const void* __restrict__ mins_v, uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask,
-                 uint32_t magic) {
+                 uint32_t magic, float* __restrict__ ws, int gps) {
     using L = MidR<R>;
     constexpr int kGS = L::kGS, kWPG = L::kWPG, kRB = L::kRB, kRPI = L::kRPI;
     __shared__ __attribute__((aligned(16))) uint8_t smem[L::kStages * L::kS];
@@ -497,7 +497,9 @@ void midr_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ co
     const int l32 = lane & 31, lh = lane >> 5;
     const int n0 = blockIdx.x * kMidCols;
     const int G = K >> 7;
-    const int P = G / kGS;  // stages' worth of groups
+    // K split over blockIdx.y (gps groups each, a multiple of kGS): this block's groups gs ..
+    const int gs = blockIdx.y * gps;
+    const int P = (min(G, gs + gps) - gs) / kGS;  // stages' worth of groups
     const uint32_t sm = lds_addr(smem);
 
     // Copy offsets (constant over the stages).  x: copy i of wave w fills the kRPI rows from
@@ -525,7 +527,7 @@ void midr_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ co
 
     // this wave's copies of stage p into LDS stage st (a stage past the last repeats it)
     auto issue = [&](int p, int st) {
-        const int g0 = min(p, P - 1) * kGS;  // first group of the stage
+        const int g0 = gs + min(p, P - 1) * kGS;  // first group of the stage
         const uint32_t base = sm + (uint32_t)(st * L::kS);
         const char* xs = reinterpret_cast<const char*>(x + (size_t)g0 * 128);
         dma16<0>(xoff[0], xs, base + 4096u * wave);
@@ -620,17 +622,25 @@ void midr_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ co
 #pragma unroll
             for (int t = 1; t < kGS; ++t) v += part[((t * kWPG + wj) * 16 + e) * 64 + lane];  // sets in order
             const int m = 32 * wm + 8 * (e / 4) + 4 * lh + (e % 4);
-            if (m < M && n < N) y[(size_t)m * N + n] = kF16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+            if (m < M && n < N) {
+                if (ws != nullptr)  // a K split's fp32 partial sums, [split][M][N]
+                    ws[((size_t)blockIdx.y * M + m) * N + n] = v;
+                else
+                    y[(size_t)m * N + n] = kF16 ? f32_to_f16_bits(v) : f32_to_bf16_bits(v);
+            }
         }
     }
 }
 
+// splits > 1: K split over gridDim.y, gps groups per split (a multiple of the stage's groups),
+// fp32 partial sums to ws [splits][M][N] (y untouched).
 template <int R, bool kF16, bool kP32>
 void launch_midr(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins, int64_t N,
-                 int64_t K, uint16_t* y, hipStream_t stream) {
-    hipLaunchKernelGGL((midr_kernel<R, kF16, kP32>), dim3((unsigned)((N + kMidCols - 1) / kMidCols)), dim3(512), 0,
-                       stream, x, codes, scales, mins, y, (int)M, (int)N, (int)K, 0x000F000Fu,
-                       kF16 ? 0x64006400u : 0x43004300u);
+                 int64_t K, uint16_t* y, hipStream_t stream, float* ws = nullptr, int splits = 1, int gps = 0) {
+    if (splits <= 1) gps = (int)(K / 128);
+    hipLaunchKernelGGL((midr_kernel<R, kF16, kP32>), dim3((unsigned)((N + kMidCols - 1) / kMidCols), (unsigned)splits),
+                       dim3(512), 0, stream, x, codes, scales, mins, y, (int)M, (int)N, (int)K, 0x000F000Fu,
+                       kF16 ? 0x64006400u : 0x43004300u, ws, gps);
 }
 
 }  // namespace
@@ -664,6 +674,18 @@ hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
     if (act_f16) launch_midr<64, true, true>(x, M, codes, scales, mins, N, K, y, stream);
     else launch_midr<64, false, true>(x, M, codes, scales, mins, N, K, y, stream);
     return hipGetLastError();
+}
+
+hipError_t launch_mid_g128_split(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                 const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* ws, hipStream_t stream) {
+    const MidSplit sp = mid_split(M, N, K);
+    if (M <= 32)
+        launch_midr<32, false, false>(x, M, codes, scales, mins, N, K, y, stream, ws, sp.splits, sp.gps);
+    else
+        launch_midr<64, false, false>(x, M, codes, scales, mins, N, K, y, stream, ws, sp.splits, sp.gps);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_splitk_reduce(ws, M * N, sp.splits, y, stream);
 }
 
 hipError_t launch_mid_g128(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,

@@ -144,7 +144,11 @@ def test_gemm_validation_and_workspace():
     assert w.w4a16_gemm_workspace_bytes(G128, 1, 8192, 4096) == 0       # 256 blocks of 32 columns
     assert w.w4a16_gemm_workspace_bytes(G128, 1, 4096, 4096) == 0       # 8 MiB of codes
     assert w.w4a16_gemm_workspace_bytes(G128, 16, 14336, 4096) == 0     # 224 column blocks
-    assert w.w4a16_gemm_workspace_bytes(G128, 17, 4096, 14336) == 0     # the 32-row kernel
+    # 17..64 rows: the R-row kernels' K split at small N (64-column blocks, codes >= 8 MiB)
+    assert w.w4a16_gemm_workspace_bytes(G128, 17, 4096, 14336) == 4 * 17 * 4096 * 4
+    assert w.w4a16_gemm_workspace_bytes(G128, 64, 4100, 8192) == 3 * 64 * 4100 * 4
+    assert w.w4a16_gemm_workspace_bytes(G128, 64, 4097, 8192) == 0      # N % 4: no R-row kernel
+    assert w.w4a16_gemm_workspace_bytes(G128, 48, 14336, 4096) == 0     # 224 column blocks
     assert w.w4a16_gemm_workspace_bytes(ZP, 16, 4096, 14336) == 0
     g = w.w4a16_gemm
     assert _status(g, G128, BF16, FAKE, 300, FAKE, FAKE, FAKE, 256, 4096, FAKE, FAKE, need - 4, 0) == w.W4A16_ERR_INVALID

@@ -448,6 +448,30 @@ def test_matmul_small_n_splits_k(M, N, K, splits):
     refcheck.check(yv, refcheck.g128(x, rc, rs, rm), "bf16", f"gemv M={M} N={N}")
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(24, 4096, 8192, 4), (48, 4096, 14336, 4), (64, 4100, 8192, 3),
+                                          (17, 2048, 16384, 8)])
+def test_gemm_mid_rows_small_n_splits_k(M, N, K, splits):
+    """17..64 rows at small N with a workspace: the R-row kernels split K over blocks (whole
+    stages per split; a ragged last split at N = 4100, G = 64 over 3) and the partials are summed
+    in split order: against the oracle, bitwise repeatable, and the unsplit kernel (no workspace)
+    within the same bound."""
+    say(f"mid-rows K split M={M} N={N} K={K}")
+    assert w.w4a16_gemm_workspace_bytes(G128, M, N, K) == splits * M * N * 4
+    W = workloads.weights(N, K, outliers=True, seed=111)
+    x = workloads.activations(M, K, "bf16", seed=112)
+    rc, rs, rm = oracle.quantize_g128(W)
+    packed = (dev(rc), dev(rs), dev(rm))
+    ref = refcheck.g128(x, rc, rs, rm)
+    y = run_matmul(w.w4a16_gemm, G128, x, packed, N, K, BF16)
+    np.testing.assert_array_equal(y, run_matmul(w.w4a16_matmul, G128, x, packed, N, K, BF16))
+    err, worst = refcheck.check(bf16_f32(y), ref, "bf16", f"mid split M={M} N={N}")
+    say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
+    codes, scales, mins = packed
+    y0 = torch.full((M, N), NAN16, dtype=torch.int16, device="cuda")
+    w.w4a16_gemm(G128, BF16, dev(x), M, codes, scales, mins, N, K, y0, None, 0)
+    refcheck.check(bf16_f32(host(y0, np.uint16)), ref, "bf16", f"mid unsplit M={M} N={N}")
+
+
 def test_matmul_dispatch_matches_both_paths():
     N, K = 384, 1024
     W = workloads.weights(N, K, seed=24)
