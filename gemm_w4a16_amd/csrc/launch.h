@@ -91,18 +91,20 @@ inline bool midr_fits(int R, int64_t N, int64_t K) { return N % 4 == 0 && (K / 1
 // number fewer than 192 and the codes are at least 8 MiB, enough splits for 256 blocks, 2..8,
 // each a whole number of stages and at least 16 groups of K.
 struct MidSplit {
-    int splits, gps;
+    int splits, gps, rows;  // rows: the R-row kernel (32, or 64 also for 17..32 rows where
+                            // K / 128 is not a multiple of 4)
 };
 inline MidSplit mid_split(int64_t M, int64_t N, int64_t K) {
-    const int R = M <= 32 ? 32 : 64, gsz = R == 64 ? 2 : 4;  // groups per stage
+    const int R = M <= 32 && midr_fits(32, N, K) ? 32 : 64, gsz = R == 64 ? 2 : 4;  // groups per stage
     const int64_t nb = (N + 63) / 64, G = K / 128;
-    if (M <= kGemvMaxRows || M > 64 || !midr_fits(R, N, K) || nb >= 192 || N * K / 2 < ((int64_t)8 << 20)) return {1, 0};
+    if (M <= kGemvMaxRows || M > 64 || !midr_fits(R, N, K) || nb >= 192 || N * K / 2 < ((int64_t)8 << 20))
+        return {1, 0, R};
     int s = (int)(256 / nb);
     s = s < 2 ? 2 : (s > 8 ? 8 : s);
     while (s > 1 && G / s < 16) --s;
-    if (s <= 1) return {1, 0};
+    if (s <= 1) return {1, 0, R};
     const int gps = (int)((G + s - 1) / s + gsz - 1) / gsz * gsz;
-    return {(int)((G + gps - 1) / gps), gps};
+    return {(int)((G + gps - 1) / gps), gps, R};
 }
 inline size_t mid_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const MidSplit sp = mid_split(M, N, K);

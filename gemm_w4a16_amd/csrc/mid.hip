@@ -679,7 +679,7 @@ hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
 hipError_t launch_mid_g128_split(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                  const uint16_t* mins, int64_t N, int64_t K, uint16_t* y, float* ws, hipStream_t stream) {
     const MidSplit sp = mid_split(M, N, K);
-    if (M <= 32)
+    if (sp.rows == 32)
         launch_midr<32, false, false>(x, M, codes, scales, mins, N, K, y, stream, ws, sp.splits, sp.gps);
     else
         launch_midr<64, false, false>(x, M, codes, scales, mins, N, K, y, stream, ws, sp.splits, sp.gps);

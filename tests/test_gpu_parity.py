@@ -449,7 +449,9 @@ def test_matmul_small_n_splits_k(M, N, K, splits):
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(24, 4096, 8192, 4), (48, 4096, 14336, 4), (64, 4100, 8192, 3),
-                                          (17, 2048, 16384, 8)])
+                                          (17, 2048, 16384, 8),
+                                          # K / 128 = 86, not a multiple of 4: 32 rows on the 64-row kernel
+                                          (32, 4096, 11008, 4)])
 def test_gemm_mid_rows_small_n_splits_k(M, N, K, splits):
     """17..64 rows at small N with a workspace: the R-row kernels split K over blocks (whole
     stages per split; a ragged last split at N = 4100, G = 64 over 3) and the partials are summed
