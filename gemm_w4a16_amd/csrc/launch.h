@@ -88,8 +88,9 @@ hipError_t launch_rows64_prepared_zp(const uint16_t* x, int64_t M, bool act_f16,
 // others use the general kernels.
 inline bool midr_fits(int R, int64_t N, int64_t K) { return N % 4 == 0 && (K / 128) % (R == 64 ? 2 : 4) == 0; }
 // K split for the R-row kernels (17..64 rows, G128; splits 1: none): where their 64-column blocks
-// number fewer than 192 and the codes are at least 8 MiB, enough splits for 256 blocks, 2..8,
-// each a whole number of stages and at least 16 groups of K.
+// number at most 128 (so that two or more splits still fit one wave of 256 blocks; at N = 11008,
+// 172 blocks, a second wave made the split 1.5x slower) and the codes are at least 8 MiB, enough
+// splits for 256 blocks, 2..8, each a whole number of stages and at least 16 groups of K.
 struct MidSplit {
     int splits, gps, rows;  // rows: the R-row kernel (32, or 64 also for 17..32 rows where
                             // K / 128 is not a multiple of 4)
@@ -97,7 +98,7 @@ struct MidSplit {
 inline MidSplit mid_split(int64_t M, int64_t N, int64_t K) {
     const int R = M <= 32 && midr_fits(32, N, K) ? 32 : 64, gsz = R == 64 ? 2 : 4;  // groups per stage
     const int64_t nb = (N + 63) / 64, G = K / 128;
-    if (M <= kGemvMaxRows || M > 64 || !midr_fits(R, N, K) || nb >= 192 || N * K / 2 < ((int64_t)8 << 20))
+    if (M <= kGemvMaxRows || M > 64 || !midr_fits(R, N, K) || nb > 128 || N * K / 2 < ((int64_t)8 << 20))
         return {1, 0, R};
     int s = (int)(256 / nb);
     s = s < 2 ? 2 : (s > 8 ? 8 : s);

@@ -182,7 +182,7 @@ size_t w4a16_gemm_workspace_bytes(w4a16_format_t fmt, int64_t M, int64_t N, int6
  * dequantized (fmaf(q, s, m) rounded to bf16, as vidyal.ai Step 2 builds its B tile) and fed to the
  * matrix cores; otherwise, up to 64 rows, the factored per-group form of w4a16_gemv
  * (s * sum(x*(128+q)) + (min - 128 s) * sum(x), fp32) is used instead -- with K split over 2..8
- * blocks per 64 columns, the fp32 partials summed in split order, when N is small (fewer than 192
+ * blocks per 64 columns, the fp32 partials summed in split order, when N is small (at most 128
  * column blocks), the codes are at least 8 MiB and the workspace holds the partials
  * (w4a16_gemm_workspace_bytes); without one that path runs unsplit.  When a K
  * split is used, partial sums go to `workspace` and are added in a fixed order; every path is

@@ -149,6 +149,8 @@ def test_gemm_validation_and_workspace():
     assert w.w4a16_gemm_workspace_bytes(G128, 64, 4100, 8192) == 3 * 64 * 4100 * 4
     assert w.w4a16_gemm_workspace_bytes(G128, 64, 4097, 8192) == 0      # N % 4: no R-row kernel
     assert w.w4a16_gemm_workspace_bytes(G128, 48, 14336, 4096) == 0     # 224 column blocks
+    assert w.w4a16_gemm_workspace_bytes(G128, 32, 11008, 4096) == 0     # 172: two splits need two waves
+    assert w.w4a16_gemm_workspace_bytes(G128, 32, 8192, 4096) == 2 * 32 * 8192 * 4
     assert w.w4a16_gemm_workspace_bytes(G128, 32, 4096, 11008) == 4 * 32 * 4096 * 4  # on the 64-row kernel
     assert w.w4a16_gemm_workspace_bytes(ZP, 16, 4096, 14336) == 0
     g = w.w4a16_gemm
