@@ -135,7 +135,7 @@ __device__ __forceinline__ void load_params32(const float* __restrict__ p, int N
 // groups per pass.  kVec: N % TPL == 0 (vector loads of a lane's columns).  kF16: fp16
 // activations and output on the fp16 matrix cores, codes as 1024 + q (else bf16 and 128 + q).
 // kP32: scales and minimums are fp32 [K/128][N] (the prepared zero-point copy), else bf16.
-template <int MR, int TPL, int GPP, bool kVec, bool kF16 = false, bool kP32 = false>
+template <int MR, int TPL, int GPP, bool kVec, bool kF16 = false, bool kP32 = false, bool kSplit = false>
 __global__ __launch_bounds__(64 * kSkinnyWaves)
 __attribute__((amdgpu_waves_per_eu(kSkinnyWaves / 4, kSkinnyWaves / 4)))
 void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
@@ -156,9 +156,9 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     const int lane = lane_id(), wave = wave_id();
     const int lr = lane & 15, lg = lane >> 4;
     const int n0 = blockIdx.x * COLS;
-    // K split over blockIdx.y: this block's groups gs .. G - 1 (all of K when gridDim.y == 1)
-    const int gs = blockIdx.y * gps;
-    const int G = min(K >> 7, gs + gps);
+    // kSplit: K split over blockIdx.y, this block's groups gs .. G - 1; else all of K
+    const int gs = kSplit ? blockIdx.y * gps : 0;
+    const int G = kSplit ? min(K >> 7, gs + gps) : K >> 7;
     // this lane's TPL adjacent columns; a lane past N re-reads in-range columns, never stores
     int cbase = n0 + TPL * lr;
     if (kVec) cbase = min(cbase, N - TPL);
@@ -295,7 +295,7 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
 #pragma unroll
             for (int v = 0; v < kWaves; ++v)
                 sum += reinterpret_cast<const float*>(&xs[v][0][0][0])[row * COLS + c];
-            if (ws != nullptr)  // a K split's fp32 partial sums, [split][M][N]
+            if constexpr (kSplit)  // the split's fp32 partial sums, [split][M][N]
                 ws[((size_t)blockIdx.y * M + row) * N + n] = sum;
             else
                 y[(size_t)row * N + n] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
@@ -303,18 +303,18 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
     }
 }
 
-// splits > 1: K split over gridDim.y, fp32 partial sums to ws [splits][M][N] (y untouched).
-template <int MR, int TPL, int GPP, bool kF16, bool kP32>
+// kSplit: K split over gridDim.y (splits), fp32 partial sums to ws [splits][M][N] (y untouched).
+template <int MR, int TPL, int GPP, bool kF16, bool kP32, bool kSplit>
 void launch_gpp(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
                 int64_t N, int64_t K, uint16_t* y, float* ws, int splits, int gps, hipStream_t stream) {
     constexpr int COLS = 16 * TPL;
     constexpr uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
     const dim3 grid((unsigned)((N + COLS - 1) / COLS), (unsigned)splits), block(64 * kSkinnyWaves);
     if (N % TPL == 0)
-        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, true, kF16, kP32>), grid, block, 0, stream, x, codes, scales,
-                           mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
+        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, true, kF16, kP32, kSplit>), grid, block, 0, stream, x, codes,
+                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
     else
-        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, false, kF16, kP32>), grid, block, 0, stream, x, codes,
+        hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, false, kF16, kP32, kSplit>), grid, block, 0, stream, x, codes,
                            scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
 }
 
@@ -322,10 +322,18 @@ template <int MR, int TPL, bool kF16 = false, bool kP32 = false>
 void launch_mr(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
                int64_t N, int64_t K, uint16_t* y, hipStream_t stream, float* ws = nullptr, int splits = 1) {
     const int G = (int)(K >> 7), gps = (G + splits - 1) / splits;  // groups per split
-    if (gps <= kSkinnyWaves)
-        launch_gpp<MR, TPL, 1, kF16, kP32>(x, M, codes, scales, mins, N, K, y, ws, splits, gps, stream);
-    else
-        launch_gpp<MR, TPL, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, ws, splits, gps, stream);
+    if (splits > 1) {
+        if constexpr (!kF16 && !kP32) {  // the split serves the G128 path only
+            if (gps <= kSkinnyWaves)
+                launch_gpp<MR, TPL, 1, false, false, true>(x, M, codes, scales, mins, N, K, y, ws, splits, gps, stream);
+            else
+                launch_gpp<MR, TPL, 2, false, false, true>(x, M, codes, scales, mins, N, K, y, ws, splits, gps, stream);
+        }
+    } else if (gps <= kSkinnyWaves) {
+        launch_gpp<MR, TPL, 1, kF16, kP32, false>(x, M, codes, scales, mins, N, K, y, nullptr, 1, gps, stream);
+    } else {
+        launch_gpp<MR, TPL, 2, kF16, kP32, false>(x, M, codes, scales, mins, N, K, y, nullptr, 1, gps, stream);
+    }
 }
 
 }  // namespace
