@@ -49,7 +49,7 @@ WARM_SECONDS = 0.25            # untimed run-up of each workload before its time
 ROUNDS = 3                     # timed replays of a kernel's graph; the median is reported
 MIN_LAUNCHES = 100             # launches per timed replay (rounded up to whole rotations)
 METRIC = "W4A16 effective weight GB/s (% HBM peak) at M=1; TFLOPS (% MFMA) at M=1024"
-DECODE_KERNEL = "skinny_g128_kernel<1, 4, 2, true, false, false>"
+DECODE_KERNEL = "skinny_g128_kernel<1, 4, 2, true, false, false, false>"
 PREFILL_KERNEL = "gemm_g128_kernel<256, 224, 4, 1, 3, true, 1>"
 
 
