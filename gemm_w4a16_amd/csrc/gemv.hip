@@ -139,10 +139,12 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
             }
         };
         // The activations of the two blocks (L2-resident, read by every block) and the first steps'
-        // weight loads.  A wave's loads return in order, so with 4-bit codes the activations go
-        // first: behind the weights they held back the first step's math and with it the rolling
-        // window (zero-point decode shape 8.49 -> 7.90 us); the int8 codes keep the weights first
-        // (10.63 against 10.85 us).
+        // weight loads.  A wave's loads return in order, so where a wave has few row steps of 4-bit
+        // codes the activations go first: behind the weights they held back the first step's math
+        // and with it the rolling window (zero-point decode shape 8.49 -> 7.90 us).  The int8 codes
+        // keep the weights first (10.63 against 10.85 us), and so do long rows (Q4 16384^2 alike
+        // either way, and the activations held across the first loads spilled there).
+        constexpr bool kXFirst = !kW8 && kMySteps <= 4;
         GvStep r[kMySteps];
         constexpr int kXd = kBlockK / 8;  // 16-byte activation chunks per block
         u32x4_t xraw[2][kXd];
@@ -153,14 +155,13 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
                 for (int d = 0; d < kXd; ++d)
                     xraw[h][d] = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * kBlockK)[d];
         };
-        if constexpr (!kW8) {
+        if constexpr (kXFirst) {
             load_x();
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < kAhead; ++i) load(rg + kR * i, r[i]);
-        if constexpr (kW8) load_x();
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kXFirst) __builtin_amdgcn_sched_barrier(0);
         // The activations paired per 8 k, and the per-block constants that remove the magic offset
         // (and, for Q4, the code bias; see the top of this file).
         uint32_t xq[2][kXq];
@@ -168,12 +169,13 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const bool has = h ? has1 : has0;
+            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * kBlockK);
             float sum_a = 0.0f, sum_b = 0.0f;
             if constexpr (kW8) {
                 // per 4 k of a code dword: (x0, x2) and (x1, x3), which meet the byte pairs below
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
-                    const u32x4_t xl = xraw[h][d];
+                    const u32x4_t xl = kXFirst ? xraw[h][d] : xr[d];
                     const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
                     xq[h][4 * d + 0] = pack_lo(xv.x, xv.y);
                     xq[h][4 * d + 1] = pack_hi(xv.x, xv.y);
@@ -189,7 +191,7 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
             }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const u32x4_t xl = xraw[h][d];
+                const u32x4_t xl = kXFirst ? xraw[h][d] : xr[d];
                 const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
                 // (x0,x4) (x1,x5) (x2,x6) (x3,x7) of these 8 k
                 xq[h][4 * d + 0] = pack_lo(xv.x, xv.z);
