@@ -291,7 +291,9 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
                                                   static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
                                                   stream));
     }
-    if (M > 1 && act == W4A16_FP16) return launch_rowmajor_rows(fmt, x, M, codes, scales, mins, N, K, y, stream);
+    // two fp16 rows: one pass of the row-major GEMV with both rows (faster than the matrix-core
+    // kernel's 16-row pass); more rows: the matrix-core kernel
+    if (M > 2 && act == W4A16_FP16) return launch_rowmajor_rows(fmt, x, M, codes, scales, mins, N, K, y, stream);
     if (fmt == W4A16_FMT_W8_ROW_FP32)
         return from_hip(w4a16::launch_gemv_w8row(static_cast<const uint16_t*>(x), M, static_cast<const int8_t*>(codes),
                                                  static_cast<const float*>(scales), N, K, static_cast<uint16_t*>(y),

@@ -69,10 +69,17 @@ struct GvStep {
 // each row); W8 has 16 bytes per 16 k (signed bytes) and one scale per row.
 enum RowFmt { kRowQ4 = 0, kRowZP = 1, kRowW8 = 2 };
 
+// Code blocks per lane and row step: two (a K-slice of 32 blocks), or one (16 blocks) where a lane
+// carries two rows of 4-bit activations, whose paired fp16 values for two blocks would not fit in
+// the 128 VGPRs of a 1024-thread block beside the load window.
+__host__ __device__ constexpr int rowmajor_blocks_per_lane(int fmt, int mr) { return mr == 2 && fmt != kRowW8 ? 1 : 2; }
+
 // kF16: fp16 (else bf16) activations.  kFmt: kRowQ4 (a scale per block, decode (q - 8) s),
 // kRowZP (a scale and an fp16 zero point per group of 4 blocks, decode (q - z) s) or kRowW8 (int8
-// codes, one fp32 scale per row applied to the row's sum; fp16 activations only).
-template <bool kF16, int kFmt, int kS>
+// codes, one fp32 scale per row applied to the row's sum; fp16 activations only).  kMR: activation
+// rows (1 or 2, rows of x and y K and N elements apart) against one pass over the weights; each
+// unpacked word then feeds kMR dot products.
+template <bool kF16, int kFmt, int kS, int kMR>
 __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __restrict__ x,
                                                              const uint32_t* __restrict__ codes,
                                                              const uint16_t* __restrict__ scales,
@@ -84,8 +91,12 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
     constexpr int kXq = kBlockK / 2;          // paired activation dwords per block
     constexpr int kR = kGvWaves / kS;         // row groups
     constexpr int kMySteps = kGvSteps / kR;   // row steps per wave: rg, rg + kR, ...
-    constexpr int kAhead = kGvAhead < kMySteps ? kGvAhead : kMySteps;
-    __shared__ float part[kGvWaves][kGvRows];
+    constexpr int kNB = rowmajor_blocks_per_lane(kFmt, kMR);
+    constexpr int kSW = 16 * kNB;             // blocks per K-slice
+    // with one block per lane a step's loads are half as large: twice as many steps in flight
+    constexpr int kAheadW = kNB == 1 ? 2 * kGvAhead : kGvAhead;
+    constexpr int kAhead = kAheadW < kMySteps ? kAheadW : kMySteps;
+    __shared__ float part[kMR][kGvWaves][kGvRows];
     const int lane = lane_id(), wave = wave_id();
     const int sub = lane & 15;   // position along k inside the slice
     const int rsub = lane >> 4;  // which of the 4 rows of a step
@@ -106,13 +117,15 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
     asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "i"(kF16 ? kF16Magic : kBf16Magic));
 
     // Per-row partial of this wave; each K-slice a wave owns adds into its own LDS slot.
-    for (int t = threadIdx.x & 63; t < kGvRows; t += 64) part[wave][t] = 0.0f;
+    for (int t = threadIdx.x & 63; t < kGvRows; t += 64)
+#pragma unroll
+        for (int m = 0; m < kMR; ++m) part[m][wave][t] = 0.0f;
 
-    for (int slice = my_slice; slice * 32 < B; slice += kS) {
-        // this lane's two blocks, 16 apart: each load instruction of a row's 16 lanes then reads
+    for (int slice = my_slice; slice * kSW < B; slice += kS) {
+        // this lane's blocks, 16 apart: each load instruction of a row's 16 lanes then reads
         // 256 contiguous bytes (whole cache lines) rather than every other 16 bytes of 512
-        const int b0 = slice * 32 + sub, b1 = b0 + 16;
-        const bool has0 = b0 < B, has1 = b1 < B;
+        const int b0 = slice * kSW + sub, b1 = b0 + 16;
+        const bool has0 = b0 < B, has1 = kNB == 2 && b1 < B;
         // A block past the row's end is read at a clamped index and its contribution dropped by a
         // zero scale after the load: no load sits under a branch (a branch would make every load
         // wait for all earlier ones).
@@ -125,17 +138,19 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
             // byte offsets in 32 bits, so that each load is SGPR base + VGPR offset
             const uint32_t o0 = r * (uint32_t)B + (uint32_t)bb0, o1 = r * (uint32_t)B + (uint32_t)bb1;
             R.c[0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o0 * 16u));
-            R.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o1 * 16u));
+            if constexpr (kNB == 2) R.c[1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cblk + o1 * 16u));
             if constexpr (kW8) return;  // the row's scale is applied to its total
             const uint32_t p0 = kZP ? r * (uint32_t)G + (uint32_t)(bb0 >> 2) : o0;
             const uint32_t p1 = kZP ? r * (uint32_t)G + (uint32_t)(bb1 >> 2) : o1;
             const uint32_t s0 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + p0 * 2u));
-            const uint32_t s1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + p1 * 2u));
             R.s[0] = has0 ? s0 : 0u;  // fp16 +0: the block contributes nothing
-            R.s[1] = has1 ? s1 : 0u;
+            if constexpr (kNB == 2) {
+                const uint32_t s1 = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(sblk + p1 * 2u));
+                R.s[1] = has1 ? s1 : 0u;
+            }
             if constexpr (kZP) {
                 R.z[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zblk + p0 * 2u));
-                R.z[1] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zblk + p1 * 2u));
+                if constexpr (kNB == 2) R.z[1] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(zblk + p1 * 2u));
             }
         };
         // The activations of the two blocks (L2-resident, read by every block) and the first steps'
@@ -147,13 +162,16 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
         constexpr bool kXFirst = !kW8 && kMySteps <= 4;
         GvStep r[kMySteps];
         constexpr int kXd = kBlockK / 8;  // 16-byte activation chunks per block
-        u32x4_t xraw[2][kXd];
+        u32x4_t xraw[kMR][kNB][kXd];
         auto load_x = [&] {
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int m = 0; m < kMR; ++m)
 #pragma unroll
-                for (int d = 0; d < kXd; ++d)
-                    xraw[h][d] = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * kBlockK)[d];
+                for (int h = 0; h < kNB; ++h)
+#pragma unroll
+                    for (int d = 0; d < kXd; ++d)
+                        xraw[m][h][d] =
+                            reinterpret_cast<const u32x4_t*>(x + (size_t)m * K + (size_t)(h ? bb1 : bb0) * kBlockK)[d];
         };
         if constexpr (kXFirst) {
             load_x();
@@ -164,81 +182,91 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
         if constexpr (kXFirst) __builtin_amdgcn_sched_barrier(0);
         // The activations paired per 8 k, and the per-block constants that remove the magic offset
         // (and, for Q4, the code bias; see the top of this file).
-        uint32_t xq[2][kXq];
-        float cst[2][2], sx[2];
+        uint32_t xq[kMR][kNB][kXq];
+        float cst[kMR][kNB][2], sx[kMR][kNB];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int hm = 0; hm < kNB * kMR; ++hm) {
+            const int h = hm % kNB, m = hm / kNB;
             const bool has = h ? has1 : has0;
-            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)(h ? bb1 : bb0) * kBlockK);
+            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)m * K + (size_t)(h ? bb1 : bb0) * kBlockK);
             float sum_a = 0.0f, sum_b = 0.0f;
             if constexpr (kW8) {
                 // per 4 k of a code dword: (x0, x2) and (x1, x3), which meet the byte pairs below
 #pragma unroll
                 for (int d = 0; d < 2; ++d) {
-                    const u32x4_t xl = kXFirst ? xraw[h][d] : xr[d];
+                    const u32x4_t xl = kXFirst ? xraw[m][h][d] : xr[d];
                     const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
-                    xq[h][4 * d + 0] = pack_lo(xv.x, xv.y);
-                    xq[h][4 * d + 1] = pack_hi(xv.x, xv.y);
-                    xq[h][4 * d + 2] = pack_lo(xv.z, xv.w);
-                    xq[h][4 * d + 3] = pack_hi(xv.z, xv.w);
+                    xq[m][h][4 * d + 0] = pack_lo(xv.x, xv.y);
+                    xq[m][h][4 * d + 1] = pack_hi(xv.x, xv.y);
+                    xq[m][h][4 * d + 2] = pack_lo(xv.z, xv.w);
+                    xq[m][h][4 * d + 3] = pack_hi(xv.z, xv.w);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sum_a = dot2_f16(xq[h][4 * d + e], kF16OnePair, sum_a);
+                    for (int e = 0; e < 4; ++e) sum_a = dot2_f16(xq[m][h][4 * d + e], kF16OnePair, sum_a);
                 }
-                sx[h] = sum_a;
-                cst[h][0] = -1152.0f * sum_a;  // sum (1024 + 128 + q) x - 1152 sum x = sum q x
-                cst[h][1] = 0.0f;
+                sx[m][h] = sum_a;
+                cst[m][h][0] = -1152.0f * sum_a;  // sum (1024 + 128 + q) x - 1152 sum x = sum q x
+                cst[m][h][1] = 0.0f;
                 continue;
             }
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                const u32x4_t xl = kXFirst ? xraw[h][d] : xr[d];
+                const u32x4_t xl = kXFirst ? xraw[m][h][d] : xr[d];
                 const uint4 xv = has ? make_uint4(xl[0], xl[1], xl[2], xl[3]) : make_uint4(0, 0, 0, 0);
                 // (x0,x4) (x1,x5) (x2,x6) (x3,x7) of these 8 k
-                xq[h][4 * d + 0] = pack_lo(xv.x, xv.z);
-                xq[h][4 * d + 1] = pack_hi(xv.x, xv.z);
-                xq[h][4 * d + 2] = pack_lo(xv.y, xv.w);
-                xq[h][4 * d + 3] = pack_hi(xv.y, xv.w);
+                xq[m][h][4 * d + 0] = pack_lo(xv.x, xv.z);
+                xq[m][h][4 * d + 1] = pack_hi(xv.x, xv.z);
+                xq[m][h][4 * d + 2] = pack_lo(xv.y, xv.w);
+                xq[m][h][4 * d + 3] = pack_hi(xv.y, xv.w);
                 if (kF16) {
                     // even-position pairs (x0,x4), (x2,x6) meet 1024 + q; odd ones (x1,x5),
                     // (x3,x7) meet 1024 + 16q
-                    sum_a = dot2_f16(xq[h][4 * d + 0], kF16OnePair, sum_a);
-                    sum_a = dot2_f16(xq[h][4 * d + 2], kF16OnePair, sum_a);
-                    sum_b = dot2_f16(xq[h][4 * d + 1], kF16OnePair, sum_b);
-                    sum_b = dot2_f16(xq[h][4 * d + 3], kF16OnePair, sum_b);
+                    sum_a = dot2_f16(xq[m][h][4 * d + 0], kF16OnePair, sum_a);
+                    sum_a = dot2_f16(xq[m][h][4 * d + 2], kF16OnePair, sum_a);
+                    sum_b = dot2_f16(xq[m][h][4 * d + 1], kF16OnePair, sum_b);
+                    sum_b = dot2_f16(xq[m][h][4 * d + 3], kF16OnePair, sum_b);
                 } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sum_a = dot2_bf16(xq[h][4 * d + e], kBf16OnePair, sum_a);
+                    for (int e = 0; e < 4; ++e) sum_a = dot2_bf16(xq[m][h][4 * d + e], kBf16OnePair, sum_a);
                 }
             }
-            sx[h] = sum_a + sum_b;
+            sx[m][h] = sum_a + sum_b;
             if (kF16) {
                 // Q4: sum (1024 + q) x - 1032 sum x = sum (q - 8) x and
                 //     (sum (1024 + 16q) x - 1152 sum x) / 16 = sum (q - 8) x;
                 // zero point: the offsets 1024 only, z sum x is taken off per row
-                cst[h][0] = (kZP ? -1024.0f : -1032.0f) * sum_a;
-                cst[h][1] = (kZP ? -1024.0f : -1152.0f) * sum_b;
+                cst[m][h][0] = (kZP ? -1024.0f : -1032.0f) * sum_a;
+                cst[m][h][1] = (kZP ? -1024.0f : -1152.0f) * sum_b;
             } else {
-                cst[h][0] = (kZP ? -128.0f : -136.0f) * sum_a;  // 128 + q, less 128 (and the bias 8)
-                cst[h][1] = 0.0f;
+                cst[m][h][0] = (kZP ? -128.0f : -136.0f) * sum_a;  // 128 + q, less 128 (and the bias 8)
+                cst[m][h][1] = 0.0f;
             }
         }
         auto compute = [&](int t, const GvStep& R) {
-            float part_row = 0.0f;
+            float part_row[kMR];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float dot;
+            for (int m = 0; m < kMR; ++m) part_row[m] = 0.0f;
+#pragma unroll
+            for (int h = 0; h < kNB; ++h) {
+                float dot[kMR];
                 if constexpr (kW8) {
                     // Signed bytes with the top bit flipped are u = q + 128 in 0..255; OR-ed into
                     // the fp16 exponent of 1024 they are 1024 + u, exact: bytes 0 and 2 of a
                     // dword with mask 0x00FF00FF, bytes 1 and 3 after a shift by 8.
-                    float acc = cst[h][0];
+                    float acc[kMR];
+#pragma unroll
+                    for (int m = 0; m < kMR; ++m) acc[m] = cst[m][h][0];
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const uint32_t u = R.c[h][d] ^ 0x80808080u;
-                        acc = dot2_f16((u & mask_lo) | magic_v, xq[h][2 * d + 0], acc);
-                        acc = dot2_f16(((u >> 8) & mask_lo) | magic_v, xq[h][2 * d + 1], acc);
+                        const uint32_t u0 = (u & mask_lo) | magic_v, u1 = ((u >> 8) & mask_lo) | magic_v;
+#pragma unroll
+                        for (int m = 0; m < kMR; ++m) {
+                            acc[m] = dot2_f16(u0, xq[m][h][2 * d + 0], acc[m]);
+                            acc[m] = dot2_f16(u1, xq[m][h][2 * d + 1], acc[m]);
+                        }
                     }
-                    part_row += acc;
+#pragma unroll
+                    for (int m = 0; m < kMR; ++m) part_row[m] += acc[m];
                     continue;
                 }
                 if (kF16) {
@@ -246,31 +274,52 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
                     // of 1024 OR-ed in, mask 0x000F000F keeps k = 0 and 4 as 1024 + q and mask
                     // 0x00F000F0 keeps k = 1 and 5 as 1024 + 16q, both exact; the word shifted
                     // by 8 gives k = 2, 6 and 3, 7 the same way: five instructions per 8 codes.
-                    float acc_a = cst[h][0], acc_b = cst[h][1];
+                    float acc_a[kMR], acc_b[kMR];
+#pragma unroll
+                    for (int m = 0; m < kMR; ++m) acc_a[m] = cst[m][h][0], acc_b[m] = cst[m][h][1];
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
                         const uint32_t w = R.c[h][d], w8 = w >> 8;
-                        acc_a = dot2_f16((w & mask_lo) | magic_v, xq[h][4 * d + 0], acc_a);
-                        acc_b = dot2_f16((w & mask_hi) | magic_v, xq[h][4 * d + 1], acc_b);
-                        acc_a = dot2_f16((w8 & mask_lo) | magic_v, xq[h][4 * d + 2], acc_a);
-                        acc_b = dot2_f16((w8 & mask_hi) | magic_v, xq[h][4 * d + 3], acc_b);
+                        const uint32_t u0 = (w & mask_lo) | magic_v, u1 = (w & mask_hi) | magic_v;
+                        const uint32_t u2 = (w8 & mask_lo) | magic_v, u3 = (w8 & mask_hi) | magic_v;
+#pragma unroll
+                        for (int m = 0; m < kMR; ++m) {
+                            acc_a[m] = dot2_f16(u0, xq[m][h][4 * d + 0], acc_a[m]);
+                            acc_b[m] = dot2_f16(u1, xq[m][h][4 * d + 1], acc_b[m]);
+                            acc_a[m] = dot2_f16(u2, xq[m][h][4 * d + 2], acc_a[m]);
+                            acc_b[m] = dot2_f16(u3, xq[m][h][4 * d + 3], acc_b[m]);
+                        }
                     }
-                    dot = __builtin_fmaf(acc_b, 0.0625f, acc_a);
+#pragma unroll
+                    for (int m = 0; m < kMR; ++m) dot[m] = __builtin_fmaf(acc_b[m], 0.0625f, acc_a[m]);
                 } else {
-                    float acc = cst[h][0];
+                    float acc[kMR];
+#pragma unroll
+                    for (int m = 0; m < kMR; ++m) acc[m] = cst[m][h][0];
 #pragma unroll
                     for (int d = 0; d < 4; ++d)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc = dot2_bf16(((R.c[h][d] >> (4 * e)) & mask_lo) | magic_v, xq[h][4 * d + e], acc);
-                    dot = acc;
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t u = ((R.c[h][d] >> (4 * e)) & mask_lo) | magic_v;
+#pragma unroll
+                            for (int m = 0; m < kMR; ++m) acc[m] = dot2_bf16(u, xq[m][h][4 * d + e], acc[m]);
+                        }
+#pragma unroll
+                    for (int m = 0; m < kMR; ++m) dot[m] = acc[m];
                 }
-                if constexpr (kZP) dot = __builtin_fmaf(-f16_bits_to_f32(R.z[h]), sx[h], dot);
-                part_row = __builtin_fmaf(f16_bits_to_f32(R.s[h]), dot, part_row);
+                const float sc = f16_bits_to_f32(R.s[h]);
+#pragma unroll
+                for (int m = 0; m < kMR; ++m) {
+                    if constexpr (kZP) dot[m] = __builtin_fmaf(-f16_bits_to_f32(R.z[h]), sx[m][h], dot[m]);
+                    part_row[m] = __builtin_fmaf(sc, dot[m], part_row[m]);
+                }
             }
             // the 16 lanes of a row -> one value, added to this wave's slot for the row
-            const float v = row16_sum(part_row);
-            if (sub == 15) part[wave][4 * t + rsub] += v;
+#pragma unroll
+            for (int m = 0; m < kMR; ++m) {
+                const float v = row16_sum(part_row[m]);
+                if (sub == 15) part[m][wave][4 * t + rsub] += v;
+            }
         };
         // A rolling window: the loads of step i + kAhead are issued before the math of step i.
 #pragma unroll
@@ -285,33 +334,49 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
     // the 16 waves' partials of each row (zero where a wave has no part in it), added through LDS
     // in a fixed order
     __syncthreads();
-    const int t = threadIdx.x;
-    if (t < kGvRows && n0 + t < N) {
+    const int t = threadIdx.x & 63, m = threadIdx.x >> 6;
+    if (m < kMR && n0 + t < N) {
         float sum = 0.0f;
 #pragma unroll
-        for (int v = 0; v < kGvWaves; ++v) sum += part[v][t];
+        for (int v = 0; v < kGvWaves; ++v) sum += part[m][v][t];
         if constexpr (kW8) sum *= reinterpret_cast<const float*>(scales)[n0 + t];
-        y[n0 + t] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
+        y[(size_t)m * N + n0 + t] = kF16 ? f32_to_f16_bits(sum) : f32_to_bf16_bits(sum);
     }
 }
 
-template <bool kF16, int kFmt>
+template <bool kF16, int kFmt, int kMR>
 void launch_rowmajor(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros,
                      int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), block(1024);
-    // K-slices of 32 blocks: as many as K has, rounded up to a power of two, at most 16
-    const int64_t slices = (K / (kFmt == kRowW8 ? 16 : 32) + 31) / 32;
+    // K-slices of 16 or 32 blocks: as many as K has, rounded up to a power of two, at most 16
+    constexpr int kSW = 16 * rowmajor_blocks_per_lane(kFmt, kMR);
+    const int64_t slices = (K / (kFmt == kRowW8 ? 16 : 32) + kSW - 1) / kSW;
     const int n = (int)N, k = (int)K;
     if (slices >= 9)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 16>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 16, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else if (slices >= 5)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 8>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 8, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else if (slices >= 3)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 4>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 4, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else if (slices == 2)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 2>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 2, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
     else
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 1>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 1, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+}
+
+// M activation rows in passes of two over the weights (the last pass one row when M is odd).
+template <bool kF16, int kFmt>
+hipError_t launch_rowmajor_rows(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
+                                const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+    for (int64_t m = 0; m < M; m += 2) {
+        if (M - m >= 2)
+            launch_rowmajor<kF16, kFmt, 2>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+        else
+            launch_rowmajor<kF16, kFmt, 1>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -319,40 +384,21 @@ void launch_rowmajor(const uint16_t* x, const uint32_t* codes, const uint16_t* s
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
     const uint32_t* words = reinterpret_cast<const uint32_t*>(codes);
-    for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
-        if (act_f16)
-            launch_rowmajor<true, kRowQ4>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
-        else
-            launch_rowmajor<false, kRowQ4>(x + m * K, words, scales, nullptr, N, K, y + m * N, stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return act_f16 ? launch_rowmajor_rows<true, kRowQ4>(x, M, words, scales, nullptr, N, K, y, stream)
+                   : launch_rowmajor_rows<false, kRowQ4>(x, M, words, scales, nullptr, N, K, y, stream);
 }
 
 hipError_t launch_gemv_g128zp(const uint16_t* x, int64_t M, bool act_f16, const uint32_t* codes,
                               const uint16_t* scales, const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y,
                               hipStream_t stream) {
-    for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
-        if (act_f16)
-            launch_rowmajor<true, kRowZP>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
-        else
-            launch_rowmajor<false, kRowZP>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return act_f16 ? launch_rowmajor_rows<true, kRowZP>(x, M, codes, scales, zeros, N, K, y, stream)
+                   : launch_rowmajor_rows<false, kRowZP>(x, M, codes, scales, zeros, N, K, y, stream);
 }
 
 hipError_t launch_gemv_w8row(const uint16_t* x, int64_t M, const int8_t* codes, const float* scales, int64_t N,
                              int64_t K, uint16_t* y, hipStream_t stream) {
-    for (int64_t m = 0; m < M; ++m) {  // one pass per activation row
-        launch_rowmajor<true, kRowW8>(x + m * K, reinterpret_cast<const uint32_t*>(codes),
-                                      reinterpret_cast<const uint16_t*>(scales), nullptr, N, K, y + m * N, stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return hipSuccess;
+    return launch_rowmajor_rows<true, kRowW8>(x, M, reinterpret_cast<const uint32_t*>(codes),
+                                              reinterpret_cast<const uint16_t*>(scales), nullptr, N, K, y, stream);
 }
 
 }  // namespace w4a16

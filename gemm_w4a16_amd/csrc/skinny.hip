@@ -128,7 +128,7 @@ __device__ __forceinline__ void load_params32(const float* __restrict__ p, int N
     }
 }
 
-// MR: activation rows staged (M <= MR; 1, 4, 8 or 16).  TPL: adjacent columns per lane (4 or 2),
+// MR: activation rows staged (M <= MR; 1, 2, 4, 8 or 16).  TPL: adjacent columns per lane (4 or 2),
 // i.e. 16 * TPL columns per block.  GPP: groups of 128 k per wave and pass (a pass of the 16 waves
 // covers 16 * GPP groups: 2 for K > 2048, where one pass covers K = 4096; 1 up to K = 2048, where
 // a second group per wave would only repeat a clamped one)
@@ -351,11 +351,13 @@ void launch_rows(const uint16_t* x, int64_t M, const uint32_t* codes, const void
     const int tpl = W4A16_SKINNY_TPL ? W4A16_SKINNY_TPL : ((N + 63) / 64 >= 192 ? 4 : 2);
     if (tpl == 4) {
         if (M == 1) launch_mr<1, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else if (M == 2) launch_mr<2, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else if (M <= 4) launch_mr<4, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else if (M <= 8) launch_mr<8, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else launch_mr<16, 4, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
     } else {
         if (M == 1) launch_mr<1, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
+        else if (M == 2) launch_mr<2, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else if (M <= 4) launch_mr<4, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else if (M <= 8) launch_mr<8, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
         else launch_mr<16, 2, kF16, kP32>(x, M, codes, scales, mins, N, K, y, stream);
@@ -374,6 +376,7 @@ hipError_t launch_skinny_g128_split(const uint16_t* x, int64_t M, const uint32_t
                                     hipStream_t stream) {
     // 64-column blocks times `splits` K-slices, then the partials summed in split order
     if (M == 1) launch_mr<1, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
+    else if (M == 2) launch_mr<2, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
     else if (M <= 4) launch_mr<4, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
     else if (M <= 8) launch_mr<8, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
     else launch_mr<16, 4>(x, M, codes, scales, mins, N, K, y, stream, ws, splits);
