@@ -291,9 +291,10 @@ w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, 
                                                   static_cast<const uint16_t*>(mins), N, K, static_cast<uint16_t*>(y),
                                                   stream));
     }
-    // two fp16 rows: one pass of the row-major GEMV with both rows (faster than the matrix-core
-    // kernel's 16-row pass); more rows: the matrix-core kernel
-    if (M > 2 && act == W4A16_FP16) return launch_rowmajor_rows(fmt, x, M, codes, scales, mins, N, K, y, stream);
+    // up to four fp16 rows (two for the zero-point format): one pass of the row-major GEMV with
+    // all of them (faster than the matrix-core kernel's 16-row pass); more rows: the matrix cores
+    const int64_t gemv_rows = fmt == W4A16_FMT_G128_ZP_FP16 ? w4a16::kRowGemvRowsZP : w4a16::kRowGemvRows;
+    if (M > gemv_rows && act == W4A16_FP16) return launch_rowmajor_rows(fmt, x, M, codes, scales, mins, N, K, y, stream);
     if (fmt == W4A16_FMT_W8_ROW_FP32)
         return from_hip(w4a16::launch_gemv_w8row(static_cast<const uint16_t*>(x), M, static_cast<const int8_t*>(codes),
                                                  static_cast<const float*>(scales), N, K, static_cast<uint16_t*>(y),

@@ -72,19 +72,20 @@ enum RowFmt { kRowQ4 = 0, kRowZP = 1, kRowW8 = 2 };
 // Code blocks per lane and row step: two (a K-slice of 32 blocks), or one (16 blocks) where a lane
 // carries two rows of 4-bit activations, whose paired fp16 values for two blocks would not fit in
 // the 128 VGPRs of a 1024-thread block beside the load window.
-__host__ __device__ constexpr int rowmajor_blocks_per_lane(int fmt, int mr) { return mr == 2 && fmt != kRowW8 ? 1 : 2; }
+__host__ __device__ constexpr int rowmajor_blocks_per_lane(int fmt, int mr) { return mr >= 4 || (mr == 2 && fmt != kRowW8) ? 1 : 2; }
 
 // kF16: fp16 (else bf16) activations.  kFmt: kRowQ4 (a scale per block, decode (q - 8) s),
 // kRowZP (a scale and an fp16 zero point per group of 4 blocks, decode (q - z) s) or kRowW8 (int8
 // codes, one fp32 scale per row applied to the row's sum; fp16 activations only).  kMR: activation
-// rows (1 or 2, rows of x and y K and N elements apart) against one pass over the weights; each
+// rows (1, 2 or 4; rows of x and y K and N elements apart) against one pass over the weights, of
+// which the first `rows` are real (a row past them repeats the last one and is not stored); each
 // unpacked word then feeds kMR dot products.
 template <bool kF16, int kFmt, int kS, int kMR>
 __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __restrict__ x,
                                                              const uint32_t* __restrict__ codes,
                                                              const uint16_t* __restrict__ scales,
                                                              const uint16_t* __restrict__ zeros,
-                                                             uint16_t* __restrict__ y, int N, int K) {
+                                                             uint16_t* __restrict__ y, int N, int K, int rows) {
     constexpr bool kZP = kFmt == kRowZP, kW8 = kFmt == kRowW8;
     static_assert(!kW8 || kF16, "int8 codes need fp16 activations (1024 + u with u < 256)");
     constexpr int kBlockK = kW8 ? 16 : 32;    // k per 16-byte block of codes
@@ -93,8 +94,9 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
     constexpr int kMySteps = kGvSteps / kR;   // row steps per wave: rg, rg + kR, ...
     constexpr int kNB = rowmajor_blocks_per_lane(kFmt, kMR);
     constexpr int kSW = 16 * kNB;             // blocks per K-slice
-    // with one block per lane a step's loads are half as large: twice as many steps in flight
-    constexpr int kAheadW = kNB == 1 ? 2 * kGvAhead : kGvAhead;
+    // with one block per lane a step's loads are half as large: twice as many steps in flight, but
+    // for two rows only (four rows' activations leave no registers for them)
+    constexpr int kAheadW = kNB == 1 && kMR <= 2 ? 2 * kGvAhead : kGvAhead;
     constexpr int kAhead = kAheadW < kMySteps ? kAheadW : kMySteps;
     __shared__ float part[kMR][kGvWaves][kGvRows];
     const int lane = lane_id(), wave = wave_id();
@@ -170,8 +172,8 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
                 for (int h = 0; h < kNB; ++h)
 #pragma unroll
                     for (int d = 0; d < kXd; ++d)
-                        xraw[m][h][d] =
-                            reinterpret_cast<const u32x4_t*>(x + (size_t)m * K + (size_t)(h ? bb1 : bb0) * kBlockK)[d];
+                        xraw[m][h][d] = reinterpret_cast<const u32x4_t*>(x + (size_t)min(m, rows - 1) * K +
+                                                                         (size_t)(h ? bb1 : bb0) * kBlockK)[d];
         };
         if constexpr (kXFirst) {
             load_x();
@@ -188,7 +190,8 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
         for (int hm = 0; hm < kNB * kMR; ++hm) {
             const int h = hm % kNB, m = hm / kNB;
             const bool has = h ? has1 : has0;
-            const u32x4_t* xr = reinterpret_cast<const u32x4_t*>(x + (size_t)m * K + (size_t)(h ? bb1 : bb0) * kBlockK);
+            const u32x4_t* xr =
+                reinterpret_cast<const u32x4_t*>(x + (size_t)min(m, rows - 1) * K + (size_t)(h ? bb1 : bb0) * kBlockK);
             float sum_a = 0.0f, sum_b = 0.0f;
             if constexpr (kW8) {
                 // per 4 k of a code dword: (x0, x2) and (x1, x3), which meet the byte pairs below
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
     // in a fixed order
     __syncthreads();
     const int t = threadIdx.x & 63, m = threadIdx.x >> 6;
-    if (m < kMR && n0 + t < N) {
+    if (m < rows && n0 + t < N) {
         float sum = 0.0f;
 #pragma unroll
         for (int v = 0; v < kGvWaves; ++v) sum += part[m][v][t];
@@ -346,33 +349,40 @@ __global__ __launch_bounds__(1024) void gemv_rowmajor_kernel(const uint16_t* __r
 
 template <bool kF16, int kFmt, int kMR>
 void launch_rowmajor(const uint16_t* x, const uint32_t* codes, const uint16_t* scales, const uint16_t* zeros,
-                     int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+                     int64_t N, int64_t K, uint16_t* y, int rows, hipStream_t stream) {
     const dim3 grid((unsigned)((N + kGvRows - 1) / kGvRows)), block(1024);
     // K-slices of 16 or 32 blocks: as many as K has, rounded up to a power of two, at most 16
     constexpr int kSW = 16 * rowmajor_blocks_per_lane(kFmt, kMR);
     const int64_t slices = (K / (kFmt == kRowW8 ? 16 : 32) + kSW - 1) / kSW;
     const int n = (int)N, k = (int)K;
     if (slices >= 9)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 16, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 16, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k, rows);
     else if (slices >= 5)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 8, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 8, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k, rows);
     else if (slices >= 3)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 4, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 4, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k, rows);
     else if (slices == 2)
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 2, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 2, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k, rows);
     else
-        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 1, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k);
+        hipLaunchKernelGGL((gemv_rowmajor_kernel<kF16, kFmt, 1, kMR>), grid, block, 0, stream, x, codes, scales, zeros, y, n, k, rows);
 }
 
-// M activation rows in passes of two over the weights (the last pass one row when M is odd).
+// M activation rows in passes of kRowGemvRows(format) over the weights (a last pass of three rows
+// as a four-row pass, of two or one row as such).
 template <bool kF16, int kFmt>
 hipError_t launch_rowmajor_rows(const uint16_t* x, int64_t M, const uint32_t* codes, const uint16_t* scales,
                                 const uint16_t* zeros, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-    for (int64_t m = 0; m < M; m += 2) {
-        if (M - m >= 2)
-            launch_rowmajor<kF16, kFmt, 2>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
-        else
-            launch_rowmajor<kF16, kFmt, 1>(x + m * K, codes, scales, zeros, N, K, y + m * N, stream);
+    constexpr int kMax = kFmt == kRowZP ? kRowGemvRowsZP : kRowGemvRows;
+    for (int64_t m = 0; m < M; m += kMax) {
+        const int rows = (int)(M - m < kMax ? M - m : kMax);
+        if (rows >= 3) {
+            if constexpr (kMax >= 4)
+                launch_rowmajor<kF16, kFmt, 4>(x + m * K, codes, scales, zeros, N, K, y + m * N, rows, stream);
+        } else if (rows == 2) {
+            launch_rowmajor<kF16, kFmt, 2>(x + m * K, codes, scales, zeros, N, K, y + m * N, rows, stream);
+        } else {
+            launch_rowmajor<kF16, kFmt, 1>(x + m * K, codes, scales, zeros, N, K, y + m * N, rows, stream);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -66,8 +66,12 @@ inline size_t skinny_split_workspace_bytes(int64_t M, int64_t N, int64_t K) {
     const int s = skinny_splits(M, N, K);
     return s > 1 ? (size_t)s * (size_t)M * (size_t)N * 4 : 0;
 }
-// Q4 path, two activation rows per pass over the weights; act_f16: fp16 (true) or bf16 (false)
-// activations.  (The zero-point and W8 GEMVs above pass over the weights the same way.)
+// Rows of activations that the row-major GEMV takes against one pass over the weights: four for
+// Q4 and W8, two for the zero-point format (whose four-row form spills registers).
+constexpr int kRowGemvRows = 4;
+constexpr int kRowGemvRowsZP = 2;
+// Q4 path, kRowGemvRows activation rows per pass over the weights; act_f16: fp16 (true) or bf16
+// (false) activations.  (The zero-point and W8 GEMVs above pass over the weights the same way.)
 hipError_t launch_gemv_q4b32(const uint16_t* x, int64_t M, bool act_f16, const uint8_t* codes,
                              const uint16_t* scales, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 

@@ -153,12 +153,13 @@ w4a16_status_t w4a16_dequant(w4a16_format_t fmt, const void* codes, const void* 
  * (the factored form s * sum(x*q) + min * sum(x) that vidyal.ai's M = 1 kernel uses, section
  * "How the measurements were taken"; P3's one-row-per-warp GEMV, "Writing a GEMV kernel").
  * act: BF16 for G128; FP16 (or BF16) for Q4 and the zero-point format; FP16 for W8.  For Q4,
- * the zero-point format and W8, one or two rows of fp16 activations take the row-major GEMV (dot2
- * with the scale applied once per block, both rows against one weight pass); three or more fp16
- * rows share one weight pass per 16 rows on the fp16 matrix cores: Q4 and W8 dequantized to fp16
- * in registers ((q - 8) s rounded once, or q exactly, the W8 row scale applied to each total), the
- * zero-point format in the factored per-group form s * sum(x*(1024+q)) - (1024 + z) s * sum(x) in
- * fp32; bf16 activations run one weight pass per two rows.  y has
+ * the zero-point format and W8, up to four rows of fp16 activations (two for the zero-point
+ * format) take the row-major GEMV (dot2 with the scale applied once per block, all rows against
+ * one weight pass); more fp16 rows share one weight pass per 16 rows on the fp16 matrix cores: Q4
+ * and W8 dequantized to fp16 in registers ((q - 8) s rounded once, or q exactly, the W8 row scale
+ * applied to each total), the zero-point format in the factored per-group form
+ * s * sum(x*(1024+q)) - (1024 + z) s * sum(x) in fp32; bf16 activations run one weight pass per
+ * four rows (two for the zero-point format).  y has
  * the activation dtype, rounded to nearest even from fp32.  Row-major x and y; x, y 16-byte
  * aligned. */
 w4a16_status_t w4a16_gemv(w4a16_format_t fmt, w4a16_dtype_t act, const void* x, int64_t M,

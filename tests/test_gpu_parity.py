@@ -835,12 +835,16 @@ def _rowfmt_pack(fmt, W):
 
 
 @pytest.mark.parametrize("fmt", [Q4, ZP, W8])
-@pytest.mark.parametrize("M,N,K", [(2, 1000, 1152), (3, 65, 4224), (8, 1000, 1152), (16, 130, 2048), (17, 1000, 1152),
+@pytest.mark.parametrize("M,N,K", [(2, 1000, 1152), (3, 65, 4224), (4, 1000, 1152), (4, 200, 16384), (3, 70, 8320),
+                                   (8, 1000, 1152), (16, 130, 2048), (17, 1000, 1152),
                                    (33, 200, 640), (64, 1000, 1152), (65, 70, 1152), (130, 300, 512)])
 def test_rowmajor_formats_many_rows(fmt, M, N, K):
     """Ragged N (64-row blocks), K with a partial last unit of 4 blocks for Q4 and W8 (1152 = 36
-    Q4 blocks, 72 W8 blocks; 4224 = 132 and 264), one to three activation tiles of 16 rows, and
-    above 64 rows two passes over the weights.  Every output element-wise against the oracle."""
+    Q4 blocks, 72 W8 blocks; 4224 = 132 and 264), the row-major GEMV's multi-row passes (two rows
+    for the zero-point format, up to four for Q4 and W8, three of four real; K = 16384 and 8320
+    give each wave several K-slices, the last one partial), one to three activation tiles of 16
+    rows, and above 64 rows two passes over the weights.  Every output element-wise against the
+    oracle."""
     say(f"rowmajor many rows fmt={fmt} M={M} N={N} K={K}")
     W = workloads.weights(N, K, outliers=True, seed=300 + M + fmt)
     x = workloads.activations(M, K, "f16", seed=301 + M)
@@ -865,7 +869,7 @@ def test_rowmajor_ragged_last_unit(fmt, M):
     refcheck.check(workloads.bits_to_f32(y, "f16"), ref(x), "f16", f"ragged fmt={fmt} M={M}")
 
 
-@pytest.mark.parametrize("fmt,M", [(ZP, 2), (ZP, 8), (ZP, 16), (ZP, 64), (W8, 16), (Q4, 16)])
+@pytest.mark.parametrize("fmt,M", [(ZP, 2), (ZP, 8), (ZP, 16), (ZP, 64), (W8, 3), (W8, 16), (Q4, 4), (Q4, 16)])
 def test_rowmajor_decode_shape_many_rows(decode_weights, fmt, M):
     """The decode weights (K = 4096, N = 14336, with outliers) in the zero-point and W8 formats,
     and Q4, with 2 to 64 rows of fp16 activations, as the benchmark runs them."""
@@ -879,8 +883,30 @@ def test_rowmajor_decode_shape_many_rows(decode_weights, fmt, M):
     say(f"  rel err {err:.3e}, worst element at {worst:.2f} of its bound")
 
 
+@pytest.mark.parametrize("fmt", [Q4, ZP])
+@pytest.mark.parametrize("M", [5, 6, 7, 16])
+def test_rowmajor_bf16_row_passes(fmt, M):
+    """bf16 activations with the 4-bit row-major formats: passes of up to four rows (two for the
+    zero-point format) over the weights, the last one with one, two or three rows; every output
+    element-wise against the oracle, and the same bits as the one-row passes give each row."""
+    N, K = 300, 2176
+    say(f"rowmajor bf16 row passes fmt={fmt} M={M}")
+    W = workloads.weights(N, K, outliers=True, seed=330 + fmt)
+    x = workloads.activations(M, K, "bf16", seed=331 + M)
+    if fmt == Q4:
+        rc, rs = oracle.quantize_q4b32(W)
+        packed, ref = (dev(rc), dev(rs), None), refcheck.q4b32(x, rc, rs, x_kind="bf16")
+    else:
+        rc, rs, rz = oracle.quantize_g128zp(W)
+        packed, ref = (dev(rc), dev(rs), dev(rz)), refcheck.g128zp(x, rc, rs, rz, x_kind="bf16")
+    y = run_matmul(w.w4a16_gemv, fmt, x, packed, N, K, BF16)
+    refcheck.check(workloads.bits_to_f32(y, "bf16"), ref, "bf16", f"bf16 rows fmt={fmt} M={M}")
+    for m in (0, M - 1):
+        np.testing.assert_array_equal(run_matmul(w.w4a16_gemv, fmt, x[m:m + 1], packed, N, K, BF16)[0], y[m])
+
+
 def test_rowmajor_bf16_rows_rejected_above_gemv():
-    """bf16 activations with the row-major formats run one GEMV pass per row up to 16 rows; the
+    """bf16 activations with the row-major formats run on the row-major GEMV up to 16 rows; the
     large-M path takes fp16 activations only."""
     N, K = 64, 128
     W = workloads.weights(N, K, seed=310)
