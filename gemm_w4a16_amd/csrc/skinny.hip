@@ -38,7 +38,8 @@ constexpr uint32_t kF16Magic = 0x64006400u;   // fp16 1024.0 in both halves
 // small, so that there are more blocks; two of them per CU would halve the register budget and
 // spill, for a grid that rarely exceeds the CU count.)
 
-// `mask` and `magic` arrive as kernel arguments (0x000F000F and 0x43004300) so that they sit in
+// `mask` arrives as a kernel argument (0x000F000F) and `magic` (0x43004300) is set by a v_mov of an
+// immediate, both opaque to the compiler, so that they sit in
 // registers and each pair is one v_and_or_b32 (VOP3 cannot take a literal on gfx9).
 __device__ __forceinline__ bf16x8_t unpack_b_fragment(uint32_t w, uint32_t mask, uint32_t magic) {
     const u32x4_t p = {(w & mask) | magic, ((w >> 4) & mask) | magic, ((w >> 8) & mask) | magic,
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves)
 __attribute__((amdgpu_waves_per_eu(kSkinnyWaves / 4, kSkinnyWaves / 4)))
 void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ codes,
                         const void* __restrict__ scales_v, const void* __restrict__ mins_v,
-                        uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask, uint32_t magic,
+                        uint16_t* __restrict__ y, int M, int N, int K, uint32_t mask,
                         float* __restrict__ ws, int gps) {
     const uint16_t* __restrict__ scales = static_cast<const uint16_t*>(scales_v);
     const uint16_t* __restrict__ mins = static_cast<const uint16_t*>(mins_v);
@@ -174,10 +175,12 @@ void skinny_g128_kernel(const uint16_t* __restrict__ x, const uint32_t* __restri
 #pragma unroll
         for (int e = 0; e < E; ++e) yacc[t][e] = 0.0f;
 
-    // the magic exponent in a VGPR (the mask stays in an SGPR): one v_and_or_b32 per pair
-    uint32_t magic_v;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(magic_v) : "s"(magic));
-    magic = magic_v;
+    // the magic exponent in a VGPR (the mask stays in an SGPR): one v_and_or_b32 per pair.  An
+    // immediate rather than an argument: every argument an unsplit launch reads then fits the 14
+    // dwords that are preloaded into SGPRs, so a wave issues its loads without a kernel-argument
+    // fetch first.
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(magic) : "i"(kF16 ? kF16Magic : kBf16Magic));
     constexpr uint32_t kOne = kF16 ? 0x3C003C00u : 0x3F803F80u;  // 1.0 in both halves
     const u32x4_t ones_u = {kOne, kOne, kOne, kOne};
     const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, ones_u);
@@ -308,14 +311,13 @@ template <int MR, int TPL, int GPP, bool kF16, bool kP32, bool kSplit>
 void launch_gpp(const uint16_t* x, int64_t M, const uint32_t* codes, const void* scales, const void* mins,
                 int64_t N, int64_t K, uint16_t* y, float* ws, int splits, int gps, hipStream_t stream) {
     constexpr int COLS = 16 * TPL;
-    constexpr uint32_t magic = kF16 ? kF16Magic : kBf16Magic;
     const dim3 grid((unsigned)((N + COLS - 1) / COLS), (unsigned)splits), block(64 * kSkinnyWaves);
     if (N % TPL == 0)
         hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, true, kF16, kP32, kSplit>), grid, block, 0, stream, x, codes,
-                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
+                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, ws, gps);
     else
         hipLaunchKernelGGL((skinny_g128_kernel<MR, TPL, GPP, false, kF16, kP32, kSplit>), grid, block, 0, stream, x, codes,
-                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, magic, ws, gps);
+                           scales, mins, y, (int)M, (int)N, (int)K, kNibblePairMask, ws, gps);
 }
 
 template <int MR, int TPL, bool kF16 = false, bool kP32 = false>
