@@ -28,13 +28,14 @@ SOURCES = ["api.hip", "pack.hip", "gemv.hip", "rowmma.hip", "skinny.hip", "mid.h
 # The benchmark's measured roofs (a streaming read, an empty launch): a library of their own, so
 # that nothing in libw4a16 exists only to be timed.
 ROOF_SOURCE, ROOF_LIB = "roof.hip", PKG / "libw4a16_roof.so"
-# Per-file extra flags.  The GEMVs' first kernel arguments arrive in SGPRs at wave launch, so a
-# wave's first loads wait for no scalar fetch of the argument block (a code object still runs where
-# the dispatcher does not preload: it then starts at a short block that loads the same SGPRs).
-# Measured: 0.4-1.7% faster for 1..16 rows and the row-major GEMVs; the 17..64-row kernels ran
-# 1-4% slower with it and the GEMM alike, so they do without.
+# Per-file extra flags.  In the weight-streaming kernels the first kernel arguments arrive in SGPRs
+# at wave launch, so a wave's first loads wait for no scalar fetch of the argument block (a code
+# object still runs where the dispatcher does not preload: it then starts at a short block that
+# loads the same SGPRs).  Measured: 0.4-1.7% faster for 1..16 rows and the row-major GEMVs, 0.5-2.6%
+# for the row-major matrix-core kernel, 2% for W4A8's quantize-and-product step; the 17..64-row
+# kernels ran 1-4% slower with it and the GEMM alike, so they do without.
 PRELOAD = ["-mllvm", "-amdgpu-kernarg-preload-count=16"]
-FILE_FLAGS: dict = {"skinny.hip": PRELOAD, "gemv.hip": PRELOAD}
+FILE_FLAGS: dict = {"skinny.hip": PRELOAD, "gemv.hip": PRELOAD, "rowmma.hip": PRELOAD, "w4a8.hip": PRELOAD}
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
